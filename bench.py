@@ -1,0 +1,271 @@
+"""Benchmark: forward convolution TFLOPS and roofline fraction on one MI355X.
+
+A step is one conv2d_fwd call -- every step of the path (the lowering
+structure build, the MFMA main loop and its fused epilogue, and any split-K
+finish) -- over one batch of seeded synthetic input that is already resident
+in HBM.  Before each timed step the 256 MB last-level cache (MALL) is
+overwritten, outside the timed interval, so the input really comes from HBM.
+Each step is bracketed by HIP events on the stream the library launches on;
+ms_per_step is their mean.
+
+Headline: the 3x3 stride-1 pad-1 layer N=32, C_in=64, 56x56, C_out=128 in
+bf16, NCHW, algo auto -- the verification layer of "Unifying Convolutions and
+GEMM", section 5.  The JSON line also carries a per-layer table over every
+layer shape (TFLOPS, roofline fraction, workspace vs im2col bytes), the
+dominant kernel's roofline entry (its duration measured with HIP events on
+the main loop alone), and the fp64 oracle's throughput on this host's cores
+over a bounded sample (a baseline only).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers all|headline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "conv fwd TFLOPS & fraction of MFMA peak per layer; workspace bytes"
+PEAK = {"bf16": 2500.0, "fp32": 157.3}  # MI355X dense MFMA, TFLOP/s
+HBM_PEAK = 8000.0  # GB/s
+ESIZE = {"bf16": 2, "fp32": 4}
+
+
+def layer_geometry(L):
+    import convolution_lowering_amd as cl
+    Ho, Wo = cl.output_size(L.H, L.W, L.KH, L.KW, L.stride, L.pad, L.dilation)
+    return Ho, Wo
+
+
+def layer_flops(L, Ho, Wo):
+    return 2.0 * L.N * L.Co * Ho * Wo * L.C * L.KH * L.KW
+
+
+def algorithmic_bytes(L, Ho, Wo, dtype):
+    """Each tensor moved once: |x| + |w| + |bias| + |y|."""
+    e = ESIZE[dtype]
+    return e * (L.N * L.C * L.H * L.W + L.Co * L.C * L.KH * L.KW + L.Co + L.N * L.Co * Ho * Wo)
+
+
+def roofline(flops, nbytes, seconds, dtype):
+    intensity = flops / nbytes
+    ridge = PEAK[dtype] * 1e12 / (HBM_PEAK * 1e9)
+    if intensity >= ridge:
+        ach = flops / seconds / 1e12
+        return {"bound": "mfma", "achieved": ach, "peak": PEAK[dtype], "unit": "TFLOP/s", "frac": ach / PEAK[dtype]}
+    ach = nbytes / seconds / 1e9
+    return {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK, "unit": "GB/s", "frac": ach / HBM_PEAK}
+
+
+class Flusher:
+    """Overwrites 512 MB so the 256 MB MALL holds none of the next step's inputs."""
+
+    def __init__(self):
+        import torch
+        self.buf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        self.i = 0
+
+    def __call__(self):
+        self.i = (self.i + 1) & 0xFF
+        self.buf.fill_(self.i)
+
+
+def time_steps(fn, steps, warmup, flush):
+    """Mean milliseconds of fn() over `steps` calls, each between HIP events on
+    torch's current stream (the stream the library launches on)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        if flush:
+            flush()
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    times = [a.elapsed_time(b) for a, b in ev]
+    return sum(times) / len(times), min(times)
+
+
+def bench_layer(L, dtype, layout, algo, steps, warmup, flush):
+    import torch
+    import convolution_lowering_amd as cl
+    from convolution_lowering_amd.workloads import make_inputs
+    x, w, b = make_inputs(L, dtype, layout)
+    x, w, b = x.cuda(), w.cuda(), b.cuda()
+    Ho, Wo = layer_geometry(L)
+    shape = (L.N, L.Co, Ho, Wo) if layout == "NCHW" else (L.N, Ho, Wo, L.Co)
+    y = torch.empty(shape, dtype=x.dtype, device="cuda")
+    ws_bytes = cl.workspace_size(L.N, L.C, L.H, L.W, L.Co, L.KH, L.KW, L.stride, L.pad, L.dilation, layout, dtype, algo)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+
+    def step():
+        cl.conv2d_fwd(x, w, b, L.stride, L.pad, L.dilation, layout, algo, out=y, workspace=ws[:ws_bytes])
+
+    ms, ms_min = time_steps(step, steps, warmup, flush)
+    flops = layer_flops(L, Ho, Wo)
+    nbytes = algorithmic_bytes(L, Ho, Wo, dtype)
+    im2col = cl.im2col_bytes(L.N, L.C, L.H, L.W, L.KH, L.KW, L.stride, L.pad, L.dilation, dtype)
+    row = {"layer": L.name, "shape": L.note, "dtype": dtype, "layout": layout, "algo": algo,
+           "ms": ms, "ms_min": ms_min, "tflops": flops / ms / 1e9, "gbps": nbytes / ms / 1e6,
+           "workspace_bytes": ws_bytes, "im2col_bytes": im2col,
+           "workspace_over_im2col": ws_bytes / im2col}
+    row["roofline"] = roofline(flops, nbytes, ms / 1e3, dtype)
+    del x, w, b, y, ws
+    return row
+
+
+def main_loop_time(L, dtype, layout, steps, warmup, flush):
+    """HIP-event time of the INDIRECT main loop alone (the dominant kernel),
+    reading a prebuilt indirection buffer."""
+    import torch
+    import convolution_lowering_amd as cl
+    from convolution_lowering_amd.workloads import make_inputs
+    x, w, b = make_inputs(L, dtype, layout)
+    x, w, b = x.cuda(), w.cuda(), b.cuda()
+    Ho, Wo = layer_geometry(L)
+    shape = (L.N, L.Co, Ho, Wo) if layout == "NCHW" else (L.N, Ho, Wo, L.Co)
+    y = torch.empty(shape, dtype=x.dtype, device="cuda")
+    ib = cl.build_indirection(L.C, L.H, L.W, L.KH, L.KW, L.stride, L.pad, L.dilation, layout)
+    ws_bytes = cl.workspace_size(L.N, L.C, L.H, L.W, L.Co, L.KH, L.KW, L.stride, L.pad, L.dilation, layout, dtype,
+                                 "indirect")
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+
+    def step():
+        cl.conv2d_fwd_indirect_prebuilt(x, w, b, ib, L.stride, L.pad, L.dilation, layout, out=y,
+                                        workspace=ws[:ws_bytes])
+
+    return time_steps(step, steps, warmup, flush)
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "convolution_lowering_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it
+    was taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    ent = rec.get(workload)
+    if not ent or ent.get("source_digest") != kernel_source_digest():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(L, dtype, layout, budget_s=12.0):
+    """The fp64 oracle (untuned) on a bounded sample of the headline layer:
+    whole images, as many as fit in about budget_s seconds (at least one)."""
+    import oracle
+    from convolution_lowering_amd.workloads import make_inputs
+    Ho, Wo = layer_geometry(L)
+    lay = oracle.NCHW if layout == "NCHW" else oracle.NHWC
+    x, w, b = make_inputs(L, dtype, layout, N=1)
+    t0 = time.perf_counter()
+    oracle.conv2d(x, w, b, L.stride, L.pad, L.dilation, lay, want_norm=False)
+    t1 = time.perf_counter() - t0
+    n = int(max(1, min(L.N, budget_s // max(t1, 1e-3))))
+    x, w, b = make_inputs(L, dtype, layout, N=n)
+    t0 = time.perf_counter()
+    oracle.conv2d(x, w, b, L.stride, L.pad, L.dilation, lay, want_norm=False)
+    t = time.perf_counter() - t0
+    flops = 2.0 * n * L.Co * Ho * Wo * L.C * L.KH * L.KW
+    return {"value": flops / t / 1e12, "unit": "TFLOPS", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{n} of {L.N} images of the headline layer, full output, fp64, {t:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", choices=["all", "headline"], default="all")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path (each GPU would run its own "
+              "share of the batch independently; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import convolution_lowering_amd as cl
+    from convolution_lowering_amd.workloads import LAYERS
+    cl.lib()
+    torch.cuda.init()
+    flush = Flusher()
+
+    H = LAYERS["C2"]
+    head_dtype, head_layout, head_algo = "bf16", "NCHW", "auto"
+    head = bench_layer(H, head_dtype, head_layout, head_algo, args.steps, args.warmup, flush)
+    print(f"# headline {H.name} {head_dtype} {head_layout} {head_algo}: {head['ms']:.4f} ms "
+          f"{head['tflops']:.1f} TFLOPS", file=sys.stderr, flush=True)
+
+    # Roofline entry of the dominant kernel: the main loop alone.
+    ml_ms, ml_min = main_loop_time(H, head_dtype, head_layout, args.steps, args.warmup, flush)
+    Ho, Wo = layer_geometry(H)
+    flops = layer_flops(H, Ho, Wo)
+    nbytes = algorithmic_bytes(H, Ho, Wo, head_dtype)
+    rl = roofline(flops, nbytes, ml_ms / 1e3, head_dtype)
+    rl["traffic"] = measured_traffic("igemm_kernel", "C2-bf16-NCHW-indirect")
+    rl["kernel"] = "igemm_kernel (implicit-GEMM main loop + fused epilogue, indirect feed)"
+    rl["ms"] = ml_ms
+    rl["per_launch_flops"] = flops
+    rl["per_launch_algorithmic_bytes"] = nbytes
+
+    rows = []
+    if args.layers == "all":
+        for name, L in LAYERS.items():
+            for dtype in L.dtypes:
+                for layout in ("NCHW", "NHWC"):
+                    algos = ["auto"]
+                    if name == "C2":
+                        algos = ["auto", "indirect", "im2win"]
+                    for algo in algos:
+                        try:
+                            r = bench_layer(L, dtype, layout, algo, max(3, args.steps // 4), 2, flush)
+                        except Exception as e:  # report, keep going
+                            r = {"layer": name, "dtype": dtype, "layout": layout, "algo": algo, "error": str(e)}
+                        rows.append(r)
+                        print(f"# {name} {dtype} {layout} {algo}: "
+                              f"{r.get('ms', float('nan')):.4f} ms {r.get('tflops', float('nan')):.1f} TFLOPS "
+                              f"{r.get('roofline', {}).get('bound', '?')} "
+                              f"frac {r.get('roofline', {}).get('frac', float('nan')):.3f}", file=sys.stderr, flush=True)
+                        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(H, head_dtype, head_layout)
+
+    line = {
+        "metric": METRIC, "value": head["tflops"], "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": head["ms"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": head_dtype,
+        "data": "synthetic (seeded torch CPU generator; x, w, bias ~ N(0,1)), MALL flushed before each step",
+        "config": {"workload": "conv2d fwd 3x3 s1 p1 N=32 C_in=64 56x56 C_out=128 (C2)", "layout": head_layout,
+                   "algo": head_algo, "global_batch": H.N,
+                   "workspace_bytes": head["workspace_bytes"], "im2col_bytes": head["im2col_bytes"]},
+        "roofline": rl,
+        "cpu_baseline": cpu,
+        "layers": rows,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,1 +1,223 @@
-"""MI355X-native batched 2-D convolution forward pass without im2col (binding lands next)."""
+"""MI355X-native forward convolution lowered onto an MFMA implicit GEMM.
+
+Thin binding over the C ABI of ``include/convlower.h`` (libconvlower.so,
+built in-tree by ``convolution_lowering_amd.build``).  Python here only
+marshals arguments: it allocates outputs and workspaces with torch, passes
+raw device pointers and torch's current HIP stream, and turns status codes
+into exceptions.  Every step of the computation runs in the HIP library; if
+that library is missing this module raises instead of computing anything
+another way.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libconvlower.so")
+
+LAYOUTS = {"NCHW": 0, "NHWC": 1}
+ALGOS = {"auto": 0, "indirect": 1, "im2win": 2, "gemm": 3}
+DTYPE_CODES = {"fp32": 0, "bf16": 1}
+STATUS = {0: "CONV_OK", 1: "CONV_ERR_INVALID_ARG", 2: "CONV_ERR_UNSUPPORTED", 3: "CONV_ERR_WORKSPACE",
+          4: "CONV_ERR_HIP"}
+
+# Every symbol include/convlower.h declares.
+EXPORTS = ("conv_status_string", "conv2d_output_size", "conv2d_fwd_workspace_size", "conv2d_im2col_bytes",
+           "conv2d_fwd", "conv2d_fwd_indirect_prebuilt", "conv2d_build_indirection", "conv2d_im2win_transform")
+
+
+class ConvLowerError(RuntimeError):
+    def __init__(self, fn, code):
+        super().__init__(f"{fn} returned {STATUS.get(code, code)}")
+        self.code = code
+
+
+_lib = None
+
+
+def lib():
+    """The loaded HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m convolution_lowering_amd.build` "
+                          "(or __graft_entry__.build()); there is no fallback path")
+    L = ctypes.CDLL(LIB_PATH)
+    c_int, c_size, vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
+    L.conv_status_string.argtypes = [c_int]
+    L.conv_status_string.restype = ctypes.c_char_p
+    L.conv2d_output_size.argtypes = [c_int] * 7 + [ctypes.POINTER(c_int)] * 2
+    L.conv2d_output_size.restype = c_int
+    L.conv2d_fwd_workspace_size.argtypes = [c_int] * 13 + [ctypes.POINTER(c_size)]
+    L.conv2d_fwd_workspace_size.restype = c_int
+    L.conv2d_im2col_bytes.argtypes = [c_int] * 10 + [ctypes.POINTER(c_size)]
+    L.conv2d_im2col_bytes.restype = c_int
+    L.conv2d_fwd.argtypes = [vp] * 4 + [c_int] * 12 + [vp, vp, c_size, c_int]
+    L.conv2d_fwd.restype = c_int
+    L.conv2d_fwd_indirect_prebuilt.argtypes = [vp] * 5 + [c_int] * 12 + [vp, vp, c_size]
+    L.conv2d_fwd_indirect_prebuilt.restype = c_int
+    L.conv2d_build_indirection.argtypes = [vp] + [c_int] * 9 + [vp]
+    L.conv2d_build_indirection.restype = c_int
+    L.conv2d_im2win_transform.argtypes = [vp, vp] + [c_int] * 11 + [vp]
+    L.conv2d_im2win_transform.restype = c_int
+    _lib = L
+    return L
+
+
+def _check(fn, code):
+    if code != 0:
+        raise ConvLowerError(fn, code)
+
+
+def _dtype_code(dtype):
+    import torch
+    if dtype == torch.float32:
+        return 0
+    if dtype == torch.bfloat16:
+        return 1
+    raise TypeError(f"unsupported dtype {dtype}")
+
+
+def _stream_handle(stream, device):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def output_size(H, W, KH, KW, stride=1, pad=0, dilation=1):
+    ho, wo = ctypes.c_int(), ctypes.c_int()
+    _check("conv2d_output_size",
+           lib().conv2d_output_size(H, W, KH, KW, stride, pad, dilation, ctypes.byref(ho), ctypes.byref(wo)))
+    return ho.value, wo.value
+
+
+def workspace_size(N, C, H, W, Co, KH, KW, stride=1, pad=0, dilation=1, layout="NCHW", dtype="bf16",
+                   algo="auto"):
+    out = ctypes.c_size_t()
+    _check("conv2d_fwd_workspace_size",
+           lib().conv2d_fwd_workspace_size(N, C, H, W, Co, KH, KW, stride, pad, dilation, LAYOUTS[layout],
+                                           DTYPE_CODES[dtype], ALGOS[algo], ctypes.byref(out)))
+    return out.value
+
+
+def im2col_bytes(N, C, H, W, KH, KW, stride=1, pad=0, dilation=1, dtype="bf16"):
+    out = ctypes.c_size_t()
+    _check("conv2d_im2col_bytes",
+           lib().conv2d_im2col_bytes(N, C, H, W, KH, KW, stride, pad, dilation, DTYPE_CODES[dtype],
+                                     ctypes.byref(out)))
+    return out.value
+
+
+def _dims(x, w, layout):
+    if layout == "NCHW":
+        N, C, H, W = x.shape
+        Co, C2, KH, KW = w.shape
+    elif layout == "NHWC":
+        N, H, W, C = x.shape
+        Co, KH, KW, C2 = w.shape
+    else:
+        raise ValueError(layout)
+    if C2 != C:
+        raise ValueError("x and w disagree on C_in")
+    return N, C, H, W, Co, KH, KW
+
+
+def _check_tensor(t, name, dtype, device):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _prepare(x, w, bias, stride, pad, dilation, layout, algo, out, workspace):
+    import torch
+    N, C, H, W, Co, KH, KW = _dims(x, w, layout)
+    dev = x.device
+    _check_tensor(x, "x", x.dtype, dev)
+    _check_tensor(w, "w", x.dtype, dev)
+    if bias is not None:
+        _check_tensor(bias, "bias", x.dtype, dev)
+        if bias.numel() != Co:
+            raise ValueError("bias must hold C_out values")
+    dcode = _dtype_code(x.dtype)
+    Ho, Wo = output_size(H, W, KH, KW, stride, pad, dilation)
+    shape = (N, Co, Ho, Wo) if layout == "NCHW" else (N, Ho, Wo, Co)
+    if out is None:
+        out = torch.empty(shape, dtype=x.dtype, device=dev)
+    else:
+        _check_tensor(out, "out", x.dtype, dev)
+        if tuple(out.shape) != shape:
+            raise ValueError(f"out has shape {tuple(out.shape)}, expected {shape}")
+    need = workspace_size(N, C, H, W, Co, KH, KW, stride, pad, dilation, layout,
+                          "bf16" if dcode else "fp32", algo)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    dims = (N, C, H, W, Co, KH, KW, stride, pad, dilation, LAYOUTS[layout], dcode)
+    return out, dims, ws_ptr, ws_bytes, workspace
+
+
+def conv2d_fwd(x, w, bias=None, stride=1, pad=0, dilation=1, layout="NCHW", algo="auto", out=None,
+               workspace=None, stream=None):
+    """y = conv(x, w) + bias on the GPU through conv2d_fwd; returns y.
+
+    x, w, bias, out: contiguous device tensors of one dtype (float32 or
+    bfloat16) in `layout`.  workspace: optional uint8 device tensor of at
+    least workspace_size(...) bytes (allocated here when None)."""
+    out, dims, ws_ptr, ws_bytes, _ = _prepare(x, w, bias, stride, pad, dilation, layout, algo, out, workspace)
+    code = lib().conv2d_fwd(x.data_ptr(), w.data_ptr(), bias.data_ptr() if bias is not None else None,
+                            out.data_ptr(), *dims, _stream_handle(stream, x.device), ws_ptr, ws_bytes, ALGOS[algo])
+    _check("conv2d_fwd", code)
+    return out
+
+
+def conv2d_fwd_indirect_prebuilt(x, w, bias, indirection, stride=1, pad=0, dilation=1, layout="NCHW", out=None,
+                                 workspace=None, stream=None):
+    """The INDIRECT main loop alone, reading through a buffer from build_indirection."""
+    import torch
+    if indirection.dtype != torch.int32 or not indirection.is_cuda or not indirection.is_contiguous():
+        raise ValueError("indirection must be a contiguous int32 device tensor")
+    out, dims, ws_ptr, ws_bytes, _ = _prepare(x, w, bias, stride, pad, dilation, layout, "indirect", out,
+                                              workspace)
+    code = lib().conv2d_fwd_indirect_prebuilt(x.data_ptr(), w.data_ptr(),
+                                              bias.data_ptr() if bias is not None else None, out.data_ptr(),
+                                              indirection.data_ptr(), *dims, _stream_handle(stream, x.device),
+                                              ws_ptr, ws_bytes)
+    _check("conv2d_fwd_indirect_prebuilt", code)
+    return out
+
+
+def build_indirection(C, H, W, KH, KW, stride=1, pad=0, dilation=1, layout="NCHW", device="cuda", stream=None):
+    """The indirection buffer as an int32 [Ho*Wo, KH*KW] device tensor."""
+    import torch
+    Ho, Wo = output_size(H, W, KH, KW, stride, pad, dilation)
+    buf = torch.empty((Ho * Wo, KH * KW), dtype=torch.int32, device=device)
+    _check("conv2d_build_indirection",
+           lib().conv2d_build_indirection(buf.data_ptr(), C, H, W, KH, KW, stride, pad, dilation,
+                                          LAYOUTS[layout], _stream_handle(stream, buf.device)))
+    return buf
+
+
+def im2win_transform(x, KH, KW, stride=1, pad=0, dilation=1, layout="NCHW", stream=None):
+    """The window-ordered tensor [N][Ho][Wwin][KH][C] as a device tensor."""
+    import torch
+    if layout == "NCHW":
+        N, C, H, W = x.shape
+    else:
+        N, H, W, C = x.shape
+    _check_tensor(x, "x", x.dtype, x.device)
+    Ho, Wo = output_size(H, W, KH, KW, stride, pad, dilation)
+    Wwin = (Wo - 1) * stride + (KW - 1) * dilation + 1
+    out = torch.empty((N, Ho, Wwin, KH, C), dtype=x.dtype, device=x.device)
+    _check("conv2d_im2win_transform",
+           lib().conv2d_im2win_transform(x.data_ptr(), out.data_ptr(), N, C, H, W, KH, KW, stride, pad,
+                                         dilation, LAYOUTS[layout], _dtype_code(x.dtype),
+                                         _stream_handle(stream, x.device)))
+    return out

@@ -1,0 +1,338 @@
+// The C ABI of include/convlower.h: argument checks, the lowering plan
+// (feed, tile, split-K, workspace layout) and the launch sequence.
+//
+// Every decision here is a fixed function of the call's sizes, so the
+// workspace query and the launch agree without keeping any state.
+#include <string.h>
+
+#include "conv_internal.h"
+
+namespace convlower {
+namespace {
+
+constexpr long long kLimit = (1LL << 31) - 1;  // element counts the kernels index with 32-bit parts
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Plan {
+    Geom g;
+    bool bf16, nhwc;
+    int feed;
+    bool out_nchw;
+    int tile, splits, kps;
+    bool need_ibuf, need_win, need_wpack;
+    size_t off_ibuf, off_win, off_wpack, off_part, total;
+    size_t esize;
+};
+
+int out_extent(int in, int k, int s, int p, int d) {
+    long long span = (long long)in + 2LL * p - (long long)d * (k - 1) - 1;
+    if (span < 0) return 0;
+    return (int)(span / s) + 1;
+}
+
+conv_status_t make_geom(int N, int C, int H, int W, int Co, int KH, int KW, int s, int p, int d, Geom *g) {
+    if (N <= 0 || C <= 0 || H <= 0 || W <= 0 || Co <= 0 || KH <= 0 || KW <= 0 || s <= 0 || d <= 0 || p < 0)
+        return CONV_ERR_INVALID_ARG;
+    int Ho = out_extent(H, KH, s, p, d), Wo = out_extent(W, KW, s, p, d);
+    if (Ho <= 0 || Wo <= 0) return CONV_ERR_INVALID_ARG;
+    g->N = N; g->C = C; g->H = H; g->W = W; g->Co = Co; g->KH = KH; g->KW = KW;
+    g->s = s; g->p = p; g->d = d; g->Ho = Ho; g->Wo = Wo;
+    g->P = Ho * Wo;  // checked below against the limit via M
+    g->T = KH * KW;
+    g->Wwin = (Wo - 1) * s + (KW - 1) * d + 1;
+    g->M = (long long)N * Ho * Wo;
+    g->K = (long long)C * KH * KW;
+    return CONV_OK;
+}
+
+// Element counts of every tensor must stay inside 32-bit signed range (the
+// kernels form 64-bit addresses but index within one image in 32 bits).
+bool sizes_supported(const Geom &g) {
+    long long Hp = (long long)g.H, Wp = (long long)g.W;
+    long long x = (long long)g.N * g.C * Hp * Wp;
+    long long y = g.M * g.Co;
+    long long w = g.K * g.Co;
+    long long win = (long long)g.N * g.Ho * g.Wwin * g.KH * g.C;
+    long long ibuf = (long long)g.P * g.T;
+    return (long long)g.Ho * g.Wo <= kLimit && g.K <= kLimit && g.M <= kLimit && x <= kLimit && y <= kLimit &&
+           w <= kLimit && win <= kLimit && ibuf <= kLimit;
+}
+
+conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int s, int p, int d,
+                        conv_layout_t layout, conv_dtype_t dtype, conv_algo_t algo, Plan *pl) {
+    if (layout != CONV_LAYOUT_NCHW && layout != CONV_LAYOUT_NHWC) return CONV_ERR_INVALID_ARG;
+    if (dtype != CONV_DTYPE_FP32 && dtype != CONV_DTYPE_BF16) return CONV_ERR_INVALID_ARG;
+    if (algo < CONV_ALGO_AUTO || algo > CONV_ALGO_GEMM) return CONV_ERR_INVALID_ARG;
+    memset(pl, 0, sizeof(*pl));
+    conv_status_t st = make_geom(N, C, H, W, Co, KH, KW, s, p, d, &pl->g);
+    if (st != CONV_OK) return st;
+    const Geom &g = pl->g;
+    if (!sizes_supported(g)) return CONV_ERR_UNSUPPORTED;
+    pl->bf16 = dtype == CONV_DTYPE_BF16;
+    pl->nhwc = layout == CONV_LAYOUT_NHWC;
+    pl->esize = pl->bf16 ? 2 : 4;
+
+    // A 1x1 stride-1 unpadded convolution is a GEMM call (The Indirect
+    // Convolution Algorithm, abstract); a kernel that covers the whole
+    // unpadded input is a dense layer ("Unifying Convolutions and GEMM",
+    // section 4).  Both are fed from the input as it lies in memory.
+    const bool whole = KH == H && KW == W && p == 0;
+    const bool one = KH == 1 && KW == 1 && s == 1 && p == 0;
+    if (algo == CONV_ALGO_AUTO) algo = (whole || one) ? CONV_ALGO_GEMM : CONV_ALGO_INDIRECT;
+    switch (algo) {
+        case CONV_ALGO_GEMM:
+            if (whole)
+                pl->feed = FEED_ROWMAJOR;  // Ho = Wo = 1: both layouts store y as [N][Co]
+            else if (one)
+                pl->feed = pl->nhwc ? FEED_ROWMAJOR : FEED_NCHW_1X1;
+            else
+                return CONV_ERR_UNSUPPORTED;
+            break;
+        case CONV_ALGO_INDIRECT:
+            pl->feed = pl->nhwc ? FEED_IND_NHWC : FEED_IND_NCHW;
+            pl->need_ibuf = true;
+            break;
+        case CONV_ALGO_IM2WIN:
+            pl->feed = FEED_WIN;
+            pl->need_win = true;
+            pl->need_wpack = !pl->nhwc && g.T > 1;  // OIHW regrouped to (kh, kw, ci) order
+            break;
+        default:
+            return CONV_ERR_INVALID_ARG;
+    }
+    pl->out_nchw = !pl->nhwc && pl->feed != FEED_ROWMAJOR;
+
+    // Tile shape and split-K.
+    int BM, BN;
+    if (g.M <= 64) {
+        pl->tile = TILE_32x64; BM = 32; BN = 64;
+    } else if (g.Co <= 64) {
+        pl->tile = TILE_128x64; BM = 128; BN = 64;
+    } else {
+        pl->tile = TILE_128x128; BM = 128; BN = 128;
+    }
+    const int BK = 32;
+    long long blocks = ((g.M + BM - 1) / BM) * ((g.Co + BN - 1) / BN);
+    long long ktiles = (g.K + BK - 1) / BK;
+    int splits = 1;
+    if (blocks < 256 && ktiles >= 16) {
+        // Enough splits to give every compute unit work, each split at least
+        // 4 K tiles, and the fp32 partials kept below the im2col footprint.
+        long long want = (512 + blocks - 1) / blocks;
+        long long by_depth = ktiles / 4;
+        long long im2col_bytes = g.M * g.K * (long long)pl->esize;
+        long long per_split = g.M * g.Co * 4LL;
+        long long by_space = (im2col_bytes - 1) / per_split;
+        long long sp = want;
+        if (sp > by_depth) sp = by_depth;
+        if (sp > by_space) sp = by_space;
+        if (sp > 1) splits = (int)sp;
+    }
+    long long kps = (g.K + splits - 1) / splits;
+    kps = (kps + BK - 1) / BK * BK;
+    splits = (int)((g.K + kps - 1) / kps);
+    pl->splits = splits;
+    pl->kps = (int)kps;
+
+    size_t off = 0;
+    if (pl->need_ibuf) {
+        pl->off_ibuf = off;
+        off = align_up(off + (size_t)g.P * g.T * sizeof(int32_t));
+    }
+    if (pl->need_win) {
+        pl->off_win = off;
+        off = align_up(off + (size_t)g.N * g.Ho * g.Wwin * g.KH * g.C * pl->esize);
+    }
+    if (pl->need_wpack) {
+        pl->off_wpack = off;
+        off = align_up(off + (size_t)g.Co * g.K * pl->esize);
+    }
+    if (splits > 1) {
+        pl->off_part = off;
+        off = align_up(off + (size_t)splits * g.M * g.Co * sizeof(float));
+    }
+    pl->total = off;
+    return CONV_OK;
+}
+
+}  // namespace
+}  // namespace convlower
+
+using namespace convlower;
+
+extern "C" {
+
+const char *conv_status_string(conv_status_t s) {
+    switch (s) {
+        case CONV_OK: return "CONV_OK";
+        case CONV_ERR_INVALID_ARG: return "CONV_ERR_INVALID_ARG";
+        case CONV_ERR_UNSUPPORTED: return "CONV_ERR_UNSUPPORTED";
+        case CONV_ERR_WORKSPACE: return "CONV_ERR_WORKSPACE";
+        case CONV_ERR_HIP: return "CONV_ERR_HIP";
+        default: return "CONV_ERR_UNKNOWN";
+    }
+}
+
+conv_status_t conv2d_output_size(int H, int W, int KH, int KW, int stride, int pad, int dilation, int *ho_out,
+                                 int *wo_out) {
+    Geom g;
+    conv_status_t st = make_geom(1, 1, H, W, 1, KH, KW, stride, pad, dilation, &g);
+    if (st != CONV_OK) return st;
+    if (ho_out) *ho_out = g.Ho;
+    if (wo_out) *wo_out = g.Wo;
+    return CONV_OK;
+}
+
+conv_status_t conv2d_fwd_workspace_size(int N, int C_in, int H, int W, int C_out, int KH, int KW, int stride,
+                                        int pad, int dilation, conv_layout_t layout, conv_dtype_t dtype,
+                                        conv_algo_t algo, size_t *bytes_out) {
+    if (!bytes_out) return CONV_ERR_INVALID_ARG;
+    Plan pl;
+    conv_status_t st = make_plan(N, C_in, H, W, C_out, KH, KW, stride, pad, dilation, layout, dtype, algo, &pl);
+    if (st != CONV_OK) return st;
+    *bytes_out = pl.total;
+    return CONV_OK;
+}
+
+conv_status_t conv2d_im2col_bytes(int N, int C_in, int H, int W, int KH, int KW, int stride, int pad,
+                                  int dilation, conv_dtype_t dtype, size_t *bytes_out) {
+    if (!bytes_out) return CONV_ERR_INVALID_ARG;
+    if (dtype != CONV_DTYPE_FP32 && dtype != CONV_DTYPE_BF16) return CONV_ERR_INVALID_ARG;
+    Geom g;
+    conv_status_t st = make_geom(N, C_in, H, W, 1, KH, KW, stride, pad, dilation, &g);
+    if (st != CONV_OK) return st;
+    *bytes_out = (size_t)g.M * (size_t)g.K * (dtype == CONV_DTYPE_BF16 ? 2 : 4);
+    return CONV_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// The launch sequence of one call.  `prebuilt` (may be null) is an
+// indirection buffer the caller built before; then step (b) is skipped.
+conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias, void *y, const int32_t *prebuilt,
+                  conv_stream_t stream, void *workspace, size_t workspace_bytes) {
+    if (!x || !w || !y) return CONV_ERR_INVALID_ARG;
+    const size_t es = pl.esize;
+    if ((uintptr_t)x % es || (uintptr_t)w % es || (uintptr_t)y % es || (bias && (uintptr_t)bias % es))
+        return CONV_ERR_INVALID_ARG;
+    if (pl.total > 0 && (!workspace || workspace_bytes < pl.total)) return CONV_ERR_WORKSPACE;
+    if (pl.total > 0 && (uintptr_t)workspace % 16) return CONV_ERR_INVALID_ARG;
+
+    hipStream_t s = (hipStream_t)stream;
+    const Geom &g = pl.g;
+    char *ws = (char *)workspace;
+    const int VEC = pl.bf16 ? 8 : 4;
+    auto al16 = [](const void *ptr) { return (uintptr_t)ptr % 16 == 0; };
+
+    GemmArgs a;
+    memset(&a, 0, sizeof(a));
+    a.g = g;
+    a.bias = bias;
+    a.y = y;
+    a.k_per_split = pl.kps;
+    a.b = w;
+    a.a_src = x;
+
+    if (pl.need_ibuf) {
+        if (prebuilt) {
+            a.ibuf = prebuilt;
+        } else {
+            int32_t *ib = (int32_t *)(ws + pl.off_ibuf);
+            if (launch_build_indirection(ib, g, pl.nhwc, s) != hipSuccess) return CONV_ERR_HIP;
+            a.ibuf = ib;
+        }
+    }
+    if (pl.need_win) {
+        void *xw = ws + pl.off_win;
+        if (launch_im2win(x, xw, g, pl.nhwc, pl.bf16, s) != hipSuccess) return CONV_ERR_HIP;
+        a.a_src = xw;
+    }
+    if (pl.need_wpack) {
+        void *wp = ws + pl.off_wpack;
+        if (launch_pack_weights_ohwi(w, wp, g, pl.bf16, s) != hipSuccess) return CONV_ERR_HIP;
+        a.b = wp;
+    }
+    if (pl.splits > 1) a.part = (float *)(ws + pl.off_part);
+
+    bool a_vec;
+    switch (pl.feed) {
+        case FEED_ROWMAJOR: a_vec = g.K % VEC == 0 && al16(a.a_src); break;
+        case FEED_IND_NHWC:
+        case FEED_WIN: a_vec = g.C % VEC == 0 && al16(a.a_src); break;
+        default: a_vec = false;
+    }
+    bool b_vec = g.K % VEC == 0 && al16(a.b);
+    if (a_vec && !b_vec) a_vec = false;
+
+    hipError_t e = pl.bf16 ? launch_igemm_bf16(a, pl.feed, pl.out_nchw, a_vec, b_vec, pl.tile, pl.splits, s)
+                           : launch_igemm_f32(a, pl.feed, pl.out_nchw, a_vec, b_vec, pl.tile, pl.splits, s);
+    if (e != hipSuccess) return CONV_ERR_HIP;
+    if (pl.splits > 1) {
+        if (launch_splitk_reduce(a.part, bias, y, g, pl.splits, pl.out_nchw, pl.bf16, s) != hipSuccess)
+            return CONV_ERR_HIP;
+    }
+    return CONV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+conv_status_t conv2d_fwd(const void *x, const void *w, const void *bias, void *y, int N, int C_in, int H, int W,
+                         int C_out, int KH, int KW, int stride, int pad, int dilation, conv_layout_t layout,
+                         conv_dtype_t dtype, conv_stream_t stream, void *workspace, size_t workspace_bytes,
+                         conv_algo_t algo) {
+    Plan pl;
+    conv_status_t st = make_plan(N, C_in, H, W, C_out, KH, KW, stride, pad, dilation, layout, dtype, algo, &pl);
+    if (st != CONV_OK) return st;
+    return run(pl, x, w, bias, y, nullptr, stream, workspace, workspace_bytes);
+}
+
+conv_status_t conv2d_fwd_indirect_prebuilt(const void *x, const void *w, const void *bias, void *y,
+                                           const int32_t *indirection, int N, int C_in, int H, int W, int C_out,
+                                           int KH, int KW, int stride, int pad, int dilation, conv_layout_t layout,
+                                           conv_dtype_t dtype, conv_stream_t stream, void *workspace,
+                                           size_t workspace_bytes) {
+    Plan pl;
+    conv_status_t st =
+        make_plan(N, C_in, H, W, C_out, KH, KW, stride, pad, dilation, layout, dtype, CONV_ALGO_INDIRECT, &pl);
+    if (st != CONV_OK) return st;
+    if (!indirection || (uintptr_t)indirection % 4) return CONV_ERR_INVALID_ARG;
+    return run(pl, x, w, bias, y, indirection, stream, workspace, workspace_bytes);
+}
+
+conv_status_t conv2d_build_indirection(int32_t *buf, int C_in, int H, int W, int KH, int KW, int stride, int pad,
+                                       int dilation, conv_layout_t layout, conv_stream_t stream) {
+    if (layout != CONV_LAYOUT_NCHW && layout != CONV_LAYOUT_NHWC) return CONV_ERR_INVALID_ARG;
+    Geom g;
+    conv_status_t st = make_geom(1, C_in, H, W, 1, KH, KW, stride, pad, dilation, &g);
+    if (st != CONV_OK) return st;
+    if (!buf || (uintptr_t)buf % 4) return CONV_ERR_INVALID_ARG;
+    if (!sizes_supported(g)) return CONV_ERR_UNSUPPORTED;
+    if (launch_build_indirection(buf, g, layout == CONV_LAYOUT_NHWC, (hipStream_t)stream) != hipSuccess)
+        return CONV_ERR_HIP;
+    return CONV_OK;
+}
+
+conv_status_t conv2d_im2win_transform(const void *x, void *xwin, int N, int C_in, int H, int W, int KH, int KW,
+                                      int stride, int pad, int dilation, conv_layout_t layout, conv_dtype_t dtype,
+                                      conv_stream_t stream) {
+    if (layout != CONV_LAYOUT_NCHW && layout != CONV_LAYOUT_NHWC) return CONV_ERR_INVALID_ARG;
+    if (dtype != CONV_DTYPE_FP32 && dtype != CONV_DTYPE_BF16) return CONV_ERR_INVALID_ARG;
+    Geom g;
+    conv_status_t st = make_geom(N, C_in, H, W, 1, KH, KW, stride, pad, dilation, &g);
+    if (st != CONV_OK) return st;
+    size_t es = dtype == CONV_DTYPE_BF16 ? 2 : 4;
+    if (!x || !xwin || (uintptr_t)x % es || (uintptr_t)xwin % es) return CONV_ERR_INVALID_ARG;
+    if (!sizes_supported(g)) return CONV_ERR_UNSUPPORTED;
+    if (launch_im2win(x, xwin, g, layout == CONV_LAYOUT_NHWC, dtype == CONV_DTYPE_BF16, (hipStream_t)stream) !=
+        hipSuccess)
+        return CONV_ERR_HIP;
+    return CONV_OK;
+}
+
+}  // extern "C"

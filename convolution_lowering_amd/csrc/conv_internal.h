@@ -1,0 +1,54 @@
+// Internal declarations shared by the host planner and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "convlower.h"
+
+namespace convlower {
+
+// How the main loop reads row m, column k of the virtual X_col operand.
+// K is enumerated in the order given beside each feed; the weight operand
+// B[co][k] is read in the same order.
+enum Feed : int {
+    FEED_ROWMAJOR = 0,  // A = the input itself as an [M][K] matrix (1x1 NHWC, whole-input kernel); K natural
+    FEED_NCHW_1X1 = 1,  // A[m][ci] = x[n][ci][pixel] (1x1 stride-1 NCHW); K = ci
+    FEED_IND_NHWC = 2,  // through the indirection buffer, NHWC input; K = (kh, kw, ci)
+    FEED_IND_NCHW = 3,  // through the indirection buffer, NCHW input; K = (ci, kh, kw)
+    FEED_WIN = 4,       // out of the window-ordered tensor (either input layout); K = (kh, kw, ci)
+};
+
+struct Geom {
+    int N, C, H, W, Co, KH, KW, s, p, d;
+    int Ho, Wo, P, T, Wwin;  // P = Ho*Wo output pixels per image, T = KH*KW taps
+    long long M, K;          // GEMM rows (N*P) and depth (C*T)
+};
+
+struct GemmArgs {
+    const void *a_src;    // x, or the window-ordered tensor for FEED_WIN
+    const int32_t *ibuf;  // indirection buffer for FEED_IND_*
+    const void *b;        // weights as [Co][K] in the feed's K order
+    const void *bias;     // nullable
+    void *y;              // output (final layout)
+    float *part;          // split-K partial sums [splits][M][Co], or nullptr
+    Geom g;
+    int k_per_split;      // multiple of the K tile; == K rounded up when not split
+};
+
+// Tile shapes of the main loop (block = 256 threads = 4 wavefronts, 2x2).
+enum Tile : int { TILE_128x128 = 0, TILE_128x64 = 1, TILE_32x64 = 2, TILE_COUNT = 3 };
+
+hipError_t launch_igemm_bf16(const GemmArgs &a, int feed, bool out_nchw, bool a_vec, bool b_vec,
+                             int tile, int splits, hipStream_t st);
+hipError_t launch_igemm_f32(const GemmArgs &a, int feed, bool out_nchw, bool a_vec, bool b_vec,
+                            int tile, int splits, hipStream_t st);
+hipError_t launch_splitk_reduce(const float *part, const void *bias, void *y, const Geom &g,
+                                int splits, bool out_nchw, bool bf16, hipStream_t st);
+hipError_t launch_build_indirection(int32_t *buf, const Geom &g, bool nhwc, hipStream_t st);
+hipError_t launch_im2win(const void *x, void *xwin, const Geom &g, bool nhwc, bool bf16,
+                         hipStream_t st);
+hipError_t launch_pack_weights_ohwi(const void *w_oihw, void *w_ohwi, const Geom &g, bool bf16,
+                                    hipStream_t st);
+
+}  // namespace convlower

@@ -1,0 +1,220 @@
+// The lowering steps that run before (or after) the main loop:
+//   (b) the indirection-buffer builder (The Indirect Convolution Algorithm, abstract),
+//   (a) the im2win window reorder ("Im2win: An Efficient Convolution Paradigm on GPU", abstract),
+//   the OIHW -> OHWI weight regrouping the window feed needs for NCHW weights,
+//   and the ordered split-K finishing pass.
+#include "conv_internal.h"
+
+namespace convlower {
+
+static inline unsigned blocks_for(long long n, int per) { return (unsigned)((n + per - 1) / per); }
+
+// ---------------------------------------------------------------------------
+// (b) Indirection buffer: entry [p][t] = offset of input pixel (hi, wi) of
+// image 0, channel 0, or -1 where tap t of output pixel p is in the padding.
+// One thread per entry; consecutive threads write consecutive entries.
+__global__ __launch_bounds__(256) void build_indirection_kernel(int32_t *buf, Geom g, int nhwc) {
+    long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long long)g.P * g.T) return;
+    int p = (int)(idx / g.T), t = (int)(idx - (long long)p * g.T);
+    int ho = p / g.Wo, wo = p - ho * g.Wo;
+    int kh = t / g.KW, kw = t - kh * g.KW;
+    int hi = ho * g.s + kh * g.d - g.p;
+    int wi = wo * g.s + kw * g.d - g.p;
+    int32_t v = -1;
+    if (hi >= 0 && hi < g.H && wi >= 0 && wi < g.W) v = nhwc ? (hi * g.W + wi) * g.C : hi * g.W + wi;
+    buf[idx] = v;
+}
+
+hipError_t launch_build_indirection(int32_t *buf, const Geom &g, bool nhwc, hipStream_t st) {
+    long long n = (long long)g.P * g.T;
+    hipLaunchKernelGGL(build_indirection_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, st, buf, g,
+                       nhwc ? 1 : 0);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// (a) Window reorder: xwin[n][ho][c][kh][ci] = xpad(n, ci, ho*s + kh*d - p, c - p).
+//
+// NHWC input: every (n, ho, c, kh) destination row of C channels is one
+// contiguous source row (or zeros), so the copy runs in 16-byte chunks when C
+// allows, each thread one chunk, both sides coalesced.
+template <typename S, bool VEC>
+__global__ __launch_bounds__(256) void im2win_nhwc_kernel(const S *__restrict__ x, S *__restrict__ xw, Geom g,
+                                                          long long units) {
+    constexpr int V = VEC ? 16 / (int)sizeof(S) : 1;
+    long long u = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (u >= units) return;
+    const int cvec = g.C / V;  // chunks per channel row (exact when VEC)
+    long long row = u / cvec;
+    int ci = (int)(u - row * cvec) * V;
+    int kh = (int)(row % g.KH);
+    long long r2 = row / g.KH;
+    int c = (int)(r2 % g.Wwin);
+    long long r3 = r2 / g.Wwin;
+    int ho = (int)(r3 % g.Ho);
+    long long n = r3 / g.Ho;
+    int hi = ho * g.s + kh * g.d - g.p, wi = c - g.p;
+    bool inside = hi >= 0 && hi < g.H && wi >= 0 && wi < g.W;
+    long long src = ((n * g.H + hi) * g.W + wi) * g.C + ci;
+    long long dst = row * g.C + ci;
+    if constexpr (VEC) {
+        uint4 v = inside ? *(const uint4 *)(x + src) : make_uint4(0, 0, 0, 0);
+        *(uint4 *)(xw + dst) = v;
+    } else {
+        xw[dst] = inside ? x[src] : S(0);
+    }
+}
+
+// NCHW input: the source runs along columns c, the destination along
+// channels ci, so each block transposes a 64-channel x 64-column tile of one
+// (n, ho, kh) row through LDS: reads coalesced along c, writes along ci.
+template <typename S>
+__global__ __launch_bounds__(256) void im2win_nchw_kernel(const S *__restrict__ x, S *__restrict__ xw, Geom g) {
+    __shared__ S tile[64][65];
+    const int tiles_c = (g.Wwin + 63) / 64, tiles_ci = (g.C + 63) / 64;
+    long long b = blockIdx.x;
+    int tc = (int)(b % tiles_c);
+    b /= tiles_c;
+    int tci = (int)(b % tiles_ci);
+    long long slab = b / tiles_ci;  // (n, ho, kh)
+    int kh = (int)(slab % g.KH);
+    long long r = slab / g.KH;
+    int ho = (int)(r % g.Ho);
+    long long n = r / g.Ho;
+    int hi = ho * g.s + kh * g.d - g.p;
+    bool row_in = hi >= 0 && hi < g.H;
+    const int c0 = tc * 64, ci0 = tci * 64;
+    const int lx = threadIdx.x & 63, ly = threadIdx.x >> 6;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        int ci = ci0 + ly + 4 * j, c = c0 + lx;
+        int wi = c - g.p;
+        S v = S(0);
+        if (row_in && ci < g.C && c < g.Wwin && wi >= 0 && wi < g.W)
+            v = x[((n * g.C + ci) * g.H + hi) * (long long)g.W + wi];
+        tile[ly + 4 * j][lx] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        int c = c0 + ly + 4 * j, ci = ci0 + lx;
+        if (c < g.Wwin && ci < g.C)
+            xw[(((n * g.Ho + ho) * (long long)g.Wwin + c) * g.KH + kh) * g.C + ci] = tile[lx][ly + 4 * j];
+    }
+}
+
+template <typename S>
+static hipError_t im2win_typed(const void *x, void *xw, const Geom &g, bool nhwc, hipStream_t st) {
+    if (nhwc) {
+        constexpr int V = 16 / (int)sizeof(S);
+        bool vec = (g.C % V == 0) && ((uintptr_t)x % 16 == 0) && ((uintptr_t)xw % 16 == 0);
+        long long rows = (long long)g.N * g.Ho * g.Wwin * g.KH;
+        if (vec) {
+            long long units = rows * (g.C / V);
+            hipLaunchKernelGGL((im2win_nhwc_kernel<S, true>), dim3(blocks_for(units, 256)), dim3(256), 0, st,
+                               (const S *)x, (S *)xw, g, units);
+        } else {
+            long long units = rows * g.C;
+            hipLaunchKernelGGL((im2win_nhwc_kernel<S, false>), dim3(blocks_for(units, 256)), dim3(256), 0, st,
+                               (const S *)x, (S *)xw, g, units);
+        }
+    } else {
+        long long blocks = (long long)((g.Wwin + 63) / 64) * ((g.C + 63) / 64) * g.N * g.Ho * g.KH;
+        hipLaunchKernelGGL(im2win_nchw_kernel<S>, dim3((unsigned)blocks), dim3(256), 0, st, (const S *)x,
+                           (S *)xw, g);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_im2win(const void *x, void *xwin, const Geom &g, bool nhwc, bool bf16, hipStream_t st) {
+    return bf16 ? im2win_typed<uint16_t>(x, xwin, g, nhwc, st) : im2win_typed<float>(x, xwin, g, nhwc, st);
+}
+
+// ---------------------------------------------------------------------------
+// OIHW -> OHWI: w_ohwi[co][kh][kw][ci] = w_oihw[co][ci][kh][kw], so that the
+// window feed (K order kh, kw, ci) can read NCHW-layout weights in 16-byte
+// chunks.  One thread per destination element.
+template <typename S>
+__global__ __launch_bounds__(256) void pack_ohwi_kernel(const S *__restrict__ w, S *__restrict__ o, Geom g) {
+    long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+    long long total = (long long)g.Co * g.T * g.C;
+    if (e >= total) return;
+    int ci = (int)(e % g.C);
+    long long r = e / g.C;
+    int t = (int)(r % g.T);
+    long long co = r / g.T;
+    o[e] = w[(co * g.C + ci) * g.T + t];
+}
+
+hipError_t launch_pack_weights_ohwi(const void *w, void *o, const Geom &g, bool bf16, hipStream_t st) {
+    long long total = (long long)g.Co * g.T * g.C;
+    if (bf16)
+        hipLaunchKernelGGL(pack_ohwi_kernel<uint16_t>, dim3(blocks_for(total, 256)), dim3(256), 0, st,
+                           (const uint16_t *)w, (uint16_t *)o, g);
+    else
+        hipLaunchKernelGGL(pack_ohwi_kernel<float>, dim3(blocks_for(total, 256)), dim3(256), 0, st,
+                           (const float *)w, (float *)o, g);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Split-K finish: y = round(sum over splits, in split order, + bias).  The
+// fixed order keeps the result bit-for-bit repeatable.
+__device__ __forceinline__ uint16_t to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+template <typename S, bool OUT_NCHW>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ part, const S *bias,
+                                                            S *__restrict__ y, Geom g, int splits) {
+    long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+    long long total = g.M * g.Co;
+    if (e >= total) return;
+    long long m = e / g.Co;
+    int co = (int)(e - m * g.Co);
+    float acc = 0.f;
+    for (int z = 0; z < splits; ++z) acc += part[(long long)z * total + e];
+    if (bias) {
+        if constexpr (sizeof(S) == 2)
+            acc += __uint_as_float((uint32_t)((const uint16_t *)bias)[co] << 16);
+        else
+            acc += ((const float *)bias)[co];
+    }
+    long long yi = e;
+    if constexpr (OUT_NCHW) {
+        long long n = m / g.P;
+        yi = (n * g.Co + co) * g.P + (m - n * g.P);
+    }
+    if constexpr (sizeof(S) == 2)
+        ((uint16_t *)y)[yi] = to_bf16_rne(acc);
+    else
+        ((float *)y)[yi] = acc;
+}
+
+hipError_t launch_splitk_reduce(const float *part, const void *bias, void *y, const Geom &g, int splits,
+                                bool out_nchw, bool bf16, hipStream_t st) {
+    long long total = g.M * g.Co;
+    dim3 grid(blocks_for(total, 256));
+    if (bf16) {
+        if (out_nchw)
+            hipLaunchKernelGGL((splitk_reduce_kernel<uint16_t, true>), grid, dim3(256), 0, st, part,
+                               (const uint16_t *)bias, (uint16_t *)y, g, splits);
+        else
+            hipLaunchKernelGGL((splitk_reduce_kernel<uint16_t, false>), grid, dim3(256), 0, st, part,
+                               (const uint16_t *)bias, (uint16_t *)y, g, splits);
+    } else {
+        if (out_nchw)
+            hipLaunchKernelGGL((splitk_reduce_kernel<float, true>), grid, dim3(256), 0, st, part,
+                               (const float *)bias, (float *)y, g, splits);
+        else
+            hipLaunchKernelGGL((splitk_reduce_kernel<float, false>), grid, dim3(256), 0, st, part,
+                               (const float *)bias, (float *)y, g, splits);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace convlower

@@ -1,0 +1,167 @@
+/*
+ * convlower -- forward pass of a batched 2-D convolution on MI355X (gfx950),
+ * lowered onto a dense MFMA contraction without materialising im2col.
+ *
+ * What is computed (cross-correlation, zero padding, one stride / pad /
+ * dilation for both spatial axes):
+ *
+ *   y[n,co,ho,wo] = bias[co] + sum_{ci<C_in, kh<KH, kw<KW}
+ *                     x[n, ci, ho*stride + kh*dilation - pad, wo*stride + kw*dilation - pad] * w[co,ci,kh,kw]
+ *
+ * with x taken as zero outside the image.  This is the seven-loop definition
+ * of "Unifying Convolutions and GEMM" (section 1) with the padding and bias of
+ * its section 5 and the dilation named by The Indirect Convolution Algorithm
+ * (abstract).  Output extents: Ho = (H + 2*pad - dilation*(KH-1) - 1)/stride + 1,
+ * likewise Wo (section 5 of the same page gives the dilation-1 form).
+ *
+ * The contraction is  Y_col = X_col * W_row^T  ("Unifying Convolutions and
+ * GEMM", section 3) with M = N*Ho*Wo rows, C_out columns and K = C_in*KH*KW,
+ * but X_col is never built: the MFMA main loop gathers its rows either
+ * through an indirection buffer (The Indirect Convolution Algorithm,
+ * abstract) or out of a window-ordered copy of the input ("Im2win: An
+ * Efficient Convolution Paradigm on GPU", abstract).  1x1 stride-1 unpadded
+ * layers, and layers whose kernel covers the whole unpadded input, are
+ * already plain matrix products and are fed directly.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout (one value for x, w and y together; every tensor dense, contiguous):
+ *   CONV_LAYOUT_NCHW: x[N][C_in][H][W], w[C_out][C_in][KH][KW], y[N][C_out][Ho][Wo]
+ *   CONV_LAYOUT_NHWC: x[N][H][W][C_in], w[C_out][KH][KW][C_in], y[N][Ho][Wo][C_out]
+ * Dtype (one value for x, w, bias and y): fp32, or bf16 stored as raw 16-bit
+ *   words.  Products are accumulated in fp32; the bias is added in fp32; bf16
+ *   results are rounded once, to nearest-even, at the store.
+ * Pointers are device pointers (HIP), except where stated.  The caller owns
+ *   every buffer; the library allocates nothing, keeps no state between calls,
+ *   never synchronises the device, and enqueues all work on `stream` (NULL =
+ *   the default stream).  Buffers must not overlap.  Pointers need only the
+ *   alignment of their element type.
+ * Errors are returned as conv_status_t; no call launches anything when it
+ *   returns an error detected on the host.
+ */
+#ifndef CONVLOWER_H
+#define CONVLOWER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same underlying type as hipStream_t. */
+struct ihipStream_t;
+typedef struct ihipStream_t *conv_stream_t;
+
+typedef enum { CONV_LAYOUT_NCHW = 0, CONV_LAYOUT_NHWC = 1 } conv_layout_t;
+typedef enum { CONV_DTYPE_FP32 = 0, CONV_DTYPE_BF16 = 1 } conv_dtype_t;
+
+/* Which lowering feeds the contraction.
+ *   AUTO      1x1 stride-1 unpadded, or kernel == whole unpadded input: the
+ *             plain-GEMM (zero lowering workspace) feed; otherwise INDIRECT.
+ *   INDIRECT  indirection buffer of per-(output pixel, tap) input offsets.
+ *   IM2WIN    window-ordered copy of the input in the workspace.
+ *   GEMM      the input read as the GEMM operand as it lies in memory; only
+ *             valid for the two plain-GEMM shapes named under AUTO (The
+ *             Indirect Convolution Algorithm, abstract: a 1x1 convolution is
+ *             a GEMM call; "Unifying Convolutions and GEMM", section 4: a
+ *             whole-input kernel is a dense layer).  */
+typedef enum {
+    CONV_ALGO_AUTO = 0,
+    CONV_ALGO_INDIRECT = 1,
+    CONV_ALGO_IM2WIN = 2,
+    CONV_ALGO_GEMM = 3
+} conv_algo_t;
+
+typedef enum {
+    CONV_OK = 0,
+    CONV_ERR_INVALID_ARG = 1, /* bad size, enum, NULL pointer, or no output placement fits */
+    CONV_ERR_UNSUPPORTED = 2, /* valid request this library does not implement (e.g. GEMM on a windowed layer, sizes past 2^31 elements) */
+    CONV_ERR_WORKSPACE = 3,   /* workspace_bytes below the size the query returns, or NULL workspace when it is not 0 */
+    CONV_ERR_HIP = 4          /* a HIP launch reported an error */
+} conv_status_t;
+
+/* Human-readable name of a status code (static storage). */
+const char *conv_status_string(conv_status_t status);
+
+/* Output extents for the geometry (host only, no HIP call).  Returns
+ * CONV_ERR_INVALID_ARG if a size is not positive, pad < 0, or no window
+ * placement fits.  Formula: "Unifying Convolutions and GEMM", section 5,
+ * with the dilation term.  ho_out / wo_out may be NULL. */
+conv_status_t conv2d_output_size(int H, int W, int KH, int KW, int stride, int pad, int dilation,
+                                 int *ho_out, int *wo_out);
+
+/* Workspace bytes conv2d_fwd needs for this call (host only; no HIP call, so
+ * it works without a GPU).  The figure covers the lowering structure of the
+ * chosen algorithm (indirection buffer, or window-ordered input plus, for
+ * NCHW, the weights regrouped channel-innermost), and fp32 split-K partials
+ * on skinny layers.  It is 0 for AUTO on 1x1 layers.  *bytes_out receives the
+ * size; errors as for conv2d_fwd's host checks. */
+conv_status_t conv2d_fwd_workspace_size(int N, int C_in, int H, int W, int C_out, int KH, int KW,
+                                        int stride, int pad, int dilation,
+                                        conv_layout_t layout, conv_dtype_t dtype, conv_algo_t algo,
+                                        size_t *bytes_out);
+
+/* Bytes of the im2col matrix X_col the pages' GEMM route would build:
+ * N*Ho*Wo * C_in*KH*KW elements ("Unifying Convolutions and GEMM", section 2). */
+conv_status_t conv2d_im2col_bytes(int N, int C_in, int H, int W, int KH, int KW,
+                                  int stride, int pad, int dilation, conv_dtype_t dtype,
+                                  size_t *bytes_out);
+
+/* The forward convolution.
+ *   x, w, y    device tensors in `layout` (see above); y is fully overwritten.
+ *   bias       device vector of C_out values, or NULL for none.
+ *   workspace  device scratch of at least the queried size (NULL allowed when
+ *              that size is 0); contents undefined afterwards.
+ * Work is enqueued on `stream`; the call returns without waiting. */
+conv_status_t conv2d_fwd(const void *x, const void *w, const void *bias, void *y,
+                         int N, int C_in, int H, int W, int C_out, int KH, int KW,
+                         int stride, int pad, int dilation,
+                         conv_layout_t layout, conv_dtype_t dtype, conv_stream_t stream,
+                         void *workspace, size_t workspace_bytes, conv_algo_t algo);
+
+/* Steps (c) and (d) alone: the main loop and epilogue of the INDIRECT
+ * algorithm, reading X_col through an indirection buffer the caller built
+ * earlier with conv2d_build_indirection for the same geometry and layout.
+ * The buffer depends only on the geometry (never on x, w or the batch
+ * index), so one build can serve every later call of that shape.
+ * `workspace` needs at least conv2d_fwd_workspace_size(..., CONV_ALGO_INDIRECT)
+ * bytes (only its split-K part is used).  Other arguments and errors as for
+ * conv2d_fwd; a NULL or misaligned `indirection` is CONV_ERR_INVALID_ARG. */
+conv_status_t conv2d_fwd_indirect_prebuilt(const void *x, const void *w, const void *bias, void *y,
+                                           const int32_t *indirection,
+                                           int N, int C_in, int H, int W, int C_out, int KH, int KW,
+                                           int stride, int pad, int dilation,
+                                           conv_layout_t layout, conv_dtype_t dtype, conv_stream_t stream,
+                                           void *workspace, size_t workspace_bytes);
+
+/* Step (b) on its own: build the indirection buffer of The Indirect
+ * Convolution Algorithm (abstract) into `buf` (device, int32, Ho*Wo*KH*KW
+ * entries).  Entry [p][t] for output pixel p = ho*Wo + wo and tap
+ * t = kh*KW + kw is the element offset, within one image, of the first
+ * channel of input pixel (hi, wi) = (ho*stride + kh*dilation - pad,
+ * wo*stride + kw*dilation - pad): hi*W + wi for NCHW, (hi*W + wi)*C_in for
+ * NHWC; it is -1 where the tap falls in the zero padding.  The buffer does
+ * not depend on the batch index. */
+conv_status_t conv2d_build_indirection(int32_t *buf, int C_in, int H, int W, int KH, int KW,
+                                       int stride, int pad, int dilation, conv_layout_t layout,
+                                       conv_stream_t stream);
+
+/* Step (a) on its own: write the window-ordered tensor of "Im2win: An
+ * Efficient Convolution Paradigm on GPU" (abstract), under the reading taken
+ * here, into `xwin` (device, dtype elements):
+ *   xwin[n][ho][c][kh][ci] = xpad(n, ci, ho*stride + kh*dilation - pad, c - pad)
+ * for c < Wwin = (Wo-1)*stride + (KW-1)*dilation + 1.  For every output row
+ * it holds the KH input rows that row's windows touch, interleaved column by
+ * column with channels innermost, so the window of output pixel (ho, wo) is
+ * one contiguous run of KW*KH*C_in values when dilation is 1.  `x` is in
+ * `layout`; the result is the same for both layouts. */
+conv_status_t conv2d_im2win_transform(const void *x, void *xwin, int N, int C_in, int H, int W,
+                                      int KH, int KW, int stride, int pad, int dilation,
+                                      conv_layout_t layout, conv_dtype_t dtype, conv_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONVLOWER_H */
