@@ -15,6 +15,8 @@ constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
+int tile_rows(int tile) { return tile == TILE_32x64 ? 32 : 128; }
+
 struct Plan {
     Geom g;
     bool bf16, nhwc;
@@ -113,7 +115,7 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     } else {
         pl->tile = TILE_128x128; BM = 128; BN = 128;
     }
-    const int BK = 32;
+    const int BK = pl->bf16 ? 64 : 32;  // the main loop's K tile (128-byte LDS rows)
     long long blocks = ((g.M + BM - 1) / BM) * ((g.Co + BN - 1) / BN);
     long long ktiles = (g.K + BK - 1) / BK;
     int splits = 1;
@@ -261,11 +263,22 @@ conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias
     bool a_vec;
     switch (pl.feed) {
         case FEED_ROWMAJOR: a_vec = g.K % VEC == 0 && al16(a.a_src); break;
-        case FEED_IND_NHWC:
+        case FEED_IND_NHWC:  // the vector path keeps the block's BM x KH*KW buffer slice in LDS
+            a_vec = g.C % VEC == 0 && al16(a.a_src) && (long long)tile_rows(pl.tile) * g.T <= 4096;
+            break;
         case FEED_WIN: a_vec = g.C % VEC == 0 && al16(a.a_src); break;
         default: a_vec = false;
     }
     bool b_vec = g.K % VEC == 0 && al16(a.b);
+    // The vector paths address A and B with 32-bit buffer offsets.
+    const long long kBufMax = (1LL << 31) - 64;
+    long long a_bytes = (long long)pl.esize *
+                        (pl.need_win ? (long long)g.N * g.Ho * g.Wwin * g.KH * g.C : (long long)g.N * g.C * g.H * g.W);
+    long long b_bytes = (long long)pl.esize * g.Co * g.K;
+    if (a_bytes > kBufMax) a_vec = false;
+    if (b_bytes > kBufMax) a_vec = b_vec = false;
+    a.a_bytes = (uint32_t)(a_bytes > kBufMax ? kBufMax : a_bytes);
+    a.b_bytes = (uint32_t)(b_bytes > kBufMax ? kBufMax : b_bytes);
     if (a_vec && !b_vec) a_vec = false;
 
     hipError_t e = pl.bf16 ? launch_igemm_bf16(a, pl.feed, pl.out_nchw, a_vec, b_vec, pl.tile, pl.splits, s)

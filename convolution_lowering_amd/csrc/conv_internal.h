@@ -34,6 +34,8 @@ struct GemmArgs {
     float *part;          // split-K partial sums [splits][M][Co], or nullptr
     Geom g;
     int k_per_split;      // multiple of the K tile; == K rounded up when not split
+    uint32_t a_bytes;     // size of a_src in bytes (< 2^31 on the vector paths)
+    uint32_t b_bytes;     // size of b in bytes (< 2^31 on the vector paths)
 };
 
 // Tile shapes of the main loop (block = 256 threads = 4 wavefronts, 2x2).

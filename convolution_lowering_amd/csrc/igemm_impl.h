@@ -13,20 +13,30 @@
 // tiling, a micro-kernel, double buffering and prefetching -- recast for
 // CDNA4):
 //   * a 256-thread block owns a BM x BN tile of Y_col; its four 64-wide
-//     wavefronts split it 2 x 2;
-//   * K advances in tiles of 32; tile k+1 is fetched from memory into
-//     registers while the MFMAs consume tile k from LDS, then written to the
-//     other half of a double-buffered LDS area (one barrier per tile);
-//   * every LDS row holds the 32 K-consecutive values of one output pixel (or
-//     one output channel) in 16-byte chunks, padded by one chunk so that the
-//     per-lane 16-byte fragment reads of a wavefront do not collide on banks;
+//     wavefronts split it 2 x 2 and each keeps its (BM/2) x (BN/2) fp32
+//     accumulators in registers;
+//   * K advances in tiles of BK; the global loads of tile k+2 are issued
+//     into registers before the MFMAs consume tile k from LDS, and tile k+1
+//     (loaded one iteration earlier) is then written to the other half of a
+//     double-buffered LDS area -- one barrier per tile;
+//   * every LDS row holds the BK K-consecutive values of one output pixel (or
+//     one output channel) as 16-byte chunks whose positions are XOR-swizzled
+//     by the row index, so the per-lane 16-byte fragment reads of a
+//     wavefront (16 rows, one chunk column) hit distinct banks;
+//   * for the indirection feed the block's slice of the buffer (its BM rows
+//     times KH*KW taps) is copied to LDS once, so no global load waits on
+//     another; the (tap, channel) position of each thread's chunk advances
+//     incrementally, without divisions;
 //   * the micro-kernel is v_mfma_f32_16x16x32_bf16 (bf16) or
-//     v_mfma_f32_16x16x4_f32 (fp32), fp32 accumulators in registers;
+//     v_mfma_f32_16x16x4_f32 (fp32);
 //   * the epilogue adds the bias in fp32, rounds once to the output type
-//     (round-to-nearest-even for bf16) and stores in the output layout; the
-//     MFMA operand order is picked so that each lane's four accumulator rows
-//     run along the output's contiguous axis.  With split-K the fp32 partial
-//     sums go to the workspace instead and a separate pass finishes them.
+//     (round-to-nearest-even for bf16), stages the tile in LDS and writes it
+//     with 16-byte stores along the output's contiguous axis.  With split-K
+//     the fp32 partial sums go to the workspace instead and a separate pass
+//     finishes them;
+//   * tile indices are remapped so that each XCD (blocks are dealt to the
+//     eight XCDs round-robin) works on a contiguous run of output pixels and
+//     their shared input rows stay in that XCD's L2.
 #pragma once
 
 #include "conv_internal.h"
@@ -63,8 +73,22 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     return (uint16_t)(u >> 16);
 }
 
-__device__ __forceinline__ void store_out(uint16_t *y, long long i, float v) { y[i] = f32_to_bf16_rne(v); }
-__device__ __forceinline__ void store_out(float *y, long long i, float v) { y[i] = v; }
+__device__ __forceinline__ uint16_t to_out(uint16_t, float v) { return f32_to_bf16_rne(v); }
+__device__ __forceinline__ float to_out(float, float v) { return v; }
+
+// Buffer loads: an offset past the buffer's size reads as zeros, so padding
+// taps and out-of-range rows need neither a branch nor a select, and every
+// load is issued unconditionally (keeping the compiler's count of
+// outstanding loads exact).  Offsets are in bytes.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
 
 union Chunk {
     uint4 v;
@@ -79,11 +103,10 @@ __device__ __forceinline__ void chunk_put(Chunk &c, int j, uint32_t bits) {
         c.u[j] = bits;
 }
 
-// Per-thread, per-chunk description of one A row (one output pixel); fixed
-// for the whole K loop.
+// Per-row description of one A row (one output pixel), fixed for the K loop.
 struct ARow {
     long long base;  // feed-specific element offset of the row's origin
-    int p;           // output pixel within its image (for the indirection buffer)
+    int p;           // output pixel within its image (indirection buffer row)
     bool ok;         // row lies inside M
 };
 
@@ -110,7 +133,8 @@ __device__ __forceinline__ ARow make_arow(const Geom &g, long long m) {
     return r;
 }
 
-// One element A[m][k] of the virtual X_col (0 in the padding).
+// One element A[m][k] of the virtual X_col (0 in the padding); the general
+// path for feeds and shapes whose rows cannot be read in 16-byte chunks.
 template <typename S, int FEED>
 __device__ __forceinline__ uint32_t a_elem(const GemmArgs &A, const ARow &r, int k) {
     const S *src = (const S *)A.a_src;
@@ -134,123 +158,199 @@ __device__ __forceinline__ uint32_t a_elem(const GemmArgs &A, const ARow &r, int
     }
 }
 
-// 16 contiguous bytes A[m][k0 .. k0+VEC) (only for feeds whose chunks never
-// straddle a tap and are 16-byte aligned; the host checks when that holds).
-template <typename S, int FEED>
-__device__ __forceinline__ uint4 a_vec(const GemmArgs &A, const ARow &r, int k0) {
-    const S *src = (const S *)A.a_src;
-    const Geom &g = A.g;
-    long long addr;
-    if constexpr (FEED == FEED_ROWMAJOR) {
-        addr = r.base + k0;
-    } else if constexpr (FEED == FEED_IND_NHWC) {
-        int t = k0 / g.C, ci = k0 - t * g.C;
-        int off = A.ibuf[r.p * g.T + t];
-        if (off < 0) return make_uint4(0, 0, 0, 0);
-        addr = r.base + off + ci;
-    } else {  // FEED_WIN
-        int t = k0 / g.C, ci = k0 - t * g.C;
-        int kh = t / g.KW, kw = t - kh * g.KW;
-        addr = r.base + (long long)(kw * g.d * g.KH + kh) * g.C + ci;
-    }
-    return *(const uint4 *)(src + addr);
-}
+constexpr int kThreads = 256;
+constexpr int kIbufLdsEntries = 4096;  // LDS slots for the block's indirection-buffer slice
 
-template <typename S, int FEED, bool AVEC, bool BVEC, bool OUT_NCHW, int BM, int BN>
-__global__ __launch_bounds__(256) void igemm_kernel(GemmArgs A) {
-    constexpr int VEC = Elem<S>::VEC;
-    constexpr int BK = 32;
-    constexpr int KCH = BK / VEC;  // 16-byte chunks per LDS row
-    constexpr int RS = KCH + 1;    // padded row stride, in chunks
-    constexpr int A_CH = BM * KCH, B_CH = BN * KCH;
-    constexpr int A_PER = (A_CH + 255) / 256, B_PER = (B_CH + 255) / 256;
-    constexpr int WPM = BM / 2, WCN = BN / 2;  // wavefront tile
-    constexpr int TP = WPM / 16, TC = WCN / 16;
+// LDS position (in 16-byte chunks) of chunk c of row `row`, rows of kch chunks.
+__device__ __forceinline__ constexpr int lds_slot(int row, int c, int kch) { return row * kch + (c ^ (row & 7)); }
+
+template <typename S, int BM, int BN, int BK>
+struct TileCfg {
+    static constexpr int VEC = Elem<S>::VEC;
+    static constexpr int KCH = BK / VEC;  // 16-byte chunks per LDS row
+    static constexpr int RS = KCH;        // row stride, in chunks (chunks XOR-swizzled within a row)
+    static constexpr int A_CH = BM * KCH, B_CH = BN * KCH;
+    static constexpr int A_PER = A_CH / kThreads, B_PER = B_CH / kThreads;
+    static constexpr int STAGE = (BM + BN) * RS;  // uint4 per LDS stage
+    static constexpr int WPM = BM / 2, WCN = BN / 2;
+    static constexpr int TP = WPM / 16, TC = WCN / 16;
+    // epilogue tile in LDS: [BN][BM + EPAD] (NCHW) or [BM][BN + EPAD] (NHWC), in S
+    static constexpr int EPAD = 16 / (int)sizeof(S);
+    static constexpr int EPI_BYTES = (BM > BN ? BM : BN) * ((BM > BN ? BN : BM) + EPAD) * (int)sizeof(S);
+    static constexpr int MAIN_BYTES = 2 * STAGE * 16;
+    static constexpr int SMEM_UINT4 = ((MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES) + 15) / 16;
+    static_assert(KCH % 8 == 0, "a K tile must be 128 bytes per row (whole MFMA K steps, 8-way swizzle)");
+    static_assert(A_CH % kThreads == 0 && B_CH % kThreads == 0, "chunks must divide evenly");
+    static_assert(kThreads % KCH == 0, "rows must divide evenly");
     static_assert(TP >= 1 && TC >= 1, "tile too small");
-    // Element-wise feeds put consecutive lanes on consecutive pixels.
-    constexpr bool A_LANES_ON_M = !AVEC;
+};
 
-    __shared__ uint4 sm[2 * (BM + BN) * RS];
+template <typename S, int FEED, bool AVEC, bool BVEC, bool OUT_NCHW, int BM, int BN, int BK>
+__global__ __launch_bounds__(kThreads) void igemm_kernel(GemmArgs A) {
+    using C = TileCfg<S, BM, BN, BK>;
+    constexpr int VEC = C::VEC, KCH = C::KCH, RS = C::RS;
+    constexpr int A_PER = C::A_PER, B_PER = C::B_PER;
+    constexpr int WPM = C::WPM, WCN = C::WCN, TP = C::TP, TC = C::TC;
+    constexpr bool IND = FEED == FEED_IND_NHWC || FEED == FEED_IND_NCHW;
+
+    __shared__ uint4 sm[C::SMEM_UINT4];
+    __shared__ int ib_lds[IND && AVEC ? kIbufLdsEntries : 1];
 
     const Geom &g = A.g;
     const int tid = threadIdx.x;
-    const long long m0 = (long long)blockIdx.x * BM;
+
+    // XCD-aware tile order: consecutive pixel tiles stay on one XCD.
+    int bx = blockIdx.x;
+    const int nbx = gridDim.x;
+    if ((nbx & 7) == 0) bx = (bx & 7) * (nbx >> 3) + (bx >> 3);
+    const long long m0 = (long long)bx * BM;
     const int co0 = blockIdx.y * BN;
     const int kbeg = blockIdx.z * A.k_per_split;
-    const int kend = min((long long)kbeg + A.k_per_split, g.K);
+    const int kend = (int)min((long long)kbeg + A.k_per_split, g.K);
     const int nk = (kend - kbeg + BK - 1) / BK;
 
-    // Fixed per-thread chunk assignment.
+    // The block's slice of the indirection buffer, rows m0 .. m0+BM-1 (the
+    // vector path requires BM * KH*KW <= kIbufLdsEntries; the host checks).
+    if constexpr (IND && AVEC) {
+        for (int e = tid; e < BM * g.T; e += kThreads) {
+            int row = e / g.T, t = e - row * g.T;
+            long long m = m0 + row;
+            int v = -1;
+            if (m < g.M) {
+                long long n = m / g.P;
+                int p = (int)(m - n * g.P);
+                v = A.ibuf[p * g.T + t];
+            }
+            ib_lds[e] = v;
+        }
+    }
+
+    // ---- A operand assignment --------------------------------------------
+    // Vector feeds: thread owns chunk column kc = tid % KCH of rows
+    // tid / KCH + i * (256 / KCH).  Element-wise feeds: lanes run along rows.
+    constexpr bool LANES_ON_M = !AVEC;
     ARow arow[A_PER];
-    int a_lds[A_PER], a_kc[A_PER];
-    bool a_act[A_PER];
+    int a_lds[A_PER];
+    int a_rowl[A_PER];
+    const int a_kc_vec = (tid % KCH) * VEC;
 #pragma unroll
     for (int i = 0; i < A_PER; ++i) {
-        int c = tid + i * 256;
-        a_act[i] = c < A_CH;
-        int row = A_LANES_ON_M ? c % BM : c / KCH;
-        int kc = A_LANES_ON_M ? c / BM : c % KCH;
-        if (!a_act[i]) row = 0, kc = 0;
-        a_lds[i] = row * RS + kc;
-        a_kc[i] = kc * VEC;
+        int c = tid + i * kThreads;
+        int row = LANES_ON_M ? c % BM : c / KCH;
+        int kc = LANES_ON_M ? c / BM : c % KCH;
+        a_lds[i] = lds_slot(row, kc, KCH);
+        a_rowl[i] = row;
         arow[i] = make_arow<FEED>(g, m0 + row);
     }
-    const S *bsrc = (const S *)A.b;
-    long long b_off[B_PER];
-    int b_lds[B_PER], b_kc[B_PER];
-    bool b_ok[B_PER];
+    int a_kc_el[A_PER];
 #pragma unroll
-    for (int i = 0; i < B_PER; ++i) {
-        int c = tid + i * 256;
-        int row = c / KCH, kc = c % KCH;
-        bool act = c < B_CH;
-        if (!act) row = 0, kc = 0;
-        int co = co0 + row;
-        b_ok[i] = act && co < g.Co;
-        b_off[i] = (long long)(b_ok[i] ? co : 0) * g.K;
-        b_lds[i] = act ? row * RS + kc : -1;
-        b_kc[i] = kc * VEC;
+    for (int i = 0; i < A_PER; ++i) {
+        int c = tid + i * kThreads;
+        a_kc_el[i] = (LANES_ON_M ? c / BM : c % KCH) * VEC;
     }
 
-    Chunk ra[A_PER], rb[B_PER];
+    // (tap, channel) of this thread's vector chunk, advanced per K tile.
+    int cur_t = 0, cur_ci = 0, cur_kh = 0, cur_kw = 0;
+    if constexpr (AVEC && (FEED == FEED_IND_NHWC || FEED == FEED_WIN)) {
+        int k0 = kbeg + a_kc_vec;
+        cur_t = k0 / g.C;
+        cur_ci = k0 - cur_t * g.C;
+        cur_kh = cur_t / g.KW;
+        cur_kw = cur_t - cur_kh * g.KW;
+    }
 
-    auto fetch = [&](int kt0) {
+    // ---- B operand assignment ----------------------------------------------
+    const S *bsrc = (const S *)A.b;
+    long long b_off[B_PER];
+    int b_lds[B_PER];
+    bool b_ok[B_PER];
+    const int b_kc = (tid % KCH) * VEC;
 #pragma unroll
-        for (int i = 0; i < A_PER; ++i) {
-            int k0 = kt0 + a_kc[i];
-            ra[i].v = make_uint4(0, 0, 0, 0);
-            if (!a_act[i] || !arow[i].ok) continue;
-            if constexpr (AVEC) {
-                if (k0 < kend) ra[i].v = a_vec<S, FEED>(A, arow[i], k0);
-            } else {
+    for (int i = 0; i < B_PER; ++i) {
+        int c = tid + i * kThreads;
+        int row = c / KCH;
+        int co = co0 + row;
+        b_ok[i] = co < g.Co;
+        b_off[i] = (long long)(b_ok[i] ? co : 0) * g.K;
+        b_lds[i] = lds_slot(row, c % KCH, KCH);
+    }
+
+    __syncthreads();  // ib_lds ready
+
+    Chunk ra[2][A_PER], rb[2][B_PER];
+
+    // Global -> registers for K tile starting at kt0 (register set `set`).
+    // The vector paths use buffer loads, issued unconditionally, so the
+    // compiler can count outstanding loads exactly and wait only for the tile
+    // it is about to store.
+    const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(A.a_src, A.a_bytes);
+    const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(A.b, A.b_bytes);
+    auto fetch = [&](int kt0, auto set_c) {
+        constexpr int set = decltype(set_c)::value;
+        if constexpr (AVEC) {
+            const int k0 = kt0 + a_kc_vec;
+            const bool kin = k0 < kend;
+            long long koff = 0;
+            if constexpr (FEED == FEED_ROWMAJOR) koff = k0;
+            if constexpr (FEED == FEED_IND_NHWC) koff = cur_ci;
+            if constexpr (FEED == FEED_WIN) koff = (long long)(cur_kw * g.d * g.KH + cur_kh) * g.C + cur_ci;
+#pragma unroll
+            for (int i = 0; i < A_PER; ++i) {
+                bool valid = arow[i].ok && kin;
+                long long addr = arow[i].base + koff;
+                if constexpr (FEED == FEED_IND_NHWC) {
+                    int off = ib_lds[a_rowl[i] * g.T + cur_t];
+                    valid = valid && off >= 0;
+                    addr += off;
+                }
+                ra[set][i].v = buf_load16(a_rsrc, valid ? (uint32_t)(addr * (long long)sizeof(S)) : kOutOfRange);
+            }
+            // advance the (tap, channel) position by one K tile
+            if constexpr (FEED == FEED_IND_NHWC || FEED == FEED_WIN) {
+                cur_ci += BK;
+                while (cur_ci >= g.C) {
+                    cur_ci -= g.C;
+                    ++cur_t;
+                    if (++cur_kw == g.KW) {
+                        cur_kw = 0;
+                        ++cur_kh;
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < A_PER; ++i) {
+                ra[set][i].v = make_uint4(0, 0, 0, 0);
+                if (!arow[i].ok) continue;
+                int k0 = kt0 + a_kc_el[i];
 #pragma unroll
                 for (int j = 0; j < VEC; ++j)
-                    if (k0 + j < kend) chunk_put<S>(ra[i], j, a_elem<S, FEED>(A, arow[i], k0 + j));
+                    if (k0 + j < kend) chunk_put<S>(ra[set][i], j, a_elem<S, FEED>(A, arow[i], k0 + j));
             }
         }
+        const int kb = kt0 + b_kc;
 #pragma unroll
         for (int i = 0; i < B_PER; ++i) {
-            int k0 = kt0 + b_kc[i];
-            rb[i].v = make_uint4(0, 0, 0, 0);
-            if (!b_ok[i]) continue;
             if constexpr (BVEC) {
-                if (k0 < kend) rb[i].v = *(const uint4 *)(bsrc + b_off[i] + k0);
+                bool valid = b_ok[i] && kb < kend;
+                rb[set][i].v = buf_load16(b_rsrc, valid ? (uint32_t)((b_off[i] + kb) * (long long)sizeof(S)) : kOutOfRange);
             } else {
+                rb[set][i].v = make_uint4(0, 0, 0, 0);
+                if (!b_ok[i]) continue;
 #pragma unroll
                 for (int j = 0; j < VEC; ++j)
-                    if (k0 + j < kend) chunk_put<S>(rb[i], j, elem_bits(bsrc, b_off[i] + k0 + j));
+                    if (kb + j < kend) chunk_put<S>(rb[set][i], j, elem_bits(bsrc, b_off[i] + kb + j));
             }
         }
     };
-    auto stash = [&](int stage) {
-        uint4 *As = sm + stage * (BM + BN) * RS;
+    auto stash = [&](int stage, auto set_c) {
+        constexpr int set = decltype(set_c)::value;
+        uint4 *As = sm + stage * C::STAGE;
         uint4 *Bs = As + BM * RS;
 #pragma unroll
-        for (int i = 0; i < A_PER; ++i)
-            if (a_act[i]) As[a_lds[i]] = ra[i].v;
+        for (int i = 0; i < A_PER; ++i) As[a_lds[i]] = ra[set][i].v;
 #pragma unroll
-        for (int i = 0; i < B_PER; ++i)
-            if (b_lds[i] >= 0) Bs[b_lds[i]] = rb[i].v;
+        for (int i = 0; i < B_PER; ++i) Bs[b_lds[i]] = rb[set][i].v;
     };
 
     f32x4_t acc[TP][TC];
@@ -264,15 +364,15 @@ __global__ __launch_bounds__(256) void igemm_kernel(GemmArgs A) {
     const int frow = lane & 15, fchunk = lane >> 4;
 
     auto compute = [&](int stage) {
-        const uint4 *As = sm + stage * (BM + BN) * RS;
+        const uint4 *As = sm + stage * C::STAGE;
         const uint4 *Bs = As + BM * RS;
 #pragma unroll
         for (int grp = 0; grp < KCH / 4; ++grp) {
             uint4 af[TP], bf[TC];
 #pragma unroll
-            for (int ip = 0; ip < TP; ++ip) af[ip] = As[(wp * WPM + ip * 16 + frow) * RS + grp * 4 + fchunk];
+            for (int ip = 0; ip < TP; ++ip) af[ip] = As[lds_slot(wp * WPM + ip * 16 + frow, grp * 4 + fchunk, KCH)];
 #pragma unroll
-            for (int ic = 0; ic < TC; ++ic) bf[ic] = Bs[(wc * WCN + ic * 16 + frow) * RS + grp * 4 + fchunk];
+            for (int ic = 0; ic < TC; ++ic) bf[ic] = Bs[lds_slot(wc * WCN + ic * 16 + frow, grp * 4 + fchunk, KCH)];
 #pragma unroll
             for (int ip = 0; ip < TP; ++ip)
 #pragma unroll
@@ -299,73 +399,158 @@ __global__ __launch_bounds__(256) void igemm_kernel(GemmArgs A) {
         }
     };
 
+    using Z = std::integral_constant<int, 0>;
+    using O = std::integral_constant<int, 1>;
     if (nk > 0) {
-        fetch(kbeg);
-        stash(0);
+        // Fetches and stores run unconditionally (tiles past the end read as
+        // zeros and land in a stage nobody reads), so the loads in flight are
+        // the same on every path and each wait covers exactly one tile.
+        fetch(kbeg, Z{});
+        fetch(kbeg + BK, O{});
+        stash(0, Z{});
         __syncthreads();
-        for (int kt = 0; kt < nk; ++kt) {
-            const bool more = kt + 1 < nk;
-            if (more) fetch(kbeg + (kt + 1) * BK);
-            compute(kt & 1);
-            if (more) stash((kt + 1) & 1);
+        // Two K tiles per trip so the register sets are named statically.
+        for (int kt = 0;; kt += 2) {
+            fetch(kbeg + (kt + 2) * BK, Z{});
+            compute(0);
+            stash(1, O{});
             __syncthreads();
+            if (kt + 1 >= nk) break;
+            fetch(kbeg + (kt + 3) * BK, O{});
+            compute(1);
+            stash(0, Z{});
+            __syncthreads();
+            if (kt + 2 >= nk) break;
         }
     }
 
-    // Epilogue.  MFMA 16x16 result: lane holds column (lane & 15) and rows
-    // 4*(lane >> 4) + v, v = 0..3.
-    S *y = (S *)A.y;
+    // ---- epilogue ------------------------------------------------------------
+    // MFMA 16x16 result: lane holds column (lane & 15), rows 4*(lane >> 4) + v.
     const S *bias = (const S *)A.bias;
+    if (A.part) {  // split-K: raw fp32 partials, finished by the reduce pass
 #pragma unroll
-    for (int ip = 0; ip < TP; ++ip)
+        for (int ip = 0; ip < TP; ++ip)
 #pragma unroll
-        for (int ic = 0; ic < TC; ++ic)
+            for (int ic = 0; ic < TC; ++ic)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    long long m;
+                    int co;
+                    if constexpr (OUT_NCHW) {
+                        m = m0 + wp * WPM + ip * 16 + 4 * fchunk + v;
+                        co = co0 + wc * WCN + ic * 16 + frow;
+                    } else {
+                        m = m0 + wp * WPM + ip * 16 + frow;
+                        co = co0 + wc * WCN + ic * 16 + 4 * fchunk + v;
+                    }
+                    if (m < g.M && co < g.Co) A.part[((long long)blockIdx.z * g.M + m) * g.Co + co] = acc[ip][ic][v];
+                }
+        return;
+    }
+
+    // Stage the rounded tile in LDS, laid out along the output's contiguous
+    // axis, then write it out in 16-byte chunks.
+    S *E = (S *)sm;
+    constexpr int EPAD = C::EPAD;
+    constexpr int ER = OUT_NCHW ? BM + EPAD : BN + EPAD;  // elements per LDS row
+#pragma unroll
+    for (int ic = 0; ic < TC; ++ic) {
+#pragma unroll
+        for (int ip = 0; ip < TP; ++ip) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                long long m;
-                int co;
+                int ml, cl;
                 if constexpr (OUT_NCHW) {
-                    m = m0 + wp * WPM + ip * 16 + 4 * fchunk + v;
-                    co = co0 + wc * WCN + ic * 16 + frow;
+                    ml = wp * WPM + ip * 16 + 4 * fchunk + v;
+                    cl = wc * WCN + ic * 16 + frow;
                 } else {
-                    m = m0 + wp * WPM + ip * 16 + frow;
-                    co = co0 + wc * WCN + ic * 16 + 4 * fchunk + v;
+                    ml = wp * WPM + ip * 16 + frow;
+                    cl = wc * WCN + ic * 16 + 4 * fchunk + v;
                 }
-                if (m >= g.M || co >= g.Co) continue;
                 float val = acc[ip][ic][v];
-                if (A.part) {
-                    A.part[((long long)blockIdx.z * g.M + m) * g.Co + co] = val;
-                    continue;
-                }
-                if (bias) val += bits_to_f32(S(), elem_bits(bias, co));
-                long long yi;
-                if constexpr (OUT_NCHW) {
-                    long long n = m / g.P;
-                    yi = (n * g.Co + co) * g.P + (m - n * g.P);
-                } else {
-                    yi = m * g.Co + co;
-                }
-                store_out(y, yi, val);
+                int co = co0 + cl;
+                if (bias && co < g.Co) val += bits_to_f32(S(), elem_bits(bias, co));
+                if constexpr (OUT_NCHW)
+                    E[cl * ER + ml] = to_out(S(), val);
+                else
+                    E[ml * ER + cl] = to_out(S(), val);
             }
+        }
+    }
+    __syncthreads();
+
+    S *y = (S *)A.y;
+    if constexpr (OUT_NCHW) {
+        // rows: output channels; columns: BM consecutive pixels
+        constexpr int CPR = BM / VEC;  // chunks per row
+        for (int c = tid; c < BN * CPR; c += kThreads) {
+            int cl = c / CPR, mc = (c - cl * CPR) * VEC;
+            int co = co0 + cl;
+            if (co >= g.Co) continue;
+            long long m = m0 + mc;
+            if (m >= g.M) continue;
+            long long n = m / g.P;
+            long long p = m - n * g.P;
+            long long yi = (n * g.Co + co) * g.P + p;
+            const S *src = E + cl * ER + mc;
+            if (p + VEC <= g.P && m + VEC <= g.M && ((uintptr_t)(y + yi) & 15) == 0) {
+                *(uint4 *)(y + yi) = *(const uint4 *)src;
+            } else {
+                for (int j = 0; j < VEC; ++j) {
+                    long long mj = m + j;
+                    if (mj >= g.M) break;
+                    long long nj = mj / g.P;
+                    y[(nj * g.Co + co) * g.P + (mj - nj * g.P)] = src[j];
+                }
+            }
+        }
+    } else {
+        constexpr int CPR = BN / VEC;
+        for (int c = tid; c < BM * CPR; c += kThreads) {
+            int ml = c / CPR, cc = (c - ml * CPR) * VEC;
+            long long m = m0 + ml;
+            int co = co0 + cc;
+            if (m >= g.M || co >= g.Co) continue;
+            long long yi = m * g.Co + co;
+            const S *src = E + ml * ER + cc;
+            if (co + VEC <= g.Co && ((uintptr_t)(y + yi) & 15) == 0) {
+                *(uint4 *)(y + yi) = *(const uint4 *)src;
+            } else {
+                for (int j = 0; j < VEC && co + j < g.Co; ++j) y[yi + j] = src[j];
+            }
+        }
+    }
 }
+
+}  // namespace convlower
+
+#include "igemm_dma.h"
+
+namespace convlower {
 
 template <typename S, int FEED, bool AVEC, bool BVEC, bool OUT_NCHW>
 static hipError_t launch_tile(const GemmArgs &a, int tile, int splits, hipStream_t st) {
     const Geom &g = a.g;
     auto go = [&](auto kern, int BM, int BN) {
         dim3 grid((unsigned)((g.M + BM - 1) / BM), (unsigned)((g.Co + BN - 1) / BN), (unsigned)splits);
-        hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, st, a);
         return hipGetLastError();
     };
-    switch (tile) {
-        case TILE_128x128:
-            return go(igemm_kernel<S, FEED, AVEC, BVEC, OUT_NCHW, 128, 128>, 128, 128);
-        case TILE_128x64:
-            return go(igemm_kernel<S, FEED, AVEC, BVEC, OUT_NCHW, 128, 64>, 128, 64);
-        case TILE_32x64:
-            return go(igemm_kernel<S, FEED, AVEC, BVEC, OUT_NCHW, 32, 64>, 32, 64);
-        default:
-            return hipErrorInvalidValue;
+    constexpr int BKW = sizeof(S) == 2 ? 64 : 32;  // 128-byte LDS rows
+    if constexpr (AVEC) {  // 16-byte rows: straight-to-LDS pipeline
+        switch (tile) {
+            case TILE_128x128: return go(igemm_dma_kernel<S, FEED, OUT_NCHW, 128, 128, BKW>, 128, 128);
+            case TILE_128x64: return go(igemm_dma_kernel<S, FEED, OUT_NCHW, 128, 64, BKW>, 128, 64);
+            case TILE_32x64: return go(igemm_dma_kernel<S, FEED, OUT_NCHW, 32, 64, BKW>, 32, 64);
+            default: return hipErrorInvalidValue;
+        }
+    } else {  // element gathers through registers
+        switch (tile) {
+            case TILE_128x128: return go(igemm_kernel<S, FEED, AVEC, BVEC, OUT_NCHW, 128, 128, BKW>, 128, 128);
+            case TILE_128x64: return go(igemm_kernel<S, FEED, AVEC, BVEC, OUT_NCHW, 128, 64, BKW>, 128, 64);
+            case TILE_32x64: return go(igemm_kernel<S, FEED, AVEC, BVEC, OUT_NCHW, 32, 64, BKW>, 32, 64);
+            default: return hipErrorInvalidValue;
+        }
     }
 }
 
