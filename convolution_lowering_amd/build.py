@@ -62,6 +62,13 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    # Every kernel entry point the host code launches must be defined in the
+    # library (a template kernel whose host stub was not emitted would
+    # otherwise only show up as a load failure on the GPU).
+    r = subprocess.run(["nm", "-C", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [ln.strip() for ln in r.stdout.splitlines() if "convlower::" in ln]
+    if missing:
+        raise RuntimeError("undefined library symbols:\n" + "\n".join(missing))
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

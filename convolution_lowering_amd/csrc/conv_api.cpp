@@ -15,7 +15,7 @@ constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
-int tile_rows(int tile) { return tile == TILE_32x64 ? 32 : 128; }
+int tile_rows(int tile) { return tile == TILE_32x64 ? 32 : tile == TILE_256x128 ? 256 : 128; }
 
 struct Plan {
     Geom g;
@@ -24,6 +24,7 @@ struct Plan {
     bool out_nchw;
     int tile, splits, kps;
     bool need_ibuf, need_win, need_wpack;
+    bool rows16;  // the feed can read X_col rows in 16-byte chunks (by shape)
     size_t off_ibuf, off_win, off_wpack, off_part, total;
     size_t esize;
 };
@@ -106,12 +107,24 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     }
     pl->out_nchw = !pl->nhwc && pl->feed != FEED_ROWMAJOR;
 
-    // Tile shape and split-K.
+    // Tile shape and split-K.  The 256x128 tile (wavefront tiles of 128x64,
+    // a quarter less LDS and L2 traffic per MFMA) needs the 16-byte-row feeds.
+    const int VEC = pl->bf16 ? 8 : 4;
+    bool rows16;
+    switch (pl->feed) {
+        case FEED_ROWMAJOR: rows16 = g.K % VEC == 0; break;
+        case FEED_IND_NHWC: rows16 = g.C % VEC == 0 && 256LL * g.T <= 3072; break;
+        case FEED_WIN: rows16 = g.C % VEC == 0; break;
+        default: rows16 = false;
+    }
+    pl->rows16 = rows16;
     int BM, BN;
     if (g.M <= 64) {
         pl->tile = TILE_32x64; BM = 32; BN = 64;
     } else if (g.Co <= 64) {
         pl->tile = TILE_128x64; BM = 128; BN = 64;
+    } else if (rows16 && g.M >= 65536) {
+        pl->tile = TILE_256x128; BM = 256; BN = 128;
     } else {
         pl->tile = TILE_128x128; BM = 128; BN = 128;
     }
@@ -264,7 +277,7 @@ conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias
     switch (pl.feed) {
         case FEED_ROWMAJOR: a_vec = g.K % VEC == 0 && al16(a.a_src); break;
         case FEED_IND_NHWC:  // the vector path keeps the block's BM x KH*KW buffer slice in LDS
-            a_vec = g.C % VEC == 0 && al16(a.a_src) && (long long)tile_rows(pl.tile) * g.T <= 4096;
+            a_vec = pl.rows16 && al16(a.a_src) && (long long)tile_rows(pl.tile) * g.T <= 3072;
             break;
         case FEED_WIN: a_vec = g.C % VEC == 0 && al16(a.a_src); break;
         default: a_vec = false;
@@ -281,8 +294,12 @@ conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias
     a.b_bytes = (uint32_t)(b_bytes > kBufMax ? kBufMax : b_bytes);
     if (a_vec && !b_vec) a_vec = false;
 
-    hipError_t e = pl.bf16 ? launch_igemm_bf16(a, pl.feed, pl.out_nchw, a_vec, b_vec, pl.tile, pl.splits, s)
-                           : launch_igemm_f32(a, pl.feed, pl.out_nchw, a_vec, b_vec, pl.tile, pl.splits, s);
+    // Misaligned pointers fall back to the element-gather loop, which has no
+    // 256x128 variant; the split count (and so the workspace) is unchanged.
+    int tile = pl.tile;
+    if (!a_vec && tile == TILE_256x128) tile = TILE_128x128;
+    hipError_t e = pl.bf16 ? launch_igemm_bf16(a, pl.feed, pl.out_nchw, a_vec, b_vec, tile, pl.splits, s)
+                           : launch_igemm_f32(a, pl.feed, pl.out_nchw, a_vec, b_vec, tile, pl.splits, s);
     if (e != hipSuccess) return CONV_ERR_HIP;
     if (pl.splits > 1) {
         if (launch_splitk_reduce(a.part, bias, y, g, pl.splits, pl.out_nchw, pl.bf16, s) != hipSuccess)

@@ -39,7 +39,7 @@ struct GemmArgs {
 };
 
 // Tile shapes of the main loop (block = 256 threads = 4 wavefronts, 2x2).
-enum Tile : int { TILE_128x128 = 0, TILE_128x64 = 1, TILE_32x64 = 2, TILE_COUNT = 3 };
+enum Tile : int { TILE_128x128 = 0, TILE_128x64 = 1, TILE_32x64 = 2, TILE_256x128 = 3, TILE_COUNT = 4 };
 
 hipError_t launch_igemm_bf16(const GemmArgs &a, int feed, bool out_nchw, bool a_vec, bool b_vec,
                              int tile, int splits, hipStream_t st);

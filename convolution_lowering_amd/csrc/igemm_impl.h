@@ -34,9 +34,7 @@
 //     with 16-byte stores along the output's contiguous axis.  With split-K
 //     the fp32 partial sums go to the workspace instead and a separate pass
 //     finishes them;
-//   * tile indices are remapped so that each XCD (blocks are dealt to the
-//     eight XCDs round-robin) works on a contiguous run of output pixels and
-//     their shared input rows stay in that XCD's L2.
+//   * tile order: see tile_coords.
 #pragma once
 
 #include "conv_internal.h"
@@ -45,6 +43,7 @@ namespace convlower {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 template <typename S>
 struct Elem;
@@ -158,8 +157,36 @@ __device__ __forceinline__ uint32_t a_elem(const GemmArgs &A, const ARow &r, int
     }
 }
 
+
+// Tile order.  The grid is one-dimensional over the (pixel tile, channel
+// tile) pairs; blocks are dealt to the eight XCDs round-robin, so block b
+// runs on XCD b % 8 as that XCD's (b / 8)-th block.  When the channel-tile
+// count divides 8, each XCD is given one channel tile -- its slice of W_row
+// then stays in that XCD's L2 -- and a contiguous share of the pixel tiles
+// (the input rows of neighbouring pixel tiles overlap).  Otherwise each XCD
+// takes a contiguous run of pairs, channel tiles of one pixel tile adjacent
+// (those blocks read the same X_col rows).
+__device__ __forceinline__ void tile_coords(int ntile_m, int ntile_n, int &mt, int &nt) {
+    const int b = blockIdx.x, total = gridDim.x;
+    if ((total & 7) == 0) {
+        const int xcd = b & 7, j = b >> 3;
+        if ((8 % ntile_n) == 0 && (ntile_m % (8 / ntile_n)) == 0) {
+            const int groups = 8 / ntile_n;
+            nt = xcd % ntile_n;
+            mt = (xcd / ntile_n) * (ntile_m / groups) + j;
+            return;
+        }
+        const int l = xcd * (total >> 3) + j;
+        mt = l / ntile_n;
+        nt = l - mt * ntile_n;
+        return;
+    }
+    mt = b / ntile_n;
+    nt = b - mt * ntile_n;
+}
+
 constexpr int kThreads = 256;
-constexpr int kIbufLdsEntries = 4096;  // LDS slots for the block's indirection-buffer slice
+constexpr int kIbufLdsEntries = 3072;  // LDS slots for the block's indirection-buffer slice
 
 // LDS position (in 16-byte chunks) of chunk c of row `row`, rows of kch chunks.
 __device__ __forceinline__ constexpr int lds_slot(int row, int c, int kch) { return row * kch + (c ^ (row & 7)); }
@@ -199,12 +226,10 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(GemmArgs A) {
     const Geom &g = A.g;
     const int tid = threadIdx.x;
 
-    // XCD-aware tile order: consecutive pixel tiles stay on one XCD.
-    int bx = blockIdx.x;
-    const int nbx = gridDim.x;
-    if ((nbx & 7) == 0) bx = (bx & 7) * (nbx >> 3) + (bx >> 3);
-    const long long m0 = (long long)bx * BM;
-    const int co0 = blockIdx.y * BN;
+    int mt, nt;
+    tile_coords((int)((g.M + BM - 1) / BM), (g.Co + BN - 1) / BN, mt, nt);
+    const long long m0 = (long long)mt * BM;
+    const int co0 = nt * BN;
     const int kbeg = blockIdx.z * A.k_per_split;
     const int kend = (int)min((long long)kbeg + A.k_per_split, g.K);
     const int nk = (kend - kbeg + BK - 1) / BK;
@@ -532,7 +557,7 @@ template <typename S, int FEED, bool AVEC, bool BVEC, bool OUT_NCHW>
 static hipError_t launch_tile(const GemmArgs &a, int tile, int splits, hipStream_t st) {
     const Geom &g = a.g;
     auto go = [&](auto kern, int BM, int BN) {
-        dim3 grid((unsigned)((g.M + BM - 1) / BM), (unsigned)((g.Co + BN - 1) / BN), (unsigned)splits);
+        dim3 grid((unsigned)(((g.M + BM - 1) / BM) * ((g.Co + BN - 1) / BN)), 1, (unsigned)splits);
         hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, st, a);
         return hipGetLastError();
     };
@@ -542,6 +567,7 @@ static hipError_t launch_tile(const GemmArgs &a, int tile, int splits, hipStream
             case TILE_128x128: return go(igemm_dma_kernel<S, FEED, OUT_NCHW, 128, 128, BKW>, 128, 128);
             case TILE_128x64: return go(igemm_dma_kernel<S, FEED, OUT_NCHW, 128, 64, BKW>, 128, 64);
             case TILE_32x64: return go(igemm_dma_kernel<S, FEED, OUT_NCHW, 32, 64, BKW>, 32, 64);
+            case TILE_256x128: return go(igemm_dma_kernel<S, FEED, OUT_NCHW, 256, 128, BKW>, 256, 128);
             default: return hipErrorInvalidValue;
         }
     } else {  // element gathers through registers
