@@ -24,8 +24,9 @@ struct Plan {
     bool out_nchw;
     int tile, splits, kps;
     bool need_ibuf, need_win, need_wpack;
+    bool need_xcl;  // channels-last copy of an NCHW input
     bool rows16;  // the feed can read X_col rows in 16-byte chunks (by shape)
-    size_t off_ibuf, off_win, off_wpack, off_part, total;
+    size_t off_ibuf, off_win, off_xcl, off_wpack, off_part, total;
     size_t esize;
 };
 
@@ -94,8 +95,22 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
                 return CONV_ERR_UNSUPPORTED;
             break;
         case CONV_ALGO_INDIRECT:
-            pl->feed = pl->nhwc ? FEED_IND_NHWC : FEED_IND_NCHW;
+            // The indirection buffer addresses each input pixel's row of C
+            // channels.  An NCHW input whose rows can be read in 16-byte
+            // chunks is first copied channels-last (|x| bytes of workspace);
+            // otherwise the buffer addresses channel 0 of the pixel and the
+            // main loop steps through the channel planes element by element.
             pl->need_ibuf = true;
+            if (pl->nhwc) {
+                pl->feed = FEED_IND_NHWC;
+            } else if (g.C % (pl->bf16 ? 8 : 4) == 0 && 256LL * g.T <= 3072 &&
+                       (long long)g.T * g.Ho * g.Wo >= 2LL * g.H * g.W) {  // copy well below im2col
+                pl->feed = FEED_IND_NHWC;
+                pl->need_xcl = true;
+                pl->need_wpack = g.T > 1;  // OIHW regrouped to (kh, kw, ci) order
+            } else {
+                pl->feed = FEED_IND_NCHW;
+            }
             break;
         case CONV_ALGO_IM2WIN:
             pl->feed = FEED_WIN;
@@ -159,6 +174,10 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     if (pl->need_win) {
         pl->off_win = off;
         off = align_up(off + (size_t)g.N * g.Ho * g.Wwin * g.KH * g.C * pl->esize);
+    }
+    if (pl->need_xcl) {
+        pl->off_xcl = off;
+        off = align_up(off + (size_t)g.N * g.C * g.H * g.W * pl->esize);
     }
     if (pl->need_wpack) {
         pl->off_wpack = off;
@@ -252,14 +271,21 @@ conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias
     a.b = w;
     a.a_src = x;
 
+    // Offsets of the indirection buffer follow the layout the main loop reads.
+    const bool ib_rows = pl.feed == FEED_IND_NHWC;
     if (pl.need_ibuf) {
         if (prebuilt) {
             a.ibuf = prebuilt;
         } else {
             int32_t *ib = (int32_t *)(ws + pl.off_ibuf);
-            if (launch_build_indirection(ib, g, pl.nhwc, s) != hipSuccess) return CONV_ERR_HIP;
+            if (launch_build_indirection(ib, g, ib_rows, s) != hipSuccess) return CONV_ERR_HIP;
             a.ibuf = ib;
         }
+    }
+    if (pl.need_xcl) {
+        void *xc = ws + pl.off_xcl;
+        if (launch_nchw_to_nhwc(x, xc, g, pl.bf16, s) != hipSuccess) return CONV_ERR_HIP;
+        a.a_src = xc;
     }
     if (pl.need_win) {
         void *xw = ws + pl.off_win;

@@ -14,7 +14,7 @@ namespace convlower {
 enum Feed : int {
     FEED_ROWMAJOR = 0,  // A = the input itself as an [M][K] matrix (1x1 NHWC, whole-input kernel); K natural
     FEED_NCHW_1X1 = 1,  // A[m][ci] = x[n][ci][pixel] (1x1 stride-1 NCHW); K = ci
-    FEED_IND_NHWC = 2,  // through the indirection buffer, NHWC input; K = (kh, kw, ci)
+    FEED_IND_NHWC = 2,  // through the indirection buffer, channels-last input; K = (kh, kw, ci)
     FEED_IND_NCHW = 3,  // through the indirection buffer, NCHW input; K = (ci, kh, kw)
     FEED_WIN = 4,       // out of the window-ordered tensor (either input layout); K = (kh, kw, ci)
 };
@@ -50,6 +50,7 @@ hipError_t launch_splitk_reduce(const float *part, const void *bias, void *y, co
 hipError_t launch_build_indirection(int32_t *buf, const Geom &g, bool nhwc, hipStream_t st);
 hipError_t launch_im2win(const void *x, void *xwin, const Geom &g, bool nhwc, bool bf16,
                          hipStream_t st);
+hipError_t launch_nchw_to_nhwc(const void *x, void *x_cl, const Geom &g, bool bf16, hipStream_t st);
 hipError_t launch_pack_weights_ohwi(const void *w_oihw, void *w_ohwi, const Geom &g, bool bf16,
                                     hipStream_t st);
 

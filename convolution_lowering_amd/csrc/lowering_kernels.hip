@@ -1,7 +1,8 @@
 // The lowering steps that run before (or after) the main loop:
 //   (b) the indirection-buffer builder (The Indirect Convolution Algorithm, abstract),
 //   (a) the im2win window reorder ("Im2win: An Efficient Convolution Paradigm on GPU", abstract),
-//   the OIHW -> OHWI weight regrouping the window feed needs for NCHW weights,
+//   the NCHW -> NHWC copy and the OIHW -> OHWI weight regrouping that let
+//   NCHW tensors use the channels-last feeds,
 //   and the ordered split-K finishing pass.
 #include "conv_internal.h"
 
@@ -129,6 +130,82 @@ static hipError_t im2win_typed(const void *x, void *xw, const Geom &g, bool nhwc
 
 hipError_t launch_im2win(const void *x, void *xwin, const Geom &g, bool nhwc, bool bf16, hipStream_t st) {
     return bf16 ? im2win_typed<uint16_t>(x, xwin, g, nhwc, st) : im2win_typed<float>(x, xwin, g, nhwc, st);
+}
+
+// NCHW -> NHWC copy (each image's [C][H*W] matrix transposed to [H*W][C]).
+// A block moves a tile of 64 channels x 64*VEC/... pixels: 16-byte loads run
+// along the pixels of one channel, the tile is transposed through LDS, and
+// 16-byte stores run along the channels of one pixel.  Used when H*W and C
+// are multiples of the 16-byte element count (otherwise the window reorder
+// of a 1x1 kernel, which is the same copy element by element, does it).
+template <typename S>
+__global__ __launch_bounds__(256) void nchw_to_nhwc_kernel(const S *__restrict__ x, S *__restrict__ xc, int C,
+                                                           int HW, int tiles_hw) {
+    constexpr int V = 16 / (int)sizeof(S);  // elements per 16 bytes
+    constexpr int TC = 64;                  // channels per tile
+    constexpr int THW = 128;                // pixels per tile
+    __shared__ S tile[TC][THW + 2];
+    const int tid = threadIdx.x;
+    const long long n = blockIdx.y;
+    const int c0 = blockIdx.z * TC;
+    const int hw0 = blockIdx.x * THW;
+    const S *src = x + n * (long long)C * HW;
+    S *dst = xc + n * (long long)C * HW;
+    // load: chunk q covers pixels hw0 + (q % (THW/V))*V .. +V of channel q / (THW/V)
+    constexpr int CPR = THW / V;  // chunks per channel row
+    for (int q = tid; q < TC * CPR; q += 256) {
+        const int cl = q / CPR, hl = (q % CPR) * V;
+        const int c = c0 + cl, hw = hw0 + hl;
+        union {
+            uint4 v;
+            S e[V];
+        } u;
+        u.v = make_uint4(0, 0, 0, 0);
+        if (c < C && hw < HW) u.v = *(const uint4 *)(src + (long long)c * HW + hw);  // HW % V == 0
+#pragma unroll
+        for (int j = 0; j < V; ++j) tile[cl][hl + j] = u.e[j];
+    }
+    __syncthreads();
+    // store: chunk q covers channels c0 + (q % (TC/V))*V .. +V of pixel q / (TC/V)
+    constexpr int CPP = TC / V;  // chunks per pixel
+    for (int q = tid; q < THW * CPP; q += 256) {
+        const int hl = q / CPP, cl = (q % CPP) * V;
+        const int c = c0 + cl, hw = hw0 + hl;
+        if (c >= C || hw >= HW) continue;
+        union {
+            uint4 v;
+            S e[V];
+        } u;
+#pragma unroll
+        for (int j = 0; j < V; ++j) u.e[j] = tile[cl + j][hl];
+        *(uint4 *)(dst + (long long)hw * C + c) = u.v;  // C % V == 0
+    }
+}
+
+hipError_t launch_nchw_to_nhwc(const void *x, void *x_cl, const Geom &g, bool bf16, hipStream_t st) {
+    const int HW = g.H * g.W, V = bf16 ? 8 : 4;
+    const bool aligned = (uintptr_t)x % 16 == 0 && (uintptr_t)x_cl % 16 == 0;
+    if (HW % V == 0 && g.C % V == 0 && aligned) {
+        const int tiles_hw = (HW + 127) / 128;
+        dim3 grid(tiles_hw, g.N, (g.C + 63) / 64);
+        if (bf16)
+            hipLaunchKernelGGL(nchw_to_nhwc_kernel<uint16_t>, grid, dim3(256), 0, st, (const uint16_t *)x,
+                               (uint16_t *)x_cl, g.C, HW, tiles_hw);
+        else
+            hipLaunchKernelGGL(nchw_to_nhwc_kernel<float>, grid, dim3(256), 0, st, (const float *)x, (float *)x_cl,
+                               g.C, HW, tiles_hw);
+        return hipGetLastError();
+    }
+    // The window-ordered tensor of a 1x1 stride-1 unpadded kernel is [N][H][W][1][C].
+    Geom one = g;
+    one.KH = one.KW = one.s = one.d = 1;
+    one.p = 0;
+    one.Ho = g.H;
+    one.Wo = g.W;
+    one.Wwin = g.W;
+    one.P = HW;
+    one.T = 1;
+    return launch_im2win(x, x_cl, one, false, bf16, st);
 }
 
 // ---------------------------------------------------------------------------

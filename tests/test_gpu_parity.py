@@ -194,6 +194,8 @@ EDGE = [
     ("Co-1", 2, 8, 10, 10, 1, 3, 3, 1, 1, 1),
     ("many-channels-skinny", 2, 300, 3, 3, 40, 3, 3, 1, 0, 1),
     ("C-multiple-of-8", 2, 24, 13, 15, 130, 3, 3, 1, 1, 1),
+    ("channels-last-copy", 3, 16, 8, 12, 20, 3, 3, 1, 1, 1),     # NCHW copied channels-last, ragged tiles
+    ("channels-last-copy-wide", 2, 72, 16, 10, 40, 3, 3, 2, 1, 1),
 ]
 
 
