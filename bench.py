@@ -124,24 +124,26 @@ def bench_layer(L, dtype, layout, algo, steps, warmup, flush):
 
 
 def main_loop_time(L, dtype, layout, steps, warmup, flush):
-    """HIP-event time of the INDIRECT main loop alone (the dominant kernel),
-    reading a prebuilt indirection buffer."""
+    """HIP-event time of the dominant kernel -- the MFMA main loop with its
+    fused epilogue -- alone, via conv2d_main_loop on operands lowered
+    beforehand (channels-last input, NHWC indirection buffer, OHWI weights;
+    the lowering itself is not timed here).  Output in `layout`."""
     import torch
     import convolution_lowering_amd as cl
     from convolution_lowering_amd.workloads import make_inputs
-    x, w, b = make_inputs(L, dtype, layout)
+    x, w, b = make_inputs(L, dtype, "NHWC")
     x, w, b = x.cuda(), w.cuda(), b.cuda()
     Ho, Wo = layer_geometry(L)
     shape = (L.N, L.Co, Ho, Wo) if layout == "NCHW" else (L.N, Ho, Wo, L.Co)
     y = torch.empty(shape, dtype=x.dtype, device="cuda")
-    ib = cl.build_indirection(L.C, L.H, L.W, L.KH, L.KW, L.stride, L.pad, L.dilation, layout)
-    ws_bytes = cl.workspace_size(L.N, L.C, L.H, L.W, L.Co, L.KH, L.KW, L.stride, L.pad, L.dilation, layout, dtype,
+    ib = cl.build_indirection(L.C, L.H, L.W, L.KH, L.KW, L.stride, L.pad, L.dilation, "NHWC")
+    ws_bytes = cl.workspace_size(L.N, L.C, L.H, L.W, L.Co, L.KH, L.KW, L.stride, L.pad, L.dilation, "NHWC", dtype,
                                  "indirect")
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
 
     def step():
-        cl.conv2d_fwd_indirect_prebuilt(x, w, b, ib, L.stride, L.pad, L.dilation, layout, out=y,
-                                        workspace=ws[:ws_bytes])
+        cl.conv2d_main_loop(x, ib, w, b, None, L.stride, L.pad, L.dilation, "indirect", layout, out=y,
+                            workspace=ws[:ws_bytes], x_dims=(L.N, L.C, L.H, L.W))
 
     return time_steps(step, steps, warmup, flush)
 
@@ -169,25 +171,36 @@ def measured_traffic(kernel, workload):
     return ent.get("bytes_per_launch")
 
 
-def cpu_baseline(L, dtype, layout, budget_s=12.0):
-    """The fp64 oracle (untuned) on a bounded sample of the headline layer:
-    whole images, as many as fit in about budget_s seconds (at least one)."""
+def cpu_baseline(L, dtype, layout, budget_s=10.0):
+    """The fp64 oracle (untuned) on the headline layer's whole batch, repeated
+    until about budget_s seconds have passed (at least once); its mean rate."""
     import oracle
     from convolution_lowering_amd.workloads import make_inputs
     Ho, Wo = layer_geometry(L)
     lay = oracle.NCHW if layout == "NCHW" else oracle.NHWC
-    x, w, b = make_inputs(L, dtype, layout, N=1)
-    t0 = time.perf_counter()
-    oracle.conv2d(x, w, b, L.stride, L.pad, L.dilation, lay, want_norm=False)
-    t1 = time.perf_counter() - t0
-    n = int(max(1, min(L.N, budget_s // max(t1, 1e-3))))
-    x, w, b = make_inputs(L, dtype, layout, N=n)
-    t0 = time.perf_counter()
-    oracle.conv2d(x, w, b, L.stride, L.pad, L.dilation, lay, want_norm=False)
-    t = time.perf_counter() - t0
-    flops = 2.0 * n * L.Co * Ho * Wo * L.C * L.KH * L.KW
+    x, w, b = make_inputs(L, dtype, layout)
+    reps, t = 0, 0.0
+    while reps == 0 or t < budget_s:
+        t0 = time.perf_counter()
+        oracle.conv2d(x, w, b, L.stride, L.pad, L.dilation, lay, want_norm=False)
+        t += time.perf_counter() - t0
+        reps += 1
+    flops = layer_flops(L, Ho, Wo) * reps
     return {"value": flops / t / 1e12, "unit": "TFLOPS", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{n} of {L.N} images of the headline layer, full output, fp64, {t:.1f} s"}
+            "sample": f"the whole batch ({L.N} images) of the headline layer, full fp64 output, "
+                      f"{reps} repetition(s), {t:.1f} s"}
+
+
+def calibration_copy(nbytes=256 << 20):
+    """One plain device copy of known size, so HBM byte counters read in the
+    same profiled run can be scaled (bytes read and written = nbytes each)."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    a.fill_(3)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
 
 
 def main():
@@ -197,6 +210,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--layers", choices=["all", "headline"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="also run one 256 MiB device copy (scale reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path (each GPU would run its own "
@@ -222,8 +237,8 @@ def main():
     flops = layer_flops(H, Ho, Wo)
     nbytes = algorithmic_bytes(H, Ho, Wo, head_dtype)
     rl = roofline(flops, nbytes, ml_ms / 1e3, head_dtype)
-    rl["traffic"] = measured_traffic("igemm_kernel", "C2-bf16-NCHW-indirect")
-    rl["kernel"] = "igemm_kernel (implicit-GEMM main loop + fused epilogue, indirect feed)"
+    rl["traffic"] = measured_traffic("igemm_dma_kernel", "C2-bf16-NCHW-main-loop")
+    rl["kernel"] = "igemm_dma_kernel (MFMA implicit-GEMM main loop + fused bias epilogue, indirect feed)"
     rl["ms"] = ml_ms
     rl["per_launch_flops"] = flops
     rl["per_launch_algorithmic_bytes"] = nbytes
@@ -247,6 +262,9 @@ def main():
                               f"{r.get('roofline', {}).get('bound', '?')} "
                               f"frac {r.get('roofline', {}).get('frac', float('nan')):.3f}", file=sys.stderr, flush=True)
                         torch.cuda.empty_cache()
+
+    if args.calibration_copy:
+        calibration_copy()
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -24,7 +24,7 @@ STATUS = {0: "CONV_OK", 1: "CONV_ERR_INVALID_ARG", 2: "CONV_ERR_UNSUPPORTED", 3:
 
 # Every symbol include/convlower.h declares.
 EXPORTS = ("conv_status_string", "conv2d_output_size", "conv2d_fwd_workspace_size", "conv2d_im2col_bytes",
-           "conv2d_fwd", "conv2d_fwd_indirect_prebuilt", "conv2d_build_indirection", "conv2d_im2win_transform")
+           "conv2d_fwd", "conv2d_main_loop", "conv2d_build_indirection", "conv2d_im2win_transform")
 
 
 class ConvLowerError(RuntimeError):
@@ -56,8 +56,8 @@ def lib():
     L.conv2d_im2col_bytes.restype = c_int
     L.conv2d_fwd.argtypes = [vp] * 4 + [c_int] * 12 + [vp, vp, c_size, c_int]
     L.conv2d_fwd.restype = c_int
-    L.conv2d_fwd_indirect_prebuilt.argtypes = [vp] * 5 + [c_int] * 12 + [vp, vp, c_size]
-    L.conv2d_fwd_indirect_prebuilt.restype = c_int
+    L.conv2d_main_loop.argtypes = [vp] * 5 + [c_int] * 13 + [vp, vp, c_size]
+    L.conv2d_main_loop.restype = c_int
     L.conv2d_build_indirection.argtypes = [vp] + [c_int] * 9 + [vp]
     L.conv2d_build_indirection.restype = c_int
     L.conv2d_im2win_transform.argtypes = [vp, vp] + [c_int] * 11 + [vp]
@@ -178,19 +178,33 @@ def conv2d_fwd(x, w, bias=None, stride=1, pad=0, dilation=1, layout="NCHW", algo
     return out
 
 
-def conv2d_fwd_indirect_prebuilt(x, w, bias, indirection, stride=1, pad=0, dilation=1, layout="NCHW", out=None,
-                                 workspace=None, stream=None):
-    """The INDIRECT main loop alone, reading through a buffer from build_indirection."""
+def conv2d_main_loop(lowered, indirection, w_ohwi, bias, out_shape_nchw, stride=1, pad=0, dilation=1,
+                     algo="indirect", out_layout="NCHW", out=None, workspace=None, stream=None, x_dims=None):
+    """Steps (c)+(d) on already-lowered operands (see conv2d_main_loop in
+    include/convlower.h).  x_dims = (N, C, H, W) of the original input."""
     import torch
-    if indirection.dtype != torch.int32 or not indirection.is_cuda or not indirection.is_contiguous():
-        raise ValueError("indirection must be a contiguous int32 device tensor")
-    out, dims, ws_ptr, ws_bytes, _ = _prepare(x, w, bias, stride, pad, dilation, layout, "indirect", out,
-                                              workspace)
-    code = lib().conv2d_fwd_indirect_prebuilt(x.data_ptr(), w.data_ptr(),
-                                              bias.data_ptr() if bias is not None else None, out.data_ptr(),
-                                              indirection.data_ptr(), *dims, _stream_handle(stream, x.device),
-                                              ws_ptr, ws_bytes)
-    _check("conv2d_fwd_indirect_prebuilt", code)
+    N, C, H, W = x_dims
+    Co, KH, KW = w_ohwi.shape[0], w_ohwi.shape[1], w_ohwi.shape[2]
+    dev = lowered.device
+    _check_tensor(lowered, "lowered", lowered.dtype, dev)
+    _check_tensor(w_ohwi, "w_ohwi", lowered.dtype, dev)
+    if bias is not None:
+        _check_tensor(bias, "bias", lowered.dtype, dev)
+    dcode = _dtype_code(lowered.dtype)
+    Ho, Wo = output_size(H, W, KH, KW, stride, pad, dilation)
+    shape = (N, Co, Ho, Wo) if out_layout == "NCHW" else (N, Ho, Wo, Co)
+    if out is None:
+        out = torch.empty(shape, dtype=lowered.dtype, device=dev)
+    need = workspace_size(N, C, H, W, Co, KH, KW, stride, pad, dilation, "NHWC", "bf16" if dcode else "fp32", algo)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    code = lib().conv2d_main_loop(lowered.data_ptr(), indirection.data_ptr() if indirection is not None else None,
+                                  w_ohwi.data_ptr(), bias.data_ptr() if bias is not None else None, out.data_ptr(),
+                                  N, C, H, W, Co, KH, KW, stride, pad, dilation, ALGOS[algo], LAYOUTS[out_layout],
+                                  dcode, _stream_handle(stream, dev),
+                                  workspace.data_ptr() if workspace is not None else None,
+                                  workspace.numel() if workspace is not None else 0)
+    _check("conv2d_main_loop", code)
     return out
 
 

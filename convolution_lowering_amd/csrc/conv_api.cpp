@@ -247,6 +247,7 @@ namespace {
 
 // The launch sequence of one call.  `prebuilt` (may be null) is an
 // indirection buffer the caller built before; then step (b) is skipped.
+// Steps the plan does not ask for (need_*) are not run.
 conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias, void *y, const int32_t *prebuilt,
                   conv_stream_t stream, void *workspace, size_t workspace_bytes) {
     if (!x || !w || !y) return CONV_ERR_INVALID_ARG;
@@ -273,14 +274,12 @@ conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias
 
     // Offsets of the indirection buffer follow the layout the main loop reads.
     const bool ib_rows = pl.feed == FEED_IND_NHWC;
-    if (pl.need_ibuf) {
-        if (prebuilt) {
-            a.ibuf = prebuilt;
-        } else {
-            int32_t *ib = (int32_t *)(ws + pl.off_ibuf);
-            if (launch_build_indirection(ib, g, ib_rows, s) != hipSuccess) return CONV_ERR_HIP;
-            a.ibuf = ib;
-        }
+    if (prebuilt) {
+        a.ibuf = prebuilt;
+    } else if (pl.need_ibuf) {
+        int32_t *ib = (int32_t *)(ws + pl.off_ibuf);
+        if (launch_build_indirection(ib, g, ib_rows, s) != hipSuccess) return CONV_ERR_HIP;
+        a.ibuf = ib;
     }
     if (pl.need_xcl) {
         void *xc = ws + pl.off_xcl;
@@ -311,8 +310,10 @@ conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias
     bool b_vec = g.K % VEC == 0 && al16(a.b);
     // The vector paths address A and B with 32-bit buffer offsets.
     const long long kBufMax = (1LL << 31) - 64;
-    long long a_bytes = (long long)pl.esize *
-                        (pl.need_win ? (long long)g.N * g.Ho * g.Wwin * g.KH * g.C : (long long)g.N * g.C * g.H * g.W);
+    // The extent of what the A feed reads: the window tensor for im2win
+    // (built here or handed in), else the input or its channels-last copy.
+    long long a_bytes = (long long)pl.esize * (pl.feed == FEED_WIN ? (long long)g.N * g.Ho * g.Wwin * g.KH * g.C
+                                                                   : (long long)g.N * g.C * g.H * g.W);
     long long b_bytes = (long long)pl.esize * g.Co * g.K;
     if (a_bytes > kBufMax) a_vec = false;
     if (b_bytes > kBufMax) a_vec = b_vec = false;
@@ -348,17 +349,21 @@ conv_status_t conv2d_fwd(const void *x, const void *w, const void *bias, void *y
     return run(pl, x, w, bias, y, nullptr, stream, workspace, workspace_bytes);
 }
 
-conv_status_t conv2d_fwd_indirect_prebuilt(const void *x, const void *w, const void *bias, void *y,
-                                           const int32_t *indirection, int N, int C_in, int H, int W, int C_out,
-                                           int KH, int KW, int stride, int pad, int dilation, conv_layout_t layout,
-                                           conv_dtype_t dtype, conv_stream_t stream, void *workspace,
-                                           size_t workspace_bytes) {
+conv_status_t conv2d_main_loop(const void *lowered, const int32_t *indirection, const void *w_ohwi, const void *bias,
+                               void *y, int N, int C_in, int H, int W, int C_out, int KH, int KW, int stride, int pad,
+                               int dilation, conv_algo_t algo, conv_layout_t out_layout, conv_dtype_t dtype,
+                               conv_stream_t stream, void *workspace, size_t workspace_bytes) {
+    if (algo != CONV_ALGO_INDIRECT && algo != CONV_ALGO_IM2WIN) return CONV_ERR_INVALID_ARG;
+    if (out_layout != CONV_LAYOUT_NCHW && out_layout != CONV_LAYOUT_NHWC) return CONV_ERR_INVALID_ARG;
+    // The lowered operands are channels-last, so plan as for an NHWC call.
     Plan pl;
     conv_status_t st =
-        make_plan(N, C_in, H, W, C_out, KH, KW, stride, pad, dilation, layout, dtype, CONV_ALGO_INDIRECT, &pl);
+        make_plan(N, C_in, H, W, C_out, KH, KW, stride, pad, dilation, CONV_LAYOUT_NHWC, dtype, algo, &pl);
     if (st != CONV_OK) return st;
-    if (!indirection || (uintptr_t)indirection % 4) return CONV_ERR_INVALID_ARG;
-    return run(pl, x, w, bias, y, indirection, stream, workspace, workspace_bytes);
+    if (algo == CONV_ALGO_INDIRECT && (!indirection || (uintptr_t)indirection % 4)) return CONV_ERR_INVALID_ARG;
+    pl.out_nchw = out_layout == CONV_LAYOUT_NCHW;
+    pl.need_ibuf = pl.need_win = pl.need_xcl = pl.need_wpack = false;
+    return run(pl, lowered, w_ohwi, bias, y, indirection, stream, workspace, workspace_bytes);
 }
 
 conv_status_t conv2d_build_indirection(int32_t *buf, int C_in, int H, int W, int KH, int KW, int stride, int pad,

@@ -120,20 +120,28 @@ conv_status_t conv2d_fwd(const void *x, const void *w, const void *bias, void *y
                          conv_layout_t layout, conv_dtype_t dtype, conv_stream_t stream,
                          void *workspace, size_t workspace_bytes, conv_algo_t algo);
 
-/* Steps (c) and (d) alone: the main loop and epilogue of the INDIRECT
- * algorithm, reading X_col through an indirection buffer the caller built
- * earlier with conv2d_build_indirection for the same geometry and layout.
- * The buffer depends only on the geometry (never on x, w or the batch
- * index), so one build can serve every later call of that shape.
- * `workspace` needs at least conv2d_fwd_workspace_size(..., CONV_ALGO_INDIRECT)
- * bytes (only its split-K part is used).  Other arguments and errors as for
- * conv2d_fwd; a NULL or misaligned `indirection` is CONV_ERR_INVALID_ARG. */
-conv_status_t conv2d_fwd_indirect_prebuilt(const void *x, const void *w, const void *bias, void *y,
-                                           const int32_t *indirection,
-                                           int N, int C_in, int H, int W, int C_out, int KH, int KW,
-                                           int stride, int pad, int dilation,
-                                           conv_layout_t layout, conv_dtype_t dtype, conv_stream_t stream,
-                                           void *workspace, size_t workspace_bytes);
+/* Steps (c) and (d) alone -- the MFMA main loop and its fused epilogue -- on
+ * operands that are already lowered, for callers that keep the lowering
+ * between calls (the indirection buffer depends only on the geometry, the
+ * regrouped weights only on w):
+ *   lowered      CONV_ALGO_INDIRECT: the input channels-last, [N][H][W][C_in];
+ *                CONV_ALGO_IM2WIN: the window-ordered tensor that
+ *                conv2d_im2win_transform writes.
+ *   indirection  CONV_ALGO_INDIRECT: a buffer from conv2d_build_indirection
+ *                for the same geometry with CONV_LAYOUT_NHWC; ignored (may
+ *                be NULL) for CONV_ALGO_IM2WIN.
+ *   w_ohwi       weights as [C_out][KH][KW][C_in].
+ *   out_layout   layout of y: [N][C_out][Ho][Wo] (NCHW) or [N][Ho][Wo][C_out].
+ *   workspace    at least conv2d_fwd_workspace_size(..., CONV_LAYOUT_NHWC,
+ *                dtype, algo) bytes (only its split-K part is used).
+ * Other arguments and errors as for conv2d_fwd; any algo other than INDIRECT
+ * or IM2WIN is CONV_ERR_INVALID_ARG. */
+conv_status_t conv2d_main_loop(const void *lowered, const int32_t *indirection, const void *w_ohwi,
+                               const void *bias, void *y,
+                               int N, int C_in, int H, int W, int C_out, int KH, int KW,
+                               int stride, int pad, int dilation, conv_algo_t algo,
+                               conv_layout_t out_layout, conv_dtype_t dtype, conv_stream_t stream,
+                               void *workspace, size_t workspace_bytes);
 
 /* Step (b) on its own: build the indirection buffer of The Indirect
  * Convolution Algorithm (abstract) into `buf` (device, int32, Ho*Wo*KH*KW

@@ -138,6 +138,11 @@ def test_fwd_rejects_before_launch():
     bad = (2, 4, 8, 8, 4, 30, 3, 1, 1, 1, 0, 1, None)
     assert L.conv2d_fwd(fake, fake, None, fake, *bad, fake, 1 << 20, 1) == INVALID
     assert L.conv2d_build_indirection(None, 4, 8, 8, 3, 3, 1, 1, 1, 0, None) == INVALID
+    # the main-loop entry takes only the two lowerings, and needs the buffer for INDIRECT
+    assert L.conv2d_main_loop(fake, fake, fake, None, fake, 2, 8, 8, 8, 4, 3, 3, 1, 1, 1, 0, 0, 1, None, fake,
+                              1 << 20) == INVALID
+    assert L.conv2d_main_loop(fake, None, fake, None, fake, 2, 8, 8, 8, 4, 3, 3, 1, 1, 1, 1, 0, 1, None, fake,
+                              1 << 20) == INVALID
     assert L.conv2d_im2win_transform(None, fake, 1, 4, 8, 8, 3, 3, 1, 1, 1, 0, 1, None) == INVALID
 
 

@@ -291,3 +291,31 @@ def test_im2win_contents(geom, layout, dtype):
     torch.cuda.synchronize()
     ref = oracle.im2win(x, KH, KW, s, p, d, oracle.NCHW)
     assert np.array_equal(out.double().cpu().numpy(), ref)
+
+
+# --- the main loop on its own, on operands lowered beforehand -------------------
+
+@pytest.mark.parametrize("algo", ["indirect", "im2win"])
+@pytest.mark.parametrize("out_layout", ["NCHW", "NHWC"])
+@pytest.mark.parametrize("name", ["C2", "C5a", "C3e"])
+def test_main_loop_entry_matches_full_call(name, algo, out_layout):
+    """conv2d_main_loop on a channels-last input (or window tensor), an NHWC
+    indirection buffer and OHWI weights gives the same bits as conv2d_fwd."""
+    L = LAYERS[name]
+    n = 2
+    x, w, b = make_inputs(L, "bf16", "NHWC", N=n)
+    _say(f"[gpu] main-loop {name} {algo} {out_layout}")
+    xd, wd, bd = x.to(DEV), w.to(DEV), b.to(DEV)
+    y_ref = cl.conv2d_fwd(xd, wd, bd, L.stride, L.pad, L.dilation, "NHWC", algo)
+    if algo == "indirect":
+        lowered = xd
+        ib = cl.build_indirection(L.C, L.H, L.W, L.KH, L.KW, L.stride, L.pad, L.dilation, "NHWC")
+    else:
+        lowered = cl.im2win_transform(xd, L.KH, L.KW, L.stride, L.pad, L.dilation, "NHWC")
+        ib = None
+    y = cl.conv2d_main_loop(lowered, ib, wd, bd, None, L.stride, L.pad, L.dilation, algo, out_layout,
+                            x_dims=(n, L.C, L.H, L.W))
+    torch.cuda.synchronize()
+    if out_layout == "NCHW":
+        y = y.permute(0, 2, 3, 1)
+    assert torch.equal(y.contiguous().view(torch.int16), y_ref.view(torch.int16))
