@@ -15,7 +15,9 @@ constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
-int tile_rows(int tile) { return tile == TILE_32x64 ? 32 : tile == TILE_256x128 ? 256 : 128; }
+int tile_rows(int tile) {
+    return tile == TILE_32x64 ? 32 : (tile == TILE_256x128 || tile == TILE_256x128_DUAL) ? 256 : 128;
+}
 
 struct Plan {
     Geom g;
@@ -133,28 +135,50 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
         default: rows16 = false;
     }
     pl->rows16 = rows16;
+    // The two-blocks-per-CU main loop: 64-byte K tiles that stay inside one
+    // tap (C a multiple of the tile), and an indirection slice of at most 12
+    // taps whose entries divided by C fit 16 bits.
+    const int BKD = pl->bf16 ? 32 : 16;
+    bool dual = rows16;
+    switch (pl->feed) {
+        case FEED_ROWMAJOR: break;
+        case FEED_WIN: dual = dual && g.C % BKD == 0; break;
+        case FEED_IND_NHWC: dual = dual && g.C % BKD == 0 && g.T <= 12 && (long long)g.H * g.W <= 65535; break;
+        default: dual = false;
+    }
     int BM, BN;
     if (g.M <= 64) {
         pl->tile = TILE_32x64; BM = 32; BN = 64;
     } else if (g.Co <= 64) {
         pl->tile = TILE_128x64; BM = 128; BN = 64;
+    } else if (dual) {
+        pl->tile = TILE_256x128_DUAL; BM = 256; BN = 128;
     } else if (rows16 && g.M >= 65536) {
         pl->tile = TILE_256x128; BM = 256; BN = 128;
     } else {
         pl->tile = TILE_128x128; BM = 128; BN = 128;
     }
+    // Workspace regions other than the split-K partials.
+    size_t lowered = 0;
+    if (pl->need_ibuf) lowered = align_up(lowered + (size_t)g.P * g.T * sizeof(int32_t));
+    if (pl->need_win) lowered = align_up(lowered + (size_t)g.N * g.Ho * g.Wwin * g.KH * g.C * pl->esize);
+    if (pl->need_xcl) lowered = align_up(lowered + (size_t)g.N * g.C * g.H * g.W * pl->esize);
+    if (pl->need_wpack) lowered = align_up(lowered + (size_t)g.Co * g.K * pl->esize);
+
     const int BK = pl->bf16 ? 64 : 32;  // the main loop's K tile (128-byte LDS rows)
     long long blocks = ((g.M + BM - 1) / BM) * ((g.Co + BN - 1) / BN);
     long long ktiles = (g.K + BK - 1) / BK;
     int splits = 1;
     if (blocks < 256 && ktiles >= 16) {
         // Enough splits to give every compute unit work, each split at least
-        // 4 K tiles, and the fp32 partials kept below the im2col footprint.
+        // 4 K tiles, and the whole workspace (partials included) kept below
+        // the im2col footprint.
         long long want = (512 + blocks - 1) / blocks;
         long long by_depth = ktiles / 4;
         long long im2col_bytes = g.M * g.K * (long long)pl->esize;
-        long long per_split = g.M * g.Co * 4LL;
-        long long by_space = (im2col_bytes - 1) / per_split;
+        long long per_split = (long long)align_up((size_t)(g.M * g.Co * 4LL));
+        long long room = im2col_bytes - (long long)lowered - 1;
+        long long by_space = room > 0 ? room / per_split : 0;
         long long sp = want;
         if (sp > by_depth) sp = by_depth;
         if (sp > by_space) sp = by_space;
@@ -324,7 +348,18 @@ conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias
     // Misaligned pointers fall back to the element-gather loop, which has no
     // 256x128 variant; the split count (and so the workspace) is unchanged.
     int tile = pl.tile;
-    if (!a_vec && tile == TILE_256x128) tile = TILE_128x128;
+    if (!a_vec && (tile == TILE_256x128 || tile == TILE_256x128_DUAL)) tile = TILE_128x128;
+    {
+        uint32_t c = (uint32_t)g.C, sh = 0;
+        while (!(c & 1u)) {
+            c >>= 1;
+            ++sh;
+        }
+        uint32_t inv = c;  // Newton's iteration for the inverse of an odd number modulo 2^32
+        for (int i = 0; i < 5; ++i) inv *= 2u - c * inv;
+        a.c_shift = sh;
+        a.c_inv = inv;
+    }
     hipError_t e = pl.bf16 ? launch_igemm_bf16(a, pl.feed, pl.out_nchw, a_vec, b_vec, tile, pl.splits, s)
                            : launch_igemm_f32(a, pl.feed, pl.out_nchw, a_vec, b_vec, tile, pl.splits, s);
     if (e != hipSuccess) return CONV_ERR_HIP;

@@ -36,10 +36,21 @@ struct GemmArgs {
     int k_per_split;      // multiple of the K tile; == K rounded up when not split
     uint32_t a_bytes;     // size of a_src in bytes (< 2^31 on the vector paths)
     uint32_t b_bytes;     // size of b in bytes (< 2^31 on the vector paths)
+    uint32_t c_shift;     // C = c_odd << c_shift; c_inv * c_odd == 1 (mod 2^32): exact
+    uint32_t c_inv;       // division of a channels-last indirection entry by C
 };
 
 // Tile shapes of the main loop (block = 256 threads = 4 wavefronts, 2x2).
-enum Tile : int { TILE_128x128 = 0, TILE_128x64 = 1, TILE_32x64 = 2, TILE_256x128 = 3, TILE_COUNT = 4 };
+// TILE_256x128_DUAL is the 256 x 128 main loop sized for two resident blocks
+// per compute unit (16-byte-row feeds whose K tiles stay inside one tap).
+enum Tile : int {
+    TILE_128x128 = 0,
+    TILE_128x64 = 1,
+    TILE_32x64 = 2,
+    TILE_256x128 = 3,
+    TILE_256x128_DUAL = 4,
+    TILE_COUNT = 5
+};
 
 hipError_t launch_igemm_bf16(const GemmArgs &a, int feed, bool out_nchw, bool a_vec, bool b_vec,
                              int tile, int splits, hipStream_t st);

@@ -1,0 +1,390 @@
+// The main loop sized so that two blocks share each compute unit: every
+// SIMD then holds one wavefront of each block, and while one of them waits
+// (at its barrier, for its loads, in its prologue or epilogue) or issues its
+// address arithmetic, the other keeps the matrix core busy.
+//
+//   * Block tile 256 x 128 of Y_col, four wavefronts of 128 x 64 each
+//     (v_mfma_f32_32x32x16_bf16 or v_mfma_f32_32x32x2_f32 tiles).  The
+//     fragment reads then cost 6 KB of LDS per 8 MFMAs and the global loads
+//     48 KB per 2 x 512 MFMA cycles per compute unit, both inside what one
+//     compute unit moves.
+//   * K tiles of 64 bytes per row (32 bf16 or 16 fp32 values), three LDS
+//     stages of 24 KB filled by the buffer-load-to-LDS instructions; tile k+3
+//     is issued while tile k is multiplied, so two tiles cover the load
+//     latency.
+//   * The K order is (kh, kw, ci) and every K tile lies inside one tap (the
+//     host asks C to be a multiple of the K tile), so a tile's loads share
+//     one tap and one channel offset.
+//   * The indirection buffer's slice for the block (256 rows x KH*KW taps)
+//     is copied to LDS once, as 16-bit pixel indices (entry / C, 0xFFFF for
+//     a padding tap), which keeps the block at 80 KB of LDS.  The indices a
+//     tile's loads need are read one tile ahead.
+//   * The bias of the block's 128 output channels is staged in LDS.
+//
+// All LDS-refill and read ordering follows the pipeline of igemm_dma.h: each
+// wavefront waits (vmcnt) for its own loads of the tile it is about to read
+// and (lgkmcnt) for its own reads of the stage about to be refilled, then
+// the block barrier makes both hold for all four wavefronts.
+#pragma once
+
+namespace convlower {
+
+constexpr int kDualMaxTaps = 12;  // KH*KW taps the LDS slice of the indirection buffer holds
+
+template <typename S>
+struct DualCfg {
+    static constexpr int BM = 256, BN = 128;
+    static constexpr int ES = (int)sizeof(S);
+    static constexpr int VEC = 16 / ES;
+    static constexpr int KCH = 4;                    // 16-byte chunks per stage row
+    static constexpr int BK = KCH * VEC;             // K values per tile
+    static constexpr int NSLOT = (BM + BN) * KCH;    // 16-byte slots per stage (24 KB)
+    static constexpr int IPW_A = BM * KCH / 64 / 4;  // A loads per wavefront per tile
+    static constexpr int IPW_B = BN * KCH / 64 / 4;  // B loads per wavefront per tile
+    static constexpr int IPW = IPW_A + IPW_B;
+    static constexpr int WPM = BM / 2, WCN = BN / 2;  // wavefront tile
+    static constexpr int MT = 32, TP = WPM / MT, TC = WCN / MT;
+    static constexpr int NG = KCH / 2;  // MFMA K steps per tile (two chunks per step)
+};
+
+// Stage slot of chunk c of row r: rows of 4 chunks (64 bytes); the XOR with
+// bits 1..2 of the row spreads any 8 consecutive rows of one chunk column
+// over distinct 16-byte bank groups.
+__device__ __forceinline__ constexpr int dual_slot(int r, int c) { return r * 4 + (c ^ ((r >> 1) & 3)); }
+
+template <typename S, int FEED, bool OUT_NCHW>
+__device__ __forceinline__ void igemm_dual_body(const GemmArgs &A) {
+    using C = DualCfg<S>;
+    constexpr int BM = C::BM, BN = C::BN, BK = C::BK, VEC = C::VEC, KCH = C::KCH, NSLOT = C::NSLOT;
+    constexpr int IPW_A = C::IPW_A, IPW_B = C::IPW_B, IPW = C::IPW;
+    constexpr int WPM = C::WPM, WCN = C::WCN, TP = C::TP, TC = C::TC, NG = C::NG;
+    constexpr uint32_t ES = (uint32_t)sizeof(S);
+    constexpr bool IND = FEED == FEED_IND_NHWC;
+    constexpr bool TAPS = FEED == FEED_IND_NHWC || FEED == FEED_WIN;  // K tiles inside one tap
+    using MF = MfmaShape<S, 32>;
+    constexpr int NQ = MF::NQ;
+    static_assert(IPW_A * 4 * 64 == BM * KCH && IPW_B * 4 * 64 == BN * KCH, "loads must split evenly");
+
+    __shared__ uint4 st0[NSLOT];
+    __shared__ uint4 st1[NSLOT];
+    __shared__ uint4 st2[NSLOT];
+    __shared__ uint16_t ibs[IND ? BM * kDualMaxTaps : 2];
+    __shared__ float bias_s[BN];
+
+    const Geom &g = A.g;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    int mt, nt;
+    tile_coords((int)((g.M + BM - 1) / BM), (g.Co + BN - 1) / BN, mt, nt);
+    const uint32_t M = (uint32_t)g.M;
+    const uint32_t m0 = (uint32_t)mt * BM;
+    const int co0 = nt * BN;
+    const int kbeg = blockIdx.z * A.k_per_split;
+    const int kend = (int)min((long long)kbeg + A.k_per_split, g.K);
+    const int nk = (kend - kbeg + BK - 1) / BK;
+
+    // ---- prologue: indirection slice and bias to LDS ------------------------
+    // Element e of the slice is tap e % T of tile row e / T, i.e. entry
+    // ((m0 + e / T) mod P) * T + e % T = (m0 mod P) * T + e (mod P*T) of the
+    // buffer: consecutive threads read consecutive entries.  Rows past M
+    // read some valid entry; their loads are out of range anyway.
+    if constexpr (IND) {
+        const uint32_t PT = (uint32_t)g.P * (uint32_t)g.T;
+        uint32_t idx = ((m0 % (uint32_t)g.P) * (uint32_t)g.T + (uint32_t)tid) % PT;
+        int v[kDualMaxTaps];
+#pragma unroll
+        for (int j = 0; j < kDualMaxTaps; ++j) {
+            v[j] = 0;
+            if (j < g.T) v[j] = A.ibuf[idx];
+            idx += kThreads;
+            if (idx >= PT) idx -= PT;
+            if (idx >= PT) idx %= PT;
+        }
+#pragma unroll
+        for (int j = 0; j < kDualMaxTaps; ++j)
+            if (j < g.T)
+                ibs[tid + kThreads * j] =
+                    v[j] < 0 ? (uint16_t)0xFFFF : (uint16_t)(((uint32_t)v[j] >> A.c_shift) * A.c_inv);
+    }
+    if (tid < BN) {
+        const int co = co0 + tid;
+        float b = 0.f;
+        if (A.bias && co < g.Co) b = bits_to_f32(S(), elem_bits((const S *)A.bias, co));
+        bias_s[tid] = b;
+    }
+
+    // ---- per-lane load geometry ---------------------------------------------
+    // Load i of this wavefront covers stage rows (i*4 + wave)*16 .. +15 (A
+    // rows for i < IPW_A, B rows after); lane L fills slot L of it, i.e. row
+    // L/4, chunk (L%4) ^ ((L/8)%4) -- a fixed chunk column kc per lane.
+    const int lrow = lane >> 2;
+    const uint32_t kc = (uint32_t)(((lane & 3) ^ ((lane >> 3) & 3)) * VEC);
+    uint32_t rbA[IPW_A], rbB[IPW_B];
+    int ib_row[IPW_A];
+#pragma unroll
+    for (int i = 0; i < IPW_A; ++i) {
+        const int r = (i * 4 + wave) * 16 + lrow;
+        ib_row[i] = r * g.T;
+        const uint32_t m = m0 + (uint32_t)r;
+        const bool ok = m < M;
+        const uint32_t mm = ok ? m : 0u;
+        const uint32_t n = mm / (uint32_t)g.P;
+        uint32_t base;
+        if constexpr (FEED == FEED_ROWMAJOR) {
+            base = mm * (uint32_t)g.K;
+        } else if constexpr (FEED == FEED_IND_NHWC) {
+            base = n * ((uint32_t)g.H * (uint32_t)g.W * (uint32_t)g.C);
+        } else {  // FEED_WIN
+            const uint32_t p = mm - n * (uint32_t)g.P;
+            const uint32_t ho = p / (uint32_t)g.Wo, wo = p - ho * (uint32_t)g.Wo;
+            base = ((n * (uint32_t)g.Ho + ho) * (uint32_t)g.Wwin + wo * (uint32_t)g.s) * (uint32_t)(g.KH * g.C);
+        }
+        rbA[i] = ok ? base * ES : kOutOfRange;
+    }
+#pragma unroll
+    for (int j = 0; j < IPW_B; ++j) {
+        const int co = co0 + (j * 4 + wave) * 16 + lrow;
+        rbB[j] = co < g.Co ? (uint32_t)co * (uint32_t)g.K * ES : kOutOfRange;
+    }
+
+    const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(A.a_src, A.a_bytes);
+    const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(A.b, A.b_bytes);
+    const uint32_t lds_w = (uint32_t)wave * 1024u;  // this wavefront's first slot group, in bytes
+
+    // Tap and channel offset of the K tiles, advanced one tile at a time:
+    // `iss` for the next tile to issue, `pre` for the tile whose pixel
+    // indices are read next (one ahead of `iss`).
+    int iss_t = 0, iss_ci = 0, pre_t = 0, pre_ci = 0;
+    if constexpr (TAPS) {
+        iss_t = kbeg / g.C;
+        iss_ci = kbeg - iss_t * g.C;
+        pre_t = iss_t;
+        pre_ci = iss_ci;
+    }
+    auto advance = [&](int &t, int &ci) {
+        ci += BK;
+        if (ci >= g.C) {
+            ci -= g.C;
+            ++t;
+        }
+    };
+
+    // Pixel indices (entry / C) of this lane's A rows for the tile at `pre`.
+    uint32_t pix[IPW_A];
+    auto read_pix = [&]() {
+        if constexpr (IND) {
+            const int t = pre_t < g.T ? pre_t : g.T - 1;  // tiles past the end read any valid tap
+#pragma unroll
+            for (int i = 0; i < IPW_A; ++i) pix[i] = ibs[ib_row[i] + t];
+        }
+        if constexpr (TAPS) advance(pre_t, pre_ci);
+    };
+
+    // Issue the loads of K tile kt (block-relative) into stage st.
+    auto issue = [&](int kt, uint4 *st) {
+        const bool live = kt < nk;
+        const uint32_t k0 = (uint32_t)(kbeg + kt * BK);
+        const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr_t)st + lds_w;
+        uint32_t voff[IPW];
+        uint32_t ua = 0;  // this tile's offset within an A row, less kc
+        if constexpr (FEED == FEED_WIN) {
+            const int kh = iss_t / g.KW, kw = iss_t - kh * g.KW;
+            ua = (uint32_t)((kw * g.d * g.KH + kh) * g.C + iss_ci);
+        }
+#pragma unroll
+        for (int i = 0; i < IPW_A; ++i) {
+            uint32_t o;
+            bool valid;
+            if constexpr (FEED == FEED_ROWMAJOR) {
+                o = rbA[i] + (k0 + kc) * ES;
+                valid = k0 + kc < (uint32_t)kend;
+            } else if constexpr (FEED == FEED_IND_NHWC) {
+                o = rbA[i] + (pix[i] * (uint32_t)g.C + (uint32_t)iss_ci + kc) * ES;
+                valid = live && pix[i] != 0xFFFFu;
+            } else {
+                o = rbA[i] + (ua + kc) * ES;
+                valid = live;
+            }
+            voff[i] = valid ? o : kOutOfRange;
+        }
+#pragma unroll
+        for (int j = 0; j < IPW_B; ++j) {
+            const uint32_t o = rbB[j] + (k0 + kc) * ES;
+            voff[IPW_A + j] = k0 + kc < (uint32_t)kend ? o : kOutOfRange;
+        }
+#pragma unroll
+        for (int i = 0; i < IPW_A; ++i) lds_dma16(a_rsrc, voff[i], lds0 + (uint32_t)i * 4096u);
+#pragma unroll
+        for (int j = 0; j < IPW_B; ++j)
+            lds_dma16(b_rsrc, voff[IPW_A + j], lds0 + (uint32_t)(BM * KCH * 16) + (uint32_t)j * 4096u);
+        if constexpr (TAPS) advance(iss_t, iss_ci);
+    };
+
+    typename MF::acc_t acc[TP][TC];
+#pragma unroll
+    for (int ip = 0; ip < TP; ++ip)
+#pragma unroll
+        for (int ic = 0; ic < TC; ++ic) acc[ip][ic] = typename MF::acc_t{};
+
+    const int wp = wave >> 1, wc = wave & 1;
+    const int frow = lane & 31, fch = lane >> 5;
+    uint4 fa[NG][TP], fb[NG][TC];
+    auto lds_read = [&](const uint4 *st, int grp) {
+#pragma unroll
+        for (int ip = 0; ip < TP; ++ip) fa[grp][ip] = st[dual_slot(wp * WPM + ip * 32 + frow, grp * 2 + fch)];
+#pragma unroll
+        for (int ic = 0; ic < TC; ++ic)
+            fb[grp][ic] = st[BM * KCH + dual_slot(wc * WCN + ic * 32 + frow, grp * 2 + fch)];
+    };
+    auto mfma_group = [&](int grp) {
+#pragma unroll
+        for (int ip = 0; ip < TP; ++ip)
+#pragma unroll
+            for (int ic = 0; ic < TC; ++ic) {
+                if constexpr (OUT_NCHW)
+                    MF::mma(fa[grp][ip], fb[grp][ic], acc[ip][ic]);
+                else
+                    MF::mma(fb[grp][ic], fa[grp][ip], acc[ip][ic]);
+            }
+    };
+    // Tile kt: its fragments are in registers; st_cur (where it came from)
+    // receives tile kt+3 after the barrier, and tile kt+1's fragments are read
+    // from st_next, each register group as soon as its MFMAs are issued.
+    auto phase = [&](int kt, uint4 *st_cur, const uint4 *st_next) {
+        mfma_group(0);
+        __builtin_amdgcn_sched_barrier(0);
+        CONVLOWER_WAIT_VMCNT_LDS(IPW);
+        block_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        issue(kt + 3, st_cur);
+        __builtin_amdgcn_sched_barrier(0);
+        lds_read(st_next, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int grp = 1; grp < NG; ++grp) {
+            mfma_group(grp);
+            __builtin_amdgcn_sched_barrier(0);
+            lds_read(st_next, grp);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        read_pix();  // for tile kt+4, issued in the next phase
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    __syncthreads();  // ibs and bias_s written
+
+    if (nk > 0) {
+        read_pix();
+        issue(0, st0);
+        read_pix();
+        issue(1, st1);
+        read_pix();
+        issue(2, st2);
+        read_pix();
+        CONVLOWER_WAIT_VMCNT(2 * IPW);
+        block_barrier();
+#pragma unroll
+        for (int grp = 0; grp < NG; ++grp) lds_read(st0, grp);
+        for (int kt = 0;; kt += 3) {
+            phase(kt, st0, st1);
+            if (kt + 1 >= nk) break;
+            phase(kt + 1, st1, st2);
+            if (kt + 2 >= nk) break;
+            phase(kt + 2, st2, st0);
+            if (kt + 3 >= nk) break;
+        }
+        CONVLOWER_WAIT_VMCNT(0);  // no load may still write LDS when the block ends
+    }
+
+    // ---- epilogue: bias, one rounding, direct stores --------------------------
+    S *y = (S *)A.y;
+    if constexpr (OUT_NCHW) {
+        // Rows are pixels: this lane's rows m0 + wp*WPM + ip*32 + qrow(q) + v
+        // are visited in increasing order with a fixed step.
+        constexpr int STEP = MF::QSTEP;
+        int m = (int)m0 + wp * WPM + MF::qrow(0, lane);
+        int n = m / g.P;
+        int p = m - n * g.P;
+#pragma unroll
+        for (int ip = 0; ip < TP; ++ip) {
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                if (m < g.M) {
+#pragma unroll
+                    for (int ic = 0; ic < TC; ++ic) {
+                        const int cl = wc * WCN + ic * 32 + frow;
+                        const int co = co0 + cl;
+                        if (co >= g.Co) continue;
+                        const float a4[4] = {acc[ip][ic][4 * q], acc[ip][ic][4 * q + 1], acc[ip][ic][4 * q + 2],
+                                             acc[ip][ic][4 * q + 3]};
+                        if (A.part) {
+                            for (int v = 0; v < 4 && m + v < g.M; ++v)
+                                A.part[((long long)blockIdx.z * g.M + m + v) * g.Co + co] = a4[v];
+                            continue;
+                        }
+                        const float b = bias_s[cl];
+                        const long long yi = ((long long)n * g.Co + co) * g.P + p;
+                        if (p + 4 <= g.P && m + 4 <= g.M && ((uintptr_t)(y + yi) % (4 * sizeof(S))) == 0) {
+                            store4(y + yi, a4[0] + b, a4[1] + b, a4[2] + b, a4[3] + b);
+                        } else {
+                            int nv = n, pv = p;
+                            for (int v = 0; v < 4 && m + v < g.M; ++v) {
+                                y[((long long)nv * g.Co + co) * g.P + pv] = to_out(S(), a4[v] + b);
+                                if (++pv == g.P) {
+                                    pv = 0;
+                                    ++nv;
+                                }
+                            }
+                        }
+                    }
+                }
+                m += STEP;
+                p += STEP;
+                while (p >= g.P) {
+                    p -= g.P;
+                    ++n;
+                }
+            }
+        }
+    } else {
+        // Rows are output channels: each lane's 4 consecutive rows are 4
+        // consecutive channels of one output pixel.
+#pragma unroll
+        for (int ip = 0; ip < TP; ++ip) {
+            const long long m = (long long)m0 + wp * WPM + ip * 32 + frow;
+            if (m >= g.M) continue;
+#pragma unroll
+            for (int ic = 0; ic < TC; ++ic) {
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) {
+                    const int cl = wc * WCN + ic * 32 + MF::qrow(q, lane);
+                    const int co = co0 + cl;
+                    if (co >= g.Co) continue;
+                    const float a4[4] = {acc[ip][ic][4 * q], acc[ip][ic][4 * q + 1], acc[ip][ic][4 * q + 2],
+                                         acc[ip][ic][4 * q + 3]};
+                    if (A.part) {
+                        for (int v = 0; v < 4 && co + v < g.Co; ++v)
+                            A.part[((long long)blockIdx.z * g.M + m) * g.Co + co + v] = a4[v];
+                        continue;
+                    }
+                    const long long yi = m * g.Co + co;
+                    if (co + 4 <= g.Co && ((uintptr_t)(y + yi) % (4 * sizeof(S))) == 0) {
+                        store4(y + yi, a4[0] + bias_s[cl], a4[1] + bias_s[cl + 1], a4[2] + bias_s[cl + 2],
+                               a4[3] + bias_s[cl + 3]);
+                    } else {
+                        for (int v = 0; v < 4 && co + v < g.Co; ++v) y[yi + v] = to_out(S(), a4[v] + bias_s[cl + v]);
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <typename S, int FEED, bool OUT_NCHW>
+__global__ __launch_bounds__(kThreads, 2) void igemm_dual_kernel(GemmArgs A) {
+    igemm_dual_body<S, FEED, OUT_NCHW>(A);
+}
+
+}  // namespace convlower

@@ -550,6 +550,7 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(GemmArgs A) {
 }  // namespace convlower
 
 #include "igemm_dma.h"
+#include "igemm_dual.h"
 
 namespace convlower {
 
@@ -568,6 +569,7 @@ static hipError_t launch_tile(const GemmArgs &a, int tile, int splits, hipStream
             case TILE_128x64: return go(igemm_dma_kernel<S, FEED, OUT_NCHW, 128, 64, BKW>, 128, 64);
             case TILE_32x64: return go(igemm_dma_kernel<S, FEED, OUT_NCHW, 32, 64, BKW>, 32, 64);
             case TILE_256x128: return go(igemm_dma_kernel<S, FEED, OUT_NCHW, 256, 128, BKW>, 256, 128);
+            case TILE_256x128_DUAL: return go(igemm_dual_kernel<S, FEED, OUT_NCHW>, 256, 128);
             default: return hipErrorInvalidValue;
         }
     } else {  // element gathers through registers
