@@ -238,7 +238,7 @@ def main():
     nbytes = algorithmic_bytes(H, Ho, Wo, head_dtype)
     rl = roofline(flops, nbytes, ml_ms / 1e3, head_dtype)
     rl["traffic"] = measured_traffic("igemm_dma_kernel", "C2-bf16-NCHW-main-loop")
-    rl["kernel"] = "igemm_dma_kernel (MFMA implicit-GEMM main loop + fused bias epilogue, indirect feed)"
+    rl["kernel"] = "igemm_dual_kernel (MFMA implicit-GEMM main loop + fused bias epilogue, indirection feed)"
     rl["ms"] = ml_ms
     rl["per_launch_flops"] = flops
     rl["per_launch_algorithmic_bytes"] = nbytes

@@ -15,8 +15,14 @@ constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
+// Main loops whose indirection slice in LDS holds up to 12 taps at any
+// tile height (the others hold 3072 entries).
+bool wide_slice(int tile) { return tile == TILE_256x128_DUAL || tile == TILE_256x128_OCT; }
+
 int tile_rows(int tile) {
-    return tile == TILE_32x64 ? 32 : (tile == TILE_256x128 || tile == TILE_256x128_DUAL) ? 256 : 128;
+    return tile == TILE_32x64                                                                   ? 32
+           : (tile == TILE_256x128 || tile == TILE_256x128_DUAL || tile == TILE_256x128_OCT) ? 256
+                                                                                             : 128;
 }
 
 struct Plan {
@@ -135,24 +141,41 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
         default: rows16 = false;
     }
     pl->rows16 = rows16;
-    // The two-blocks-per-CU main loop: 64-byte K tiles that stay inside one
-    // tap (C a multiple of the tile), and an indirection slice of at most 12
-    // taps whose entries divided by C fit 16 bits.
-    const int BKD = pl->bf16 ? 32 : 16;
-    bool dual = rows16;
+    // The main loops with two wavefronts per SIMD: K tiles that stay inside
+    // one tap (C a multiple of the tile: 128-byte rows for the 512-thread
+    // loop, 64-byte rows for the two-blocks-per-CU loop), and an indirection
+    // slice of at most 12 taps whose entries divided by C fit 16 bits.
+    const int BK8 = pl->bf16 ? 64 : 32, BK4 = pl->bf16 ? 32 : 16;
+    bool dual = rows16, oct = rows16;
     switch (pl->feed) {
         case FEED_ROWMAJOR: break;
-        case FEED_WIN: dual = dual && g.C % BKD == 0; break;
-        case FEED_IND_NHWC: dual = dual && g.C % BKD == 0 && g.T <= 12 && (long long)g.H * g.W <= 65535; break;
-        default: dual = false;
+        case FEED_WIN:
+            dual = dual && g.C % BK4 == 0;
+            oct = oct && g.C % BK8 == 0;
+            break;
+        case FEED_IND_NHWC: {
+            const bool slice = g.T <= 12 && (long long)g.H * g.W <= 65535;
+            dual = dual && slice && g.C % BK4 == 0;
+            oct = oct && slice && g.C % BK8 == 0;
+            break;
+        }
+        default: dual = oct = false;
     }
     int BM, BN;
     if (g.M <= 64) {
         pl->tile = TILE_32x64; BM = 32; BN = 64;
     } else if (g.Co <= 64) {
         pl->tile = TILE_128x64; BM = 128; BN = 64;
+    } else if (oct && ((g.M + 255) / 256) * ((g.Co + 127) / 128) > 512) {
+        // More tiles than two resident blocks per CU can hold in one round:
+        // one 512-thread block per CU, with whole-cache-line loads.
+        pl->tile = TILE_256x128_OCT; BM = 256; BN = 128;
     } else if (dual) {
+        // Up to one round of two blocks per CU (their prologues and epilogues
+        // overlap each other's main loops).
         pl->tile = TILE_256x128_DUAL; BM = 256; BN = 128;
+    } else if (oct) {
+        pl->tile = TILE_256x128_OCT; BM = 256; BN = 128;
     } else if (rows16 && g.M >= 65536) {
         pl->tile = TILE_256x128; BM = 256; BN = 128;
     } else {
@@ -326,7 +349,7 @@ conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias
     switch (pl.feed) {
         case FEED_ROWMAJOR: a_vec = g.K % VEC == 0 && al16(a.a_src); break;
         case FEED_IND_NHWC:  // the vector path keeps the block's BM x KH*KW buffer slice in LDS
-            a_vec = pl.rows16 && al16(a.a_src) && (long long)tile_rows(pl.tile) * g.T <= 3072;
+            a_vec = pl.rows16 && al16(a.a_src) && (wide_slice(pl.tile) || (long long)tile_rows(pl.tile) * g.T <= 3072);
             break;
         case FEED_WIN: a_vec = g.C % VEC == 0 && al16(a.a_src); break;
         default: a_vec = false;
@@ -348,7 +371,7 @@ conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias
     // Misaligned pointers fall back to the element-gather loop, which has no
     // 256x128 variant; the split count (and so the workspace) is unchanged.
     int tile = pl.tile;
-    if (!a_vec && (tile == TILE_256x128 || tile == TILE_256x128_DUAL)) tile = TILE_128x128;
+    if (!a_vec && (tile == TILE_256x128 || wide_slice(tile))) tile = TILE_128x128;
     {
         uint32_t c = (uint32_t)g.C, sh = 0;
         while (!(c & 1u)) {

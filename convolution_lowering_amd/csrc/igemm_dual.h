@@ -1,74 +1,107 @@
-// The main loop sized so that two blocks share each compute unit: every
-// SIMD then holds one wavefront of each block, and while one of them waits
+// The main loop with two wavefronts on every SIMD, so that while one waits
 // (at its barrier, for its loads, in its prologue or epilogue) or issues its
-// address arithmetic, the other keeps the matrix core busy.
+// address arithmetic, the other keeps the matrix core busy.  Two shapes:
 //
-//   * Block tile 256 x 128 of Y_col, four wavefronts of 128 x 64 each
-//     (v_mfma_f32_32x32x16_bf16 or v_mfma_f32_32x32x2_f32 tiles).  The
-//     fragment reads then cost 6 KB of LDS per 8 MFMAs and the global loads
-//     48 KB per 2 x 512 MFMA cycles per compute unit, both inside what one
-//     compute unit moves.
-//   * K tiles of 64 bytes per row (32 bf16 or 16 fp32 values), three LDS
-//     stages of 24 KB filled by the buffer-load-to-LDS instructions; tile k+3
-//     is issued while tile k is multiplied, so two tiles cover the load
+//   * DualCfg4: two blocks per compute unit, each 256 threads with 80 KB of
+//     LDS; K tiles of 64-byte rows (32 bf16 / 16 fp32 values); wavefront
+//     tiles 128 x 64.
+//   * DualCfg8: one block of 512 threads per compute unit with 150 KB of
+//     LDS; K tiles of 128-byte rows (64 bf16 / 32 fp32 values), so every
+//     load moves whole cache lines; wavefront tiles 64 x 64.
+//
+// Common structure:
+//   * Block tile 256 x 128 of Y_col (v_mfma_f32_32x32x16_bf16 or
+//     v_mfma_f32_32x32x2_f32 tiles).
+//   * Three LDS stages filled by the buffer-load-to-LDS instructions; tile
+//     k+3 is issued while tile k is multiplied, so two tiles cover the load
 //     latency.
-//   * The K order is (kh, kw, ci) and every K tile lies inside one tap (the
-//     host asks C to be a multiple of the K tile), so a tile's loads share
-//     one tap and one channel offset.
+//   * Every K tile lies inside one tap (the host asks C to be a multiple of
+//     the K tile), so a tile's loads share one tap and one channel offset.
+//     The tiles are visited tap-fastest: all KH*KW taps of one channel
+//     slice, then the next slice.  Consecutive tiles then read the same input
+//     rows shifted by one tap, which the L2 still holds; (kh, kw, ci) order
+//     would come back to a row only after streaming C / (K tile) tiles of
+//     every resident block through the L2.  A and B walk the same order, so
+//     the sum is unchanged.
 //   * The indirection buffer's slice for the block (256 rows x KH*KW taps)
 //     is copied to LDS once, as 16-bit pixel indices (entry / C, 0xFFFF for
-//     a padding tap), which keeps the block at 80 KB of LDS.  The indices a
-//     tile's loads need are read one tile ahead.
+//     a padding tap).  The indices a tile's loads need are read one tile
+//     ahead.
 //   * The bias of the block's 128 output channels is staged in LDS.
 //
 // All LDS-refill and read ordering follows the pipeline of igemm_dma.h: each
 // wavefront waits (vmcnt) for its own loads of the tile it is about to read
 // and (lgkmcnt) for its own reads of the stage about to be refilled, then
-// the block barrier makes both hold for all four wavefronts.
+// the block barrier makes both hold for all wavefronts.
 #pragma once
 
 namespace convlower {
 
 constexpr int kDualMaxTaps = 12;  // KH*KW taps the LDS slice of the indirection buffer holds
 
-template <typename S>
+// Shape of one main-loop variant: block tile 256 x 128, KCH 16-byte chunks
+// per stage row, NW wavefronts in a WGM x (NW / WGM) grid.
+template <typename S, int KCH_, int NW_, int WGM_>
 struct DualCfg {
     static constexpr int BM = 256, BN = 128;
     static constexpr int ES = (int)sizeof(S);
     static constexpr int VEC = 16 / ES;
-    static constexpr int KCH = 4;                    // 16-byte chunks per stage row
+    static constexpr int KCH = KCH_;                 // 16-byte chunks per stage row
+    static constexpr int NW = NW_, NTHR = 64 * NW_;  // wavefronts, threads
+    static constexpr int RPI = 64 / KCH;             // stage rows one 64-lane load fills
+    static constexpr int RPL = 16 / KCH;             // stage rows per 256-byte LDS line
     static constexpr int BK = KCH * VEC;             // K values per tile
-    static constexpr int NSLOT = (BM + BN) * KCH;    // 16-byte slots per stage (24 KB)
-    static constexpr int IPW_A = BM * KCH / 64 / 4;  // A loads per wavefront per tile
-    static constexpr int IPW_B = BN * KCH / 64 / 4;  // B loads per wavefront per tile
+    static constexpr int NSLOT = (BM + BN) * KCH;    // 16-byte slots per stage
+    static constexpr int IPW_A = BM * KCH / 64 / NW;  // A loads per wavefront per tile
+    static constexpr int IPW_B = BN * KCH / 64 / NW;  // B loads per wavefront per tile
     static constexpr int IPW = IPW_A + IPW_B;
-    static constexpr int WPM = BM / 2, WCN = BN / 2;  // wavefront tile
+    static constexpr int WGM = WGM_, WGN = NW_ / WGM_;
+    static constexpr int WPM = BM / WGM, WCN = BN / WGN;  // wavefront tile
     static constexpr int MT = 32, TP = WPM / MT, TC = WCN / MT;
     static constexpr int NG = KCH / 2;  // MFMA K steps per tile (two chunks per step)
+    static constexpr int MIN_BLOCKS = NW_ == 4 ? 2 : 1;
+    static_assert(IPW_A * NW * 64 == BM * KCH && IPW_B * NW * 64 == BN * KCH, "loads must split evenly");
+    static_assert(TP >= 1 && TC >= 1 && WGM * WGN == NW, "wavefront grid");
 };
+// 64-byte rows, four wavefronts of 128 x 64, two blocks per compute unit
+// (80 KB of LDS each).
+template <typename S>
+using DualCfg4 = DualCfg<S, 4, 4, 2>;
+// 128-byte rows, eight wavefronts of 64 x 64, one block per compute unit
+// (150 KB of LDS): whole-cache-line loads, two wavefronts per SIMD.
+template <typename S>
+using DualCfg8 = DualCfg<S, 8, 8, 4>;
 
-// Stage slot of chunk c of row r: rows of 4 chunks (64 bytes); the XOR with
-// bits 1..2 of the row spreads any 8 consecutive rows of one chunk column
-// over distinct 16-byte bank groups.
-__device__ __forceinline__ constexpr int dual_slot(int r, int c) { return r * 4 + (c ^ ((r >> 1) & 3)); }
+// Stage slot of chunk c of row r (rows of KCH chunks).  A b128 LDS read is
+// served 16 lanes per cycle from one 256-byte line of banks; XOR-ing the
+// chunk with (r / rows-per-line) mod KCH puts any 16 consecutive rows of one
+// chunk column on 16 distinct 16-byte bank groups.
+template <int KCH>
+__device__ __forceinline__ constexpr int dual_swz(int r) {
+    return (r / (16 / KCH)) & (KCH - 1);
+}
+template <int KCH>
+__device__ __forceinline__ constexpr int dual_slot(int r, int c) {
+    return r * KCH + (c ^ dual_swz<KCH>(r));
+}
 
-template <typename S, int FEED, bool OUT_NCHW>
+template <typename S, int FEED, bool OUT_NCHW, typename C>
 __device__ __forceinline__ void igemm_dual_body(const GemmArgs &A) {
-    using C = DualCfg<S>;
     constexpr int BM = C::BM, BN = C::BN, BK = C::BK, VEC = C::VEC, KCH = C::KCH, NSLOT = C::NSLOT;
     constexpr int IPW_A = C::IPW_A, IPW_B = C::IPW_B, IPW = C::IPW;
     constexpr int WPM = C::WPM, WCN = C::WCN, TP = C::TP, TC = C::TC, NG = C::NG;
+    constexpr int NW = C::NW, NTHR = C::NTHR, RPI = C::RPI;
     constexpr uint32_t ES = (uint32_t)sizeof(S);
     constexpr bool IND = FEED == FEED_IND_NHWC;
     constexpr bool TAPS = FEED == FEED_IND_NHWC || FEED == FEED_WIN;  // K tiles inside one tap
     using MF = MfmaShape<S, 32>;
     constexpr int NQ = MF::NQ;
-    static_assert(IPW_A * 4 * 64 == BM * KCH && IPW_B * 4 * 64 == BN * KCH, "loads must split evenly");
 
     __shared__ uint4 st0[NSLOT];
     __shared__ uint4 st1[NSLOT];
     __shared__ uint4 st2[NSLOT];
     __shared__ uint16_t ibs[IND ? BM * kDualMaxTaps : 2];
+    static_assert((BM * kDualMaxTaps) % NTHR == 0, "slice must split evenly");
     __shared__ float bias_s[BN];
 
     const Geom &g = A.g;
@@ -92,20 +125,22 @@ __device__ __forceinline__ void igemm_dual_body(const GemmArgs &A) {
     // read some valid entry; their loads are out of range anyway.
     if constexpr (IND) {
         const uint32_t PT = (uint32_t)g.P * (uint32_t)g.T;
+        constexpr int NJ = BM * kDualMaxTaps / NTHR;
+        const int nent = BM * g.T;
         uint32_t idx = ((m0 % (uint32_t)g.P) * (uint32_t)g.T + (uint32_t)tid) % PT;
-        int v[kDualMaxTaps];
+        int v[NJ];
 #pragma unroll
-        for (int j = 0; j < kDualMaxTaps; ++j) {
+        for (int j = 0; j < NJ; ++j) {
             v[j] = 0;
-            if (j < g.T) v[j] = A.ibuf[idx];
-            idx += kThreads;
+            if (j * NTHR < nent) v[j] = A.ibuf[idx];  // (entries past the slice read a valid one)
+            idx += NTHR;
             if (idx >= PT) idx -= PT;
             if (idx >= PT) idx %= PT;
         }
 #pragma unroll
-        for (int j = 0; j < kDualMaxTaps; ++j)
-            if (j < g.T)
-                ibs[tid + kThreads * j] =
+        for (int j = 0; j < NJ; ++j)
+            if (j * NTHR + tid < nent)
+                ibs[tid + NTHR * j] =
                     v[j] < 0 ? (uint16_t)0xFFFF : (uint16_t)(((uint32_t)v[j] >> A.c_shift) * A.c_inv);
     }
     if (tid < BN) {
@@ -116,16 +151,17 @@ __device__ __forceinline__ void igemm_dual_body(const GemmArgs &A) {
     }
 
     // ---- per-lane load geometry ---------------------------------------------
-    // Load i of this wavefront covers stage rows (i*4 + wave)*16 .. +15 (A
-    // rows for i < IPW_A, B rows after); lane L fills slot L of it, i.e. row
-    // L/4, chunk (L%4) ^ ((L/8)%4) -- a fixed chunk column kc per lane.
-    const int lrow = lane >> 2;
-    const uint32_t kc = (uint32_t)(((lane & 3) ^ ((lane >> 3) & 3)) * VEC);
+    // Load i of this wavefront covers stage rows (i*NW + wave)*RPI .. +RPI-1
+    // (A rows for i < IPW_A, B rows after); lane L fills slot L of it, i.e.
+    // row L/KCH, chunk (L%KCH) ^ swz(row).  swz(row) does not depend on i,
+    // so each lane always fetches the same chunk column kc.
+    const int lrow = lane / KCH;
+    const uint32_t kc = (uint32_t)(((lane % KCH) ^ dual_swz<KCH>(wave * RPI + lrow)) * VEC);
     uint32_t rbA[IPW_A], rbB[IPW_B];
     int ib_row[IPW_A];
 #pragma unroll
     for (int i = 0; i < IPW_A; ++i) {
-        const int r = (i * 4 + wave) * 16 + lrow;
+        const int r = (i * NW + wave) * RPI + lrow;
         ib_row[i] = r * g.T;
         const uint32_t m = m0 + (uint32_t)r;
         const bool ok = m < M;
@@ -145,7 +181,7 @@ __device__ __forceinline__ void igemm_dual_body(const GemmArgs &A) {
     }
 #pragma unroll
     for (int j = 0; j < IPW_B; ++j) {
-        const int co = co0 + (j * 4 + wave) * 16 + lrow;
+        const int co = co0 + (j * NW + wave) * RPI + lrow;
         rbB[j] = co < g.Co ? (uint32_t)co * (uint32_t)g.K * ES : kOutOfRange;
     }
 
@@ -153,21 +189,23 @@ __device__ __forceinline__ void igemm_dual_body(const GemmArgs &A) {
     const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(A.b, A.b_bytes);
     const uint32_t lds_w = (uint32_t)wave * 1024u;  // this wavefront's first slot group, in bytes
 
-    // Tap and channel offset of the K tiles, advanced one tile at a time:
-    // `iss` for the next tile to issue, `pre` for the tile whose pixel
-    // indices are read next (one ahead of `iss`).
+    // Tap and channel offset of the K tiles (tile j of the whole K range is
+    // tap j % T of channel slice j / T), advanced one tile at a time: `iss`
+    // for the next tile to issue, `pre` for the tile whose pixel indices are
+    // read next (one ahead of `iss`).  Past the last tile the channel offset
+    // runs beyond C; those tiles load nothing.
     int iss_t = 0, iss_ci = 0, pre_t = 0, pre_ci = 0;
     if constexpr (TAPS) {
-        iss_t = kbeg / g.C;
-        iss_ci = kbeg - iss_t * g.C;
+        const int j0 = kbeg / BK;
+        iss_t = j0 % g.T;
+        iss_ci = (j0 / g.T) * BK;
         pre_t = iss_t;
         pre_ci = iss_ci;
     }
     auto advance = [&](int &t, int &ci) {
-        ci += BK;
-        if (ci >= g.C) {
-            ci -= g.C;
-            ++t;
+        if (++t == g.T) {
+            t = 0;
+            ci += BK;
         }
     };
 
@@ -175,9 +213,8 @@ __device__ __forceinline__ void igemm_dual_body(const GemmArgs &A) {
     uint32_t pix[IPW_A];
     auto read_pix = [&]() {
         if constexpr (IND) {
-            const int t = pre_t < g.T ? pre_t : g.T - 1;  // tiles past the end read any valid tap
 #pragma unroll
-            for (int i = 0; i < IPW_A; ++i) pix[i] = ibs[ib_row[i] + t];
+            for (int i = 0; i < IPW_A; ++i) pix[i] = ibs[ib_row[i] + pre_t];
         }
         if constexpr (TAPS) advance(pre_t, pre_ci);
     };
@@ -211,14 +248,19 @@ __device__ __forceinline__ void igemm_dual_body(const GemmArgs &A) {
         }
 #pragma unroll
         for (int j = 0; j < IPW_B; ++j) {
-            const uint32_t o = rbB[j] + (k0 + kc) * ES;
-            voff[IPW_A + j] = k0 + kc < (uint32_t)kend ? o : kOutOfRange;
+            if constexpr (TAPS) {  // W_row column t*C + ci of the same tile
+                const uint32_t o = rbB[j] + ((uint32_t)(iss_t * g.C + iss_ci) + kc) * ES;
+                voff[IPW_A + j] = live ? o : kOutOfRange;
+            } else {
+                const uint32_t o = rbB[j] + (k0 + kc) * ES;
+                voff[IPW_A + j] = k0 + kc < (uint32_t)kend ? o : kOutOfRange;
+            }
         }
 #pragma unroll
-        for (int i = 0; i < IPW_A; ++i) lds_dma16(a_rsrc, voff[i], lds0 + (uint32_t)i * 4096u);
+        for (int i = 0; i < IPW_A; ++i) lds_dma16(a_rsrc, voff[i], lds0 + (uint32_t)(i * NW * 1024));
 #pragma unroll
         for (int j = 0; j < IPW_B; ++j)
-            lds_dma16(b_rsrc, voff[IPW_A + j], lds0 + (uint32_t)(BM * KCH * 16) + (uint32_t)j * 4096u);
+            lds_dma16(b_rsrc, voff[IPW_A + j], lds0 + (uint32_t)(BM * KCH * 16 + j * NW * 1024));
         if constexpr (TAPS) advance(iss_t, iss_ci);
     };
 
@@ -228,15 +270,15 @@ __device__ __forceinline__ void igemm_dual_body(const GemmArgs &A) {
 #pragma unroll
         for (int ic = 0; ic < TC; ++ic) acc[ip][ic] = typename MF::acc_t{};
 
-    const int wp = wave >> 1, wc = wave & 1;
+    const int wp = wave / C::WGN, wc = wave % C::WGN;
     const int frow = lane & 31, fch = lane >> 5;
     uint4 fa[NG][TP], fb[NG][TC];
     auto lds_read = [&](const uint4 *st, int grp) {
 #pragma unroll
-        for (int ip = 0; ip < TP; ++ip) fa[grp][ip] = st[dual_slot(wp * WPM + ip * 32 + frow, grp * 2 + fch)];
+        for (int ip = 0; ip < TP; ++ip) fa[grp][ip] = st[dual_slot<KCH>(wp * WPM + ip * 32 + frow, grp * 2 + fch)];
 #pragma unroll
         for (int ic = 0; ic < TC; ++ic)
-            fb[grp][ic] = st[BM * KCH + dual_slot(wc * WCN + ic * 32 + frow, grp * 2 + fch)];
+            fb[grp][ic] = st[BM * KCH + dual_slot<KCH>(wc * WCN + ic * 32 + frow, grp * 2 + fch)];
     };
     auto mfma_group = [&](int grp) {
 #pragma unroll
@@ -383,8 +425,13 @@ __device__ __forceinline__ void igemm_dual_body(const GemmArgs &A) {
 }
 
 template <typename S, int FEED, bool OUT_NCHW>
-__global__ __launch_bounds__(kThreads, 2) void igemm_dual_kernel(GemmArgs A) {
-    igemm_dual_body<S, FEED, OUT_NCHW>(A);
+__global__ __launch_bounds__(256, 2) void igemm_dual_kernel(GemmArgs A) {
+    igemm_dual_body<S, FEED, OUT_NCHW, DualCfg4<S>>(A);
+}
+
+template <typename S, int FEED, bool OUT_NCHW>
+__global__ __launch_bounds__(512, 1) void igemm_oct_kernel(GemmArgs A) {
+    igemm_dual_body<S, FEED, OUT_NCHW, DualCfg8<S>>(A);
 }
 
 }  // namespace convlower

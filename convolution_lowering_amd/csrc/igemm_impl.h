@@ -557,9 +557,9 @@ namespace convlower {
 template <typename S, int FEED, bool AVEC, bool BVEC, bool OUT_NCHW>
 static hipError_t launch_tile(const GemmArgs &a, int tile, int splits, hipStream_t st) {
     const Geom &g = a.g;
-    auto go = [&](auto kern, int BM, int BN) {
+    auto go = [&](auto kern, int BM, int BN, int threads = kThreads) {
         dim3 grid((unsigned)(((g.M + BM - 1) / BM) * ((g.Co + BN - 1) / BN)), 1, (unsigned)splits);
-        hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, st, a);
+        hipLaunchKernelGGL(kern, grid, dim3(threads), 0, st, a);
         return hipGetLastError();
     };
     constexpr int BKW = sizeof(S) == 2 ? 64 : 32;  // 128-byte LDS rows
@@ -570,6 +570,7 @@ static hipError_t launch_tile(const GemmArgs &a, int tile, int splits, hipStream
             case TILE_32x64: return go(igemm_dma_kernel<S, FEED, OUT_NCHW, 32, 64, BKW>, 32, 64);
             case TILE_256x128: return go(igemm_dma_kernel<S, FEED, OUT_NCHW, 256, 128, BKW>, 256, 128);
             case TILE_256x128_DUAL: return go(igemm_dual_kernel<S, FEED, OUT_NCHW>, 256, 128);
+            case TILE_256x128_OCT: return go(igemm_oct_kernel<S, FEED, OUT_NCHW>, 256, 128, 512);
             default: return hipErrorInvalidValue;
         }
     } else {  // element gathers through registers
