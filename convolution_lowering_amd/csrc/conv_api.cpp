@@ -321,26 +321,32 @@ conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias
 
     // Offsets of the indirection buffer follow the layout the main loop reads.
     const bool ib_rows = pl.feed == FEED_IND_NHWC;
+    int32_t *ib_build = nullptr;  // buffer still to build
     if (prebuilt) {
         a.ibuf = prebuilt;
     } else if (pl.need_ibuf) {
-        int32_t *ib = (int32_t *)(ws + pl.off_ibuf);
-        if (launch_build_indirection(ib, g, ib_rows, s) != hipSuccess) return CONV_ERR_HIP;
-        a.ibuf = ib;
+        ib_build = (int32_t *)(ws + pl.off_ibuf);
+        a.ibuf = ib_build;
     }
+    void *wp = pl.need_wpack ? (void *)(ws + pl.off_wpack) : nullptr;
+    bool wp_done = false;
     if (pl.need_xcl) {
+        // One launch: the channels-last copy of x, the indirection buffer and
+        // the regrouped weights.
         void *xc = ws + pl.off_xcl;
-        if (launch_nchw_to_nhwc(x, xc, g, pl.bf16, s) != hipSuccess) return CONV_ERR_HIP;
+        if (launch_prep_nchw(x, xc, ib_build, w, wp, g, pl.bf16, s) != hipSuccess) return CONV_ERR_HIP;
         a.a_src = xc;
+        ib_build = nullptr;
+        wp_done = true;
     }
+    if (ib_build && launch_build_indirection(ib_build, g, ib_rows, s) != hipSuccess) return CONV_ERR_HIP;
     if (pl.need_win) {
         void *xw = ws + pl.off_win;
         if (launch_im2win(x, xw, g, pl.nhwc, pl.bf16, s) != hipSuccess) return CONV_ERR_HIP;
         a.a_src = xw;
     }
-    if (pl.need_wpack) {
-        void *wp = ws + pl.off_wpack;
-        if (launch_pack_weights_ohwi(w, wp, g, pl.bf16, s) != hipSuccess) return CONV_ERR_HIP;
+    if (wp) {
+        if (!wp_done && launch_pack_weights_ohwi(w, wp, g, pl.bf16, s) != hipSuccess) return CONV_ERR_HIP;
         a.b = wp;
     }
     if (pl.splits > 1) a.part = (float *)(ws + pl.off_part);

@@ -64,7 +64,10 @@ hipError_t launch_splitk_reduce(const float *part, const void *bias, void *y, co
 hipError_t launch_build_indirection(int32_t *buf, const Geom &g, bool nhwc, hipStream_t st);
 hipError_t launch_im2win(const void *x, void *xwin, const Geom &g, bool nhwc, bool bf16,
                          hipStream_t st);
-hipError_t launch_nchw_to_nhwc(const void *x, void *x_cl, const Geom &g, bool bf16, hipStream_t st);
+// One launch: x NCHW -> channels-last copy, plus (when given) the channels-last
+// indirection buffer and the OIHW -> OHWI weights.
+hipError_t launch_prep_nchw(const void *x, void *x_cl, int32_t *ib, const void *w, void *w_ohwi, const Geom &g,
+                            bool bf16, hipStream_t st);
 hipError_t launch_pack_weights_ohwi(const void *w_oihw, void *w_ohwi, const Geom &g, bool bf16,
                                     hipStream_t st);
 

@@ -35,6 +35,8 @@
 // the block barrier makes both hold for all wavefronts.
 #pragma once
 
+#include <type_traits>
+
 namespace convlower {
 
 constexpr int kDualMaxTaps = 12;  // KH*KW taps the LDS slice of the indirection buffer holds
@@ -97,9 +99,8 @@ __device__ __forceinline__ void igemm_dual_body(const GemmArgs &A) {
     using MF = MfmaShape<S, 32>;
     constexpr int NQ = MF::NQ;
 
-    __shared__ uint4 st0[NSLOT];
-    __shared__ uint4 st1[NSLOT];
-    __shared__ uint4 st2[NSLOT];
+    __shared__ uint4 stg[3][NSLOT];  // the three stages; the epilogue reuses them
+    uint4 *const st0 = stg[0], *const st1 = stg[1], *const st2 = stg[2];
     __shared__ uint16_t ibs[IND ? BM * kDualMaxTaps : 2];
     static_assert((BM * kDualMaxTaps) % NTHR == 0, "slice must split evenly");
     __shared__ float bias_s[BN];
@@ -340,84 +341,155 @@ __device__ __forceinline__ void igemm_dual_body(const GemmArgs &A) {
         CONVLOWER_WAIT_VMCNT(0);  // no load may still write LDS when the block ends
     }
 
-    // ---- epilogue: bias, one rounding, direct stores --------------------------
+    // ---- epilogue -------------------------------------------------------------
     S *y = (S *)A.y;
-    if constexpr (OUT_NCHW) {
-        // Rows are pixels: this lane's rows m0 + wp*WPM + ip*32 + qrow(q) + v
-        // are visited in increasing order with a fixed step.
-        constexpr int STEP = MF::QSTEP;
-        int m = (int)m0 + wp * WPM + MF::qrow(0, lane);
-        int n = m / g.P;
-        int p = m - n * g.P;
+    if (A.part) {
+        // Split K: this split's fp32 sums go to its slice of the workspace;
+        // the reduce pass adds the bias and rounds.
 #pragma unroll
-        for (int ip = 0; ip < TP; ++ip) {
+        for (int ip = 0; ip < TP; ++ip)
 #pragma unroll
-            for (int q = 0; q < NQ; ++q) {
-                if (m < g.M) {
+            for (int ic = 0; ic < TC; ++ic)
 #pragma unroll
-                    for (int ic = 0; ic < TC; ++ic) {
-                        const int cl = wc * WCN + ic * 32 + frow;
+                for (int q = 0; q < NQ; ++q)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int pr = wp * WPM + ip * 32, cr = wc * WCN + ic * 32;
+                        const int ml = OUT_NCHW ? pr + MF::qrow(q, lane) + v : pr + frow;
+                        const int cl = OUT_NCHW ? cr + frow : cr + MF::qrow(q, lane) + v;
+                        const long long m = (long long)m0 + ml;
                         const int co = co0 + cl;
-                        if (co >= g.Co) continue;
-                        const float a4[4] = {acc[ip][ic][4 * q], acc[ip][ic][4 * q + 1], acc[ip][ic][4 * q + 2],
-                                             acc[ip][ic][4 * q + 3]};
-                        if (A.part) {
-                            for (int v = 0; v < 4 && m + v < g.M; ++v)
-                                A.part[((long long)blockIdx.z * g.M + m + v) * g.Co + co] = a4[v];
-                            continue;
-                        }
-                        const float b = bias_s[cl];
-                        const long long yi = ((long long)n * g.Co + co) * g.P + p;
-                        if (p + 4 <= g.P && m + 4 <= g.M && ((uintptr_t)(y + yi) % (4 * sizeof(S))) == 0) {
-                            store4(y + yi, a4[0] + b, a4[1] + b, a4[2] + b, a4[3] + b);
-                        } else {
-                            int nv = n, pv = p;
-                            for (int v = 0; v < 4 && m + v < g.M; ++v) {
-                                y[((long long)nv * g.Co + co) * g.P + pv] = to_out(S(), a4[v] + b);
-                                if (++pv == g.P) {
-                                    pv = 0;
-                                    ++nv;
-                                }
-                            }
-                        }
+                        if (m < g.M && co < g.Co)
+                            A.part[((long long)blockIdx.z * g.M + m) * g.Co + co] = acc[ip][ic][4 * q + v];
                     }
-                }
-                m += STEP;
-                p += STEP;
-                while (p >= g.P) {
-                    p -= g.P;
-                    ++n;
-                }
-            }
+        return;
+    }
+    // The tile goes through LDS (the stage memory, free once every wavefront
+    // has passed the barrier below) so that it leaves as whole rows along the
+    // output's contiguous axis: [channel][pixel] for NCHW, [pixel][channel]
+    // for NHWC, each row padded by 16 bytes to spread the bank groups.  A
+    // tile larger than the stage memory (fp32 with 80 KB blocks) goes in two
+    // passes over halves of its rows.
+    constexpr int ROWS = OUT_NCHW ? BN : BM;  // output runs in the tile
+    constexpr int COLS = OUT_NCHW ? BM : BN;  // elements per run
+    constexpr int PADE = 16 / (int)sizeof(S);
+    constexpr int RSTR = COLS + PADE;  // LDS row stride, elements
+    constexpr int NPASS = (long long)ROWS * RSTR * (int)sizeof(S) <= 3LL * NSLOT * 16 ? 1 : 2;
+    constexpr int PROWS = ROWS / NPASS;
+    constexpr int CPR = COLS / VEC;  // 16-byte chunks per run
+    static_assert((long long)PROWS * RSTR * (int)sizeof(S) <= 3LL * NSLOT * 16, "epilogue tile fits the stages");
+    static_assert(NTHR % CPR == 0, "each thread keeps one chunk column");
+    S *tile = (S *)&stg[0][0];
+
+    // This thread's chunk column and, for NCHW, the output pixel it starts
+    // at (the same for every run it stores).
+    const int cc = tid % CPR;
+    int n0 = 0, p0 = 0;
+    bool fast = false;  // whole 16-byte chunk inside one image, aligned
+    int sub = 1;        // NCHW: widest piece (elements) that never crosses an image
+    if constexpr (OUT_NCHW) {
+        const long long m = (long long)m0 + cc * VEC;
+        n0 = (int)(m / g.P);
+        p0 = (int)(m - (long long)n0 * g.P);
+        if ((uintptr_t)y % 16 == 0) {
+            sub = VEC;
+            while (g.P % sub != 0) sub >>= 1;
         }
+        fast = sub == VEC && m + VEC <= g.M;
     } else {
-        // Rows are output channels: each lane's 4 consecutive rows are 4
-        // consecutive channels of one output pixel.
+        fast = g.Co % VEC == 0 && co0 + cc * VEC + VEC <= g.Co && ((uintptr_t)y % 16) == 0;
+    }
+
 #pragma unroll
-        for (int ip = 0; ip < TP; ++ip) {
-            const long long m = (long long)m0 + wp * WPM + ip * 32 + frow;
-            if (m >= g.M) continue;
+    for (int pass = 0; pass < NPASS; ++pass) {
+        __syncthreads();  // stages (or the previous pass's rows) no longer read
+        const int r_lo = pass * PROWS;
+        // Accumulators -> LDS, bias added in fp32, rounded once.
 #pragma unroll
-            for (int ic = 0; ic < TC; ++ic) {
+        for (int ip = 0; ip < TP; ++ip)
+#pragma unroll
+            for (int ic = 0; ic < TC; ++ic)
 #pragma unroll
                 for (int q = 0; q < NQ; ++q) {
-                    const int cl = wc * WCN + ic * 32 + MF::qrow(q, lane);
-                    const int co = co0 + cl;
-                    if (co >= g.Co) continue;
-                    const float a4[4] = {acc[ip][ic][4 * q], acc[ip][ic][4 * q + 1], acc[ip][ic][4 * q + 2],
-                                         acc[ip][ic][4 * q + 3]};
-                    if (A.part) {
-                        for (int v = 0; v < 4 && co + v < g.Co; ++v)
-                            A.part[((long long)blockIdx.z * g.M + m) * g.Co + co + v] = a4[v];
-                        continue;
-                    }
-                    const long long yi = m * g.Co + co;
-                    if (co + 4 <= g.Co && ((uintptr_t)(y + yi) % (4 * sizeof(S))) == 0) {
-                        store4(y + yi, a4[0] + bias_s[cl], a4[1] + bias_s[cl + 1], a4[2] + bias_s[cl + 2],
-                               a4[3] + bias_s[cl + 3]);
+                    const int pr = wp * WPM + ip * 32, cr = wc * WCN + ic * 32;
+                    const float a0 = acc[ip][ic][4 * q], a1 = acc[ip][ic][4 * q + 1];
+                    const float a2 = acc[ip][ic][4 * q + 2], a3 = acc[ip][ic][4 * q + 3];
+                    if constexpr (OUT_NCHW) {
+                        const int row = cr + frow, col = pr + MF::qrow(q, lane);
+                        if (row < r_lo || row >= r_lo + PROWS) continue;
+                        const float b = bias_s[row];
+                        store4(tile + (row - r_lo) * RSTR + col, a0 + b, a1 + b, a2 + b, a3 + b);
                     } else {
-                        for (int v = 0; v < 4 && co + v < g.Co; ++v) y[yi + v] = to_out(S(), a4[v] + bias_s[cl + v]);
+                        const int row = pr + frow, col = cr + MF::qrow(q, lane);
+                        if (row < r_lo || row >= r_lo + PROWS) continue;
+                        store4(tile + (row - r_lo) * RSTR + col, a0 + bias_s[col], a1 + bias_s[col + 1],
+                               a2 + bias_s[col + 2], a3 + bias_s[col + 3]);
                     }
+                }
+        __syncthreads();
+        // LDS -> global, one 16-byte chunk per thread per run.
+        for (int r = tid / CPR; r < PROWS; r += NTHR / CPR) {
+            const int row = r_lo + r;
+            const uint4 val = *(const uint4 *)(tile + r * RSTR + cc * VEC);
+            if constexpr (OUT_NCHW) {
+                const int co = co0 + row;
+                if (co >= g.Co) continue;
+                if (fast) {
+                    *(uint4 *)(y + ((long long)n0 * g.Co + co) * g.P + p0) = val;
+                } else {
+                    // Pieces of `sub` elements: P and the chunk start are
+                    // multiples of sub, so no piece crosses an image and each
+                    // is aligned to its size.
+                    S e[VEC];
+                    __builtin_memcpy(e, &val, 16);
+                    const long long m = (long long)m0 + cc * VEC;
+                    auto pieces = [&](auto sub_c) {
+                        constexpr int SUB = decltype(sub_c)::value;
+                        int n = n0, p = p0;
+#pragma unroll
+                        for (int v = 0; v < VEC; v += SUB) {
+                            S *dst = y + ((long long)n * g.Co + co) * g.P + p;
+                            if constexpr (SUB * sizeof(S) == 8) {
+                                if (m + v + SUB <= g.M) {
+                                    *(uint2 *)dst = make_uint2(*(const uint32_t *)&e[v], *(const uint32_t *)&e[v + SUB / 2]);
+                                    goto next;
+                                }
+                            } else if constexpr (SUB * sizeof(S) == 4) {
+                                if (m + v + SUB <= g.M) {
+                                    *(uint32_t *)dst = *(const uint32_t *)&e[v];
+                                    goto next;
+                                }
+                            }
+#pragma unroll
+                            for (int u = 0; u < SUB; ++u)
+                                if (m + v + u < g.M) dst[u] = e[v + u];
+                        next:
+                            p += SUB;
+                            if (p == g.P) {
+                                p = 0;
+                                ++n;
+                            }
+                        }
+                    };
+                    if (sub == VEC / 2)
+                        pieces(std::integral_constant<int, VEC / 2>{});
+                    else if (sub == 2 && VEC >= 4)
+                        pieces(std::integral_constant<int, (VEC >= 4 ? 2 : 1)>{});
+                    else
+                        pieces(std::integral_constant<int, 1>{});
+                }
+            } else {
+                const long long m = (long long)m0 + row;
+                if (m >= g.M) continue;
+                const int co = co0 + cc * VEC;
+                if (fast) {
+                    *(uint4 *)(y + m * g.Co + co) = val;
+                } else {
+                    S e[VEC];
+                    __builtin_memcpy(e, &val, 16);
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v)
+                        if (co + v < g.Co) y[m * g.Co + co + v] = e[v];
                 }
             }
         }

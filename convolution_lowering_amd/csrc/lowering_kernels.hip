@@ -4,6 +4,8 @@
 //   the NCHW -> NHWC copy and the OIHW -> OHWI weight regrouping that let
 //   NCHW tensors use the channels-last feeds,
 //   and the ordered split-K finishing pass.
+#include <type_traits>
+
 #include "conv_internal.h"
 
 namespace convlower {
@@ -133,79 +135,148 @@ hipError_t launch_im2win(const void *x, void *xwin, const Geom &g, bool nhwc, bo
 }
 
 // NCHW -> NHWC copy (each image's [C][H*W] matrix transposed to [H*W][C]).
-// A block moves a tile of 64 channels x 64*VEC/... pixels: 16-byte loads run
-// along the pixels of one channel, the tile is transposed through LDS, and
-// 16-byte stores run along the channels of one pixel.  Used when H*W and C
-// are multiples of the 16-byte element count (otherwise the window reorder
-// of a 1x1 kernel, which is the same copy element by element, does it).
-template <typename S>
-__global__ __launch_bounds__(256) void nchw_to_nhwc_kernel(const S *__restrict__ x, S *__restrict__ xc, int C,
-                                                           int HW, int tiles_hw) {
-    constexpr int V = 16 / (int)sizeof(S);  // elements per 16 bytes
-    constexpr int TC = 64;                  // channels per tile
-    constexpr int THW = 128;                // pixels per tile
-    __shared__ S tile[TC][THW + 2];
+// NCHW -> NHWC copy of x, transposed through LDS in tiles of 64 channels x 64
+// pixels.  Loads run along the pixels of one channel plane in LW-byte chunks
+// (the widest that the plane length H*W and the pointer alignment allow, so a
+// chunk never leaves its plane); stores run along the channels of one pixel
+// in 16-byte chunks (C is a multiple of the 16-byte element count).
+constexpr int kTrC = 64, kTrP = 64;  // tile: channels x pixels
+
+template <typename S, int LW>
+__device__ __forceinline__ void transpose_tile(const S *__restrict__ x, S *__restrict__ xc, int C, int HW,
+                                               int n, int c0, int p0, S (*tile)[kTrP + 2]) {
+    constexpr int LE = LW / (int)sizeof(S);  // elements per load
+    constexpr int CPR = kTrP / LE;           // loads per channel row
+    constexpr int NL = kTrC * CPR / 256;     // loads per thread
+    static_assert(NL >= 1 && (kTrC * CPR) % 256 == 0, "tile must split evenly");
+    typedef typename std::conditional<LW == 16, uint4,
+            typename std::conditional<LW == 8, uint2,
+            typename std::conditional<LW == 4, uint32_t, S>::type>::type>::type chunk_t;
     const int tid = threadIdx.x;
-    const long long n = blockIdx.y;
-    const int c0 = blockIdx.z * TC;
-    const int hw0 = blockIdx.x * THW;
-    const S *src = x + n * (long long)C * HW;
-    S *dst = xc + n * (long long)C * HW;
-    // load: chunk q covers pixels hw0 + (q % (THW/V))*V .. +V of channel q / (THW/V)
-    constexpr int CPR = THW / V;  // chunks per channel row
-    for (int q = tid; q < TC * CPR; q += 256) {
-        const int cl = q / CPR, hl = (q % CPR) * V;
-        const int c = c0 + cl, hw = hw0 + hl;
-        union {
-            uint4 v;
-            S e[V];
-        } u;
-        u.v = make_uint4(0, 0, 0, 0);
-        if (c < C && hw < HW) u.v = *(const uint4 *)(src + (long long)c * HW + hw);  // HW % V == 0
+    const S *src = x + (long long)n * C * HW;
+    chunk_t v[NL];
 #pragma unroll
-        for (int j = 0; j < V; ++j) tile[cl][hl + j] = u.e[j];
+    for (int i = 0; i < NL; ++i) {  // every load first, then the LDS writes
+        const int q = tid + 256 * i;
+        const int cl = q / CPR, pl = (q % CPR) * LE;
+        const int c = c0 + cl, p = p0 + pl;
+        v[i] = chunk_t{};
+        if (c < C && p < HW) v[i] = *(const chunk_t *)(src + (long long)c * HW + p);
+    }
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        const int q = tid + 256 * i;
+        const int cl = q / CPR, pl = (q % CPR) * LE;
+        S e[LE];
+        __builtin_memcpy(e, &v[i], LW);
+#pragma unroll
+        for (int j = 0; j < LE; ++j) tile[cl][pl + j] = e[j];
     }
     __syncthreads();
-    // store: chunk q covers channels c0 + (q % (TC/V))*V .. +V of pixel q / (TC/V)
-    constexpr int CPP = TC / V;  // chunks per pixel
-    for (int q = tid; q < THW * CPP; q += 256) {
-        const int hl = q / CPP, cl = (q % CPP) * V;
-        const int c = c0 + cl, hw = hw0 + hl;
-        if (c >= C || hw >= HW) continue;
-        union {
-            uint4 v;
-            S e[V];
-        } u;
+    constexpr int V = 16 / (int)sizeof(S);
+    constexpr int CPP = kTrC / V;  // 16-byte chunks per pixel
+    S *dst = xc + (long long)n * C * HW;
 #pragma unroll
-        for (int j = 0; j < V; ++j) u.e[j] = tile[cl + j][hl];
-        *(uint4 *)(dst + (long long)hw * C + c) = u.v;  // C % V == 0
+    for (int i = 0; i < kTrP * CPP / 256; ++i) {
+        const int q = tid + 256 * i;
+        const int pl = q / CPP, cl = (q % CPP) * V;
+        const int c = c0 + cl, p = p0 + pl;
+        if (c >= C || p >= HW) continue;
+        S e[V];
+#pragma unroll
+        for (int j = 0; j < V; ++j) e[j] = tile[cl + j][pl];
+        uint4 out;
+        __builtin_memcpy(&out, e, 16);
+        *(uint4 *)(dst + (long long)p * C + c) = out;
     }
 }
 
-hipError_t launch_nchw_to_nhwc(const void *x, void *x_cl, const Geom &g, bool bf16, hipStream_t st) {
-    const int HW = g.H * g.W, V = bf16 ? 8 : 4;
-    const bool aligned = (uintptr_t)x % 16 == 0 && (uintptr_t)x_cl % 16 == 0;
-    if (HW % V == 0 && g.C % V == 0 && aligned) {
-        const int tiles_hw = (HW + 127) / 128;
-        dim3 grid(tiles_hw, g.N, (g.C + 63) / 64);
-        if (bf16)
-            hipLaunchKernelGGL(nchw_to_nhwc_kernel<uint16_t>, grid, dim3(256), 0, st, (const uint16_t *)x,
-                               (uint16_t *)x_cl, g.C, HW, tiles_hw);
-        else
-            hipLaunchKernelGGL(nchw_to_nhwc_kernel<float>, grid, dim3(256), 0, st, (const float *)x, (float *)x_cl,
-                               g.C, HW, tiles_hw);
-        return hipGetLastError();
+// One launch for the preparation of an NCHW call on the indirection path:
+// blocks [0, nt) copy x channels-last, the next nib blocks build the
+// indirection buffer (channels-last offsets), the rest regroup the weights
+// OIHW -> OHWI (when nw > 0).
+struct PrepArgs {
+    const void *x;
+    void *xc;
+    int32_t *ib;
+    const void *w;
+    void *wo;
+    Geom g;
+    int tiles_p, tiles_c;  // transpose tiles per image along pixels, channels
+    int nt, nib;           // blocks of the first two kinds
+    long long nw;          // weight elements to regroup (0: none)
+};
+
+template <typename S, int LW>
+__global__ __launch_bounds__(256) void prep_nchw_kernel(PrepArgs a) {
+    __shared__ S tile[kTrC][kTrP + 2];
+    const Geom &g = a.g;
+    int b = blockIdx.x;
+    if (b < a.nt) {
+        const int pt = b % a.tiles_p;
+        b /= a.tiles_p;
+        const int ct = b % a.tiles_c, n = b / a.tiles_c;
+        transpose_tile<S, LW>((const S *)a.x, (S *)a.xc, g.C, g.H * g.W, n, ct * kTrC, pt * kTrP, tile);
+        return;
     }
-    // The window-ordered tensor of a 1x1 stride-1 unpadded kernel is [N][H][W][1][C].
-    Geom one = g;
-    one.KH = one.KW = one.s = one.d = 1;
-    one.p = 0;
-    one.Ho = g.H;
-    one.Wo = g.W;
-    one.Wwin = g.W;
-    one.P = HW;
-    one.T = 1;
-    return launch_im2win(x, x_cl, one, false, bf16, st);
+    b -= a.nt;
+    if (b < a.nib) {
+        const long long idx = (long long)b * 256 + threadIdx.x;
+        if (idx >= (long long)g.P * g.T) return;
+        const int p = (int)(idx / g.T), t = (int)(idx - (long long)p * g.T);
+        const int ho = p / g.Wo, wo = p - ho * g.Wo;
+        const int kh = t / g.KW, kw = t - kh * g.KW;
+        const int hi = ho * g.s + kh * g.d - g.p, wi = wo * g.s + kw * g.d - g.p;
+        a.ib[idx] = (hi >= 0 && hi < g.H && wi >= 0 && wi < g.W) ? (hi * g.W + wi) * g.C : -1;
+        return;
+    }
+    b -= a.nib;
+    const long long e = (long long)b * 256 + threadIdx.x;
+    if (e >= a.nw) return;
+    const int ci = (int)(e % g.C);
+    const long long r = e / g.C;
+    const int t = (int)(r % g.T);
+    const long long co = r / g.T;
+    ((S *)a.wo)[e] = ((const S *)a.w)[(co * g.C + ci) * g.T + t];
+}
+
+hipError_t launch_prep_nchw(const void *x, void *x_cl, int32_t *ib, const void *w, void *w_ohwi, const Geom &g,
+                            bool bf16, hipStream_t st) {
+    const int ES = bf16 ? 2 : 4, HW = g.H * g.W;
+    PrepArgs a;
+    a.x = x;
+    a.xc = x_cl;
+    a.ib = ib;
+    a.w = w;
+    a.wo = w_ohwi;
+    a.g = g;
+    a.tiles_p = (HW + kTrP - 1) / kTrP;
+    a.tiles_c = (g.C + kTrC - 1) / kTrC;
+    a.nt = g.N * a.tiles_c * a.tiles_p;
+    a.nib = ib ? (int)blocks_for((long long)g.P * g.T, 256) : 0;
+    a.nw = w_ohwi ? (long long)g.Co * g.T * g.C : 0;
+    const long long blocks = (long long)a.nt + a.nib + blocks_for(a.nw, 256);
+    // Widest load that keeps every chunk inside its channel plane and aligned.
+    int lw = 16;
+    while (lw > ES && ((long long)HW * ES % lw != 0 || (uintptr_t)x % lw != 0)) lw >>= 1;
+    if ((uintptr_t)x_cl % 16 != 0 || (g.C * ES) % 16 != 0) return hipErrorInvalidValue;
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, st, a);
+        return hipGetLastError();
+    };
+    if (bf16) {
+        switch (lw) {
+            case 16: return go(prep_nchw_kernel<uint16_t, 16>);
+            case 8: return go(prep_nchw_kernel<uint16_t, 8>);
+            case 4: return go(prep_nchw_kernel<uint16_t, 4>);
+            default: return go(prep_nchw_kernel<uint16_t, 2>);
+        }
+    }
+    switch (lw) {
+        case 16: return go(prep_nchw_kernel<float, 16>);
+        case 8: return go(prep_nchw_kernel<float, 8>);
+        default: return go(prep_nchw_kernel<float, 4>);
+    }
 }
 
 // ---------------------------------------------------------------------------

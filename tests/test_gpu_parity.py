@@ -179,6 +179,32 @@ def test_full_size_integer_exact_sampled(name, layout):
     assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("layout", ["NCHW", "NHWC"])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_many_tiles_odd_planes_sampled(layout, dtype):
+    """More than 512 output tiles select the 512-thread main loop; planes of
+    225 pixels (odd) make its NCHW stores go element by element.  fp32 runs
+    on integer inputs and must be exact; bf16 within the tolerance."""
+    from convolution_lowering_amd.workloads import Layer
+    L = Layer("many-tiles-odd-planes", 160, 64, 15, 15, 512, 3, 3, 1, 1, 1, seed=91)
+    integer = dtype == "fp32"
+    x, w, b = make_inputs(L, dtype, layout, integer=integer)
+    _say(f"[gpu] many-tiles {dtype} {layout}")
+    y = cl.conv2d_fwd(x.to(DEV), w.to(DEV), b.to(DEV), L.stride, L.pad, L.dilation, layout, "indirect")
+    torch.cuda.synchronize()
+    pts = _sample_points(L, L.N, 3000, L.seed)
+    yn = _to_nchw(y, layout)
+    idx = torch.from_numpy(pts.astype(np.int64)).to(DEV)
+    got = yn[idx[:, 0], idx[:, 1], idx[:, 2], idx[:, 3]].double().cpu().numpy()
+    lay = oracle.NCHW if layout == "NCHW" else oracle.NHWC
+    ref, dn = oracle.conv2d_points(x, w, b, pts, L.stride, L.pad, L.dilation, lay)
+    if integer:
+        assert np.array_equal(got, ref)
+    else:
+        err = np.abs(got - ref) / np.where(dn > 0, dn, 1.0)
+        assert float(err.max()) <= TOL[dtype], f"{err.max():.3e}"
+
+
 # --- edge cases ----------------------------------------------------------------
 
 EDGE = [
@@ -196,6 +222,11 @@ EDGE = [
     ("C-multiple-of-8", 2, 24, 13, 15, 130, 3, 3, 1, 1, 1),
     ("channels-last-copy", 3, 16, 8, 12, 20, 3, 3, 1, 1, 1),     # NCHW copied channels-last, ragged tiles
     ("channels-last-copy-wide", 2, 72, 16, 10, 40, 3, 3, 2, 1, 1),
+    # 256 x 128 main loops with output planes whose pixel count is odd, or 2
+    # or 4 modulo 8 (NCHW stores in pieces that never cross an image)
+    ("planes-odd", 3, 64, 7, 9, 96, 3, 3, 1, 1, 1),
+    ("planes-2-mod-8", 4, 32, 9, 10, 130, 3, 3, 1, 1, 1),
+    ("planes-4-mod-8", 3, 64, 10, 10, 128, 3, 3, 1, 1, 1),
 ]
 
 
