@@ -17,11 +17,13 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 // Main loops whose indirection slice in LDS holds up to 12 taps at any
 // tile height (the others hold 3072 entries).
-bool wide_slice(int tile) { return tile == TILE_256x128_DUAL || tile == TILE_256x128_OCT; }
+bool wide_slice(int tile) {
+    return tile == TILE_256x128_DUAL || tile == TILE_256x128_OCT || tile == TILE_256x64_DUAL;
+}
 
 int tile_rows(int tile) {
     return tile == TILE_32x64                                                                   ? 32
-           : (tile == TILE_256x128 || tile == TILE_256x128_DUAL || tile == TILE_256x128_OCT) ? 256
+           : (tile == TILE_256x128 || wide_slice(tile))                                      ? 256
                                                                                              : 128;
 }
 
@@ -161,14 +163,19 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
         }
         default: dual = oct = false;
     }
+    const long long tiles256 = ((g.M + 255) / 256) * ((g.Co + 127) / 128);
     int BM, BN;
     if (g.M <= 64) {
         pl->tile = TILE_32x64; BM = 32; BN = 64;
+    } else if (g.Co <= 64 && dual) {
+        pl->tile = TILE_256x64_DUAL; BM = 256; BN = 64;
     } else if (g.Co <= 64) {
         pl->tile = TILE_128x64; BM = 128; BN = 64;
-    } else if (oct && ((g.M + 255) / 256) * ((g.Co + 127) / 128) > 512) {
-        // More tiles than two resident blocks per CU can hold in one round:
-        // one 512-thread block per CU, with whole-cache-line loads.
+    } else if (oct && (tiles256 > 512 || tiles256 <= 256)) {
+        // One 512-thread block per CU (two wavefronts on every SIMD from one
+        // block, whole-cache-line loads): grids of more tiles than two
+        // resident blocks per CU hold in one round, or of no more tiles than
+        // there are CUs.
         pl->tile = TILE_256x128_OCT; BM = 256; BN = 128;
     } else if (dual) {
         // Up to one round of two blocks per CU (their prologues and epilogues
@@ -192,7 +199,12 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     long long blocks = ((g.M + BM - 1) / BM) * ((g.Co + BN - 1) / BN);
     long long ktiles = (g.K + BK - 1) / BK;
     int splits = 1;
-    if (blocks < 256 && ktiles >= 16) {
+    // Split K only where too few tiles leave most CUs idle: the two-wavefront
+    // loops keep a CU busy with a single block, and the partials cost a pass
+    // over M x Co fp32 values per split.
+    const bool two_wave =
+        pl->tile == TILE_256x128_DUAL || pl->tile == TILE_256x128_OCT || pl->tile == TILE_256x64_DUAL;
+    if (blocks < (two_wave ? 64 : 256) && ktiles >= 16) {
         // Enough splits to give every compute unit work, each split at least
         // 4 K tiles, and the whole workspace (partials included) kept below
         // the im2col footprint.
@@ -377,7 +389,8 @@ conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias
     // Misaligned pointers fall back to the element-gather loop, which has no
     // 256x128 variant; the split count (and so the workspace) is unchanged.
     int tile = pl.tile;
-    if (!a_vec && (tile == TILE_256x128 || wide_slice(tile))) tile = TILE_128x128;
+    if (!a_vec && (tile == TILE_256x128 || wide_slice(tile)))
+        tile = tile == TILE_256x64_DUAL ? TILE_128x64 : TILE_128x128;
     {
         uint32_t c = (uint32_t)g.C, sh = 0;
         while (!(c & 1u)) {

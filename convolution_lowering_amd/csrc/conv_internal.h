@@ -43,8 +43,9 @@ struct GemmArgs {
 // Tile shapes of the main loop (block = 256 threads = 4 wavefronts, 2x2).
 // TILE_256x128_DUAL and TILE_256x128_OCT are the 256 x 128 main loops with
 // two wavefronts per SIMD (two 256-thread blocks per compute unit with 64-byte
-// K tiles, or one 512-thread block with 128-byte K tiles), for 16-byte-row
-// feeds whose K tiles stay inside one tap.
+// K tiles, or one 512-thread block with 128-byte K tiles; TILE_256x64_DUAL is
+// the two-blocks-per-CU loop for at most 64 output channels), for
+// 16-byte-row feeds whose K tiles stay inside one tap.
 enum Tile : int {
     TILE_128x128 = 0,
     TILE_128x64 = 1,
@@ -52,7 +53,8 @@ enum Tile : int {
     TILE_256x128 = 3,
     TILE_256x128_DUAL = 4,
     TILE_256x128_OCT = 5,
-    TILE_COUNT = 6
+    TILE_256x64_DUAL = 6,
+    TILE_COUNT = 7
 };
 
 hipError_t launch_igemm_bf16(const GemmArgs &a, int feed, bool out_nchw, bool a_vec, bool b_vec,

@@ -41,11 +41,11 @@ namespace convlower {
 
 constexpr int kDualMaxTaps = 12;  // KH*KW taps the LDS slice of the indirection buffer holds
 
-// Shape of one main-loop variant: block tile 256 x 128, KCH 16-byte chunks
+// Shape of one main-loop variant: block tile BM x BN, KCH 16-byte chunks
 // per stage row, NW wavefronts in a WGM x (NW / WGM) grid.
-template <typename S, int KCH_, int NW_, int WGM_>
+template <typename S, int KCH_, int NW_, int WGM_, int BM_ = 256, int BN_ = 128>
 struct DualCfg {
-    static constexpr int BM = 256, BN = 128;
+    static constexpr int BM = BM_, BN = BN_;
     static constexpr int ES = (int)sizeof(S);
     static constexpr int VEC = 16 / ES;
     static constexpr int KCH = KCH_;                 // 16-byte chunks per stage row
@@ -61,7 +61,7 @@ struct DualCfg {
     static constexpr int WPM = BM / WGM, WCN = BN / WGN;  // wavefront tile
     static constexpr int MT = 32, TP = WPM / MT, TC = WCN / MT;
     static constexpr int NG = KCH / 2;  // MFMA K steps per tile (two chunks per step)
-    static constexpr int MIN_BLOCKS = NW_ == 4 ? 2 : 1;
+
     static_assert(IPW_A * NW * 64 == BM * KCH && IPW_B * NW * 64 == BN * KCH, "loads must split evenly");
     static_assert(TP >= 1 && TC >= 1 && WGM * WGN == NW, "wavefront grid");
 };
@@ -73,6 +73,11 @@ using DualCfg4 = DualCfg<S, 4, 4, 2>;
 // (150 KB of LDS): whole-cache-line loads, two wavefronts per SIMD.
 template <typename S>
 using DualCfg8 = DualCfg<S, 8, 8, 4>;
+// Block tile 256 x 64 for layers with at most 64 output channels: four
+// wavefronts of 64 x 64 stacked along the pixels, two blocks per compute
+// unit (66 KB of LDS each).
+template <typename S>
+using DualCfg4N64 = DualCfg<S, 4, 4, 4, 256, 64>;
 
 // Stage slot of chunk c of row r (rows of KCH chunks).  A b128 LDS read is
 // served 16 lanes per cycle from one 256-byte line of banks; XOR-ing the
@@ -504,6 +509,11 @@ __global__ __launch_bounds__(256, 2) void igemm_dual_kernel(GemmArgs A) {
 template <typename S, int FEED, bool OUT_NCHW>
 __global__ __launch_bounds__(512, 1) void igemm_oct_kernel(GemmArgs A) {
     igemm_dual_body<S, FEED, OUT_NCHW, DualCfg8<S>>(A);
+}
+
+template <typename S, int FEED, bool OUT_NCHW>
+__global__ __launch_bounds__(256, 2) void igemm_dual64_kernel(GemmArgs A) {
+    igemm_dual_body<S, FEED, OUT_NCHW, DualCfg4N64<S>>(A);
 }
 
 }  // namespace convlower

@@ -571,6 +571,7 @@ static hipError_t launch_tile(const GemmArgs &a, int tile, int splits, hipStream
             case TILE_256x128: return go(igemm_dma_kernel<S, FEED, OUT_NCHW, 256, 128, BKW>, 256, 128);
             case TILE_256x128_DUAL: return go(igemm_dual_kernel<S, FEED, OUT_NCHW>, 256, 128);
             case TILE_256x128_OCT: return go(igemm_oct_kernel<S, FEED, OUT_NCHW>, 256, 128, 512);
+            case TILE_256x64_DUAL: return go(igemm_dual64_kernel<S, FEED, OUT_NCHW>, 256, 64);
             default: return hipErrorInvalidValue;
         }
     } else {  // element gathers through registers
