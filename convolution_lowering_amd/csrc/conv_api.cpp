@@ -18,7 +18,8 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 // Main loops whose indirection slice in LDS holds up to 12 taps at any
 // tile height (the others hold 3072 entries).
 bool wide_slice(int tile) {
-    return tile == TILE_256x128_DUAL || tile == TILE_256x128_OCT || tile == TILE_256x64_DUAL;
+    return tile == TILE_256x128_DUAL || tile == TILE_256x128_OCT || tile == TILE_256x64_DUAL ||
+           tile == TILE_256x256_OCT;
 }
 
 int tile_rows(int tile) {
@@ -169,6 +170,10 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
         pl->tile = TILE_32x64; BM = 32; BN = 64;
     } else if (g.Co <= 64 && dual) {
         pl->tile = TILE_256x64_DUAL; BM = 256; BN = 64;
+    } else if (dual && g.Co >= 256 && g.K >= 512 && ((g.M + 255) / 256) * ((g.Co + 255) / 256) > 256) {
+        // Deep layers with many output channels and more 256 x 256 tiles
+        // than CUs: the larger block tile loads a third fewer bytes per MFMA.
+        pl->tile = TILE_256x256_OCT; BM = 256; BN = 256;
     } else if (g.Co <= 64) {
         pl->tile = TILE_128x64; BM = 128; BN = 64;
     } else if (oct && (tiles256 > 512 || tiles256 <= 256)) {
@@ -202,8 +207,7 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     // Split K only where too few tiles leave most CUs idle: the two-wavefront
     // loops keep a CU busy with a single block, and the partials cost a pass
     // over M x Co fp32 values per split.
-    const bool two_wave =
-        pl->tile == TILE_256x128_DUAL || pl->tile == TILE_256x128_OCT || pl->tile == TILE_256x64_DUAL;
+    const bool two_wave = wide_slice(pl->tile);
     if (blocks < (two_wave ? 64 : 256) && ktiles >= 16) {
         // Enough splits to give every compute unit work, each split at least
         // 4 K tiles, and the whole workspace (partials included) kept below

@@ -44,8 +44,9 @@ struct GemmArgs {
 // TILE_256x128_DUAL and TILE_256x128_OCT are the 256 x 128 main loops with
 // two wavefronts per SIMD (two 256-thread blocks per compute unit with 64-byte
 // K tiles, or one 512-thread block with 128-byte K tiles; TILE_256x64_DUAL is
-// the two-blocks-per-CU loop for at most 64 output channels), for
-// 16-byte-row feeds whose K tiles stay inside one tap.
+// the two-blocks-per-CU loop for at most 64 output channels; the 256x256 OCT
+// tile is a 512-thread block of eight 128 x 64 wavefront tiles),
+// for 16-byte-row feeds whose K tiles stay inside one tap.
 enum Tile : int {
     TILE_128x128 = 0,
     TILE_128x64 = 1,
@@ -54,7 +55,8 @@ enum Tile : int {
     TILE_256x128_DUAL = 4,
     TILE_256x128_OCT = 5,
     TILE_256x64_DUAL = 6,
-    TILE_COUNT = 7
+    TILE_256x256_OCT = 7,
+    TILE_COUNT = 8
 };
 
 hipError_t launch_igemm_bf16(const GemmArgs &a, int feed, bool out_nchw, bool a_vec, bool b_vec,

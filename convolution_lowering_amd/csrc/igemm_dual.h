@@ -78,6 +78,12 @@ using DualCfg8 = DualCfg<S, 8, 8, 4>;
 // unit (66 KB of LDS each).
 template <typename S>
 using DualCfg4N64 = DualCfg<S, 4, 4, 4, 256, 64>;
+// Eight wavefronts of 128 x 64 (two per SIMD), one block per compute unit,
+// 64-byte rows, block tile 256 x 256 (wavefront grid 2 x 4, 103 KB of LDS):
+// it loads 32 bytes per MFMA cycle of the compute unit, against 48 for
+// 256 x 128.
+template <typename S>
+using DualCfg8Sq = DualCfg<S, 4, 8, 2, 256, 256>;
 
 // Stage slot of chunk c of row r (rows of KCH chunks).  A b128 LDS read is
 // served 16 lanes per cycle from one 256-byte line of banks; XOR-ing the
@@ -379,7 +385,10 @@ __device__ __forceinline__ void igemm_dual_body(const GemmArgs &A) {
     constexpr int COLS = OUT_NCHW ? BM : BN;  // elements per run
     constexpr int PADE = 16 / (int)sizeof(S);
     constexpr int RSTR = COLS + PADE;  // LDS row stride, elements
-    constexpr int NPASS = (long long)ROWS * RSTR * (int)sizeof(S) <= 3LL * NSLOT * 16 ? 1 : 2;
+    constexpr long long TILE_BYTES = (long long)ROWS * RSTR * (int)sizeof(S);
+    constexpr int NPASS = TILE_BYTES <= 3LL * NSLOT * 16       ? 1
+                          : TILE_BYTES <= 2 * 3LL * NSLOT * 16 ? 2
+                                                               : 4;
     constexpr int PROWS = ROWS / NPASS;
     constexpr int CPR = COLS / VEC;  // 16-byte chunks per run
     static_assert((long long)PROWS * RSTR * (int)sizeof(S) <= 3LL * NSLOT * 16, "epilogue tile fits the stages");
@@ -514,6 +523,11 @@ __global__ __launch_bounds__(512, 1) void igemm_oct_kernel(GemmArgs A) {
 template <typename S, int FEED, bool OUT_NCHW>
 __global__ __launch_bounds__(256, 2) void igemm_dual64_kernel(GemmArgs A) {
     igemm_dual_body<S, FEED, OUT_NCHW, DualCfg4N64<S>>(A);
+}
+
+template <typename S, int FEED, bool OUT_NCHW>
+__global__ __launch_bounds__(512, 1) void igemm_oct_sq_kernel(GemmArgs A) {
+    igemm_dual_body<S, FEED, OUT_NCHW, DualCfg8Sq<S>>(A);
 }
 
 }  // namespace convlower
