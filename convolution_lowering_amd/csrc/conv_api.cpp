@@ -36,6 +36,7 @@ struct Plan {
     int tile, splits, kps;
     bool need_ibuf, need_win, need_wpack;
     bool need_xcl;  // channels-last copy of an NCHW input
+    int chunk_n;    // images per main-loop pass (< N: the batch goes through the copy in parts)
     bool rows16;  // the feed can read X_col rows in 16-byte chunks (by shape)
     size_t off_ibuf, off_win, off_xcl, off_wpack, off_part, total;
     size_t esize;
@@ -83,6 +84,7 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     memset(pl, 0, sizeof(*pl));
     conv_status_t st = make_geom(N, C, H, W, Co, KH, KW, s, p, d, &pl->g);
     if (st != CONV_OK) return st;
+    pl->chunk_n = N;
     const Geom &g = pl->g;
     if (!sizes_supported(g)) return CONV_ERR_UNSUPPORTED;
     pl->bf16 = dtype == CONV_DTYPE_BF16;
@@ -98,12 +100,22 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     if (algo == CONV_ALGO_AUTO) algo = (whole || one) ? CONV_ALGO_GEMM : CONV_ALGO_INDIRECT;
     switch (algo) {
         case CONV_ALGO_GEMM:
-            if (whole)
+            if (whole) {
                 pl->feed = FEED_ROWMAJOR;  // Ho = Wo = 1: both layouts store y as [N][Co]
-            else if (one)
-                pl->feed = pl->nhwc ? FEED_ROWMAJOR : FEED_NCHW_1X1;
-            else
+            } else if (one && pl->nhwc) {
+                pl->feed = FEED_ROWMAJOR;
+            } else if (one && g.C % (pl->bf16 ? 8 : 4) == 0 && g.N >= 2) {
+                // NCHW 1x1: half the batch at a time is copied channels-last
+                // and multiplied as a plain GEMM (the copy of all of x would
+                // be as large as X_col itself).
+                pl->feed = FEED_ROWMAJOR;
+                pl->need_xcl = true;
+                pl->chunk_n = (g.N + 1) / 2;
+            } else if (one) {
+                pl->feed = FEED_NCHW_1X1;
+            } else {
                 return CONV_ERR_UNSUPPORTED;
+            }
             break;
         case CONV_ALGO_INDIRECT:
             // The indirection buffer addresses each input pixel's row of C
@@ -131,7 +143,9 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
         default:
             return CONV_ERR_INVALID_ARG;
     }
-    pl->out_nchw = !pl->nhwc && pl->feed != FEED_ROWMAJOR;
+    pl->out_nchw = !pl->nhwc && !(pl->feed == FEED_ROWMAJOR && whole);
+    // GEMM rows of one main-loop pass.
+    const long long Mt = (long long)pl->chunk_n * g.P;
 
     // Tile shape and split-K.  The 256x128 tile (wavefront tiles of 128x64,
     // a quarter less LDS and L2 traffic per MFMA) needs the 16-byte-row feeds.
@@ -164,13 +178,13 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
         }
         default: dual = oct = false;
     }
-    const long long tiles256 = ((g.M + 255) / 256) * ((g.Co + 127) / 128);
+    const long long tiles256 = ((Mt + 255) / 256) * ((g.Co + 127) / 128);
     int BM, BN;
-    if (g.M <= 64) {
+    if (Mt <= 64) {
         pl->tile = TILE_32x64; BM = 32; BN = 64;
     } else if (g.Co <= 64 && dual) {
         pl->tile = TILE_256x64_DUAL; BM = 256; BN = 64;
-    } else if (dual && g.Co >= 256 && g.K >= 512 && ((g.M + 255) / 256) * ((g.Co + 255) / 256) > 256) {
+    } else if (dual && g.Co >= 256 && g.K >= 512 && ((Mt + 255) / 256) * ((g.Co + 255) / 256) > 256) {
         // Deep layers with many output channels and more 256 x 256 tiles
         // than CUs: the larger block tile loads a third fewer bytes per MFMA.
         pl->tile = TILE_256x256_OCT; BM = 256; BN = 256;
@@ -188,7 +202,7 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
         pl->tile = TILE_256x128_DUAL; BM = 256; BN = 128;
     } else if (oct) {
         pl->tile = TILE_256x128_OCT; BM = 256; BN = 128;
-    } else if (rows16 && g.M >= 65536) {
+    } else if (rows16 && Mt >= 65536) {
         pl->tile = TILE_256x128; BM = 256; BN = 128;
     } else {
         pl->tile = TILE_128x128; BM = 128; BN = 128;
@@ -197,11 +211,11 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     size_t lowered = 0;
     if (pl->need_ibuf) lowered = align_up(lowered + (size_t)g.P * g.T * sizeof(int32_t));
     if (pl->need_win) lowered = align_up(lowered + (size_t)g.N * g.Ho * g.Wwin * g.KH * g.C * pl->esize);
-    if (pl->need_xcl) lowered = align_up(lowered + (size_t)g.N * g.C * g.H * g.W * pl->esize);
+    if (pl->need_xcl) lowered = align_up(lowered + (size_t)pl->chunk_n * g.C * g.H * g.W * pl->esize);
     if (pl->need_wpack) lowered = align_up(lowered + (size_t)g.Co * g.K * pl->esize);
 
     const int BK = pl->bf16 ? 64 : 32;  // the main loop's K tile (128-byte LDS rows)
-    long long blocks = ((g.M + BM - 1) / BM) * ((g.Co + BN - 1) / BN);
+    long long blocks = ((Mt + BM - 1) / BM) * ((g.Co + BN - 1) / BN);
     long long ktiles = (g.K + BK - 1) / BK;
     int splits = 1;
     // Split K only where too few tiles leave most CUs idle: the two-wavefront
@@ -215,7 +229,7 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
         long long want = (512 + blocks - 1) / blocks;
         long long by_depth = ktiles / 4;
         long long im2col_bytes = g.M * g.K * (long long)pl->esize;
-        long long per_split = (long long)align_up((size_t)(g.M * g.Co * 4LL));
+        long long per_split = (long long)align_up((size_t)(Mt * g.Co * 4LL));
         long long room = im2col_bytes - (long long)lowered - 1;
         long long by_space = room > 0 ? room / per_split : 0;
         long long sp = want;
@@ -240,7 +254,7 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     }
     if (pl->need_xcl) {
         pl->off_xcl = off;
-        off = align_up(off + (size_t)g.N * g.C * g.H * g.W * pl->esize);
+        off = align_up(off + (size_t)pl->chunk_n * g.C * g.H * g.W * pl->esize);
     }
     if (pl->need_wpack) {
         pl->off_wpack = off;
@@ -248,7 +262,7 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     }
     if (splits > 1) {
         pl->off_part = off;
-        off = align_up(off + (size_t)splits * g.M * g.Co * sizeof(float));
+        off = align_up(off + (size_t)splits * Mt * g.Co * sizeof(float));
     }
     pl->total = off;
     return CONV_OK;
@@ -311,62 +325,12 @@ namespace {
 // The launch sequence of one call.  `prebuilt` (may be null) is an
 // indirection buffer the caller built before; then step (b) is skipped.
 // Steps the plan does not ask for (need_*) are not run.
-conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias, void *y, const int32_t *prebuilt,
-                  conv_stream_t stream, void *workspace, size_t workspace_bytes) {
-    if (!x || !w || !y) return CONV_ERR_INVALID_ARG;
-    const size_t es = pl.esize;
-    if ((uintptr_t)x % es || (uintptr_t)w % es || (uintptr_t)y % es || (bias && (uintptr_t)bias % es))
-        return CONV_ERR_INVALID_ARG;
-    if (pl.total > 0 && (!workspace || workspace_bytes < pl.total)) return CONV_ERR_WORKSPACE;
-    if (pl.total > 0 && (uintptr_t)workspace % 16) return CONV_ERR_INVALID_ARG;
-
-    hipStream_t s = (hipStream_t)stream;
-    const Geom &g = pl.g;
-    char *ws = (char *)workspace;
+// The main loop (and the split-K finish) for one pass: a.g is the pass's
+// geometry, a.a_src / a.b / a.y its operands.
+conv_status_t launch_main(const Plan &pl, GemmArgs &a, hipStream_t s) {
+    const Geom &g = a.g;
     const int VEC = pl.bf16 ? 8 : 4;
     auto al16 = [](const void *ptr) { return (uintptr_t)ptr % 16 == 0; };
-
-    GemmArgs a;
-    memset(&a, 0, sizeof(a));
-    a.g = g;
-    a.bias = bias;
-    a.y = y;
-    a.k_per_split = pl.kps;
-    a.b = w;
-    a.a_src = x;
-
-    // Offsets of the indirection buffer follow the layout the main loop reads.
-    const bool ib_rows = pl.feed == FEED_IND_NHWC;
-    int32_t *ib_build = nullptr;  // buffer still to build
-    if (prebuilt) {
-        a.ibuf = prebuilt;
-    } else if (pl.need_ibuf) {
-        ib_build = (int32_t *)(ws + pl.off_ibuf);
-        a.ibuf = ib_build;
-    }
-    void *wp = pl.need_wpack ? (void *)(ws + pl.off_wpack) : nullptr;
-    bool wp_done = false;
-    if (pl.need_xcl) {
-        // One launch: the channels-last copy of x, the indirection buffer and
-        // the regrouped weights.
-        void *xc = ws + pl.off_xcl;
-        if (launch_prep_nchw(x, xc, ib_build, w, wp, g, pl.bf16, s) != hipSuccess) return CONV_ERR_HIP;
-        a.a_src = xc;
-        ib_build = nullptr;
-        wp_done = true;
-    }
-    if (ib_build && launch_build_indirection(ib_build, g, ib_rows, s) != hipSuccess) return CONV_ERR_HIP;
-    if (pl.need_win) {
-        void *xw = ws + pl.off_win;
-        if (launch_im2win(x, xw, g, pl.nhwc, pl.bf16, s) != hipSuccess) return CONV_ERR_HIP;
-        a.a_src = xw;
-    }
-    if (wp) {
-        if (!wp_done && launch_pack_weights_ohwi(w, wp, g, pl.bf16, s) != hipSuccess) return CONV_ERR_HIP;
-        a.b = wp;
-    }
-    if (pl.splits > 1) a.part = (float *)(ws + pl.off_part);
-
     bool a_vec;
     switch (pl.feed) {
         case FEED_ROWMAJOR: a_vec = g.K % VEC == 0 && al16(a.a_src); break;
@@ -410,10 +374,90 @@ conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias
                            : launch_igemm_f32(a, pl.feed, pl.out_nchw, a_vec, b_vec, tile, pl.splits, s);
     if (e != hipSuccess) return CONV_ERR_HIP;
     if (pl.splits > 1) {
-        if (launch_splitk_reduce(a.part, bias, y, g, pl.splits, pl.out_nchw, pl.bf16, s) != hipSuccess)
+        if (launch_splitk_reduce(a.part, a.bias, a.y, g, pl.splits, pl.out_nchw, pl.bf16, s) != hipSuccess)
             return CONV_ERR_HIP;
     }
     return CONV_OK;
+}
+
+
+conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias, void *y, const int32_t *prebuilt,
+                  conv_stream_t stream, void *workspace, size_t workspace_bytes) {
+    if (!x || !w || !y) return CONV_ERR_INVALID_ARG;
+    const size_t es = pl.esize;
+    if ((uintptr_t)x % es || (uintptr_t)w % es || (uintptr_t)y % es || (bias && (uintptr_t)bias % es))
+        return CONV_ERR_INVALID_ARG;
+    if (pl.total > 0 && (!workspace || workspace_bytes < pl.total)) return CONV_ERR_WORKSPACE;
+    if (pl.total > 0 && (uintptr_t)workspace % 16) return CONV_ERR_INVALID_ARG;
+
+    hipStream_t s = (hipStream_t)stream;
+    const Geom &g = pl.g;
+    char *ws = (char *)workspace;
+
+    GemmArgs a;
+    memset(&a, 0, sizeof(a));
+    if (pl.chunk_n < g.N) {
+        // NCHW 1x1 in parts: each part of the batch is copied channels-last
+        // into the same workspace region, then multiplied as a plain GEMM
+        // whose NCHW output lands in that part's slice of y.
+        void *xc = ws + pl.off_xcl;
+        for (int n0 = 0; n0 < g.N; n0 += pl.chunk_n) {
+            Geom gc = g;
+            gc.N = g.N - n0 < pl.chunk_n ? g.N - n0 : pl.chunk_n;
+            gc.M = (long long)gc.N * g.P;
+            const char *xs = (const char *)x + (size_t)n0 * g.C * g.H * g.W * es;
+            if (launch_prep_nchw(xs, xc, nullptr, nullptr, nullptr, gc, pl.bf16, s) != hipSuccess) return CONV_ERR_HIP;
+            a.g = gc;
+            a.bias = bias;
+            a.y = (char *)y + (size_t)n0 * g.Co * g.P * es;
+            a.k_per_split = pl.kps;
+            a.b = w;
+            a.a_src = xc;
+            conv_status_t st = launch_main(pl, a, s);
+            if (st != CONV_OK) return st;
+        }
+        return CONV_OK;
+    }
+    a.g = g;
+    a.bias = bias;
+    a.y = y;
+    a.k_per_split = pl.kps;
+    a.b = w;
+    a.a_src = x;
+
+    // Offsets of the indirection buffer follow the layout the main loop reads.
+    const bool ib_rows = pl.feed == FEED_IND_NHWC;
+    int32_t *ib_build = nullptr;  // buffer still to build
+    if (prebuilt) {
+        a.ibuf = prebuilt;
+    } else if (pl.need_ibuf) {
+        ib_build = (int32_t *)(ws + pl.off_ibuf);
+        a.ibuf = ib_build;
+    }
+    void *wp = pl.need_wpack ? (void *)(ws + pl.off_wpack) : nullptr;
+    bool wp_done = false;
+    if (pl.need_xcl) {
+        // One launch: the channels-last copy of x, the indirection buffer and
+        // the regrouped weights.
+        void *xc = ws + pl.off_xcl;
+        if (launch_prep_nchw(x, xc, ib_build, w, wp, g, pl.bf16, s) != hipSuccess) return CONV_ERR_HIP;
+        a.a_src = xc;
+        ib_build = nullptr;
+        wp_done = true;
+    }
+    if (ib_build && launch_build_indirection(ib_build, g, ib_rows, s) != hipSuccess) return CONV_ERR_HIP;
+    if (pl.need_win) {
+        void *xw = ws + pl.off_win;
+        if (launch_im2win(x, xw, g, pl.nhwc, pl.bf16, s) != hipSuccess) return CONV_ERR_HIP;
+        a.a_src = xw;
+    }
+    if (wp) {
+        if (!wp_done && launch_pack_weights_ohwi(w, wp, g, pl.bf16, s) != hipSuccess) return CONV_ERR_HIP;
+        a.b = wp;
+    }
+    if (pl.splits > 1) a.part = (float *)(ws + pl.off_part);
+
+    return launch_main(pl, a, s);
 }
 
 }  // namespace

@@ -590,7 +590,7 @@ template <typename S, int FEED>
 hipError_t launch_feed(const GemmArgs &a, bool out_nchw, bool a_vec, bool b_vec, int tile, int splits,
                        hipStream_t st) {
     constexpr bool CAN_AVEC = FEED == FEED_ROWMAJOR || FEED == FEED_IND_NHWC || FEED == FEED_WIN;
-    constexpr bool CAN_NCHW = FEED == FEED_NCHW_1X1 || FEED == FEED_IND_NCHW || FEED == FEED_IND_NHWC || FEED == FEED_WIN;
+    constexpr bool CAN_NCHW = true;  // every feed can write NCHW output
     constexpr bool CAN_NHWC = FEED == FEED_ROWMAJOR || FEED == FEED_IND_NHWC || FEED == FEED_WIN;
     if (a_vec && !b_vec) return hipErrorInvalidValue;
     if (out_nchw) {

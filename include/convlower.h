@@ -58,7 +58,7 @@ typedef enum { CONV_DTYPE_FP32 = 0, CONV_DTYPE_BF16 = 1 } conv_dtype_t;
 
 /* Which lowering feeds the contraction.
  *   AUTO      1x1 stride-1 unpadded, or kernel == whole unpadded input: the
- *             plain-GEMM (zero lowering workspace) feed; otherwise INDIRECT.
+ *             plain-GEMM feed; otherwise INDIRECT.
  *   INDIRECT  indirection buffer of per-(output pixel, tap) input offsets.
  *   IM2WIN    window-ordered copy of the input in the workspace.
  *   GEMM      the input read as the GEMM operand as it lies in memory; only
@@ -94,9 +94,12 @@ conv_status_t conv2d_output_size(int H, int W, int KH, int KW, int stride, int p
 /* Workspace bytes conv2d_fwd needs for this call (host only; no HIP call, so
  * it works without a GPU).  The figure covers the lowering structure of the
  * chosen algorithm (indirection buffer, or window-ordered input plus, for
- * NCHW, the weights regrouped channel-innermost), and fp32 split-K partials
- * on skinny layers.  It is 0 for AUTO on 1x1 layers.  *bytes_out receives the
- * size; errors as for conv2d_fwd's host checks. */
+ * NCHW, the weights regrouped channel-innermost), the channels-last copy of
+ * an NCHW input where the path reads one (for a 1x1 layer, of half the
+ * batch at a time), and fp32 split-K partials on skinny layers.  It is 0 for
+ * the plain-GEMM feed on NHWC input, and always below the im2col footprint
+ * N*Ho*Wo*C_in*KH*KW elements.  *bytes_out receives the size; errors as for
+ * conv2d_fwd's host checks. */
 conv_status_t conv2d_fwd_workspace_size(int N, int C_in, int H, int W, int C_out, int KH, int KW,
                                         int stride, int pad, int dilation,
                                         conv_layout_t layout, conv_dtype_t dtype, conv_algo_t algo,

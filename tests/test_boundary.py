@@ -70,17 +70,29 @@ def test_workspace_below_im2col(name, layout, dtype):
         assert cl.workspace_size(*_args(L, layout, dtype, "im2win")) < im2col
         assert auto == ind
     else:
-        # 1x1: no workspace at all; whole-input kernel: only the split-K partials
-        assert auto == 0 or (L.KH == L.H and L.KW == L.W)
+        # 1x1 NHWC: no workspace at all; 1x1 NCHW: the channels-last copy of
+        # half the batch; whole-input kernel: only the split-K partials
+        whole = L.KH == L.H and L.KW == L.W
+        if not whole:
+            es = 2 if dtype == "bf16" else 4
+            half = (L.N + 1) // 2 * L.C * L.H * L.W * es
+            assert auto == (0 if layout == "NHWC" else (half + 255) // 256 * 256)
         assert cl.workspace_size(*_args(L, layout, dtype, "gemm")) == auto
 
 
 @pytest.mark.parametrize("name", ["C3b", "C3d", "C5b"])
-def test_auto_is_zero_workspace_on_1x1(name):
+def test_auto_workspace_on_1x1(name):
+    """NHWC 1x1 reads x as the GEMM operand in place; NCHW 1x1 copies half
+    the batch at a time channels-last (half of the im2col footprint, which
+    for 1x1 is |x|); a single NCHW image stays on the in-place NCHW feed."""
     L = LAYERS[name]
-    for layout in ("NCHW", "NHWC"):
-        assert cl.workspace_size(*_args(L, layout, "bf16", "auto")) == 0
-        assert cl.workspace_size(*_args(L, layout, "bf16", "gemm")) == 0
+    assert cl.workspace_size(*_args(L, "NHWC", "bf16", "auto")) == 0
+    assert cl.workspace_size(*_args(L, "NHWC", "bf16", "gemm")) == 0
+    im2col = cl.im2col_bytes(L.N, L.C, L.H, L.W, L.KH, L.KW, L.stride, L.pad, L.dilation, "bf16")
+    ws = cl.workspace_size(*_args(L, "NCHW", "bf16", "auto"))
+    assert 0 < ws <= (im2col // 2 + 255) // 256 * 256 < im2col
+    one = L.with_batch(1)
+    assert cl.workspace_size(*_args(one, "NCHW", "bf16", "auto")) == 0
 
 
 def test_gemm_algo_rejected_on_windowed_layer():

@@ -227,6 +227,9 @@ EDGE = [
     ("planes-odd", 3, 64, 7, 9, 96, 3, 3, 1, 1, 1),
     ("planes-2-mod-8", 4, 32, 9, 10, 130, 3, 3, 1, 1, 1),
     ("planes-4-mod-8", 3, 64, 10, 10, 128, 3, 3, 1, 1, 1),
+    # NCHW 1x1 in two parts of the batch (odd N), odd planes
+    ("1x1-batch-halves", 3, 16, 7, 9, 24, 1, 1, 1, 0, 1),
+    ("1x1-batch-halves-wide", 5, 64, 6, 6, 200, 1, 1, 1, 0, 1),
 ]
 
 
