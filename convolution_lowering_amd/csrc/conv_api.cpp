@@ -37,6 +37,8 @@ struct Plan {
     bool need_ibuf, need_win, need_wpack;
     bool need_xcl;  // channels-last copy of an NCHW input
     int chunk_n;    // images per main-loop pass (< N: the batch goes through the copy in parts)
+    int cp;         // channels per pixel row of the channels-last copy (> C: zero-padded)
+    Geom gm;        // geometry the main loop sees (C = cp, K = T*cp)
     bool rows16;  // the feed can read X_col rows in 16-byte chunks (by shape)
     size_t off_ibuf, off_win, off_xcl, off_wpack, off_part, total;
     size_t esize;
@@ -77,7 +79,8 @@ bool sizes_supported(const Geom &g) {
 }
 
 conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int s, int p, int d,
-                        conv_layout_t layout, conv_dtype_t dtype, conv_algo_t algo, Plan *pl) {
+                        conv_layout_t layout, conv_dtype_t dtype, conv_algo_t algo, Plan *pl,
+                        bool allow_pad = true) {
     if (layout != CONV_LAYOUT_NCHW && layout != CONV_LAYOUT_NHWC) return CONV_ERR_INVALID_ARG;
     if (dtype != CONV_DTYPE_FP32 && dtype != CONV_DTYPE_BF16) return CONV_ERR_INVALID_ARG;
     if (algo < CONV_ALGO_AUTO || algo > CONV_ALGO_GEMM) return CONV_ERR_INVALID_ARG;
@@ -85,6 +88,7 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     conv_status_t st = make_geom(N, C, H, W, Co, KH, KW, s, p, d, &pl->g);
     if (st != CONV_OK) return st;
     pl->chunk_n = N;
+    pl->cp = C;
     const Geom &g = pl->g;
     if (!sizes_supported(g)) return CONV_ERR_UNSUPPORTED;
     pl->bf16 = dtype == CONV_DTYPE_BF16;
@@ -123,8 +127,18 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
             // chunks is first copied channels-last (|x| bytes of workspace);
             // otherwise the buffer addresses channel 0 of the pixel and the
             // main loop steps through the channel planes element by element.
+            // Fewer channels than one 16-byte chunk: the copy (from either
+            // layout) pads every pixel to one chunk, and each chunk of a K
+            // tile is then one whole tap.
             pl->need_ibuf = true;
-            if (pl->nhwc) {
+            if (allow_pad && g.C * (long long)pl->esize < 16 && g.T <= 12 && (long long)g.H * g.W <= 65535 &&
+                (long long)g.N * g.H * g.W * 16 + (long long)g.Co * g.T * 16 + (long long)g.P * g.T * 4 + 1024 <
+                    g.M * g.K * (long long)pl->esize) {
+                pl->feed = FEED_IND_TAPC;
+                pl->cp = 16 / (int)pl->esize;
+                pl->need_xcl = true;
+                pl->need_wpack = true;
+            } else if (pl->nhwc) {
                 pl->feed = FEED_IND_NHWC;
             } else if (g.C % (pl->bf16 ? 8 : 4) == 0 && 256LL * g.T <= 3072 &&
                        (long long)g.T * g.Ho * g.Wo >= 2LL * g.H * g.W) {  // copy well below im2col
@@ -143,6 +157,9 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
         default:
             return CONV_ERR_INVALID_ARG;
     }
+    pl->gm = g;
+    pl->gm.C = pl->cp;
+    pl->gm.K = (long long)pl->cp * g.T;
     pl->out_nchw = !pl->nhwc && !(pl->feed == FEED_ROWMAJOR && whole);
     // GEMM rows of one main-loop pass.
     const long long Mt = (long long)pl->chunk_n * g.P;
@@ -154,6 +171,7 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     switch (pl->feed) {
         case FEED_ROWMAJOR: rows16 = g.K % VEC == 0; break;
         case FEED_IND_NHWC: rows16 = g.C % VEC == 0 && 256LL * g.T <= 3072; break;
+        case FEED_IND_TAPC: rows16 = true; break;
         case FEED_WIN: rows16 = g.C % VEC == 0; break;
         default: rows16 = false;
     }
@@ -176,6 +194,7 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
             oct = oct && slice && g.C % BK8 == 0;
             break;
         }
+        case FEED_IND_TAPC: break;  // slice checked when the feed was chosen
         default: dual = oct = false;
     }
     const long long tiles256 = ((Mt + 255) / 256) * ((g.Co + 127) / 128);
@@ -184,7 +203,7 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
         pl->tile = TILE_32x64; BM = 32; BN = 64;
     } else if (g.Co <= 64 && dual) {
         pl->tile = TILE_256x64_DUAL; BM = 256; BN = 64;
-    } else if (dual && g.Co >= 256 && g.K >= 512 && ((Mt + 255) / 256) * ((g.Co + 255) / 256) > 256) {
+    } else if (dual && g.Co >= 256 && pl->gm.K >= 512 && ((Mt + 255) / 256) * ((g.Co + 255) / 256) > 256) {
         // Deep layers with many output channels and more 256 x 256 tiles
         // than CUs: the larger block tile loads a third fewer bytes per MFMA.
         pl->tile = TILE_256x256_OCT; BM = 256; BN = 256;
@@ -211,12 +230,12 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     size_t lowered = 0;
     if (pl->need_ibuf) lowered = align_up(lowered + (size_t)g.P * g.T * sizeof(int32_t));
     if (pl->need_win) lowered = align_up(lowered + (size_t)g.N * g.Ho * g.Wwin * g.KH * g.C * pl->esize);
-    if (pl->need_xcl) lowered = align_up(lowered + (size_t)pl->chunk_n * g.C * g.H * g.W * pl->esize);
-    if (pl->need_wpack) lowered = align_up(lowered + (size_t)g.Co * g.K * pl->esize);
+    if (pl->need_xcl) lowered = align_up(lowered + (size_t)pl->chunk_n * pl->cp * g.H * g.W * pl->esize);
+    if (pl->need_wpack) lowered = align_up(lowered + (size_t)g.Co * pl->gm.K * pl->esize);
 
     const int BK = pl->bf16 ? 64 : 32;  // the main loop's K tile (128-byte LDS rows)
     long long blocks = ((Mt + BM - 1) / BM) * ((g.Co + BN - 1) / BN);
-    long long ktiles = (g.K + BK - 1) / BK;
+    long long ktiles = (pl->gm.K + BK - 1) / BK;
     int splits = 1;
     // Split K only where too few tiles leave most CUs idle: the two-wavefront
     // loops keep a CU busy with a single block, and the partials cost a pass
@@ -237,9 +256,9 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
         if (sp > by_space) sp = by_space;
         if (sp > 1) splits = (int)sp;
     }
-    long long kps = (g.K + splits - 1) / splits;
+    long long kps = (pl->gm.K + splits - 1) / splits;
     kps = (kps + BK - 1) / BK * BK;
-    splits = (int)((g.K + kps - 1) / kps);
+    splits = (int)((pl->gm.K + kps - 1) / kps);
     pl->splits = splits;
     pl->kps = (int)kps;
 
@@ -254,11 +273,11 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     }
     if (pl->need_xcl) {
         pl->off_xcl = off;
-        off = align_up(off + (size_t)pl->chunk_n * g.C * g.H * g.W * pl->esize);
+        off = align_up(off + (size_t)pl->chunk_n * pl->cp * g.H * g.W * pl->esize);
     }
     if (pl->need_wpack) {
         pl->off_wpack = off;
-        off = align_up(off + (size_t)g.Co * g.K * pl->esize);
+        off = align_up(off + (size_t)g.Co * pl->gm.K * pl->esize);
     }
     if (splits > 1) {
         pl->off_part = off;
@@ -338,6 +357,7 @@ conv_status_t launch_main(const Plan &pl, GemmArgs &a, hipStream_t s) {
             a_vec = pl.rows16 && al16(a.a_src) && (wide_slice(pl.tile) || (long long)tile_rows(pl.tile) * g.T <= 3072);
             break;
         case FEED_WIN: a_vec = g.C % VEC == 0 && al16(a.a_src); break;
+        case FEED_IND_TAPC: a_vec = al16(a.a_src) && wide_slice(pl.tile); break;
         default: a_vec = false;
     }
     bool b_vec = g.K % VEC == 0 && al16(a.b);
@@ -406,7 +426,8 @@ conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias
             gc.N = g.N - n0 < pl.chunk_n ? g.N - n0 : pl.chunk_n;
             gc.M = (long long)gc.N * g.P;
             const char *xs = (const char *)x + (size_t)n0 * g.C * g.H * g.W * es;
-            if (launch_prep_nchw(xs, xc, nullptr, nullptr, nullptr, gc, pl.bf16, s) != hipSuccess) return CONV_ERR_HIP;
+            if (launch_prep(xs, false, xc, g.C, nullptr, nullptr, false, nullptr, gc, pl.bf16, s) != hipSuccess)
+                return CONV_ERR_HIP;
             a.g = gc;
             a.bias = bias;
             a.y = (char *)y + (size_t)n0 * g.Co * g.P * es;
@@ -418,7 +439,7 @@ conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias
         }
         return CONV_OK;
     }
-    a.g = g;
+    a.g = pl.gm;
     a.bias = bias;
     a.y = y;
     a.k_per_split = pl.kps;
@@ -437,10 +458,11 @@ conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias
     void *wp = pl.need_wpack ? (void *)(ws + pl.off_wpack) : nullptr;
     bool wp_done = false;
     if (pl.need_xcl) {
-        // One launch: the channels-last copy of x, the indirection buffer and
-        // the regrouped weights.
+        // One launch: the channels-last copy of x (rows of cp channels), the
+        // indirection buffer over it and the weights in (kh, kw, ci) order.
         void *xc = ws + pl.off_xcl;
-        if (launch_prep_nchw(x, xc, ib_build, w, wp, g, pl.bf16, s) != hipSuccess) return CONV_ERR_HIP;
+        if (launch_prep(x, pl.nhwc, xc, pl.cp, ib_build, w, pl.nhwc, wp, g, pl.bf16, s) != hipSuccess)
+            return CONV_ERR_HIP;
         a.a_src = xc;
         ib_build = nullptr;
         wp_done = true;
@@ -483,7 +505,7 @@ conv_status_t conv2d_main_loop(const void *lowered, const int32_t *indirection, 
     // The lowered operands are channels-last, so plan as for an NHWC call.
     Plan pl;
     conv_status_t st =
-        make_plan(N, C_in, H, W, C_out, KH, KW, stride, pad, dilation, CONV_LAYOUT_NHWC, dtype, algo, &pl);
+        make_plan(N, C_in, H, W, C_out, KH, KW, stride, pad, dilation, CONV_LAYOUT_NHWC, dtype, algo, &pl, false);
     if (st != CONV_OK) return st;
     if (algo == CONV_ALGO_INDIRECT && (!indirection || (uintptr_t)indirection % 4)) return CONV_ERR_INVALID_ARG;
     pl.out_nchw = out_layout == CONV_LAYOUT_NCHW;

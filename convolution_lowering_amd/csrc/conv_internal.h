@@ -17,7 +17,10 @@ enum Feed : int {
     FEED_IND_NHWC = 2,  // through the indirection buffer, channels-last input; K = (kh, kw, ci)
     FEED_IND_NCHW = 3,  // through the indirection buffer, NCHW input; K = (ci, kh, kw)
     FEED_WIN = 4,       // out of the window-ordered tensor (either input layout); K = (kh, kw, ci)
+    FEED_IND_TAPC = 5,  // indirection buffer over a channels-last copy padded to 16 bytes per pixel
+                        // (C < one 16-byte chunk): every chunk of a K tile is one whole tap; K = (kh, kw, ci)
 };
+constexpr int kNumFeeds = 6;
 
 struct Geom {
     int N, C, H, W, Co, KH, KW, s, p, d;
@@ -68,10 +71,12 @@ hipError_t launch_splitk_reduce(const float *part, const void *bias, void *y, co
 hipError_t launch_build_indirection(int32_t *buf, const Geom &g, bool nhwc, hipStream_t st);
 hipError_t launch_im2win(const void *x, void *xwin, const Geom &g, bool nhwc, bool bf16,
                          hipStream_t st);
-// One launch: x NCHW -> channels-last copy, plus (when given) the channels-last
-// indirection buffer and the OIHW -> OHWI weights.
-hipError_t launch_prep_nchw(const void *x, void *x_cl, int32_t *ib, const void *w, void *w_ohwi, const Geom &g,
-                            bool bf16, hipStream_t st);
+// One launch: the channels-last copy of x with cp channels per pixel row
+// (from NCHW or NHWC input; null x_cl: none), plus (when given) the
+// indirection buffer over that copy and the weights in (kh, kw, ci) order
+// with cp channels (from OIHW or OHWI).  Channels past C are zeros.
+hipError_t launch_prep(const void *x, bool nhwc_in, void *x_cl, int cp, int32_t *ib, const void *w, bool w_ohwi,
+                       void *w_out, const Geom &g, bool bf16, hipStream_t st);
 hipError_t launch_pack_weights_ohwi(const void *w_oihw, void *w_ohwi, const Geom &g, bool bf16,
                                     hipStream_t st);
 

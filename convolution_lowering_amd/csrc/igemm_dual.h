@@ -105,7 +105,8 @@ __device__ __forceinline__ void igemm_dual_body(const GemmArgs &A) {
     constexpr int WPM = C::WPM, WCN = C::WCN, TP = C::TP, TC = C::TC, NG = C::NG;
     constexpr int NW = C::NW, NTHR = C::NTHR, RPI = C::RPI;
     constexpr uint32_t ES = (uint32_t)sizeof(S);
-    constexpr bool IND = FEED == FEED_IND_NHWC;
+    constexpr bool TAPC = FEED == FEED_IND_TAPC;  // one tap per 16-byte chunk (C == VEC)
+    constexpr bool IND = FEED == FEED_IND_NHWC || TAPC;
     constexpr bool TAPS = FEED == FEED_IND_NHWC || FEED == FEED_WIN;  // K tiles inside one tap
     using MF = MfmaShape<S, 32>;
     constexpr int NQ = MF::NQ;
@@ -182,7 +183,7 @@ __device__ __forceinline__ void igemm_dual_body(const GemmArgs &A) {
         uint32_t base;
         if constexpr (FEED == FEED_ROWMAJOR) {
             base = mm * (uint32_t)g.K;
-        } else if constexpr (FEED == FEED_IND_NHWC) {
+        } else if constexpr (IND) {
             base = n * ((uint32_t)g.H * (uint32_t)g.W * (uint32_t)g.C);
         } else {  // FEED_WIN
             const uint32_t p = mm - n * (uint32_t)g.P;
@@ -220,11 +221,21 @@ __device__ __forceinline__ void igemm_dual_body(const GemmArgs &A) {
             ci += BK;
         }
     };
+    // One tap per chunk: K tile j holds taps j*KCH .. j*KCH + KCH-1, and this
+    // lane's chunk column is tap (tile's first tap) + ccol.
+    const int ccol = (int)(kc / VEC);
+    if constexpr (TAPC) pre_t = kbeg / VEC;
 
-    // Pixel indices (entry / C) of this lane's A rows for the tile at `pre`.
+    // Pixel indices (entry / C) of this lane's A rows for the tile at `pre`
+    // (0xFFFF where the tap is padding or, one tap per chunk, past the last).
     uint32_t pix[IPW_A];
     auto read_pix = [&]() {
-        if constexpr (IND) {
+        if constexpr (TAPC) {
+            const int t = pre_t + ccol;
+#pragma unroll
+            for (int i = 0; i < IPW_A; ++i) pix[i] = t < g.T ? (uint32_t)ibs[ib_row[i] + t] : 0xFFFFu;
+            pre_t += KCH;
+        } else if constexpr (IND) {
 #pragma unroll
             for (int i = 0; i < IPW_A; ++i) pix[i] = ibs[ib_row[i] + pre_t];
         }
@@ -249,6 +260,9 @@ __device__ __forceinline__ void igemm_dual_body(const GemmArgs &A) {
             if constexpr (FEED == FEED_ROWMAJOR) {
                 o = rbA[i] + (k0 + kc) * ES;
                 valid = k0 + kc < (uint32_t)kend;
+            } else if constexpr (TAPC) {  // the whole C == VEC channel vector of this lane's tap
+                o = rbA[i] + pix[i] * (uint32_t)g.C * ES;
+                valid = live && pix[i] != 0xFFFFu;
             } else if constexpr (FEED == FEED_IND_NHWC) {
                 o = rbA[i] + (pix[i] * (uint32_t)g.C + (uint32_t)iss_ci + kc) * ES;
                 valid = live && pix[i] != 0xFFFFu;

@@ -135,15 +135,17 @@ hipError_t launch_im2win(const void *x, void *xwin, const Geom &g, bool nhwc, bo
 }
 
 // NCHW -> NHWC copy (each image's [C][H*W] matrix transposed to [H*W][C]).
-// NCHW -> NHWC copy of x, transposed through LDS in tiles of 64 channels x 64
-// pixels.  Loads run along the pixels of one channel plane in LW-byte chunks
-// (the widest that the plane length H*W and the pointer alignment allow, so a
-// chunk never leaves its plane); stores run along the channels of one pixel
-// in 16-byte chunks (C is a multiple of the 16-byte element count).
+// NCHW -> channels-last copy of x, transposed through LDS in tiles of 64
+// channels x 64 pixels.  Loads run along the pixels of one channel plane in
+// LW-byte chunks (the widest that the plane length H*W and the pointer
+// alignment allow, so a chunk never leaves its plane); stores run along the
+// channels of one pixel in 16-byte chunks.  The copy's pixel rows hold CP >= C
+// channels (CP a multiple of the 16-byte element count); channels C..CP-1 are
+// written as zeros.
 constexpr int kTrC = 64, kTrP = 64;  // tile: channels x pixels
 
 template <typename S, int LW>
-__device__ __forceinline__ void transpose_tile(const S *__restrict__ x, S *__restrict__ xc, int C, int HW,
+__device__ __forceinline__ void transpose_tile(const S *__restrict__ x, S *__restrict__ xc, int C, int CP, int HW,
                                                int n, int c0, int p0, S (*tile)[kTrP + 2]) {
     constexpr int LE = LW / (int)sizeof(S);  // elements per load
     constexpr int CPR = kTrP / LE;           // loads per channel row
@@ -175,48 +177,61 @@ __device__ __forceinline__ void transpose_tile(const S *__restrict__ x, S *__res
     __syncthreads();
     constexpr int V = 16 / (int)sizeof(S);
     constexpr int CPP = kTrC / V;  // 16-byte chunks per pixel
-    S *dst = xc + (long long)n * C * HW;
+    S *dst = xc + (long long)n * CP * HW;
 #pragma unroll
     for (int i = 0; i < kTrP * CPP / 256; ++i) {
         const int q = tid + 256 * i;
         const int pl = q / CPP, cl = (q % CPP) * V;
         const int c = c0 + cl, p = p0 + pl;
-        if (c >= C || p >= HW) continue;
+        if (c >= CP || p >= HW) continue;
         S e[V];
 #pragma unroll
         for (int j = 0; j < V; ++j) e[j] = tile[cl + j][pl];
         uint4 out;
         __builtin_memcpy(&out, e, 16);
-        *(uint4 *)(dst + (long long)p * C + c) = out;
+        *(uint4 *)(dst + (long long)p * CP + c) = out;
     }
 }
 
-// One launch for the preparation of an NCHW call on the indirection path:
-// blocks [0, nt) copy x channels-last, the next nib blocks build the
-// indirection buffer (channels-last offsets), the rest regroup the weights
-// OIHW -> OHWI (when nw > 0).
+// One launch for the preparation of a call that reads a channels-last copy
+// of x: blocks [0, nt) make the copy (transposed from NCHW, or re-strided
+// from NHWC, with pixel rows of CP channels), the next nib blocks build the
+// indirection buffer over the copy, the rest put the weights in (kh, kw, ci)
+// order with CP channels (from OIHW or OHWI; when nw > 0).
 struct PrepArgs {
     const void *x;
     void *xc;
     int32_t *ib;
     const void *w;
     void *wo;
-    Geom g;
+    Geom g;                // of the call (C = the input's channel count)
+    int cp;                // channels per pixel row of the copy and the weights
     int tiles_p, tiles_c;  // transpose tiles per image along pixels, channels
     int nt, nib;           // blocks of the first two kinds
-    long long nw;          // weight elements to regroup (0: none)
+    long long nw;          // weight elements to write (0: none)
+    int w_ohwi;            // weights given as OHWI (else OIHW)
 };
 
-template <typename S, int LW>
-__global__ __launch_bounds__(256) void prep_nchw_kernel(PrepArgs a) {
-    __shared__ S tile[kTrC][kTrP + 2];
+template <typename S, int LW, bool NHWC_IN>
+__global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
+    __shared__ S tile[NHWC_IN ? 1 : kTrC][kTrP + 2];
     const Geom &g = a.g;
+    const int CP = a.cp;
     int b = blockIdx.x;
     if (b < a.nt) {
-        const int pt = b % a.tiles_p;
-        b /= a.tiles_p;
-        const int ct = b % a.tiles_c, n = b / a.tiles_c;
-        transpose_tile<S, LW>((const S *)a.x, (S *)a.xc, g.C, g.H * g.W, n, ct * kTrC, pt * kTrP, tile);
+        if constexpr (NHWC_IN) {  // one thread per (pixel, channel) of the copy
+            const long long e = (long long)b * 256 + threadIdx.x;
+            const long long total = (long long)g.N * g.H * g.W * CP;
+            if (e >= total) return;
+            const long long pix = e / CP;
+            const int c = (int)(e - pix * CP);
+            ((S *)a.xc)[e] = c < g.C ? ((const S *)a.x)[pix * g.C + c] : S(0);
+        } else {
+            const int pt = b % a.tiles_p;
+            b /= a.tiles_p;
+            const int ct = b % a.tiles_c, n = b / a.tiles_c;
+            transpose_tile<S, LW>((const S *)a.x, (S *)a.xc, g.C, CP, g.H * g.W, n, ct * kTrC, pt * kTrP, tile);
+        }
         return;
     }
     b -= a.nt;
@@ -227,55 +242,65 @@ __global__ __launch_bounds__(256) void prep_nchw_kernel(PrepArgs a) {
         const int ho = p / g.Wo, wo = p - ho * g.Wo;
         const int kh = t / g.KW, kw = t - kh * g.KW;
         const int hi = ho * g.s + kh * g.d - g.p, wi = wo * g.s + kw * g.d - g.p;
-        a.ib[idx] = (hi >= 0 && hi < g.H && wi >= 0 && wi < g.W) ? (hi * g.W + wi) * g.C : -1;
+        a.ib[idx] = (hi >= 0 && hi < g.H && wi >= 0 && wi < g.W) ? (hi * g.W + wi) * CP : -1;
         return;
     }
     b -= a.nib;
     const long long e = (long long)b * 256 + threadIdx.x;
     if (e >= a.nw) return;
-    const int ci = (int)(e % g.C);
-    const long long r = e / g.C;
+    const int ci = (int)(e % CP);
+    const long long r = e / CP;
     const int t = (int)(r % g.T);
     const long long co = r / g.T;
-    ((S *)a.wo)[e] = ((const S *)a.w)[(co * g.C + ci) * g.T + t];
+    S v = S(0);
+    if (ci < g.C)
+        v = a.w_ohwi ? ((const S *)a.w)[(co * g.T + t) * g.C + ci] : ((const S *)a.w)[(co * g.C + ci) * g.T + t];
+    ((S *)a.wo)[e] = v;
 }
 
-hipError_t launch_prep_nchw(const void *x, void *x_cl, int32_t *ib, const void *w, void *w_ohwi, const Geom &g,
-                            bool bf16, hipStream_t st) {
+hipError_t launch_prep(const void *x, bool nhwc_in, void *x_cl, int cp, int32_t *ib, const void *w, bool w_ohwi,
+                       void *w_out, const Geom &g, bool bf16, hipStream_t st) {
     const int ES = bf16 ? 2 : 4, HW = g.H * g.W;
     PrepArgs a;
     a.x = x;
     a.xc = x_cl;
     a.ib = ib;
     a.w = w;
-    a.wo = w_ohwi;
+    a.wo = w_out;
     a.g = g;
+    a.cp = cp;
+    a.w_ohwi = w_ohwi ? 1 : 0;
     a.tiles_p = (HW + kTrP - 1) / kTrP;
-    a.tiles_c = (g.C + kTrC - 1) / kTrC;
-    a.nt = g.N * a.tiles_c * a.tiles_p;
+    a.tiles_c = (cp + kTrC - 1) / kTrC;
+    if (x_cl)
+        a.nt = nhwc_in ? (int)blocks_for((long long)g.N * HW * cp, 256) : g.N * a.tiles_c * a.tiles_p;
+    else
+        a.nt = 0;
     a.nib = ib ? (int)blocks_for((long long)g.P * g.T, 256) : 0;
-    a.nw = w_ohwi ? (long long)g.Co * g.T * g.C : 0;
+    a.nw = w_out ? (long long)g.Co * g.T * cp : 0;
     const long long blocks = (long long)a.nt + a.nib + blocks_for(a.nw, 256);
+    if (blocks == 0) return hipSuccess;
     // Widest load that keeps every chunk inside its channel plane and aligned.
     int lw = 16;
     while (lw > ES && ((long long)HW * ES % lw != 0 || (uintptr_t)x % lw != 0)) lw >>= 1;
-    if ((uintptr_t)x_cl % 16 != 0 || (g.C * ES) % 16 != 0) return hipErrorInvalidValue;
+    if (x_cl && ((uintptr_t)x_cl % 16 != 0 || (cp * ES) % 16 != 0)) return hipErrorInvalidValue;
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, st, a);
         return hipGetLastError();
     };
+    if (nhwc_in) return bf16 ? go(prep_kernel<uint16_t, 2, true>) : go(prep_kernel<float, 4, true>);
     if (bf16) {
         switch (lw) {
-            case 16: return go(prep_nchw_kernel<uint16_t, 16>);
-            case 8: return go(prep_nchw_kernel<uint16_t, 8>);
-            case 4: return go(prep_nchw_kernel<uint16_t, 4>);
-            default: return go(prep_nchw_kernel<uint16_t, 2>);
+            case 16: return go(prep_kernel<uint16_t, 16, false>);
+            case 8: return go(prep_kernel<uint16_t, 8, false>);
+            case 4: return go(prep_kernel<uint16_t, 4, false>);
+            default: return go(prep_kernel<uint16_t, 2, false>);
         }
     }
     switch (lw) {
-        case 16: return go(prep_nchw_kernel<float, 16>);
-        case 8: return go(prep_nchw_kernel<float, 8>);
-        default: return go(prep_nchw_kernel<float, 4>);
+        case 16: return go(prep_kernel<float, 16, false>);
+        case 8: return go(prep_kernel<float, 8, false>);
+        default: return go(prep_kernel<float, 4, false>);
     }
 }
 
