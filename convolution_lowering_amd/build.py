@@ -34,7 +34,7 @@ def _units():
              ("igemm_dispatch", "igemm_dispatch.hip", []),
              ("lowering_kernels", "lowering_kernels.hip", [])]
     for bf16 in (1, 0):
-        for feed in range(6):  # the Feed values of conv_internal.h
+        for feed in range(7):  # the Feed values of conv_internal.h
             units.append((f"igemm_{'bf16' if bf16 else 'f32'}_feed{feed}", "igemm_inst.hip",
                           [f"-DIGEMM_BF16={bf16}", f"-DIGEMM_FEED={feed}"]))
     return units

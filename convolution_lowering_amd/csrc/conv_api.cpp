@@ -101,7 +101,23 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     // section 4).  Both are fed from the input as it lies in memory.
     const bool whole = KH == H && KW == W && p == 0;
     const bool one = KH == 1 && KW == 1 && s == 1 && p == 0;
-    if (algo == CONV_ALGO_AUTO) algo = (whole || one) ? CONV_ALGO_GEMM : CONV_ALGO_INDIRECT;
+    // Fewer channels than one 16-byte chunk: padding each pixel (or window
+    // cell) to one chunk makes every chunk of a K tile one whole tap.  The
+    // indirection buffer then has to fit the main loop's LDS slice (at most
+    // 12 taps); larger kernels read a window tensor padded the same way.
+    const bool small_c = allow_pad && g.C * (long long)pl->esize < 16;
+    const long long im2col_bytes = g.M * g.K * (long long)pl->esize;
+    const long long pad_w_bytes = (long long)g.Co * g.T * 16;
+    const bool tapc_ind = small_c && g.T <= 12 && (long long)g.H * g.W <= 65535 &&
+                          (long long)g.N * g.H * g.W * 16 + pad_w_bytes + (long long)g.P * g.T * 4 + 1024 <
+                              im2col_bytes;
+    const long long win_pad_bytes = (long long)g.N * g.Ho * g.Wwin * g.KH * 16;
+    const bool tapc_win = small_c && win_pad_bytes / (long long)pl->esize <= kLimit &&
+                          win_pad_bytes + pad_w_bytes + 512 < im2col_bytes;
+    if (algo == CONV_ALGO_AUTO)
+        algo = (whole || one) ? CONV_ALGO_GEMM
+               : (!tapc_ind && tapc_win) ? CONV_ALGO_IM2WIN
+                                        : CONV_ALGO_INDIRECT;
     switch (algo) {
         case CONV_ALGO_GEMM:
             if (whole) {
@@ -131,9 +147,7 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
             // layout) pads every pixel to one chunk, and each chunk of a K
             // tile is then one whole tap.
             pl->need_ibuf = true;
-            if (allow_pad && g.C * (long long)pl->esize < 16 && g.T <= 12 && (long long)g.H * g.W <= 65535 &&
-                (long long)g.N * g.H * g.W * 16 + (long long)g.Co * g.T * 16 + (long long)g.P * g.T * 4 + 1024 <
-                    g.M * g.K * (long long)pl->esize) {
+            if (tapc_ind) {
                 pl->feed = FEED_IND_TAPC;
                 pl->cp = 16 / (int)pl->esize;
                 pl->need_xcl = true;
@@ -150,9 +164,15 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
             }
             break;
         case CONV_ALGO_IM2WIN:
-            pl->feed = FEED_WIN;
             pl->need_win = true;
-            pl->need_wpack = !pl->nhwc && g.T > 1;  // OIHW regrouped to (kh, kw, ci) order
+            if (tapc_win) {  // cells padded to one 16-byte chunk, weights to (kh, kw, cp)
+                pl->feed = FEED_WIN_TAPC;
+                pl->cp = 16 / (int)pl->esize;
+                pl->need_wpack = true;
+            } else {
+                pl->feed = FEED_WIN;
+                pl->need_wpack = !pl->nhwc && g.T > 1;  // OIHW regrouped to (kh, kw, ci) order
+            }
             break;
         default:
             return CONV_ERR_INVALID_ARG;
@@ -173,6 +193,7 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
         case FEED_IND_NHWC: rows16 = g.C % VEC == 0 && 256LL * g.T <= 3072; break;
         case FEED_IND_TAPC: rows16 = true; break;
         case FEED_WIN: rows16 = g.C % VEC == 0; break;
+        case FEED_WIN_TAPC: rows16 = true; break;
         default: rows16 = false;
     }
     pl->rows16 = rows16;
@@ -195,6 +216,7 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
             break;
         }
         case FEED_IND_TAPC: break;  // slice checked when the feed was chosen
+        case FEED_WIN_TAPC: break;
         default: dual = oct = false;
     }
     const long long tiles256 = ((Mt + 255) / 256) * ((g.Co + 127) / 128);
@@ -229,7 +251,7 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     // Workspace regions other than the split-K partials.
     size_t lowered = 0;
     if (pl->need_ibuf) lowered = align_up(lowered + (size_t)g.P * g.T * sizeof(int32_t));
-    if (pl->need_win) lowered = align_up(lowered + (size_t)g.N * g.Ho * g.Wwin * g.KH * g.C * pl->esize);
+    if (pl->need_win) lowered = align_up(lowered + (size_t)g.N * g.Ho * g.Wwin * g.KH * pl->cp * pl->esize);
     if (pl->need_xcl) lowered = align_up(lowered + (size_t)pl->chunk_n * pl->cp * g.H * g.W * pl->esize);
     if (pl->need_wpack) lowered = align_up(lowered + (size_t)g.Co * pl->gm.K * pl->esize);
 
@@ -247,7 +269,6 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
         // the im2col footprint.
         long long want = (512 + blocks - 1) / blocks;
         long long by_depth = ktiles / 4;
-        long long im2col_bytes = g.M * g.K * (long long)pl->esize;
         long long per_split = (long long)align_up((size_t)(Mt * g.Co * 4LL));
         long long room = im2col_bytes - (long long)lowered - 1;
         long long by_space = room > 0 ? room / per_split : 0;
@@ -269,7 +290,7 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     }
     if (pl->need_win) {
         pl->off_win = off;
-        off = align_up(off + (size_t)g.N * g.Ho * g.Wwin * g.KH * g.C * pl->esize);
+        off = align_up(off + (size_t)g.N * g.Ho * g.Wwin * g.KH * pl->cp * pl->esize);
     }
     if (pl->need_xcl) {
         pl->off_xcl = off;
@@ -357,7 +378,8 @@ conv_status_t launch_main(const Plan &pl, GemmArgs &a, hipStream_t s) {
             a_vec = pl.rows16 && al16(a.a_src) && (wide_slice(pl.tile) || (long long)tile_rows(pl.tile) * g.T <= 3072);
             break;
         case FEED_WIN: a_vec = g.C % VEC == 0 && al16(a.a_src); break;
-        case FEED_IND_TAPC: a_vec = al16(a.a_src) && wide_slice(pl.tile); break;
+        case FEED_IND_TAPC:
+        case FEED_WIN_TAPC: a_vec = al16(a.a_src) && wide_slice(pl.tile); break;
         default: a_vec = false;
     }
     bool b_vec = g.K % VEC == 0 && al16(a.b);
@@ -365,8 +387,9 @@ conv_status_t launch_main(const Plan &pl, GemmArgs &a, hipStream_t s) {
     const long long kBufMax = (1LL << 31) - 64;
     // The extent of what the A feed reads: the window tensor for im2win
     // (built here or handed in), else the input or its channels-last copy.
-    long long a_bytes = (long long)pl.esize * (pl.feed == FEED_WIN ? (long long)g.N * g.Ho * g.Wwin * g.KH * g.C
-                                                                   : (long long)g.N * g.C * g.H * g.W);
+    const bool win = pl.feed == FEED_WIN || pl.feed == FEED_WIN_TAPC;
+    long long a_bytes = (long long)pl.esize * (win ? (long long)g.N * g.Ho * g.Wwin * g.KH * g.C
+                                                   : (long long)g.N * g.C * g.H * g.W);
     long long b_bytes = (long long)pl.esize * g.Co * g.K;
     if (a_bytes > kBufMax) a_vec = false;
     if (b_bytes > kBufMax) a_vec = b_vec = false;
@@ -470,7 +493,15 @@ conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias
     if (ib_build && launch_build_indirection(ib_build, g, ib_rows, s) != hipSuccess) return CONV_ERR_HIP;
     if (pl.need_win) {
         void *xw = ws + pl.off_win;
-        if (launch_im2win(x, xw, g, pl.nhwc, pl.bf16, s) != hipSuccess) return CONV_ERR_HIP;
+        if (pl.feed == FEED_WIN_TAPC) {
+            if (launch_im2win_pad(x, xw, g, pl.nhwc, pl.bf16, s) != hipSuccess) return CONV_ERR_HIP;
+            // Weights zero-padded to (kh, kw, cp) order from either layout.
+            if (launch_prep(nullptr, pl.nhwc, nullptr, pl.cp, nullptr, w, pl.nhwc, wp, g, pl.bf16, s) != hipSuccess)
+                return CONV_ERR_HIP;
+            wp_done = true;
+        } else if (launch_im2win(x, xw, g, pl.nhwc, pl.bf16, s) != hipSuccess) {
+            return CONV_ERR_HIP;
+        }
         a.a_src = xw;
     }
     if (wp) {
@@ -510,6 +541,16 @@ conv_status_t conv2d_main_loop(const void *lowered, const int32_t *indirection, 
     if (algo == CONV_ALGO_INDIRECT && (!indirection || (uintptr_t)indirection % 4)) return CONV_ERR_INVALID_ARG;
     pl.out_nchw = out_layout == CONV_LAYOUT_NCHW;
     pl.need_ibuf = pl.need_win = pl.need_xcl = pl.need_wpack = false;
+    // Only the split-K partials live in the workspace here; with less room
+    // than they need the main loop runs unsplit.
+    pl.off_part = 0;
+    pl.total = pl.splits > 1 ? align_up((size_t)pl.splits * pl.g.M * pl.g.Co * sizeof(float)) : 0;
+    if (pl.total > 0 && (!workspace || workspace_bytes < pl.total)) {
+        const int BK = pl.bf16 ? 64 : 32;
+        pl.splits = 1;
+        pl.kps = (int)((pl.gm.K + BK - 1) / BK * BK);
+        pl.total = 0;
+    }
     return run(pl, lowered, w_ohwi, bias, y, indirection, stream, workspace, workspace_bytes);
 }
 

@@ -105,8 +105,9 @@ __device__ __forceinline__ void igemm_dual_body(const GemmArgs &A) {
     constexpr int WPM = C::WPM, WCN = C::WCN, TP = C::TP, TC = C::TC, NG = C::NG;
     constexpr int NW = C::NW, NTHR = C::NTHR, RPI = C::RPI;
     constexpr uint32_t ES = (uint32_t)sizeof(S);
-    constexpr bool TAPC = FEED == FEED_IND_TAPC;  // one tap per 16-byte chunk (C == VEC)
-    constexpr bool IND = FEED == FEED_IND_NHWC || TAPC;
+    constexpr bool WTAPC = FEED == FEED_WIN_TAPC;
+    constexpr bool TAPC = FEED == FEED_IND_TAPC || WTAPC;  // one tap per 16-byte chunk (C == VEC)
+    constexpr bool IND = FEED == FEED_IND_NHWC || FEED == FEED_IND_TAPC;
     constexpr bool TAPS = FEED == FEED_IND_NHWC || FEED == FEED_WIN;  // K tiles inside one tap
     using MF = MfmaShape<S, 32>;
     constexpr int NQ = MF::NQ;
@@ -185,7 +186,7 @@ __device__ __forceinline__ void igemm_dual_body(const GemmArgs &A) {
             base = mm * (uint32_t)g.K;
         } else if constexpr (IND) {
             base = n * ((uint32_t)g.H * (uint32_t)g.W * (uint32_t)g.C);
-        } else {  // FEED_WIN
+        } else {  // the window-ordered feeds
             const uint32_t p = mm - n * (uint32_t)g.P;
             const uint32_t ho = p / (uint32_t)g.Wo, wo = p - ho * (uint32_t)g.Wo;
             base = ((n * (uint32_t)g.Ho + ho) * (uint32_t)g.Wwin + wo * (uint32_t)g.s) * (uint32_t)(g.KH * g.C);
@@ -228,9 +229,18 @@ __device__ __forceinline__ void igemm_dual_body(const GemmArgs &A) {
 
     // Pixel indices (entry / C) of this lane's A rows for the tile at `pre`
     // (0xFFFF where the tap is padding or, one tap per chunk, past the last).
+    // From the window-ordered tensor, one tap per chunk: the offset of this
+    // lane's tap (kh, kw) within a row, (kw*d*KH + kh)*C, the same for all
+    // its rows (~0 past the last tap).
     uint32_t pix[IPW_A];
+    uint32_t wtap = 0;
     auto read_pix = [&]() {
-        if constexpr (TAPC) {
+        if constexpr (WTAPC) {
+            const int t = pre_t + ccol;
+            const int kh = t / g.KW, kw = t - kh * g.KW;
+            wtap = t < g.T ? (uint32_t)((kw * g.d * g.KH + kh) * g.C) : ~0u;
+            pre_t += KCH;
+        } else if constexpr (TAPC) {
             const int t = pre_t + ccol;
 #pragma unroll
             for (int i = 0; i < IPW_A; ++i) pix[i] = t < g.T ? (uint32_t)ibs[ib_row[i] + t] : 0xFFFFu;
@@ -260,6 +270,9 @@ __device__ __forceinline__ void igemm_dual_body(const GemmArgs &A) {
             if constexpr (FEED == FEED_ROWMAJOR) {
                 o = rbA[i] + (k0 + kc) * ES;
                 valid = k0 + kc < (uint32_t)kend;
+            } else if constexpr (WTAPC) {  // the whole C == VEC cell of this lane's tap
+                o = rbA[i] + wtap * ES;
+                valid = live && wtap != ~0u;
             } else if constexpr (TAPC) {  // the whole C == VEC channel vector of this lane's tap
                 o = rbA[i] + pix[i] * (uint32_t)g.C * ES;
                 valid = live && pix[i] != 0xFFFFu;

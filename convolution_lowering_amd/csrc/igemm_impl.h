@@ -563,7 +563,7 @@ static hipError_t launch_tile(const GemmArgs &a, int tile, int splits, hipStream
         return hipGetLastError();
     };
     constexpr int BKW = sizeof(S) == 2 ? 64 : 32;  // 128-byte LDS rows
-    if constexpr (AVEC && FEED == FEED_IND_TAPC) {  // one tap per chunk: the two-wavefront loops only
+    if constexpr (AVEC && (FEED == FEED_IND_TAPC || FEED == FEED_WIN_TAPC)) {  // one tap per chunk: the two-wavefront loops only
         switch (tile) {
             case TILE_256x128_DUAL: return go(igemm_dual_kernel<S, FEED, OUT_NCHW>, 256, 128);
             case TILE_256x128_OCT: return go(igemm_oct_kernel<S, FEED, OUT_NCHW>, 256, 128, 512);
@@ -597,11 +597,11 @@ static hipError_t launch_tile(const GemmArgs &a, int tile, int splits, hipStream
 template <typename S, int FEED>
 hipError_t launch_feed(const GemmArgs &a, bool out_nchw, bool a_vec, bool b_vec, int tile, int splits,
                        hipStream_t st) {
-    constexpr bool CAN_AVEC =
-        FEED == FEED_ROWMAJOR || FEED == FEED_IND_NHWC || FEED == FEED_WIN || FEED == FEED_IND_TAPC;
+    constexpr bool CAN_AVEC = FEED == FEED_ROWMAJOR || FEED == FEED_IND_NHWC || FEED == FEED_WIN ||
+                              FEED == FEED_IND_TAPC || FEED == FEED_WIN_TAPC;
     constexpr bool CAN_NCHW = true;  // every feed can write NCHW output
-    constexpr bool CAN_NHWC =
-        FEED == FEED_ROWMAJOR || FEED == FEED_IND_NHWC || FEED == FEED_WIN || FEED == FEED_IND_TAPC;
+    constexpr bool CAN_NHWC = FEED == FEED_ROWMAJOR || FEED == FEED_IND_NHWC || FEED == FEED_WIN ||
+                              FEED == FEED_IND_TAPC || FEED == FEED_WIN_TAPC;
     if (a_vec && !b_vec) return hipErrorInvalidValue;
     if (out_nchw) {
         if constexpr (CAN_NCHW) {

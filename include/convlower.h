@@ -58,9 +58,13 @@ typedef enum { CONV_DTYPE_FP32 = 0, CONV_DTYPE_BF16 = 1 } conv_dtype_t;
 
 /* Which lowering feeds the contraction.
  *   AUTO      1x1 stride-1 unpadded, or kernel == whole unpadded input: the
- *             plain-GEMM feed; otherwise INDIRECT.
+ *             plain-GEMM feed; fewer input channels than one 16-byte chunk
+ *             with more than 12 taps: IM2WIN (cells padded to one chunk)
+ *             when that tensor is smaller than im2col; otherwise INDIRECT.
  *   INDIRECT  indirection buffer of per-(output pixel, tap) input offsets.
- *   IM2WIN    window-ordered copy of the input in the workspace.
+ *   IM2WIN    window-ordered copy of the input in the workspace (each
+ *             (column, kernel row) cell padded to one 16-byte chunk when
+ *             that is smaller than im2col and C is below a chunk).
  *   GEMM      the input read as the GEMM operand as it lies in memory; only
  *             valid for the two plain-GEMM shapes named under AUTO (The
  *             Indirect Convolution Algorithm, abstract: a 1x1 convolution is
@@ -135,8 +139,9 @@ conv_status_t conv2d_fwd(const void *x, const void *w, const void *bias, void *y
  *                be NULL) for CONV_ALGO_IM2WIN.
  *   w_ohwi       weights as [C_out][KH][KW][C_in].
  *   out_layout   layout of y: [N][C_out][Ho][Wo] (NCHW) or [N][Ho][Wo][C_out].
- *   workspace    at least conv2d_fwd_workspace_size(..., CONV_LAYOUT_NHWC,
- *                dtype, algo) bytes (only its split-K part is used).
+ *   workspace    split-K partials only: conv2d_fwd_workspace_size(...,
+ *                CONV_LAYOUT_NHWC, dtype, algo) bytes always suffice; with
+ *                less (or NULL) the main loop runs without split-K.
  * Other arguments and errors as for conv2d_fwd; any algo other than INDIRECT
  * or IM2WIN is CONV_ERR_INVALID_ARG. */
 conv_status_t conv2d_main_loop(const void *lowered, const int32_t *indirection, const void *w_ohwi,

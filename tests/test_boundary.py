@@ -67,8 +67,13 @@ def test_workspace_below_im2col(name, layout, dtype):
     ind = cl.workspace_size(*_args(L, layout, dtype, "indirect"))
     assert ind < im2col
     if not plain_gemm:
-        assert cl.workspace_size(*_args(L, layout, dtype, "im2win")) < im2col
-        assert auto == ind
+        win = cl.workspace_size(*_args(L, layout, dtype, "im2win"))
+        assert win < im2col
+        # fewer channels than a 16-byte chunk with more than 12 taps: AUTO
+        # takes the window tensor padded to one chunk per cell
+        es = 2 if dtype == "bf16" else 4
+        padded_win = L.C * es < 16 and L.KH * L.KW > 12
+        assert auto == (win if padded_win else ind)
     else:
         # 1x1 NHWC: no workspace at all; 1x1 NCHW: the channels-last copy of
         # half the batch; whole-input kernel: only the split-K partials
@@ -93,6 +98,21 @@ def test_auto_workspace_on_1x1(name):
     assert 0 < ws <= (im2col // 2 + 255) // 256 * 256 < im2col
     one = L.with_batch(1)
     assert cl.workspace_size(*_args(one, "NCHW", "bf16", "auto")) == 0
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("layout", ["NCHW", "NHWC"])
+def test_auto_padded_window_on_the_stem(dtype, layout):
+    """The 7x7 stride-2 stem over 3 channels: AUTO's workspace is the window
+    tensor with every (column, kernel row) cell padded to 16 bytes plus the
+    weights padded to (kh, kw, 16 bytes)."""
+    L = LAYERS["C3a"]
+    Ho, Wo = cl.output_size(L.H, L.W, L.KH, L.KW, L.stride, L.pad, L.dilation)
+    Wwin = (Wo - 1) * L.stride + (L.KW - 1) * L.dilation + 1
+    up = lambda v: (v + 255) // 256 * 256
+    want = up(L.N * Ho * Wwin * L.KH * 16) + up(L.Co * L.KH * L.KW * 16)
+    assert cl.workspace_size(*_args(L, layout, dtype, "auto")) == want
+    assert cl.workspace_size(*_args(L, layout, dtype, "im2win")) == want
 
 
 def test_gemm_algo_rejected_on_windowed_layer():

@@ -230,6 +230,12 @@ EDGE = [
     # NCHW 1x1 in two parts of the batch (odd N), odd planes
     ("1x1-batch-halves", 3, 16, 7, 9, 24, 1, 1, 1, 0, 1),
     ("1x1-batch-halves-wide", 5, 64, 6, 6, 200, 1, 1, 1, 0, 1),
+    # fewer channels than one 16-byte chunk and more than 12 taps: the window
+    # tensor padded to one chunk per cell (AUTO and IM2WIN; the stem in both
+    # dtypes, the others in fp32 where the padded tensor is below im2col)
+    ("small-C-7x7-stem", 4, 3, 40, 40, 40, 7, 7, 2, 3, 1),
+    ("small-C-5x5-dilated", 3, 2, 23, 19, 70, 5, 5, 1, 4, 2),
+    ("small-C-ragged-Co", 5, 3, 21, 35, 129, 7, 7, 2, 3, 1),
 ]
 
 
