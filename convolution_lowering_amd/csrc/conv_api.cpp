@@ -101,22 +101,26 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     // section 4).  Both are fed from the input as it lies in memory.
     const bool whole = KH == H && KW == W && p == 0;
     const bool one = KH == 1 && KW == 1 && s == 1 && p == 0;
-    // Fewer channels than one 16-byte chunk: padding each pixel (or window
-    // cell) to one chunk makes every chunk of a K tile one whole tap.  The
+    // Channels that are not a whole number of 16-byte chunks: padding each
+    // pixel (or window cell) to the next chunk lets the main loop address
+    // every chunk of a K tile on its own, whatever tap it falls in.  The
     // indirection buffer then has to fit the main loop's LDS slice (at most
     // 12 taps); larger kernels read a window tensor padded the same way.
-    const bool small_c = allow_pad && g.C * (long long)pl->esize < 16;
+    const int VEC = pl->bf16 ? 8 : 4;
+    const int cpad = (g.C + VEC - 1) / VEC * VEC;
+    const bool pad_c = allow_pad && g.C % VEC != 0;
     const long long im2col_bytes = g.M * g.K * (long long)pl->esize;
-    const long long pad_w_bytes = (long long)g.Co * g.T * 16;
-    const bool tapc_ind = small_c && g.T <= 12 && (long long)g.H * g.W <= 65535 &&
-                          (long long)g.N * g.H * g.W * 16 + pad_w_bytes + (long long)g.P * g.T * 4 + 1024 <
-                              im2col_bytes;
-    const long long win_pad_bytes = (long long)g.N * g.Ho * g.Wwin * g.KH * 16;
-    const bool tapc_win = small_c && win_pad_bytes / (long long)pl->esize <= kLimit &&
-                          win_pad_bytes + pad_w_bytes + 512 < im2col_bytes;
+    const long long pad_w_bytes = (long long)g.Co * g.T * cpad * pl->esize;
+    const bool chunk_ind = pad_c && g.T <= 12 && (long long)g.H * g.W <= 65535 &&
+                           (long long)g.N * g.H * g.W * cpad * pl->esize + pad_w_bytes + (long long)g.P * g.T * 4 +
+                                   1024 <
+                               im2col_bytes;
+    const long long win_pad = (long long)g.N * g.Ho * g.Wwin * g.KH * cpad;  // elements
+    const bool chunk_win =
+        pad_c && win_pad <= kLimit && win_pad * (long long)pl->esize + pad_w_bytes + 512 < im2col_bytes;
     if (algo == CONV_ALGO_AUTO)
         algo = (whole || one) ? CONV_ALGO_GEMM
-               : (!tapc_ind && tapc_win) ? CONV_ALGO_IM2WIN
+               : (!chunk_ind && chunk_win) ? CONV_ALGO_IM2WIN
                                         : CONV_ALGO_INDIRECT;
     switch (algo) {
         case CONV_ALGO_GEMM:
@@ -143,13 +147,13 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
             // chunks is first copied channels-last (|x| bytes of workspace);
             // otherwise the buffer addresses channel 0 of the pixel and the
             // main loop steps through the channel planes element by element.
-            // Fewer channels than one 16-byte chunk: the copy (from either
-            // layout) pads every pixel to one chunk, and each chunk of a K
-            // tile is then one whole tap.
+            // Channels not a whole number of 16-byte chunks (and at most 12
+            // taps): the copy (from either layout) pads every pixel to whole
+            // chunks, each addressed on its own by the main loop.
             pl->need_ibuf = true;
-            if (tapc_ind) {
-                pl->feed = FEED_IND_TAPC;
-                pl->cp = 16 / (int)pl->esize;
+            if (chunk_ind) {
+                pl->feed = FEED_IND_CHUNK;
+                pl->cp = cpad;
                 pl->need_xcl = true;
                 pl->need_wpack = true;
             } else if (pl->nhwc) {
@@ -165,9 +169,9 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
             break;
         case CONV_ALGO_IM2WIN:
             pl->need_win = true;
-            if (tapc_win) {  // cells padded to one 16-byte chunk, weights to (kh, kw, cp)
-                pl->feed = FEED_WIN_TAPC;
-                pl->cp = 16 / (int)pl->esize;
+            if (chunk_win) {  // cells padded to whole chunks, weights to (kh, kw, cp)
+                pl->feed = FEED_WIN_CHUNK;
+                pl->cp = cpad;
                 pl->need_wpack = true;
             } else {
                 pl->feed = FEED_WIN;
@@ -186,14 +190,13 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
 
     // Tile shape and split-K.  The 256x128 tile (wavefront tiles of 128x64,
     // a quarter less LDS and L2 traffic per MFMA) needs the 16-byte-row feeds.
-    const int VEC = pl->bf16 ? 8 : 4;
     bool rows16;
     switch (pl->feed) {
         case FEED_ROWMAJOR: rows16 = g.K % VEC == 0; break;
         case FEED_IND_NHWC: rows16 = g.C % VEC == 0 && 256LL * g.T <= 3072; break;
-        case FEED_IND_TAPC: rows16 = true; break;
+        case FEED_IND_CHUNK: rows16 = true; break;
         case FEED_WIN: rows16 = g.C % VEC == 0; break;
-        case FEED_WIN_TAPC: rows16 = true; break;
+        case FEED_WIN_CHUNK: rows16 = true; break;
         default: rows16 = false;
     }
     pl->rows16 = rows16;
@@ -215,8 +218,8 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
             oct = oct && slice && g.C % BK8 == 0;
             break;
         }
-        case FEED_IND_TAPC: break;  // slice checked when the feed was chosen
-        case FEED_WIN_TAPC: break;
+        case FEED_IND_CHUNK: break;  // slice checked when the feed was chosen
+        case FEED_WIN_CHUNK: break;
         default: dual = oct = false;
     }
     const long long tiles256 = ((Mt + 255) / 256) * ((g.Co + 127) / 128);
@@ -378,8 +381,8 @@ conv_status_t launch_main(const Plan &pl, GemmArgs &a, hipStream_t s) {
             a_vec = pl.rows16 && al16(a.a_src) && (wide_slice(pl.tile) || (long long)tile_rows(pl.tile) * g.T <= 3072);
             break;
         case FEED_WIN: a_vec = g.C % VEC == 0 && al16(a.a_src); break;
-        case FEED_IND_TAPC:
-        case FEED_WIN_TAPC: a_vec = al16(a.a_src) && wide_slice(pl.tile); break;
+        case FEED_IND_CHUNK:
+        case FEED_WIN_CHUNK: a_vec = al16(a.a_src) && wide_slice(pl.tile); break;
         default: a_vec = false;
     }
     bool b_vec = g.K % VEC == 0 && al16(a.b);
@@ -387,7 +390,7 @@ conv_status_t launch_main(const Plan &pl, GemmArgs &a, hipStream_t s) {
     const long long kBufMax = (1LL << 31) - 64;
     // The extent of what the A feed reads: the window tensor for im2win
     // (built here or handed in), else the input or its channels-last copy.
-    const bool win = pl.feed == FEED_WIN || pl.feed == FEED_WIN_TAPC;
+    const bool win = pl.feed == FEED_WIN || pl.feed == FEED_WIN_CHUNK;
     long long a_bytes = (long long)pl.esize * (win ? (long long)g.N * g.Ho * g.Wwin * g.KH * g.C
                                                    : (long long)g.N * g.C * g.H * g.W);
     long long b_bytes = (long long)pl.esize * g.Co * g.K;
@@ -493,8 +496,8 @@ conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias
     if (ib_build && launch_build_indirection(ib_build, g, ib_rows, s) != hipSuccess) return CONV_ERR_HIP;
     if (pl.need_win) {
         void *xw = ws + pl.off_win;
-        if (pl.feed == FEED_WIN_TAPC) {
-            if (launch_im2win_pad(x, xw, g, pl.nhwc, pl.bf16, s) != hipSuccess) return CONV_ERR_HIP;
+        if (pl.feed == FEED_WIN_CHUNK) {
+            if (launch_im2win_pad(x, xw, g, pl.cp, pl.nhwc, pl.bf16, s) != hipSuccess) return CONV_ERR_HIP;
             // Weights zero-padded to (kh, kw, cp) order from either layout.
             if (launch_prep(nullptr, pl.nhwc, nullptr, pl.cp, nullptr, w, pl.nhwc, wp, g, pl.bf16, s) != hipSuccess)
                 return CONV_ERR_HIP;

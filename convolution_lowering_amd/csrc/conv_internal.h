@@ -17,10 +17,11 @@ enum Feed : int {
     FEED_IND_NHWC = 2,  // through the indirection buffer, channels-last input; K = (kh, kw, ci)
     FEED_IND_NCHW = 3,  // through the indirection buffer, NCHW input; K = (ci, kh, kw)
     FEED_WIN = 4,       // out of the window-ordered tensor (either input layout); K = (kh, kw, ci)
-    FEED_IND_TAPC = 5,  // indirection buffer over a channels-last copy padded to 16 bytes per pixel
-                        // (C < one 16-byte chunk): every chunk of a K tile is one whole tap; K = (kh, kw, ci)
-    FEED_WIN_TAPC = 6,  // window-ordered tensor padded to 16 bytes per (column, kernel row) cell
-                        // (C < one 16-byte chunk), one tap per chunk; K = (kh, kw, ci)
+    // C not a multiple of the 16-byte chunk: channels zero-padded to the next
+    // multiple (C = that in the main loop's geometry) and every chunk of a K
+    // tile addressed on its own, tap q / (C/VEC); K = (kh, kw, ci)
+    FEED_IND_CHUNK = 5,  // indirection buffer over the padded channels-last copy
+    FEED_WIN_CHUNK = 6,  // window-ordered tensor with padded cells
 };
 constexpr int kNumFeeds = 7;
 
@@ -73,8 +74,10 @@ hipError_t launch_splitk_reduce(const float *part, const void *bias, void *y, co
 hipError_t launch_build_indirection(int32_t *buf, const Geom &g, bool nhwc, hipStream_t st);
 hipError_t launch_im2win(const void *x, void *xwin, const Geom &g, bool nhwc, bool bf16,
                          hipStream_t st);
-// The window-ordered tensor with cells padded to one 16-byte chunk (C < it).
-hipError_t launch_im2win_pad(const void *x, void *xwin, const Geom &g, bool nhwc, bool bf16, hipStream_t st);
+// The window-ordered tensor with each cell's channels zero-padded to cp (a
+// multiple of the 16-byte chunk, >= C).
+hipError_t launch_im2win_pad(const void *x, void *xwin, const Geom &g, int cp, bool nhwc, bool bf16,
+                             hipStream_t st);
 // One launch: the channels-last copy of x with cp channels per pixel row
 // (from NCHW or NHWC input; null x_cl: none), plus (when given) the
 // indirection buffer over that copy and the weights in (kh, kw, ci) order

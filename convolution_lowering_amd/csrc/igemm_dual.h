@@ -105,9 +105,9 @@ __device__ __forceinline__ void igemm_dual_body(const GemmArgs &A) {
     constexpr int WPM = C::WPM, WCN = C::WCN, TP = C::TP, TC = C::TC, NG = C::NG;
     constexpr int NW = C::NW, NTHR = C::NTHR, RPI = C::RPI;
     constexpr uint32_t ES = (uint32_t)sizeof(S);
-    constexpr bool WTAPC = FEED == FEED_WIN_TAPC;
-    constexpr bool TAPC = FEED == FEED_IND_TAPC || WTAPC;  // one tap per 16-byte chunk (C == VEC)
-    constexpr bool IND = FEED == FEED_IND_NHWC || FEED == FEED_IND_TAPC;
+    constexpr bool WCHUNK = FEED == FEED_WIN_CHUNK;
+    constexpr bool CHUNK = FEED == FEED_IND_CHUNK || WCHUNK;  // each 16-byte chunk its own (tap, channels)
+    constexpr bool IND = FEED == FEED_IND_NHWC || FEED == FEED_IND_CHUNK;
     constexpr bool TAPS = FEED == FEED_IND_NHWC || FEED == FEED_WIN;  // K tiles inside one tap
     using MF = MfmaShape<S, 32>;
     constexpr int NQ = MF::NQ;
@@ -222,28 +222,37 @@ __device__ __forceinline__ void igemm_dual_body(const GemmArgs &A) {
             ci += BK;
         }
     };
-    // One tap per chunk: K tile j holds taps j*KCH .. j*KCH + KCH-1, and this
-    // lane's chunk column is tap (tile's first tap) + ccol.
+    // Chunk-granular K (C a multiple of VEC, padded): K chunk q is channels
+    // (q mod C/VEC)*VEC .. +VEC-1 of tap q / (C/VEC), so each chunk of a K
+    // tile has its own tap.  Tile j holds chunks j*KCH .. j*KCH + KCH-1 and
+    // this lane's column is chunk (tile's first chunk) + ccol; `pre_t` counts
+    // chunks here.
     const int ccol = (int)(kc / VEC);
-    if constexpr (TAPC) pre_t = kbeg / VEC;
+    const uint32_t cpt = (uint32_t)g.C / VEC;  // chunks per tap
+    if constexpr (CHUNK) pre_t = kbeg / VEC;
 
     // Pixel indices (entry / C) of this lane's A rows for the tile at `pre`
-    // (0xFFFF where the tap is padding or, one tap per chunk, past the last).
-    // From the window-ordered tensor, one tap per chunk: the offset of this
-    // lane's tap (kh, kw) within a row, (kw*d*KH + kh)*C, the same for all
-    // its rows (~0 past the last tap).
+    // (0xFFFF where the tap is padding or, chunk-granular, past the last) and,
+    // chunk-granular, the channel offset `pch` of this lane's chunk.  From the
+    // window-ordered tensor: the offset of this lane's chunk within a row,
+    // (kw*d*KH + kh)*C + channels, the same for all its rows (~0 past the
+    // last tap).
     uint32_t pix[IPW_A];
-    uint32_t wtap = 0;
+    uint32_t wtap = 0, pch = 0;
     auto read_pix = [&]() {
-        if constexpr (WTAPC) {
-            const int t = pre_t + ccol;
-            const int kh = t / g.KW, kw = t - kh * g.KW;
-            wtap = t < g.T ? (uint32_t)((kw * g.d * g.KH + kh) * g.C) : ~0u;
-            pre_t += KCH;
-        } else if constexpr (TAPC) {
-            const int t = pre_t + ccol;
+        if constexpr (CHUNK) {
+            const uint32_t q = (uint32_t)(pre_t + ccol);
+            const uint32_t t = q / cpt;
+            const uint32_t ch = (q - t * cpt) * VEC;
+            const bool in = t < (uint32_t)g.T;
+            if constexpr (WCHUNK) {
+                const uint32_t kh = t / (uint32_t)g.KW, kw = t - kh * (uint32_t)g.KW;
+                wtap = in ? (kw * (uint32_t)(g.d * g.KH) + kh) * (uint32_t)g.C + ch : ~0u;
+            } else {
 #pragma unroll
-            for (int i = 0; i < IPW_A; ++i) pix[i] = t < g.T ? (uint32_t)ibs[ib_row[i] + t] : 0xFFFFu;
+                for (int i = 0; i < IPW_A; ++i) pix[i] = in ? (uint32_t)ibs[ib_row[i] + t] : 0xFFFFu;
+                pch = ch;
+            }
             pre_t += KCH;
         } else if constexpr (IND) {
 #pragma unroll
@@ -270,11 +279,11 @@ __device__ __forceinline__ void igemm_dual_body(const GemmArgs &A) {
             if constexpr (FEED == FEED_ROWMAJOR) {
                 o = rbA[i] + (k0 + kc) * ES;
                 valid = k0 + kc < (uint32_t)kend;
-            } else if constexpr (WTAPC) {  // the whole C == VEC cell of this lane's tap
+            } else if constexpr (WCHUNK) {  // this lane's chunk of the window cell
                 o = rbA[i] + wtap * ES;
                 valid = live && wtap != ~0u;
-            } else if constexpr (TAPC) {  // the whole C == VEC channel vector of this lane's tap
-                o = rbA[i] + pix[i] * (uint32_t)g.C * ES;
+            } else if constexpr (CHUNK) {  // this lane's chunk of the pixel's channels
+                o = rbA[i] + (pix[i] * (uint32_t)g.C + pch) * ES;
                 valid = live && pix[i] != 0xFFFFu;
             } else if constexpr (FEED == FEED_IND_NHWC) {
                 o = rbA[i] + (pix[i] * (uint32_t)g.C + (uint32_t)iss_ci + kc) * ES;

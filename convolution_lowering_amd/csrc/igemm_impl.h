@@ -121,7 +121,7 @@ __device__ __forceinline__ ARow make_arow(const Geom &g, long long m) {
         r.base = m * g.K;
     } else if constexpr (FEED == FEED_NCHW_1X1) {
         r.base = n * g.C * (long long)g.P + p;
-    } else if constexpr (FEED == FEED_IND_NHWC || FEED == FEED_IND_TAPC) {
+    } else if constexpr (FEED == FEED_IND_NHWC || FEED == FEED_IND_CHUNK) {
         r.base = n * (long long)g.H * g.W * g.C;
     } else if constexpr (FEED == FEED_IND_NCHW) {
         r.base = n * (long long)g.C * g.H * g.W;
@@ -142,7 +142,7 @@ __device__ __forceinline__ uint32_t a_elem(const GemmArgs &A, const ARow &r, int
         return elem_bits(src, r.base + k);
     } else if constexpr (FEED == FEED_NCHW_1X1) {
         return elem_bits(src, r.base + (long long)k * g.P);
-    } else if constexpr (FEED == FEED_IND_NHWC || FEED == FEED_IND_TAPC) {
+    } else if constexpr (FEED == FEED_IND_NHWC || FEED == FEED_IND_CHUNK) {
         int t = k / g.C, ci = k - t * g.C;
         int off = A.ibuf[r.p * g.T + t];
         return off < 0 ? 0u : elem_bits(src, r.base + off + ci);
@@ -563,7 +563,7 @@ static hipError_t launch_tile(const GemmArgs &a, int tile, int splits, hipStream
         return hipGetLastError();
     };
     constexpr int BKW = sizeof(S) == 2 ? 64 : 32;  // 128-byte LDS rows
-    if constexpr (AVEC && (FEED == FEED_IND_TAPC || FEED == FEED_WIN_TAPC)) {  // one tap per chunk: the two-wavefront loops only
+    if constexpr (AVEC && (FEED == FEED_IND_CHUNK || FEED == FEED_WIN_CHUNK)) {  // one tap per chunk: the two-wavefront loops only
         switch (tile) {
             case TILE_256x128_DUAL: return go(igemm_dual_kernel<S, FEED, OUT_NCHW>, 256, 128);
             case TILE_256x128_OCT: return go(igemm_oct_kernel<S, FEED, OUT_NCHW>, 256, 128, 512);
@@ -598,10 +598,10 @@ template <typename S, int FEED>
 hipError_t launch_feed(const GemmArgs &a, bool out_nchw, bool a_vec, bool b_vec, int tile, int splits,
                        hipStream_t st) {
     constexpr bool CAN_AVEC = FEED == FEED_ROWMAJOR || FEED == FEED_IND_NHWC || FEED == FEED_WIN ||
-                              FEED == FEED_IND_TAPC || FEED == FEED_WIN_TAPC;
+                              FEED == FEED_IND_CHUNK || FEED == FEED_WIN_CHUNK;
     constexpr bool CAN_NCHW = true;  // every feed can write NCHW output
     constexpr bool CAN_NHWC = FEED == FEED_ROWMAJOR || FEED == FEED_IND_NHWC || FEED == FEED_WIN ||
-                              FEED == FEED_IND_TAPC || FEED == FEED_WIN_TAPC;
+                              FEED == FEED_IND_CHUNK || FEED == FEED_WIN_CHUNK;
     if (a_vec && !b_vec) return hipErrorInvalidValue;
     if (out_nchw) {
         if constexpr (CAN_NCHW) {

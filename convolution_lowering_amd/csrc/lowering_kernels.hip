@@ -134,17 +134,21 @@ hipError_t launch_im2win(const void *x, void *xwin, const Geom &g, bool nhwc, bo
     return bf16 ? im2win_typed<uint16_t>(x, xwin, g, nhwc, st) : im2win_typed<float>(x, xwin, g, nhwc, st);
 }
 
-// The window-ordered tensor with every (column, kernel row) cell padded to
-// one 16-byte chunk of CP = 16 / sizeof(S) channels (the input has fewer):
-// Xwin[n][ho][c][kh][cp], zero for cp >= C and in the padding.  One thread
-// per cell, cells in memory order, so the 16-byte stores are contiguous.
+// The window-ordered tensor with the channels of every (column, kernel row)
+// cell padded to cp, a multiple of the 16-byte chunk VEC = 16 / sizeof(S):
+// Xwin[n][ho][c][kh][cp], zero for channels >= C and in the padding.  One
+// thread per 16-byte chunk, chunks in memory order, so the stores are
+// contiguous.
 template <typename S, bool NHWC_IN>
-__global__ __launch_bounds__(256) void im2win_pad_kernel(const S *__restrict__ x, S *__restrict__ xw, Geom g) {
-    constexpr int CP = 16 / (int)sizeof(S);
-    const long long cell = (long long)blockIdx.x * 256 + threadIdx.x;
-    const long long cells = (long long)g.N * g.Ho * g.Wwin * g.KH;
-    if (cell >= cells) return;
-    long long r = cell;
+__global__ __launch_bounds__(256) void im2win_pad_kernel(const S *__restrict__ x, S *__restrict__ xw, Geom g,
+                                                         int cp) {
+    constexpr int VEC = 16 / (int)sizeof(S);
+    const int cpt = cp / VEC;  // chunks per cell
+    const long long q = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long chunks = (long long)g.N * g.Ho * g.Wwin * g.KH * cpt;
+    if (q >= chunks) return;
+    long long r = q / cpt;
+    const int ch = (int)(q - r * cpt) * VEC;
     const int kh = (int)(r % g.KH);
     r /= g.KH;
     const int c = (int)(r % g.Wwin);
@@ -152,38 +156,42 @@ __global__ __launch_bounds__(256) void im2win_pad_kernel(const S *__restrict__ x
     const int ho = (int)(r % g.Ho);
     const long long n = r / g.Ho;
     const int hi = ho * g.s + kh * g.d - g.p, wi = c - g.p;
-    S e[CP];
+    S e[VEC];
 #pragma unroll
-    for (int j = 0; j < CP; ++j) e[j] = S(0);
+    for (int j = 0; j < VEC; ++j) e[j] = S(0);
     if (hi >= 0 && hi < g.H && wi >= 0 && wi < g.W) {
+        const long long pix = ((long long)hi * g.W + wi);
 #pragma unroll
-        for (int j = 0; j < CP; ++j)
-            if (j < g.C)
-                e[j] = NHWC_IN ? x[((n * g.H + hi) * g.W + wi) * g.C + j] : x[((n * g.C + j) * g.H + hi) * g.W + wi];
+        for (int j = 0; j < VEC; ++j)
+            if (ch + j < g.C)
+                e[j] = NHWC_IN ? x[(n * g.H * g.W + pix) * g.C + ch + j]
+                               : x[(n * g.C + ch + j) * (long long)g.H * g.W + pix];
     }
     uint4 out;
     __builtin_memcpy(&out, e, 16);
-    *(uint4 *)(xw + cell * CP) = out;
+    *(uint4 *)(xw + q * VEC) = out;
 }
 
-hipError_t launch_im2win_pad(const void *x, void *xwin, const Geom &g, bool nhwc, bool bf16, hipStream_t st) {
-    if ((uintptr_t)xwin % 16 != 0) return hipErrorInvalidValue;
-    const long long cells = (long long)g.N * g.Ho * g.Wwin * g.KH;
-    const dim3 grid(blocks_for(cells, 256));
+hipError_t launch_im2win_pad(const void *x, void *xwin, const Geom &g, int cp, bool nhwc, bool bf16,
+                             hipStream_t st) {
+    const int VEC = bf16 ? 8 : 4;
+    if ((uintptr_t)xwin % 16 != 0 || cp % VEC != 0 || cp < g.C) return hipErrorInvalidValue;
+    const long long chunks = (long long)g.N * g.Ho * g.Wwin * g.KH * (cp / VEC);
+    const dim3 grid(blocks_for(chunks, 256));
     if (bf16) {
         if (nhwc)
             hipLaunchKernelGGL((im2win_pad_kernel<uint16_t, true>), grid, dim3(256), 0, st, (const uint16_t *)x,
-                               (uint16_t *)xwin, g);
+                               (uint16_t *)xwin, g, cp);
         else
             hipLaunchKernelGGL((im2win_pad_kernel<uint16_t, false>), grid, dim3(256), 0, st, (const uint16_t *)x,
-                               (uint16_t *)xwin, g);
+                               (uint16_t *)xwin, g, cp);
     } else {
         if (nhwc)
             hipLaunchKernelGGL((im2win_pad_kernel<float, true>), grid, dim3(256), 0, st, (const float *)x,
-                               (float *)xwin, g);
+                               (float *)xwin, g, cp);
         else
             hipLaunchKernelGGL((im2win_pad_kernel<float, false>), grid, dim3(256), 0, st, (const float *)x,
-                               (float *)xwin, g);
+                               (float *)xwin, g, cp);
     }
     return hipGetLastError();
 }

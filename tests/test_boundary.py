@@ -69,10 +69,10 @@ def test_workspace_below_im2col(name, layout, dtype):
     if not plain_gemm:
         win = cl.workspace_size(*_args(L, layout, dtype, "im2win"))
         assert win < im2col
-        # fewer channels than a 16-byte chunk with more than 12 taps: AUTO
-        # takes the window tensor padded to one chunk per cell
+        # channels not a whole number of 16-byte chunks with more than 12
+        # taps: AUTO takes the window tensor with cells padded to whole chunks
         es = 2 if dtype == "bf16" else 4
-        padded_win = L.C * es < 16 and L.KH * L.KW > 12
+        padded_win = (L.C * es) % 16 != 0 and L.KH * L.KW > 12
         assert auto == (win if padded_win else ind)
     else:
         # 1x1 NHWC: no workspace at all; 1x1 NCHW: the channels-last copy of
@@ -102,15 +102,19 @@ def test_auto_workspace_on_1x1(name):
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("layout", ["NCHW", "NHWC"])
-def test_auto_padded_window_on_the_stem(dtype, layout):
-    """The 7x7 stride-2 stem over 3 channels: AUTO's workspace is the window
-    tensor with every (column, kernel row) cell padded to 16 bytes plus the
-    weights padded to (kh, kw, 16 bytes)."""
-    L = LAYERS["C3a"]
+@pytest.mark.parametrize("name", ["C3a", "C5a"])
+def test_auto_padded_window(name, dtype, layout):
+    """The 7x7 stride-2 stem over 3 channels and the dilated 5x5 layer over
+    37: AUTO's workspace is the window tensor with every (column, kernel
+    row) cell's channels padded to whole 16-byte chunks, plus the weights
+    padded to (kh, kw, the same channel count)."""
+    L = LAYERS[name]
+    es = 2 if dtype == "bf16" else 4
+    cp = -(-L.C * es // 16) * 16 // es
     Ho, Wo = cl.output_size(L.H, L.W, L.KH, L.KW, L.stride, L.pad, L.dilation)
     Wwin = (Wo - 1) * L.stride + (L.KW - 1) * L.dilation + 1
     up = lambda v: (v + 255) // 256 * 256
-    want = up(L.N * Ho * Wwin * L.KH * 16) + up(L.Co * L.KH * L.KW * 16)
+    want = up(L.N * Ho * Wwin * L.KH * cp * es) + up(L.Co * L.KH * L.KW * cp * es)
     assert cl.workspace_size(*_args(L, layout, dtype, "auto")) == want
     assert cl.workspace_size(*_args(L, layout, dtype, "im2win")) == want
 
