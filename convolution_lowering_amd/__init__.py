@@ -24,7 +24,8 @@ STATUS = {0: "CONV_OK", 1: "CONV_ERR_INVALID_ARG", 2: "CONV_ERR_UNSUPPORTED", 3:
 
 # Every symbol include/convlower.h declares.
 EXPORTS = ("conv_status_string", "conv2d_output_size", "conv2d_fwd_workspace_size", "conv2d_im2col_bytes",
-           "conv2d_fwd", "conv2d_main_loop", "conv2d_build_indirection", "conv2d_im2win_transform")
+           "conv2d_fwd", "conv2d_main_loop", "conv2d_build_indirection", "conv2d_im2win_transform",
+           "conv2d_time_next_main_loop")
 
 
 class ConvLowerError(RuntimeError):
@@ -62,6 +63,8 @@ def lib():
     L.conv2d_build_indirection.restype = c_int
     L.conv2d_im2win_transform.argtypes = [vp, vp] + [c_int] * 11 + [vp]
     L.conv2d_im2win_transform.restype = c_int
+    L.conv2d_time_next_main_loop.argtypes = [vp, vp]
+    L.conv2d_time_next_main_loop.restype = c_int
     _lib = L
     return L
 
@@ -235,3 +238,17 @@ def im2win_transform(x, KH, KW, stride=1, pad=0, dilation=1, layout="NCHW", stre
                                          dilation, LAYOUTS[layout], _dtype_code(x.dtype),
                                          _stream_handle(stream, x.device)))
     return out
+
+
+def time_next_main_loop(start, stop):
+    """Have the next main-loop kernel this thread launches stamp two
+    torch.cuda.Event objects at its own start and end (conv2d_time_next_main_loop).
+    The events must already exist on the device: record each once first."""
+    def handle(ev):
+        if ev is None:
+            return None
+        h = ev.cuda_event
+        if not h:
+            raise ValueError("event not created yet: record it once before passing it")
+        return h
+    _check("conv2d_time_next_main_loop", lib().conv2d_time_next_main_loop(handle(start), handle(stop)))

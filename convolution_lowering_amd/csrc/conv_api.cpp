@@ -314,6 +314,18 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
 }  // namespace
 }  // namespace convlower
 
+namespace convlower {
+namespace {
+thread_local hipEvent_t t_time_start = nullptr, t_time_stop = nullptr;
+}  // namespace
+
+void take_main_loop_events(hipEvent_t *start, hipEvent_t *stop) {
+    *start = t_time_start;
+    *stop = t_time_stop;
+    t_time_start = t_time_stop = nullptr;
+}
+}  // namespace convlower
+
 using namespace convlower;
 
 extern "C" {
@@ -555,6 +567,12 @@ conv_status_t conv2d_main_loop(const void *lowered, const int32_t *indirection, 
         pl.total = 0;
     }
     return run(pl, lowered, w_ohwi, bias, y, indirection, stream, workspace, workspace_bytes);
+}
+
+conv_status_t conv2d_time_next_main_loop(void *start_event, void *stop_event) {
+    t_time_start = (hipEvent_t)start_event;
+    t_time_stop = (hipEvent_t)stop_event;
+    return CONV_OK;
 }
 
 conv_status_t conv2d_build_indirection(int32_t *buf, int C_in, int H, int W, int KH, int KW, int stride, int pad,

@@ -38,6 +38,7 @@
 #pragma once
 
 #include "conv_internal.h"
+#include <hip/hip_ext.h>
 
 namespace convlower {
 
@@ -559,7 +560,12 @@ static hipError_t launch_tile(const GemmArgs &a, int tile, int splits, hipStream
     const Geom &g = a.g;
     auto go = [&](auto kern, int BM, int BN, int threads = kThreads) {
         dim3 grid((unsigned)(((g.M + BM - 1) / BM) * ((g.Co + BN - 1) / BN)), 1, (unsigned)splits);
-        hipLaunchKernelGGL(kern, grid, dim3(threads), 0, st, a);
+        hipEvent_t t0, t1;
+        take_main_loop_events(&t0, &t1);
+        if (t0 || t1)
+            hipExtLaunchKernelGGL(kern, grid, dim3(threads), 0, st, t0, t1, 0, a);
+        else
+            hipLaunchKernelGGL(kern, grid, dim3(threads), 0, st, a);
         return hipGetLastError();
     };
     constexpr int BKW = sizeof(S) == 2 ? 64 : 32;  // 128-byte LDS rows

@@ -176,6 +176,18 @@ conv_status_t conv2d_im2win_transform(const void *x, void *xwin, int N, int C_in
                                       int KH, int KW, int stride, int pad, int dilation,
                                       conv_layout_t layout, conv_dtype_t dtype, conv_stream_t stream);
 
+/* Instrumentation for measuring the main loop on its own.  The next
+ * implicit-GEMM main-loop kernel (step c with its fused epilogue d, as
+ * launched by conv2d_fwd or conv2d_main_loop) that the calling host thread
+ * launches stamps `start_event` when it begins executing and `stop_event`
+ * when it ends, through hipExtLaunchKernel; hipEventElapsedTime on the pair
+ * is then that kernel's own duration, without the dispatch gaps an event
+ * recorded before and after the call would include.  Both are hipEvent_t
+ * handles the caller created (either may be NULL; both NULL cancels a
+ * pending request).  The request covers one launch: a split-K finish or a
+ * second part of the batch is not included.  Returns CONV_OK. */
+conv_status_t conv2d_time_next_main_loop(void *start_event, void *stop_event);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,7 @@ def _declared_functions():
 
 def test_library_loads_and_exports_every_declared_symbol():
     names = _declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 9, names
     L = cl.lib()
     for n in names:
         assert hasattr(L, n), n

@@ -372,3 +372,35 @@ def test_main_loop_entry_matches_full_call(name, algo, out_layout):
         _assert_parity(y_ref, ref, dn, "bf16", f"{name} full call")
         return
     assert torch.equal(y.contiguous().view(torch.int16), y_ref.view(torch.int16))
+
+
+# --- main-loop timing stamps ------------------------------------------------------
+
+@pytest.mark.parametrize("layout", ["NCHW", "NHWC"])
+def test_stamped_main_loop_same_bits_and_inside_the_call(layout):
+    """A main loop launched with timing stamps (conv2d_time_next_main_loop)
+    writes the same bits as one launched without; its stamped duration is
+    positive and no longer than events recorded around the whole call; the
+    request covers one launch only."""
+    L = LAYERS["C2"]
+    x, w, b = make_inputs(L, "bf16", layout, N=4)
+    _say(f"[gpu] stamped main loop {layout}")
+    xd, wd, bd = x.to(DEV), w.to(DEV), b.to(DEV)
+    y0 = cl.conv2d_fwd(xd, wd, bd, L.stride, L.pad, L.dilation, layout, "auto")
+    ka, kb, ca, cb = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+    for e in (ka, kb, ca, cb):
+        e.record()
+    torch.cuda.synchronize()
+    cl.time_next_main_loop(ka, kb)
+    ca.record()
+    y1 = cl.conv2d_fwd(xd, wd, bd, L.stride, L.pad, L.dilation, layout, "auto")
+    cb.record()
+    torch.cuda.synchronize()
+    k_ms, c_ms = ka.elapsed_time(kb), ca.elapsed_time(cb)
+    assert 0 < k_ms <= c_ms, (k_ms, c_ms)
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+    # consumed: a further call leaves the stamps where they were
+    y2 = cl.conv2d_fwd(xd, wd, bd, L.stride, L.pad, L.dilation, layout, "auto")
+    torch.cuda.synchronize()
+    assert ka.elapsed_time(kb) == k_ms
+    assert torch.equal(y0.view(torch.int16), y2.view(torch.int16))
