@@ -18,14 +18,15 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 // Main loops whose indirection slice in LDS holds up to 12 taps at any
 // tile height (the others hold 3072 entries).
 bool wide_slice(int tile) {
-    return tile == TILE_256x128_DUAL || tile == TILE_256x128_OCT || tile == TILE_256x64_DUAL ||
+    return tile == TILE_256x128_DUAL || tile == TILE_256x128_OCT || tile == TILE_128x64_QUAD ||
            tile == TILE_256x256_OCT;
 }
 
 int tile_rows(int tile) {
-    return tile == TILE_32x64                                                                   ? 32
-           : (tile == TILE_256x128 || wide_slice(tile))                                      ? 256
-                                                                                             : 128;
+    return tile == TILE_32x64                                                                     ? 32
+           : tile == TILE_128x64_QUAD                                                          ? 128
+           : (tile == TILE_256x128 || wide_slice(tile))                                        ? 256
+                                                                                               : 128;
 }
 
 struct Plan {
@@ -227,7 +228,7 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     if (Mt <= 64) {
         pl->tile = TILE_32x64; BM = 32; BN = 64;
     } else if (g.Co <= 64 && dual) {
-        pl->tile = TILE_256x64_DUAL; BM = 256; BN = 64;
+        pl->tile = TILE_128x64_QUAD; BM = 128; BN = 64;
     } else if (dual && g.Co >= 256 && pl->gm.K >= 512 && ((Mt + 255) / 256) * ((g.Co + 255) / 256) > 256) {
         // Deep layers with many output channels and more 256 x 256 tiles
         // than CUs: the larger block tile loads a third fewer bytes per MFMA.
@@ -416,7 +417,7 @@ conv_status_t launch_main(const Plan &pl, GemmArgs &a, hipStream_t s) {
     // 256x128 variant; the split count (and so the workspace) is unchanged.
     int tile = pl.tile;
     if (!a_vec && (tile == TILE_256x128 || wide_slice(tile)))
-        tile = tile == TILE_256x64_DUAL ? TILE_128x64 : TILE_128x128;
+        tile = tile == TILE_128x64_QUAD ? TILE_128x64 : TILE_128x128;
     {
         uint32_t c = (uint32_t)g.C, sh = 0;
         while (!(c & 1u)) {

@@ -49,8 +49,8 @@ struct GemmArgs {
 // Tile shapes of the main loop (block = 256 threads = 4 wavefronts, 2x2).
 // TILE_256x128_DUAL and TILE_256x128_OCT are the 256 x 128 main loops with
 // two wavefronts per SIMD (two 256-thread blocks per compute unit with 64-byte
-// K tiles, or one 512-thread block with 128-byte K tiles; TILE_256x64_DUAL is
-// the two-blocks-per-CU loop for at most 64 output channels; the 256x256 OCT
+// K tiles, or one 512-thread block with 128-byte K tiles; TILE_128x64_QUAD is
+// the four-blocks-per-CU loop for at most 64 output channels; the 256x256 OCT
 // tile is a 512-thread block of eight 128 x 64 wavefront tiles),
 // for 16-byte-row feeds whose K tiles stay inside one tap.
 enum Tile : int {
@@ -60,7 +60,7 @@ enum Tile : int {
     TILE_256x128 = 3,
     TILE_256x128_DUAL = 4,
     TILE_256x128_OCT = 5,
-    TILE_256x64_DUAL = 6,
+    TILE_128x64_QUAD = 6,
     TILE_256x256_OCT = 7,
     TILE_COUNT = 8
 };

@@ -1,33 +1,38 @@
-// The main loop with two wavefronts on every SIMD, so that while one waits
-// (at its barrier, for its loads, in its prologue or epilogue) or issues its
-// address arithmetic, the other keeps the matrix core busy.  Two shapes:
+// The main loop with two or more wavefronts on every SIMD, so that while one
+// waits (at its barrier, for its loads, in its prologue or epilogue) or
+// issues its address arithmetic, another keeps the matrix core busy.  Four
+// shapes (DualCfg instances below):
 //
 //   * DualCfg4: two blocks per compute unit, each 256 threads with 80 KB of
 //     LDS; K tiles of 64-byte rows (32 bf16 / 16 fp32 values); wavefront
-//     tiles 128 x 64.
+//     tiles 128 x 64; block tile 256 x 128.
 //   * DualCfg8: one block of 512 threads per compute unit with 150 KB of
 //     LDS; K tiles of 128-byte rows (64 bf16 / 32 fp32 values), so every
 //     load moves whole cache lines; wavefront tiles 64 x 64.
+//   * QuadCfg: four 256-thread blocks of 128 x 64 per compute unit, for at
+//     most 64 output channels.
+//   * DualCfg8Sq: one 512-thread block of 256 x 256, wavefront tiles 128 x 64.
 //
 // Common structure:
-//   * Block tile 256 x 128 of Y_col (v_mfma_f32_32x32x16_bf16 or
-//     v_mfma_f32_32x32x2_f32 tiles).
+//   * v_mfma_f32_32x32x16_bf16 or v_mfma_f32_32x32x2_f32 tiles of Y_col.
 //   * Three LDS stages filled by the buffer-load-to-LDS instructions; tile
 //     k+3 is issued while tile k is multiplied, so two tiles cover the load
 //     latency.
 //   * Every K tile lies inside one tap (the host asks C to be a multiple of
-//     the K tile), so a tile's loads share one tap and one channel offset.
+//     the K tile), so a tile's loads share one tap and one channel offset --
+//     except in the padded-channel feeds, where each 16-byte chunk of a tile
+//     is addressed on its own.
 //     The tiles are visited tap-fastest: all KH*KW taps of one channel
 //     slice, then the next slice.  Consecutive tiles then read the same input
 //     rows shifted by one tap, which the L2 still holds; (kh, kw, ci) order
 //     would come back to a row only after streaming C / (K tile) tiles of
 //     every resident block through the L2.  A and B walk the same order, so
 //     the sum is unchanged.
-//   * The indirection buffer's slice for the block (256 rows x KH*KW taps)
+//   * The indirection buffer's slice for the block (BM rows x KH*KW taps)
 //     is copied to LDS once, as 16-bit pixel indices (entry / C, 0xFFFF for
 //     a padding tap).  The indices a tile's loads need are read one tile
 //     ahead.
-//   * The bias of the block's 128 output channels is staged in LDS.
+//   * The bias of the block's BN output channels is staged in LDS.
 //
 // All LDS-refill and read ordering follows the pipeline of igemm_dma.h: each
 // wavefront waits (vmcnt) for its own loads of the tile it is about to read
@@ -73,11 +78,13 @@ using DualCfg4 = DualCfg<S, 4, 4, 2>;
 // (150 KB of LDS): whole-cache-line loads, two wavefronts per SIMD.
 template <typename S>
 using DualCfg8 = DualCfg<S, 8, 8, 4>;
-// Block tile 256 x 64 for layers with at most 64 output channels: four
-// wavefronts of 64 x 64 stacked along the pixels, two blocks per compute
-// unit (66 KB of LDS each).
+// Block tile 128 x 64 for layers with at most 64 output channels: four
+// wavefronts of 32 x 64 stacked along the pixels, four blocks per compute
+// unit (40 KB of LDS each).  With few K tiles per block (small C), four
+// blocks hide each other's prologues, pipeline fills and epilogues better
+// than two blocks of twice the size.
 template <typename S>
-using DualCfg4N64 = DualCfg<S, 4, 4, 4, 256, 64>;
+using QuadCfg = DualCfg<S, 4, 4, 4, 128, 64>;
 // Eight wavefronts of 128 x 64 (two per SIMD), one block per compute unit,
 // 64-byte rows, block tile 256 x 256 (wavefront grid 2 x 4, 103 KB of LDS):
 // it loads 32 bytes per MFMA cycle of the compute unit, against 48 for
@@ -557,8 +564,8 @@ __global__ __launch_bounds__(512, 1) void igemm_oct_kernel(GemmArgs A) {
 }
 
 template <typename S, int FEED, bool OUT_NCHW>
-__global__ __launch_bounds__(256, 2) void igemm_dual64_kernel(GemmArgs A) {
-    igemm_dual_body<S, FEED, OUT_NCHW, DualCfg4N64<S>>(A);
+__global__ __launch_bounds__(256, 4) void igemm_quad_kernel(GemmArgs A) {
+    igemm_dual_body<S, FEED, OUT_NCHW, QuadCfg<S>>(A);
 }
 
 template <typename S, int FEED, bool OUT_NCHW>

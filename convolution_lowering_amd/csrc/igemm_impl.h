@@ -573,7 +573,7 @@ static hipError_t launch_tile(const GemmArgs &a, int tile, int splits, hipStream
         switch (tile) {
             case TILE_256x128_DUAL: return go(igemm_dual_kernel<S, FEED, OUT_NCHW>, 256, 128);
             case TILE_256x128_OCT: return go(igemm_oct_kernel<S, FEED, OUT_NCHW>, 256, 128, 512);
-            case TILE_256x64_DUAL: return go(igemm_dual64_kernel<S, FEED, OUT_NCHW>, 256, 64);
+            case TILE_128x64_QUAD: return go(igemm_quad_kernel<S, FEED, OUT_NCHW>, 128, 64);
             case TILE_256x256_OCT: return go(igemm_oct_sq_kernel<S, FEED, OUT_NCHW>, 256, 256, 512);
             default: return hipErrorInvalidValue;
         }
@@ -585,7 +585,7 @@ static hipError_t launch_tile(const GemmArgs &a, int tile, int splits, hipStream
             case TILE_256x128: return go(igemm_dma_kernel<S, FEED, OUT_NCHW, 256, 128, BKW>, 256, 128);
             case TILE_256x128_DUAL: return go(igemm_dual_kernel<S, FEED, OUT_NCHW>, 256, 128);
             case TILE_256x128_OCT: return go(igemm_oct_kernel<S, FEED, OUT_NCHW>, 256, 128, 512);
-            case TILE_256x64_DUAL: return go(igemm_dual64_kernel<S, FEED, OUT_NCHW>, 256, 64);
+            case TILE_128x64_QUAD: return go(igemm_quad_kernel<S, FEED, OUT_NCHW>, 128, 64);
             case TILE_256x256_OCT: return go(igemm_oct_sq_kernel<S, FEED, OUT_NCHW>, 256, 256, 512);
             default: return hipErrorInvalidValue;
         }
