@@ -258,9 +258,11 @@ def main():
         for name, L in LAYERS.items():
             for dtype in L.dtypes:
                 for layout in ("NCHW", "NHWC"):
-                    algos = ["auto"]
+                    # every layer also through the materialised-im2col
+                    # baseline the lowering avoids
+                    algos = ["auto", "im2col"]
                     if name == "C2":
-                        algos = ["auto", "indirect", "im2win"]
+                        algos = ["auto", "indirect", "im2win", "im2col"]
                     for algo in algos:
                         try:
                             r = bench_layer(L, dtype, layout, algo, max(3, args.steps // 4), 2, flush)

@@ -17,7 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libconvlower.so")
 
 LAYOUTS = {"NCHW": 0, "NHWC": 1}
-ALGOS = {"auto": 0, "indirect": 1, "im2win": 2, "gemm": 3}
+ALGOS = {"auto": 0, "indirect": 1, "im2win": 2, "gemm": 3, "im2col": 4}
 DTYPE_CODES = {"fp32": 0, "bf16": 1}
 STATUS = {0: "CONV_OK", 1: "CONV_ERR_INVALID_ARG", 2: "CONV_ERR_UNSUPPORTED", 3: "CONV_ERR_WORKSPACE",
           4: "CONV_ERR_HIP"}
@@ -25,7 +25,7 @@ STATUS = {0: "CONV_OK", 1: "CONV_ERR_INVALID_ARG", 2: "CONV_ERR_UNSUPPORTED", 3:
 # Every symbol include/convlower.h declares.
 EXPORTS = ("conv_status_string", "conv2d_output_size", "conv2d_fwd_workspace_size", "conv2d_im2col_bytes",
            "conv2d_fwd", "conv2d_main_loop", "conv2d_build_indirection", "conv2d_im2win_transform",
-           "conv2d_time_next_main_loop")
+           "conv2d_im2col_transform", "conv2d_time_next_main_loop")
 
 
 class ConvLowerError(RuntimeError):
@@ -63,6 +63,8 @@ def lib():
     L.conv2d_build_indirection.restype = c_int
     L.conv2d_im2win_transform.argtypes = [vp, vp] + [c_int] * 11 + [vp]
     L.conv2d_im2win_transform.restype = c_int
+    L.conv2d_im2col_transform.argtypes = [vp, vp] + [c_int] * 11 + [vp]
+    L.conv2d_im2col_transform.restype = c_int
     L.conv2d_time_next_main_loop.argtypes = [vp, vp]
     L.conv2d_time_next_main_loop.restype = c_int
     _lib = L
@@ -198,6 +200,8 @@ def conv2d_main_loop(lowered, indirection, w_ohwi, bias, out_shape_nchw, stride=
     shape = (N, Co, Ho, Wo) if out_layout == "NCHW" else (N, Ho, Wo, Co)
     if out is None:
         out = torch.empty(shape, dtype=lowered.dtype, device=dev)
+    # The main loop uses only the split-K part of this (for the im2col plan
+    # the query also counts X_col itself).
     need = workspace_size(N, C, H, W, Co, KH, KW, stride, pad, dilation, "NHWC", "bf16" if dcode else "fp32", algo)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -235,6 +239,24 @@ def im2win_transform(x, KH, KW, stride=1, pad=0, dilation=1, layout="NCHW", stre
     out = torch.empty((N, Ho, Wwin, KH, C), dtype=x.dtype, device=x.device)
     _check("conv2d_im2win_transform",
            lib().conv2d_im2win_transform(x.data_ptr(), out.data_ptr(), N, C, H, W, KH, KW, stride, pad,
+                                         dilation, LAYOUTS[layout], _dtype_code(x.dtype),
+                                         _stream_handle(stream, x.device)))
+    return out
+
+
+def im2col_transform(x, KH, KW, stride=1, pad=0, dilation=1, layout="NCHW", stream=None):
+    """X_col as a [N*Ho*Wo, C*KH*KW] device tensor: columns (ci, kh, kw) for
+    NCHW input, (kh, kw, ci) for NHWC input."""
+    import torch
+    if layout == "NCHW":
+        N, C, H, W = x.shape
+    else:
+        N, H, W, C = x.shape
+    _check_tensor(x, "x", x.dtype, x.device)
+    Ho, Wo = output_size(H, W, KH, KW, stride, pad, dilation)
+    out = torch.empty((N * Ho * Wo, C * KH * KW), dtype=x.dtype, device=x.device)
+    _check("conv2d_im2col_transform",
+           lib().conv2d_im2col_transform(x.data_ptr(), out.data_ptr(), N, C, H, W, KH, KW, stride, pad,
                                          dilation, LAYOUTS[layout], _dtype_code(x.dtype),
                                          _stream_handle(stream, x.device)))
     return out

@@ -36,12 +36,13 @@ struct Plan {
     bool out_nchw;
     int tile, splits, kps;
     bool need_ibuf, need_win, need_wpack;
+    bool need_col;  // X_col materialised (the im2col baseline)
     bool need_xcl;  // channels-last copy of an NCHW input
     int chunk_n;    // images per main-loop pass (< N: the batch goes through the copy in parts)
     int cp;         // channels per pixel row of the channels-last copy (> C: zero-padded)
     Geom gm;        // geometry the main loop sees (C = cp, K = T*cp)
     bool rows16;  // the feed can read X_col rows in 16-byte chunks (by shape)
-    size_t off_ibuf, off_win, off_xcl, off_wpack, off_part, total;
+    size_t off_ibuf, off_win, off_xcl, off_wpack, off_col, off_part, total;
     size_t esize;
 };
 
@@ -84,7 +85,7 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
                         bool allow_pad = true) {
     if (layout != CONV_LAYOUT_NCHW && layout != CONV_LAYOUT_NHWC) return CONV_ERR_INVALID_ARG;
     if (dtype != CONV_DTYPE_FP32 && dtype != CONV_DTYPE_BF16) return CONV_ERR_INVALID_ARG;
-    if (algo < CONV_ALGO_AUTO || algo > CONV_ALGO_GEMM) return CONV_ERR_INVALID_ARG;
+    if (algo < CONV_ALGO_AUTO || algo > CONV_ALGO_IM2COL) return CONV_ERR_INVALID_ARG;
     memset(pl, 0, sizeof(*pl));
     conv_status_t st = make_geom(N, C, H, W, Co, KH, KW, s, p, d, &pl->g);
     if (st != CONV_OK) return st;
@@ -179,6 +180,14 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
                 pl->need_wpack = !pl->nhwc && g.T > 1;  // OIHW regrouped to (kh, kw, ci) order
             }
             break;
+        case CONV_ALGO_IM2COL:
+            // X_col in the workspace, multiplied as a plain row-major matrix.
+            // Its columns follow the weights' own order: (ci, kh, kw) for
+            // OIHW, (kh, kw, ci) for OHWI.
+            if (g.M * g.K > kLimit) return CONV_ERR_UNSUPPORTED;
+            pl->feed = FEED_ROWMAJOR;
+            pl->need_col = true;
+            break;
         default:
             return CONV_ERR_INVALID_ARG;
     }
@@ -258,6 +267,7 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     if (pl->need_win) lowered = align_up(lowered + (size_t)g.N * g.Ho * g.Wwin * g.KH * pl->cp * pl->esize);
     if (pl->need_xcl) lowered = align_up(lowered + (size_t)pl->chunk_n * pl->cp * g.H * g.W * pl->esize);
     if (pl->need_wpack) lowered = align_up(lowered + (size_t)g.Co * pl->gm.K * pl->esize);
+    if (pl->need_col) lowered = align_up(lowered + (size_t)g.M * g.K * pl->esize);
 
     const int BK = pl->bf16 ? 64 : 32;  // the main loop's K tile (128-byte LDS rows)
     long long blocks = ((Mt + BM - 1) / BM) * ((g.Co + BN - 1) / BN);
@@ -274,7 +284,9 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
         long long want = (512 + blocks - 1) / blocks;
         long long by_depth = ktiles / 4;
         long long per_split = (long long)align_up((size_t)(Mt * g.Co * 4LL));
-        long long room = im2col_bytes - (long long)lowered - 1;
+        // (The im2col baseline holds X_col itself; its partials get another
+        // im2col footprint, so it splits where the lowered paths do.)
+        long long room = pl->need_col ? im2col_bytes : im2col_bytes - (long long)lowered - 1;
         long long by_space = room > 0 ? room / per_split : 0;
         long long sp = want;
         if (sp > by_depth) sp = by_depth;
@@ -303,6 +315,10 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     if (pl->need_wpack) {
         pl->off_wpack = off;
         off = align_up(off + (size_t)g.Co * pl->gm.K * pl->esize);
+    }
+    if (pl->need_col) {
+        pl->off_col = off;
+        off = align_up(off + (size_t)g.M * g.K * pl->esize);
     }
     if (splits > 1) {
         pl->off_part = off;
@@ -404,8 +420,9 @@ conv_status_t launch_main(const Plan &pl, GemmArgs &a, hipStream_t s) {
     // The extent of what the A feed reads: the window tensor for im2win
     // (built here or handed in), else the input or its channels-last copy.
     const bool win = pl.feed == FEED_WIN || pl.feed == FEED_WIN_CHUNK;
-    long long a_bytes = (long long)pl.esize * (win ? (long long)g.N * g.Ho * g.Wwin * g.KH * g.C
-                                                   : (long long)g.N * g.C * g.H * g.W);
+    long long a_bytes = (long long)pl.esize * (win                         ? (long long)g.N * g.Ho * g.Wwin * g.KH * g.C
+                                               : pl.feed == FEED_ROWMAJOR ? g.M * g.K
+                                                                          : (long long)g.N * g.C * g.H * g.W);
     long long b_bytes = (long long)pl.esize * g.Co * g.K;
     if (a_bytes > kBufMax) a_vec = false;
     if (b_bytes > kBufMax) a_vec = b_vec = false;
@@ -507,6 +524,11 @@ conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias
         wp_done = true;
     }
     if (ib_build && launch_build_indirection(ib_build, g, ib_rows, s) != hipSuccess) return CONV_ERR_HIP;
+    if (pl.need_col) {
+        void *xcol = ws + pl.off_col;
+        if (launch_im2col(x, xcol, g, pl.nhwc, pl.bf16, s) != hipSuccess) return CONV_ERR_HIP;
+        a.a_src = xcol;
+    }
     if (pl.need_win) {
         void *xw = ws + pl.off_win;
         if (pl.feed == FEED_WIN_CHUNK) {
@@ -547,7 +569,8 @@ conv_status_t conv2d_main_loop(const void *lowered, const int32_t *indirection, 
                                void *y, int N, int C_in, int H, int W, int C_out, int KH, int KW, int stride, int pad,
                                int dilation, conv_algo_t algo, conv_layout_t out_layout, conv_dtype_t dtype,
                                conv_stream_t stream, void *workspace, size_t workspace_bytes) {
-    if (algo != CONV_ALGO_INDIRECT && algo != CONV_ALGO_IM2WIN) return CONV_ERR_INVALID_ARG;
+    if (algo != CONV_ALGO_INDIRECT && algo != CONV_ALGO_IM2WIN && algo != CONV_ALGO_IM2COL)
+        return CONV_ERR_INVALID_ARG;
     if (out_layout != CONV_LAYOUT_NCHW && out_layout != CONV_LAYOUT_NHWC) return CONV_ERR_INVALID_ARG;
     // The lowered operands are channels-last, so plan as for an NHWC call.
     Plan pl;
@@ -556,7 +579,7 @@ conv_status_t conv2d_main_loop(const void *lowered, const int32_t *indirection, 
     if (st != CONV_OK) return st;
     if (algo == CONV_ALGO_INDIRECT && (!indirection || (uintptr_t)indirection % 4)) return CONV_ERR_INVALID_ARG;
     pl.out_nchw = out_layout == CONV_LAYOUT_NCHW;
-    pl.need_ibuf = pl.need_win = pl.need_xcl = pl.need_wpack = false;
+    pl.need_ibuf = pl.need_win = pl.need_xcl = pl.need_wpack = pl.need_col = false;
     // Only the split-K partials live in the workspace here; with less room
     // than they need the main loop runs unsplit.
     pl.off_part = 0;
@@ -601,6 +624,23 @@ conv_status_t conv2d_im2win_transform(const void *x, void *xwin, int N, int C_in
     if (!x || !xwin || (uintptr_t)x % es || (uintptr_t)xwin % es) return CONV_ERR_INVALID_ARG;
     if (!sizes_supported(g)) return CONV_ERR_UNSUPPORTED;
     if (launch_im2win(x, xwin, g, layout == CONV_LAYOUT_NHWC, dtype == CONV_DTYPE_BF16, (hipStream_t)stream) !=
+        hipSuccess)
+        return CONV_ERR_HIP;
+    return CONV_OK;
+}
+
+conv_status_t conv2d_im2col_transform(const void *x, void *xcol, int N, int C_in, int H, int W, int KH, int KW,
+                                      int stride, int pad, int dilation, conv_layout_t layout, conv_dtype_t dtype,
+                                      conv_stream_t stream) {
+    if (layout != CONV_LAYOUT_NCHW && layout != CONV_LAYOUT_NHWC) return CONV_ERR_INVALID_ARG;
+    if (dtype != CONV_DTYPE_FP32 && dtype != CONV_DTYPE_BF16) return CONV_ERR_INVALID_ARG;
+    Geom g;
+    conv_status_t st = make_geom(N, C_in, H, W, 1, KH, KW, stride, pad, dilation, &g);
+    if (st != CONV_OK) return st;
+    size_t es = dtype == CONV_DTYPE_BF16 ? 2 : 4;
+    if (!x || !xcol || (uintptr_t)x % es || (uintptr_t)xcol % es) return CONV_ERR_INVALID_ARG;
+    if (!sizes_supported(g) || g.M * g.K > kLimit) return CONV_ERR_UNSUPPORTED;
+    if (launch_im2col(x, xcol, g, layout == CONV_LAYOUT_NHWC, dtype == CONV_DTYPE_BF16, (hipStream_t)stream) !=
         hipSuccess)
         return CONV_ERR_HIP;
     return CONV_OK;

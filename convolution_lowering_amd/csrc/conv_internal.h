@@ -74,6 +74,10 @@ hipError_t launch_splitk_reduce(const float *part, const void *bias, void *y, co
 hipError_t launch_build_indirection(int32_t *buf, const Geom &g, bool nhwc, hipStream_t st);
 hipError_t launch_im2win(const void *x, void *xwin, const Geom &g, bool nhwc, bool bf16,
                          hipStream_t st);
+// X_col, rows (n, ho, wo), columns (ci, kh, kw) for NCHW input, (kh, kw, ci)
+// for NHWC input.
+hipError_t launch_im2col(const void *x, void *xcol, const Geom &g, bool nhwc, bool bf16, hipStream_t st);
+
 // Events the next main-loop launch of this host thread stamps (null: none);
 // reading them clears the request.
 void take_main_loop_events(hipEvent_t *start, hipEvent_t *stop);

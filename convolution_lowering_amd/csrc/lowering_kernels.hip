@@ -134,6 +134,135 @@ hipError_t launch_im2win(const void *x, void *xwin, const Geom &g, bool nhwc, bo
     return bf16 ? im2win_typed<uint16_t>(x, xwin, g, nhwc, st) : im2win_typed<float>(x, xwin, g, nhwc, st);
 }
 
+// X_col, the im2col matrix ("Unifying Convolutions and GEMM", section 2):
+// row m = (n, ho, wo), columns (ci, kh, kw) from NCHW input or (kh, kw, ci)
+// from NHWC input, zero in the padding.  From NHWC input: one thread per
+// 16-byte chunk of a row (VEC consecutive columns), consecutive threads on
+// consecutive chunks.  CHUNK_LOAD: the chunk is VEC channels of one tap,
+// read as one 16-byte load.
+template <typename S, bool CHUNK_LOAD>
+__global__ __launch_bounds__(256) void im2col_nhwc_kernel(const S *__restrict__ x, S *__restrict__ xc, Geom g) {
+    constexpr int VEC = 16 / (int)sizeof(S);
+    const long long cpr = (g.K + VEC - 1) / VEC;  // chunks per row
+    const long long q = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (q >= g.M * cpr) return;
+    const long long m = q / cpr;
+    const int k0 = (int)(q - m * cpr) * VEC;
+    const long long n = m / g.P;
+    const int p = (int)(m - n * g.P);
+    const int ho = p / g.Wo, wo = p - ho * g.Wo;
+    const int hb = ho * g.s - g.p, wb = wo * g.s - g.p;
+    S e[VEC];
+    if constexpr (CHUNK_LOAD) {
+        const int t = k0 / g.C, ci = k0 - t * g.C;
+        const int kh = t / g.KW, kw = t - kh * g.KW;
+        const int hi = hb + kh * g.d, wi = wb + kw * g.d;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (hi >= 0 && hi < g.H && wi >= 0 && wi < g.W)
+            v = *(const uint4 *)(x + ((n * g.H + hi) * g.W + wi) * g.C + ci);
+        __builtin_memcpy(e, &v, 16);
+    } else {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+            const int k = k0 + j;
+            S v = S(0);
+            if (k < g.K) {
+                const int t = k / g.C, ci = k - t * g.C;
+                const int kh = t / g.KW, kw = t - kh * g.KW;
+                const int hi = hb + kh * g.d, wi = wb + kw * g.d;
+                if (hi >= 0 && hi < g.H && wi >= 0 && wi < g.W) v = x[((n * g.H + hi) * g.W + wi) * g.C + ci];
+            }
+            e[j] = v;
+        }
+    }
+    S *dst = xc + m * g.K + k0;
+    if (g.K % VEC == 0) {
+        uint4 out;
+        __builtin_memcpy(&out, e, 16);
+        *(uint4 *)dst = out;
+    } else {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j)
+            if (k0 + j < g.K) dst[j] = e[j];
+    }
+}
+
+// X_col from NCHW input through a 64 x 64 LDS tile (rows m, columns k): the
+// gathers walk consecutive output pixels of one column (neighbouring input
+// pixels of one channel plane) and the stores leave as whole row pieces.
+template <typename S>
+__global__ __launch_bounds__(256) void im2col_nchw_tiled_kernel(const S *__restrict__ x, S *__restrict__ xc,
+                                                                Geom g) {
+    constexpr int TM = 64, TK = 64, VEC = 16 / (int)sizeof(S);
+    __shared__ S tile[TM][TK + VEC];
+    const int ktiles = (int)((g.K + TK - 1) / TK);
+    const long long m0 = (long long)(blockIdx.x / ktiles) * TM;
+    const int kt0 = (int)(blockIdx.x % ktiles) * TK;
+    const int tid = threadIdx.x;
+    const int ml = tid % TM;
+    const long long m = m0 + ml;
+    const bool mok = m < g.M;
+    const long long n = mok ? m / g.P : 0;
+    const int p = mok ? (int)(m - n * g.P) : 0;
+    const int ho = p / g.Wo, wo = p - ho * g.Wo;
+    const int hb = ho * g.s - g.p, wb = wo * g.s - g.p;
+    const S *xn = x + n * g.C * (long long)g.H * g.W;
+#pragma unroll 4
+    for (int i = 0; i < TK / 4; ++i) {  // column kl = tid / 64 + 4 i of the tile
+        const int kl = tid / TM + 4 * i;
+        const int k = kt0 + kl;
+        S v = S(0);
+        if (mok && k < g.K) {
+            const int ci = k / g.T, t = k - ci * g.T;
+            const int kh = t / g.KW, kw = t - kh * g.KW;
+            const int hi = hb + kh * g.d, wi = wb + kw * g.d;
+            if (hi >= 0 && hi < g.H && wi >= 0 && wi < g.W) v = xn[((long long)ci * g.H + hi) * g.W + wi];
+        }
+        tile[ml][kl] = v;
+    }
+    __syncthreads();
+    constexpr int CPR = TK / VEC;  // chunks per tile row
+    const bool vec_rows = g.K % VEC == 0;
+    for (int c = tid; c < TM * CPR; c += 256) {
+        const int r = c / CPR, kc = (c - r * CPR) * VEC;
+        const long long mr = m0 + r;
+        const int k = kt0 + kc;
+        if (mr >= g.M || k >= g.K) continue;
+        S *dst = xc + mr * g.K + k;
+        if (vec_rows) {  // K % VEC == 0: the chunk is whole and aligned
+            uint4 out;
+            __builtin_memcpy(&out, &tile[r][kc], 16);
+            *(uint4 *)dst = out;
+        } else {
+            for (int j = 0; j < VEC && k + j < g.K; ++j) dst[j] = tile[r][kc + j];
+        }
+    }
+}
+
+template <typename S>
+static hipError_t im2col_typed(const void *x, void *xcol, const Geom &g, bool nhwc, hipStream_t st) {
+    constexpr int VEC = 16 / (int)sizeof(S);
+    const long long chunks = g.M * ((g.K + VEC - 1) / VEC);
+    const dim3 grid(blocks_for(chunks, 256));
+    const S *xs = (const S *)x;
+    S *xd = (S *)xcol;
+    if (nhwc && g.C % VEC == 0 && (uintptr_t)x % 16 == 0)
+        hipLaunchKernelGGL((im2col_nhwc_kernel<S, true>), grid, dim3(256), 0, st, xs, xd, g);
+    else if (nhwc)
+        hipLaunchKernelGGL((im2col_nhwc_kernel<S, false>), grid, dim3(256), 0, st, xs, xd, g);
+    else
+        hipLaunchKernelGGL(im2col_nchw_tiled_kernel<S>, dim3((unsigned)(((g.M + 63) / 64) * ((g.K + 63) / 64))),
+                           dim3(256), 0, st, xs, xd, g);
+    return hipGetLastError();
+}
+
+hipError_t launch_im2col(const void *x, void *xcol, const Geom &g, bool nhwc, bool bf16, hipStream_t st) {
+    // 16-byte stores need 16-byte rows on a 16-byte-aligned matrix.
+    const int VEC = bf16 ? 8 : 4;
+    if (g.K % VEC == 0 && (uintptr_t)xcol % 16 != 0) return hipErrorInvalidValue;
+    return bf16 ? im2col_typed<uint16_t>(x, xcol, g, nhwc, st) : im2col_typed<float>(x, xcol, g, nhwc, st);
+}
+
 // The window-ordered tensor with the channels of every (column, kernel row)
 // cell padded to cp, a multiple of the 16-byte chunk VEC = 16 / sizeof(S):
 // Xwin[n][ho][c][kh][cp], zero for channels >= C and in the padding.  One

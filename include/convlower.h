@@ -69,12 +69,18 @@ typedef enum { CONV_DTYPE_FP32 = 0, CONV_DTYPE_BF16 = 1 } conv_dtype_t;
  *             valid for the two plain-GEMM shapes named under AUTO (The
  *             Indirect Convolution Algorithm, abstract: a 1x1 convolution is
  *             a GEMM call; "Unifying Convolutions and GEMM", section 4: a
- *             whole-input kernel is a dense layer).  */
+ *             whole-input kernel is a dense layer).
+ *   IM2COL    the baseline the lowering avoids: X_col materialised in the
+ *             workspace ("Unifying Convolutions and GEMM", section 2; the
+ *             workspace is then the whole im2col footprint), then the same
+ *             MFMA main loop multiplies it as a row-major matrix (section 3).
+ *             Never chosen by AUTO.  */
 typedef enum {
     CONV_ALGO_AUTO = 0,
     CONV_ALGO_INDIRECT = 1,
     CONV_ALGO_IM2WIN = 2,
-    CONV_ALGO_GEMM = 3
+    CONV_ALGO_GEMM = 3,
+    CONV_ALGO_IM2COL = 4
 } conv_algo_t;
 
 typedef enum {
@@ -101,9 +107,11 @@ conv_status_t conv2d_output_size(int H, int W, int KH, int KW, int stride, int p
  * NCHW, the weights regrouped channel-innermost), the channels-last copy of
  * an NCHW input where the path reads one (for a 1x1 layer, of half the
  * batch at a time), and fp32 split-K partials on skinny layers.  It is 0 for
- * the plain-GEMM feed on NHWC input, and always below the im2col footprint
- * N*Ho*Wo*C_in*KH*KW elements.  *bytes_out receives the size; errors as for
- * conv2d_fwd's host checks. */
+ * the plain-GEMM feed on NHWC input, and below the im2col footprint
+ * N*Ho*Wo*C_in*KH*KW elements for every algorithm except CONV_ALGO_IM2COL,
+ * whose workspace is that footprint (plus, on skinny layers, split-K
+ * partials of at most as much again).  *bytes_out receives the size; errors
+ * as for conv2d_fwd's host checks. */
 conv_status_t conv2d_fwd_workspace_size(int N, int C_in, int H, int W, int C_out, int KH, int KW,
                                         int stride, int pad, int dilation,
                                         conv_layout_t layout, conv_dtype_t dtype, conv_algo_t algo,
@@ -132,18 +140,20 @@ conv_status_t conv2d_fwd(const void *x, const void *w, const void *bias, void *y
  * between calls (the indirection buffer depends only on the geometry, the
  * regrouped weights only on w):
  *   lowered      CONV_ALGO_INDIRECT: the input channels-last, [N][H][W][C_in];
+ *                CONV_ALGO_IM2COL: X_col as conv2d_im2col_transform writes
+ *                it for CONV_LAYOUT_NHWC;
  *                CONV_ALGO_IM2WIN: the window-ordered tensor that
  *                conv2d_im2win_transform writes.
  *   indirection  CONV_ALGO_INDIRECT: a buffer from conv2d_build_indirection
  *                for the same geometry with CONV_LAYOUT_NHWC; ignored (may
- *                be NULL) for CONV_ALGO_IM2WIN.
+ *                be NULL) for CONV_ALGO_IM2WIN and CONV_ALGO_IM2COL.
  *   w_ohwi       weights as [C_out][KH][KW][C_in].
  *   out_layout   layout of y: [N][C_out][Ho][Wo] (NCHW) or [N][Ho][Wo][C_out].
  *   workspace    split-K partials only: conv2d_fwd_workspace_size(...,
  *                CONV_LAYOUT_NHWC, dtype, algo) bytes always suffice; with
  *                less (or NULL) the main loop runs without split-K.
- * Other arguments and errors as for conv2d_fwd; any algo other than INDIRECT
- * or IM2WIN is CONV_ERR_INVALID_ARG. */
+ * Other arguments and errors as for conv2d_fwd; any algo other than INDIRECT,
+ * IM2WIN or IM2COL is CONV_ERR_INVALID_ARG. */
 conv_status_t conv2d_main_loop(const void *lowered, const int32_t *indirection, const void *w_ohwi,
                                const void *bias, void *y,
                                int N, int C_in, int H, int W, int C_out, int KH, int KW,
@@ -173,6 +183,18 @@ conv_status_t conv2d_build_indirection(int32_t *buf, int C_in, int H, int W, int
  * one contiguous run of KW*KH*C_in values when dilation is 1.  `x` is in
  * `layout`; the result is the same for both layouts. */
 conv_status_t conv2d_im2win_transform(const void *x, void *xwin, int N, int C_in, int H, int W,
+                                      int KH, int KW, int stride, int pad, int dilation,
+                                      conv_layout_t layout, conv_dtype_t dtype, conv_stream_t stream);
+
+/* The im2col matrix X_col ("Unifying Convolutions and GEMM", section 2):
+ * row m = (n, ho, wo) of N*Ho*Wo, each row the C_in*KH*KW values of that
+ * output pixel's window, zero where the window overlaps the padding.  The
+ * columns run (ci, kh, kw) for CONV_LAYOUT_NCHW -- the order of OIHW
+ * weights -- and (kh, kw, ci) for CONV_LAYOUT_NHWC, the order of OHWI
+ * weights, so either layout's weights are W_row as they lie.  `xcol` holds
+ * conv2d_im2col_bytes bytes, is fully overwritten, and is the caller's.
+ * Errors as for conv2d_im2win_transform. */
+conv_status_t conv2d_im2col_transform(const void *x, void *xcol, int N, int C_in, int H, int W,
                                       int KH, int KW, int stride, int pad, int dilation,
                                       conv_layout_t layout, conv_dtype_t dtype, conv_stream_t stream);
 

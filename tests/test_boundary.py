@@ -28,7 +28,7 @@ def _declared_functions():
 
 def test_library_loads_and_exports_every_declared_symbol():
     names = _declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     L = cl.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -119,6 +119,23 @@ def test_auto_padded_window(name, dtype, layout):
     assert cl.workspace_size(*_args(L, layout, dtype, "im2win")) == want
 
 
+@pytest.mark.parametrize("name", sorted(LAYERS))
+@pytest.mark.parametrize("layout", ["NCHW", "NHWC"])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_im2col_baseline_workspace_is_x_col(name, layout, dtype):
+    """The materialised-im2col baseline holds X_col itself: its workspace is
+    the im2col footprint (256-byte aligned), plus split-K partials of at
+    most another footprint on skinny layers (the dense C5c layer)."""
+    L = LAYERS[name]
+    im2col = cl.im2col_bytes(L.N, L.C, L.H, L.W, L.KH, L.KW, L.stride, L.pad, L.dilation, dtype)
+    up = (im2col + 255) // 256 * 256
+    ws = cl.workspace_size(*_args(L, layout, dtype, "im2col"))
+    if name == "C5c":
+        assert up < ws <= 2 * up
+    else:
+        assert ws == up
+
+
 def test_gemm_algo_rejected_on_windowed_layer():
     L = LAYERS["C2"]
     with pytest.raises(cl.ConvLowerError) as e:
@@ -152,6 +169,8 @@ def test_invalid_enums_and_null_outputs():
     assert L.conv2d_fwd_workspace_size(*base, 2, 1, 0, ctypes.byref(out)) == INVALID   # layout
     assert L.conv2d_fwd_workspace_size(*base, 0, 7, 0, ctypes.byref(out)) == INVALID   # dtype
     assert L.conv2d_fwd_workspace_size(*base, 0, 1, 9, ctypes.byref(out)) == INVALID   # algo
+    assert L.conv2d_fwd_workspace_size(*base, 0, 1, 5, ctypes.byref(out)) == INVALID   # one past IM2COL
+    assert L.conv2d_fwd_workspace_size(*base, 0, 1, -1, ctypes.byref(out)) == INVALID
     assert L.conv2d_fwd_workspace_size(*base, 0, 1, 0, None) == INVALID
 
 

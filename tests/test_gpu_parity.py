@@ -75,7 +75,7 @@ def _cases():
     out = []
     for name, L in LAYERS.items():
         plain = (L.KH == L.KW == 1 and L.stride == 1 and L.pad == 0) or (L.KH == L.H and L.KW == L.W and L.pad == 0)
-        algos = ["auto", "indirect", "im2win"] + (["gemm"] if plain else [])
+        algos = ["auto", "indirect", "im2win", "im2col"] + (["gemm"] if plain else [])
         for dtype in sorted(set(L.dtypes) | {"fp32", "bf16"} if name in ("C1", "C2", "C5a", "C5b", "C5c")
                             else L.dtypes):
             for layout in ("NCHW", "NHWC"):
@@ -247,7 +247,7 @@ EDGE = [
 @pytest.mark.parametrize("case", EDGE, ids=[e[0] for e in EDGE])
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("layout", ["NCHW", "NHWC"])
-@pytest.mark.parametrize("algo", ["auto", "indirect", "im2win"])
+@pytest.mark.parametrize("algo", ["auto", "indirect", "im2win", "im2col"])
 def test_edge_cases(case, dtype, layout, algo):
     from convolution_lowering_amd.workloads import Layer
     name, N, C, H, W, Co, KH, KW, s, p, d = case
@@ -338,9 +338,28 @@ def test_im2win_contents(geom, layout, dtype):
     assert np.array_equal(out.double().cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("geom", GEOMS)
+@pytest.mark.parametrize("layout", ["NCHW", "NHWC"])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_im2col_contents(geom, layout, dtype):
+    """X_col from the HIP transform equals the oracle's plain im2col element
+    for element: columns (ci, kh, kw) from NCHW input, (kh, kw, ci) from NHWC."""
+    C, H, W, KH, KW, s, p, d = geom
+    g = torch.Generator().manual_seed(4)
+    x = torch.randn(2, C, H, W, generator=g).to(torch.float32 if dtype == "fp32" else torch.bfloat16)
+    xl = x if layout == "NCHW" else x.permute(0, 2, 3, 1).contiguous()
+    _say(f"[gpu] im2col {geom} {layout} {dtype}")
+    out = cl.im2col_transform(xl.to(DEV), KH, KW, s, p, d, layout)
+    torch.cuda.synchronize()
+    ref = oracle.im2col(x, KH, KW, s, p, d, oracle.NCHW)
+    if layout == "NHWC":
+        ref = ref.reshape(-1, C, KH, KW).transpose(0, 2, 3, 1).reshape(ref.shape[0], -1)
+    assert np.array_equal(out.double().cpu().numpy(), ref)
+
+
 # --- the main loop on its own, on operands lowered beforehand -------------------
 
-@pytest.mark.parametrize("algo", ["indirect", "im2win"])
+@pytest.mark.parametrize("algo", ["indirect", "im2win", "im2col"])
 @pytest.mark.parametrize("out_layout", ["NCHW", "NHWC"])
 @pytest.mark.parametrize("name", ["C2", "C5a", "C3e"])
 def test_main_loop_entry_matches_full_call(name, algo, out_layout):
@@ -358,6 +377,9 @@ def test_main_loop_entry_matches_full_call(name, algo, out_layout):
     if algo == "indirect":
         lowered = xd
         ib = cl.build_indirection(L.C, L.H, L.W, L.KH, L.KW, L.stride, L.pad, L.dilation, "NHWC")
+    elif algo == "im2col":
+        lowered = cl.im2col_transform(xd, L.KH, L.KW, L.stride, L.pad, L.dilation, "NHWC")
+        ib = None
     else:
         lowered = cl.im2win_transform(xd, L.KH, L.KW, L.stride, L.pad, L.dilation, "NHWC")
         ib = None
