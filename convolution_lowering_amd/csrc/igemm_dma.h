@@ -115,8 +115,8 @@ struct MfmaShape<float, 32> {  // v_mfma_f32_32x32x2_f32, four per 16-byte chunk
 // (fp32) store; the address must be aligned to that size.
 __device__ __forceinline__ void store4(uint16_t *p, float a, float b, float c, float d) {
     uint2 pk;
-    pk.x = (uint32_t)f32_to_bf16_rne(a) | ((uint32_t)f32_to_bf16_rne(b) << 16);
-    pk.y = (uint32_t)f32_to_bf16_rne(c) | ((uint32_t)f32_to_bf16_rne(d) << 16);
+    pk.x = f32x2_to_bf16x2_rne(a, b);
+    pk.y = f32x2_to_bf16x2_rne(c, d);
     *(uint2 *)p = pk;
 }
 __device__ __forceinline__ void store4(float *p, float a, float b, float c, float d) {

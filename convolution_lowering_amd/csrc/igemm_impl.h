@@ -65,12 +65,15 @@ __device__ __forceinline__ uint32_t elem_bits(const float *p, long long i) {
 __device__ __forceinline__ float bits_to_f32(uint16_t, uint32_t b) { return __uint_as_float(b << 16); }
 __device__ __forceinline__ float bits_to_f32(float, uint32_t b) { return __uint_as_float(b); }
 
-// fp32 -> bf16, round to nearest, ties to even (NaN stays a quiet NaN).
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+// fp32 -> bf16, round to nearest, ties to even (NaN stays a NaN): gfx950's
+// v_cvt_pk_bf16_f32, one instruction for a pair, no branch.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+// Two values, a in the low half.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2_rne(float a, float b) {
+    const f32x2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 __device__ __forceinline__ uint16_t to_out(uint16_t, float v) { return f32_to_bf16_rne(v); }

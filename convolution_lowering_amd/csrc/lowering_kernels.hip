@@ -524,12 +524,8 @@ hipError_t launch_pack_weights_ohwi(const void *w, void *o, const Geom &g, bool 
 // ---------------------------------------------------------------------------
 // Split-K finish: y = round(sum over splits, in split order, + bias).  The
 // fixed order keeps the result bit-for-bit repeatable.
-__device__ __forceinline__ uint16_t to_bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
+// (Round to nearest, ties to even: gfx950's v_cvt_pk_bf16_f32.)
+__device__ __forceinline__ uint16_t to_bf16_rne(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 template <typename S, bool OUT_NCHW>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ part, const S *bias,
