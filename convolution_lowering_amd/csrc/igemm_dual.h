@@ -445,14 +445,14 @@ __device__ __forceinline__ void igemm_dual_body(const GemmArgs &A) {
     bool fast = false;  // whole 16-byte chunk inside one image, aligned
     int sub = 1;        // NCHW: widest piece (elements) that never crosses an image
     if constexpr (OUT_NCHW) {
-        const long long m = (long long)m0 + cc * VEC;
-        n0 = (int)(m / g.P);
-        p0 = (int)(m - (long long)n0 * g.P);
+        const uint32_t m = m0 + (uint32_t)(cc * VEC);  // M < 2^31
+        n0 = (int)(m / (uint32_t)g.P);
+        p0 = (int)(m - (uint32_t)n0 * (uint32_t)g.P);
         if ((uintptr_t)y % 16 == 0) {
             sub = VEC;
             while (g.P % sub != 0) sub >>= 1;
         }
-        fast = sub == VEC && m + VEC <= g.M;
+        fast = sub == VEC && (long long)m + VEC <= g.M;
     } else {
         fast = g.Co % VEC == 0 && co0 + cc * VEC + VEC <= g.Co && ((uintptr_t)y % 16) == 0;
     }
@@ -484,7 +484,31 @@ __device__ __forceinline__ void igemm_dual_body(const GemmArgs &A) {
                     }
                 }
         __syncthreads();
-        // LDS -> global, one 16-byte chunk per thread per run.
+        // LDS -> global, one 16-byte chunk per thread per run.  Where every
+        // chunk of this thread is whole and aligned (the common case), all of
+        // its LDS reads are issued before its stores, so their latencies
+        // overlap; otherwise the general loop below.
+        constexpr int RSTEP = NTHR / CPR;  // runs per sweep of the block
+        constexpr int ITER = PROWS / RSTEP;
+        static_assert(PROWS % RSTEP == 0, "runs split evenly over the threads");
+        if (fast) {
+            uint4 vals[ITER];
+#pragma unroll
+            for (int i = 0; i < ITER; ++i)
+                vals[i] = *(const uint4 *)(tile + (tid / CPR + i * RSTEP) * RSTR + cc * VEC);
+#pragma unroll
+            for (int i = 0; i < ITER; ++i) {
+                const int row = r_lo + tid / CPR + i * RSTEP;
+                if constexpr (OUT_NCHW) {
+                    const int co = co0 + row;
+                    if (co < g.Co) *(uint4 *)(y + ((long long)n0 * g.Co + co) * g.P + p0) = vals[i];
+                } else {
+                    const long long m = (long long)m0 + row;
+                    if (m < g.M) *(uint4 *)(y + m * g.Co + co0 + cc * VEC) = vals[i];
+                }
+            }
+            continue;  // next pass
+        }
         for (int r = tid / CPR; r < PROWS; r += NTHR / CPR) {
             const int row = r_lo + r;
             const uint4 val = *(const uint4 *)(tile + r * RSTR + cc * VEC);
