@@ -258,11 +258,12 @@ def main():
         for name, L in LAYERS.items():
             for dtype in L.dtypes:
                 for layout in ("NCHW", "NHWC"):
-                    # every layer also through the materialised-im2col
-                    # baseline the lowering avoids
-                    algos = ["auto", "im2col"]
+                    # every layer also through the two baselines: the
+                    # materialised im2col the lowering avoids, and direct
+                    # convolution on the vector ALUs
+                    algos = ["auto", "im2col", "direct"]
                     if name == "C2":
-                        algos = ["auto", "indirect", "im2win", "im2col"]
+                        algos = ["auto", "indirect", "im2win", "im2col", "direct"]
                     for algo in algos:
                         try:
                             r = bench_layer(L, dtype, layout, algo, max(3, args.steps // 4), 2, flush)

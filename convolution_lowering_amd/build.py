@@ -32,7 +32,8 @@ FLAGS = [
 def _units():
     units = [("conv_api", "conv_api.cpp", []),
              ("igemm_dispatch", "igemm_dispatch.hip", []),
-             ("lowering_kernels", "lowering_kernels.hip", [])]
+             ("lowering_kernels", "lowering_kernels.hip", []),
+             ("direct_conv", "direct_conv.hip", [])]
     for bf16 in (1, 0):
         for feed in range(7):  # the Feed values of conv_internal.h
             units.append((f"igemm_{'bf16' if bf16 else 'f32'}_feed{feed}", "igemm_inst.hip",

@@ -37,6 +37,7 @@ struct Plan {
     int tile, splits, kps;
     bool need_ibuf, need_win, need_wpack;
     bool need_col;  // X_col materialised (the im2col baseline)
+    bool direct;    // the direct-convolution baseline: no lowering, no main loop
     bool need_xcl;  // channels-last copy of an NCHW input
     int chunk_n;    // images per main-loop pass (< N: the batch goes through the copy in parts)
     int cp;         // channels per pixel row of the channels-last copy (> C: zero-padded)
@@ -85,7 +86,7 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
                         bool allow_pad = true) {
     if (layout != CONV_LAYOUT_NCHW && layout != CONV_LAYOUT_NHWC) return CONV_ERR_INVALID_ARG;
     if (dtype != CONV_DTYPE_FP32 && dtype != CONV_DTYPE_BF16) return CONV_ERR_INVALID_ARG;
-    if (algo < CONV_ALGO_AUTO || algo > CONV_ALGO_IM2COL) return CONV_ERR_INVALID_ARG;
+    if (algo < CONV_ALGO_AUTO || algo > CONV_ALGO_DIRECT) return CONV_ERR_INVALID_ARG;
     memset(pl, 0, sizeof(*pl));
     conv_status_t st = make_geom(N, C, H, W, Co, KH, KW, s, p, d, &pl->g);
     if (st != CONV_OK) return st;
@@ -180,6 +181,13 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
                 pl->need_wpack = !pl->nhwc && g.T > 1;  // OIHW regrouped to (kh, kw, ci) order
             }
             break;
+        case CONV_ALGO_DIRECT:
+            pl->direct = true;
+            pl->gm = g;
+            pl->out_nchw = !pl->nhwc;
+            pl->splits = 1;
+            pl->total = 0;
+            return CONV_OK;
         case CONV_ALGO_IM2COL:
             // X_col in the workspace, multiplied as a plain row-major matrix.
             // Its columns follow the weights' own order: (ci, kh, kw) for
@@ -469,6 +477,8 @@ conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias
     hipStream_t s = (hipStream_t)stream;
     const Geom &g = pl.g;
     char *ws = (char *)workspace;
+    if (pl.direct)
+        return launch_direct_conv(x, w, bias, y, g, pl.nhwc, pl.bf16, s) == hipSuccess ? CONV_OK : CONV_ERR_HIP;
 
     GemmArgs a;
     memset(&a, 0, sizeof(a));

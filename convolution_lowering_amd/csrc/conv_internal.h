@@ -74,6 +74,11 @@ hipError_t launch_splitk_reduce(const float *part, const void *bias, void *y, co
 hipError_t launch_build_indirection(int32_t *buf, const Geom &g, bool nhwc, hipStream_t st);
 hipError_t launch_im2win(const void *x, void *xwin, const Geom &g, bool nhwc, bool bf16,
                          hipStream_t st);
+// Direct convolution (no lowering, no matrix core): y from x, w and bias in
+// `nhwc` or NCHW layout.
+hipError_t launch_direct_conv(const void *x, const void *w, const void *bias, void *y, const Geom &g, bool nhwc,
+                              bool bf16, hipStream_t st);
+
 // X_col, rows (n, ho, wo), columns (ci, kh, kw) for NCHW input, (kh, kw, ci)
 // for NHWC input.
 hipError_t launch_im2col(const void *x, void *xcol, const Geom &g, bool nhwc, bool bf16, hipStream_t st);

@@ -74,13 +74,20 @@ typedef enum { CONV_DTYPE_FP32 = 0, CONV_DTYPE_BF16 = 1 } conv_dtype_t;
  *             workspace ("Unifying Convolutions and GEMM", section 2; the
  *             workspace is then the whole im2col footprint), then the same
  *             MFMA main loop multiplies it as a row-major matrix (section 3).
- *             Never chosen by AUTO.  */
+ *             Never chosen by AUTO.
+ *   DIRECT    the other baseline: the seven-loop definition ("Unifying
+ *             Convolutions and GEMM", section 1) run directly on the vector
+ *             ALUs, one thread per output pixel and 8 output channels, fp32
+ *             accumulation; no lowering, no workspace, no matrix core
+ *             ("Im2win: An Efficient Convolution Paradigm on GPU", abstract,
+ *             compares against such a kernel).  Never chosen by AUTO.  */
 typedef enum {
     CONV_ALGO_AUTO = 0,
     CONV_ALGO_INDIRECT = 1,
     CONV_ALGO_IM2WIN = 2,
     CONV_ALGO_GEMM = 3,
-    CONV_ALGO_IM2COL = 4
+    CONV_ALGO_IM2COL = 4,
+    CONV_ALGO_DIRECT = 5
 } conv_algo_t;
 
 typedef enum {

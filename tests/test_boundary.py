@@ -136,6 +136,23 @@ def test_im2col_baseline_workspace_is_x_col(name, layout, dtype):
         assert ws == up
 
 
+@pytest.mark.parametrize("name", sorted(LAYERS))
+def test_direct_baseline_needs_no_workspace(name):
+    L = LAYERS[name]
+    for layout in ("NCHW", "NHWC"):
+        for dtype in ("fp32", "bf16"):
+            assert cl.workspace_size(*_args(L, layout, dtype, "direct")) == 0
+
+
+def test_main_loop_rejects_direct_and_gemm():
+    """conv2d_main_loop takes lowered operands; the direct baseline and the
+    plain-GEMM algorithm have none, and are refused on the host."""
+    L = cl.lib()
+    for algo in (cl.ALGOS["direct"], cl.ALGOS["gemm"], cl.ALGOS["auto"]):
+        rc = L.conv2d_main_loop(8, 16, 16, None, 32, 2, 4, 8, 8, 4, 3, 3, 1, 1, 1, algo, 0, 1, None, None, 0)
+        assert rc == INVALID
+
+
 def test_gemm_algo_rejected_on_windowed_layer():
     L = LAYERS["C2"]
     with pytest.raises(cl.ConvLowerError) as e:
@@ -169,7 +186,7 @@ def test_invalid_enums_and_null_outputs():
     assert L.conv2d_fwd_workspace_size(*base, 2, 1, 0, ctypes.byref(out)) == INVALID   # layout
     assert L.conv2d_fwd_workspace_size(*base, 0, 7, 0, ctypes.byref(out)) == INVALID   # dtype
     assert L.conv2d_fwd_workspace_size(*base, 0, 1, 9, ctypes.byref(out)) == INVALID   # algo
-    assert L.conv2d_fwd_workspace_size(*base, 0, 1, 5, ctypes.byref(out)) == INVALID   # one past IM2COL
+    assert L.conv2d_fwd_workspace_size(*base, 0, 1, 6, ctypes.byref(out)) == INVALID   # one past DIRECT
     assert L.conv2d_fwd_workspace_size(*base, 0, 1, -1, ctypes.byref(out)) == INVALID
     assert L.conv2d_fwd_workspace_size(*base, 0, 1, 0, None) == INVALID
 

@@ -75,7 +75,7 @@ def _cases():
     out = []
     for name, L in LAYERS.items():
         plain = (L.KH == L.KW == 1 and L.stride == 1 and L.pad == 0) or (L.KH == L.H and L.KW == L.W and L.pad == 0)
-        algos = ["auto", "indirect", "im2win", "im2col"] + (["gemm"] if plain else [])
+        algos = ["auto", "indirect", "im2win", "im2col", "direct"] + (["gemm"] if plain else [])
         for dtype in sorted(set(L.dtypes) | {"fp32", "bf16"} if name in ("C1", "C2", "C5a", "C5b", "C5c")
                             else L.dtypes):
             for layout in ("NCHW", "NHWC"):
@@ -247,7 +247,7 @@ EDGE = [
 @pytest.mark.parametrize("case", EDGE, ids=[e[0] for e in EDGE])
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("layout", ["NCHW", "NHWC"])
-@pytest.mark.parametrize("algo", ["auto", "indirect", "im2win", "im2col"])
+@pytest.mark.parametrize("algo", ["auto", "indirect", "im2win", "im2col", "direct"])
 def test_edge_cases(case, dtype, layout, algo):
     from convolution_lowering_amd.workloads import Layer
     name, N, C, H, W, Co, KH, KW, s, p, d = case
