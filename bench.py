@@ -276,6 +276,28 @@ def main():
                               f"frac {r.get('roofline', {}).get('frac', float('nan')):.3f}", file=sys.stderr, flush=True)
                         torch.cuda.empty_cache()
 
+    # Ablation of the main loop's techniques: every variant forced on a few
+    # layers (same whole-call timing).
+    ablation = []
+    if args.layers == "all":
+        for name, dtype, layout in (("C2", "bf16", "NCHW"), ("C2", "bf16", "NHWC"), ("C3c", "bf16", "NHWC"),
+                                    ("C4d", "bf16", "NHWC")):
+            L = LAYERS[name]
+            for variant in cl.MAIN_LOOPS:
+                cl.force_main_loop(variant)
+                try:
+                    r = bench_layer(L, dtype, layout, "auto", max(3, args.steps // 4), 2, flush)
+                    ablation.append({"layer": name, "dtype": dtype, "layout": layout, "main_loop": variant,
+                                     "ms": r["ms"], "tflops": r["tflops"]})
+                    print(f"# ablation {name} {dtype} {layout} {variant}: {r['ms']:.4f} ms {r['tflops']:.1f} TFLOPS",
+                          file=sys.stderr, flush=True)
+                except cl.ConvLowerError as e:
+                    ablation.append({"layer": name, "dtype": dtype, "layout": layout, "main_loop": variant,
+                                     "error": str(e)})
+                finally:
+                    cl.force_main_loop("auto")
+                torch.cuda.empty_cache()
+
     if args.calibration_copy:
         calibration_copy()
 
@@ -294,6 +316,7 @@ def main():
         "roofline": rl,
         "cpu_baseline": cpu,
         "layers": rows,
+        "ablation": ablation,
     }
     print(json.dumps(line))
 

@@ -25,7 +25,9 @@ STATUS = {0: "CONV_OK", 1: "CONV_ERR_INVALID_ARG", 2: "CONV_ERR_UNSUPPORTED", 3:
 # Every symbol include/convlower.h declares.
 EXPORTS = ("conv_status_string", "conv2d_output_size", "conv2d_fwd_workspace_size", "conv2d_im2col_bytes",
            "conv2d_fwd", "conv2d_main_loop", "conv2d_build_indirection", "conv2d_im2win_transform",
-           "conv2d_im2col_transform", "conv2d_time_next_main_loop")
+           "conv2d_im2col_transform", "conv2d_force_main_loop", "conv2d_time_next_main_loop")
+MAIN_LOOPS = {"auto": 0, "element_128x128": 1, "dma_128x128": 2, "dma_256x128": 3, "dual_256x128": 4,
+              "oct_256x128": 5, "oct_256x256": 6, "quad_128x64": 7}
 
 
 class ConvLowerError(RuntimeError):
@@ -65,6 +67,8 @@ def lib():
     L.conv2d_im2win_transform.restype = c_int
     L.conv2d_im2col_transform.argtypes = [vp, vp] + [c_int] * 11 + [vp]
     L.conv2d_im2col_transform.restype = c_int
+    L.conv2d_force_main_loop.argtypes = [c_int]
+    L.conv2d_force_main_loop.restype = c_int
     L.conv2d_time_next_main_loop.argtypes = [vp, vp]
     L.conv2d_time_next_main_loop.restype = c_int
     _lib = L
@@ -260,6 +264,12 @@ def im2col_transform(x, KH, KW, stride=1, pad=0, dilation=1, layout="NCHW", stre
                                          dilation, LAYOUTS[layout], _dtype_code(x.dtype),
                                          _stream_handle(stream, x.device)))
     return out
+
+
+def force_main_loop(variant="auto"):
+    """Force the main-loop variant of this thread's plans (ablation); "auto"
+    restores the library's choice (conv2d_force_main_loop)."""
+    _check("conv2d_force_main_loop", lib().conv2d_force_main_loop(MAIN_LOOPS[variant]))
 
 
 def time_next_main_loop(start, stop):

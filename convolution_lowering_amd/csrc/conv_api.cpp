@@ -1,8 +1,9 @@
 // The C ABI of include/convlower.h: argument checks, the lowering plan
 // (feed, tile, split-K, workspace layout) and the launch sequence.
 //
-// Every decision here is a fixed function of the call's sizes, so the
-// workspace query and the launch agree without keeping any state.
+// Every decision here is a fixed function of the call's sizes (and of the
+// calling thread's main-loop override, when one is set for ablation), so the
+// workspace query and the launch agree.
 #include <string.h>
 
 #include "conv_internal.h"
@@ -14,6 +15,9 @@ constexpr long long kLimit = (1LL << 31) - 1;  // element counts the kernels ind
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Main-loop variant forced on this thread's plans (CONV_MAIN_LOOP_AUTO: none).
+thread_local int t_forced_main_loop = CONV_MAIN_LOOP_AUTO;
 
 // Main loops whose indirection slice in LDS holds up to 12 taps at any
 // tile height (the others hold 3072 entries).
@@ -43,6 +47,7 @@ struct Plan {
     int cp;         // channels per pixel row of the channels-last copy (> C: zero-padded)
     Geom gm;        // geometry the main loop sees (C = cp, K = T*cp)
     bool rows16;  // the feed can read X_col rows in 16-byte chunks (by shape)
+    bool force_element;  // main loop forced to the element-gather loop
     size_t off_ibuf, off_win, off_xcl, off_wpack, off_col, off_part, total;
     size_t esize;
 };
@@ -269,6 +274,42 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     } else {
         pl->tile = TILE_128x128; BM = 128; BN = 128;
     }
+    // A forced variant (ablation) replaces the choice above when the feed
+    // and shape allow it.
+    const bool chunk_feed = pl->feed == FEED_IND_CHUNK || pl->feed == FEED_WIN_CHUNK;
+    switch (t_forced_main_loop) {
+        case CONV_MAIN_LOOP_AUTO: break;
+        case CONV_MAIN_LOOP_ELEMENT_128x128:
+            pl->tile = TILE_128x128; BM = 128; BN = 128;
+            pl->force_element = true;
+            break;
+        case CONV_MAIN_LOOP_DMA_128x128:
+            if (!rows16 || chunk_feed) return CONV_ERR_UNSUPPORTED;
+            pl->tile = TILE_128x128; BM = 128; BN = 128;
+            break;
+        case CONV_MAIN_LOOP_DMA_256x128:
+            if (!rows16 || chunk_feed) return CONV_ERR_UNSUPPORTED;
+            pl->tile = TILE_256x128; BM = 256; BN = 128;
+            break;
+        case CONV_MAIN_LOOP_DUAL_256x128:
+            if (!dual) return CONV_ERR_UNSUPPORTED;
+            pl->tile = TILE_256x128_DUAL; BM = 256; BN = 128;
+            break;
+        case CONV_MAIN_LOOP_OCT_256x128:
+            if (!oct) return CONV_ERR_UNSUPPORTED;
+            pl->tile = TILE_256x128_OCT; BM = 256; BN = 128;
+            break;
+        case CONV_MAIN_LOOP_OCT_256x256:
+            if (!dual) return CONV_ERR_UNSUPPORTED;
+            pl->tile = TILE_256x256_OCT; BM = 256; BN = 256;
+            break;
+        case CONV_MAIN_LOOP_QUAD_128x64:
+            if (!dual) return CONV_ERR_UNSUPPORTED;
+            pl->tile = TILE_128x64_QUAD; BM = 128; BN = 64;
+            break;
+        default:
+            return CONV_ERR_INVALID_ARG;
+    }
     // Workspace regions other than the split-K partials.
     size_t lowered = 0;
     if (pl->need_ibuf) lowered = align_up(lowered + (size_t)g.P * g.T * sizeof(int32_t));
@@ -422,6 +463,7 @@ conv_status_t launch_main(const Plan &pl, GemmArgs &a, hipStream_t s) {
         case FEED_WIN_CHUNK: a_vec = al16(a.a_src) && wide_slice(pl.tile); break;
         default: a_vec = false;
     }
+    if (pl.force_element) a_vec = false;
     bool b_vec = g.K % VEC == 0 && al16(a.b);
     // The vector paths address A and B with 32-bit buffer offsets.
     const long long kBufMax = (1LL << 31) - 64;
@@ -601,6 +643,12 @@ conv_status_t conv2d_main_loop(const void *lowered, const int32_t *indirection, 
         pl.total = 0;
     }
     return run(pl, lowered, w_ohwi, bias, y, indirection, stream, workspace, workspace_bytes);
+}
+
+conv_status_t conv2d_force_main_loop(conv_main_loop_t variant) {
+    if (variant < CONV_MAIN_LOOP_AUTO || variant > CONV_MAIN_LOOP_QUAD_128x64) return CONV_ERR_INVALID_ARG;
+    t_forced_main_loop = variant;
+    return CONV_OK;
 }
 
 conv_status_t conv2d_time_next_main_loop(void *start_event, void *stop_event) {

@@ -205,6 +205,43 @@ conv_status_t conv2d_im2col_transform(const void *x, void *xcol, int N, int C_in
                                       int KH, int KW, int stride, int pad, int dilation,
                                       conv_layout_t layout, conv_dtype_t dtype, conv_stream_t stream);
 
+/* Main-loop variants, for ablation ("Im2win: An Efficient Convolution
+ * Paradigm on GPU", abstract, ablates its kernel's techniques the same way).
+ * Each computes the same convolution; only the summation order of the K
+ * sum may differ.
+ *   AUTO            the library's own choice (the default).
+ *   ELEMENT_128x128 element gathers through registers into LDS: no 16-byte
+ *                   vector loads, no load-to-LDS DMA.
+ *   DMA_128x128     16-byte loads straight to LDS, one wavefront per SIMD,
+ *                   128 x 128 block tile, wavefront tiles 64 x 64.
+ *   DMA_256x128     the same with a 256 x 128 block tile (wavefronts 128 x 64).
+ *   DUAL_256x128    two 256-thread blocks per CU, two wavefronts per SIMD,
+ *                   wavefront tiles 128 x 64, 64-byte K rows.
+ *   OCT_256x128     one 512-thread block per CU, two wavefronts per SIMD,
+ *                   wavefront tiles 64 x 64, 128-byte K rows.
+ *   OCT_256x256     one 512-thread block per CU, 256 x 256 block tile.
+ *   QUAD_128x64     four 256-thread blocks per CU, 128 x 64 block tile.  */
+typedef enum {
+    CONV_MAIN_LOOP_AUTO = 0,
+    CONV_MAIN_LOOP_ELEMENT_128x128 = 1,
+    CONV_MAIN_LOOP_DMA_128x128 = 2,
+    CONV_MAIN_LOOP_DMA_256x128 = 3,
+    CONV_MAIN_LOOP_DUAL_256x128 = 4,
+    CONV_MAIN_LOOP_OCT_256x128 = 5,
+    CONV_MAIN_LOOP_OCT_256x256 = 6,
+    CONV_MAIN_LOOP_QUAD_128x64 = 7
+} conv_main_loop_t;
+
+/* Force the main-loop variant of every plan the calling host thread makes
+ * from now on (workspace queries, conv2d_fwd, conv2d_main_loop), for
+ * ablation and benchmarking; CONV_MAIN_LOOP_AUTO restores the library's
+ * choice.  A call whose feed or shape the forced variant cannot serve (the
+ * two-wavefront loops need K tiles inside one tap; the DMA loops need
+ * 16-byte rows) returns CONV_ERR_UNSUPPORTED before any launch.  Query the
+ * workspace under the same setting as the call.  Returns
+ * CONV_ERR_INVALID_ARG for an unknown variant, else CONV_OK. */
+conv_status_t conv2d_force_main_loop(conv_main_loop_t variant);
+
 /* Instrumentation for measuring the main loop on its own.  The next
  * implicit-GEMM main-loop kernel (step c with its fused epilogue d, as
  * launched by conv2d_fwd or conv2d_main_loop) that the calling host thread

@@ -28,7 +28,7 @@ def _declared_functions():
 
 def test_library_loads_and_exports_every_declared_symbol():
     names = _declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     L = cl.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -151,6 +151,31 @@ def test_main_loop_rejects_direct_and_gemm():
     for algo in (cl.ALGOS["direct"], cl.ALGOS["gemm"], cl.ALGOS["auto"]):
         rc = L.conv2d_main_loop(8, 16, 16, None, 32, 2, 4, 8, 8, 4, 3, 3, 1, 1, 1, algo, 0, 1, None, None, 0)
         assert rc == INVALID
+
+
+def test_forced_main_loop_checks_on_the_host():
+    """A forced main-loop variant the feed cannot serve is refused by the
+    query; an unknown variant is an invalid argument; "auto" restores the
+    library's choice (the workspace query agrees with it again)."""
+    L = LAYERS["C2"]
+    auto = cl.workspace_size(*_args(L, "NHWC", "bf16", "auto"))
+    odd = cl.workspace_size(24, 24, 13, 15, 130, 3, 3, 1, 1, 1, "NHWC", "bf16", "indirect")
+    try:
+        for v in cl.MAIN_LOOPS:
+            cl.force_main_loop(v)
+            assert cl.workspace_size(*_args(L, "NHWC", "bf16", "auto")) >= 0  # C2 takes every variant
+        cl.force_main_loop("dual_256x128")  # K tiles would straddle taps at C = 24
+        with pytest.raises(cl.ConvLowerError) as e:
+            cl.workspace_size(24, 24, 13, 15, 130, 3, 3, 1, 1, 1, "NHWC", "bf16", "indirect")
+        assert e.value.code == UNSUPPORTED
+        cl.force_main_loop("element_128x128")
+        assert cl.workspace_size(24, 24, 13, 15, 130, 3, 3, 1, 1, 1, "NHWC", "bf16", "indirect") >= 0
+        assert cl.lib().conv2d_force_main_loop(8) == INVALID
+        assert cl.lib().conv2d_force_main_loop(-1) == INVALID
+    finally:
+        cl.force_main_loop("auto")
+    assert cl.workspace_size(*_args(L, "NHWC", "bf16", "auto")) == auto
+    assert cl.workspace_size(24, 24, 13, 15, 130, 3, 3, 1, 1, 1, "NHWC", "bf16", "indirect") == odd
 
 
 def test_gemm_algo_rejected_on_windowed_layer():

@@ -426,3 +426,34 @@ def test_stamped_main_loop_same_bits_and_inside_the_call(layout):
     torch.cuda.synchronize()
     assert ka.elapsed_time(kb) == k_ms
     assert torch.equal(y0.view(torch.int16), y2.view(torch.int16))
+
+
+# --- forced main-loop variants (ablation) ---------------------------------------
+
+FORCED_CASES = [
+    # name, N, C, H, W, Co, KH, KW, s, p, d
+    ("C2-one-image", 1, 64, 56, 56, 128, 3, 3, 1, 1, 1),
+    ("planes-odd", 3, 64, 7, 9, 96, 3, 3, 1, 1, 1),
+]
+
+
+@pytest.mark.parametrize("variant", [v for v in cl.MAIN_LOOPS if v != "auto"])
+@pytest.mark.parametrize("case", FORCED_CASES, ids=[c[0] for c in FORCED_CASES])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("layout", ["NCHW", "NHWC"])
+@pytest.mark.parametrize("algo", ["auto", "im2win"])
+def test_forced_main_loop_parity(variant, case, dtype, layout, algo):
+    """Every main-loop variant, forced, meets the parity bar on the same
+    shapes (several tiles and ragged ones, both feeds, both layouts)."""
+    from convolution_lowering_amd.workloads import Layer
+    name, N, C, H, W, Co, KH, KW, s, p, d = case
+    L = Layer(name, N, C, H, W, Co, KH, KW, s, p, d, seed=78)
+    _say(f"[gpu] forced {variant} {name} {dtype} {layout} {algo}")
+    cl.force_main_loop(variant)
+    try:
+        y = _run(L, dtype, layout, algo, N)
+    finally:
+        cl.force_main_loop("auto")
+    x, w, b = make_inputs(L, dtype, "NCHW")
+    y_ref, dn = oracle.conv2d(x, w, b, s, p, d, oracle.NCHW)
+    _assert_parity(_to_nchw(y, layout), y_ref, dn, dtype, f"{variant} {name} {dtype} {layout} {algo}")
