@@ -32,9 +32,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "conv fwd TFLOPS & fraction of MFMA peak per layer; workspace bytes"
-PEAK = {"bf16": 2500.0, "fp32": 157.3}  # MI355X dense MFMA, TFLOP/s
+PEAK = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}  # MI355X dense MFMA, TFLOP/s
 HBM_PEAK = 8000.0  # GB/s
-ESIZE = {"bf16": 2, "fp32": 4}
+ESIZE = {"bf16": 2, "fp16": 2, "fp32": 4}
 
 
 def layer_geometry(L):
@@ -256,7 +256,8 @@ def main():
     rows = []
     if args.layers == "all":
         for name, L in LAYERS.items():
-            for dtype in L.dtypes:
+            # fp16 on the verification layer too (the second 16-bit type)
+            for dtype in (L.dtypes + ("fp16",) if name == "C2" else L.dtypes):
                 for layout in ("NCHW", "NHWC"):
                     # every layer also through the two baselines: the
                     # materialised im2col the lowering avoids, and direct

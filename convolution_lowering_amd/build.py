@@ -34,10 +34,10 @@ def _units():
              ("igemm_dispatch", "igemm_dispatch.hip", []),
              ("lowering_kernels", "lowering_kernels.hip", []),
              ("direct_conv", "direct_conv.hip", [])]
-    for bf16 in (1, 0):
+    for dt, tag in ((1, "bf16"), (2, "f16"), (0, "f32")):  # IGEMM_DTYPE: 0 fp32, 1 bf16, 2 fp16
         for feed in range(7):  # the Feed values of conv_internal.h
-            units.append((f"igemm_{'bf16' if bf16 else 'f32'}_feed{feed}", "igemm_inst.hip",
-                          [f"-DIGEMM_BF16={bf16}", f"-DIGEMM_FEED={feed}"]))
+            units.append((f"igemm_{tag}_feed{feed}", "igemm_inst.hip",
+                          [f"-DIGEMM_DTYPE={dt}", f"-DIGEMM_FEED={feed}"]))
     return units
 
 

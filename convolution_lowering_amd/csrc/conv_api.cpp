@@ -16,6 +16,9 @@ constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
+bool dtype_ok(conv_dtype_t d) { return d == CONV_DTYPE_FP32 || d == CONV_DTYPE_BF16 || d == CONV_DTYPE_FP16; }
+size_t dtype_bytes(conv_dtype_t d) { return d == CONV_DTYPE_FP32 ? 4 : 2; }
+
 // Main-loop variant forced on this thread's plans (CONV_MAIN_LOOP_AUTO: none).
 thread_local int t_forced_main_loop = CONV_MAIN_LOOP_AUTO;
 
@@ -35,7 +38,8 @@ int tile_rows(int tile) {
 
 struct Plan {
     Geom g;
-    bool bf16, nhwc;
+    bool e16, nhwc;  // 16-bit elements (bf16 or fp16); channels-last tensors
+    int dtype;       // conv_dtype_t
     int feed;
     bool out_nchw;
     int tile, splits, kps;
@@ -90,7 +94,7 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
                         conv_layout_t layout, conv_dtype_t dtype, conv_algo_t algo, Plan *pl,
                         bool allow_pad = true) {
     if (layout != CONV_LAYOUT_NCHW && layout != CONV_LAYOUT_NHWC) return CONV_ERR_INVALID_ARG;
-    if (dtype != CONV_DTYPE_FP32 && dtype != CONV_DTYPE_BF16) return CONV_ERR_INVALID_ARG;
+    if (!dtype_ok(dtype)) return CONV_ERR_INVALID_ARG;
     if (algo < CONV_ALGO_AUTO || algo > CONV_ALGO_DIRECT) return CONV_ERR_INVALID_ARG;
     memset(pl, 0, sizeof(*pl));
     conv_status_t st = make_geom(N, C, H, W, Co, KH, KW, s, p, d, &pl->g);
@@ -99,9 +103,10 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     pl->cp = C;
     const Geom &g = pl->g;
     if (!sizes_supported(g)) return CONV_ERR_UNSUPPORTED;
-    pl->bf16 = dtype == CONV_DTYPE_BF16;
+    pl->e16 = dtype != CONV_DTYPE_FP32;
+    pl->dtype = dtype;
     pl->nhwc = layout == CONV_LAYOUT_NHWC;
-    pl->esize = pl->bf16 ? 2 : 4;
+    pl->esize = pl->e16 ? 2 : 4;
 
     // A 1x1 stride-1 unpadded convolution is a GEMM call (The Indirect
     // Convolution Algorithm, abstract); a kernel that covers the whole
@@ -114,7 +119,7 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     // every chunk of a K tile on its own, whatever tap it falls in.  The
     // indirection buffer then has to fit the main loop's LDS slice (at most
     // 12 taps); larger kernels read a window tensor padded the same way.
-    const int VEC = pl->bf16 ? 8 : 4;
+    const int VEC = pl->e16 ? 8 : 4;
     const int cpad = (g.C + VEC - 1) / VEC * VEC;
     const bool pad_c = allow_pad && g.C % VEC != 0;
     const long long im2col_bytes = g.M * g.K * (long long)pl->esize;
@@ -136,7 +141,7 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
                 pl->feed = FEED_ROWMAJOR;  // Ho = Wo = 1: both layouts store y as [N][Co]
             } else if (one && pl->nhwc) {
                 pl->feed = FEED_ROWMAJOR;
-            } else if (one && g.C % (pl->bf16 ? 8 : 4) == 0 && g.N >= 2) {
+            } else if (one && g.C % (pl->e16 ? 8 : 4) == 0 && g.N >= 2) {
                 // NCHW 1x1: half the batch at a time is copied channels-last
                 // and multiplied as a plain GEMM (the copy of all of x would
                 // be as large as X_col itself).
@@ -166,7 +171,7 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
                 pl->need_wpack = true;
             } else if (pl->nhwc) {
                 pl->feed = FEED_IND_NHWC;
-            } else if (g.C % (pl->bf16 ? 8 : 4) == 0 && 256LL * g.T <= 3072 &&
+            } else if (g.C % (pl->e16 ? 8 : 4) == 0 && 256LL * g.T <= 3072 &&
                        (long long)g.T * g.Ho * g.Wo >= 2LL * g.H * g.W) {  // copy well below im2col
                 pl->feed = FEED_IND_NHWC;
                 pl->need_xcl = true;
@@ -227,7 +232,7 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     // one tap (C a multiple of the tile: 128-byte rows for the 512-thread
     // loop, 64-byte rows for the two-blocks-per-CU loop), and an indirection
     // slice of at most 12 taps whose entries divided by C fit 16 bits.
-    const int BK8 = pl->bf16 ? 64 : 32, BK4 = pl->bf16 ? 32 : 16;
+    const int BK8 = pl->e16 ? 64 : 32, BK4 = pl->e16 ? 32 : 16;
     bool dual = rows16, oct = rows16;
     switch (pl->feed) {
         case FEED_ROWMAJOR: break;
@@ -318,7 +323,7 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     if (pl->need_wpack) lowered = align_up(lowered + (size_t)g.Co * pl->gm.K * pl->esize);
     if (pl->need_col) lowered = align_up(lowered + (size_t)g.M * g.K * pl->esize);
 
-    const int BK = pl->bf16 ? 64 : 32;  // the main loop's K tile (128-byte LDS rows)
+    const int BK = pl->e16 ? 64 : 32;  // the main loop's K tile (128-byte LDS rows)
     long long blocks = ((Mt + BM - 1) / BM) * ((g.Co + BN - 1) / BN);
     long long ktiles = (pl->gm.K + BK - 1) / BK;
     int splits = 1;
@@ -431,11 +436,11 @@ conv_status_t conv2d_fwd_workspace_size(int N, int C_in, int H, int W, int C_out
 conv_status_t conv2d_im2col_bytes(int N, int C_in, int H, int W, int KH, int KW, int stride, int pad,
                                   int dilation, conv_dtype_t dtype, size_t *bytes_out) {
     if (!bytes_out) return CONV_ERR_INVALID_ARG;
-    if (dtype != CONV_DTYPE_FP32 && dtype != CONV_DTYPE_BF16) return CONV_ERR_INVALID_ARG;
+    if (!dtype_ok(dtype)) return CONV_ERR_INVALID_ARG;
     Geom g;
     conv_status_t st = make_geom(N, C_in, H, W, 1, KH, KW, stride, pad, dilation, &g);
     if (st != CONV_OK) return st;
-    *bytes_out = (size_t)g.M * (size_t)g.K * (dtype == CONV_DTYPE_BF16 ? 2 : 4);
+    *bytes_out = (size_t)g.M * (size_t)g.K * dtype_bytes(dtype);
     return CONV_OK;
 }
 
@@ -450,7 +455,7 @@ namespace {
 // geometry, a.a_src / a.b / a.y its operands.
 conv_status_t launch_main(const Plan &pl, GemmArgs &a, hipStream_t s) {
     const Geom &g = a.g;
-    const int VEC = pl.bf16 ? 8 : 4;
+    const int VEC = pl.e16 ? 8 : 4;
     auto al16 = [](const void *ptr) { return (uintptr_t)ptr % 16 == 0; };
     bool a_vec;
     switch (pl.feed) {
@@ -496,11 +501,12 @@ conv_status_t launch_main(const Plan &pl, GemmArgs &a, hipStream_t s) {
         a.c_shift = sh;
         a.c_inv = inv;
     }
-    hipError_t e = pl.bf16 ? launch_igemm_bf16(a, pl.feed, pl.out_nchw, a_vec, b_vec, tile, pl.splits, s)
-                           : launch_igemm_f32(a, pl.feed, pl.out_nchw, a_vec, b_vec, tile, pl.splits, s);
+    hipError_t e = pl.dtype == CONV_DTYPE_FP16 ? launch_igemm_f16(a, pl.feed, pl.out_nchw, a_vec, b_vec, tile, pl.splits, s)
+                   : pl.e16 ? launch_igemm_bf16(a, pl.feed, pl.out_nchw, a_vec, b_vec, tile, pl.splits, s)
+                            : launch_igemm_f32(a, pl.feed, pl.out_nchw, a_vec, b_vec, tile, pl.splits, s);
     if (e != hipSuccess) return CONV_ERR_HIP;
     if (pl.splits > 1) {
-        if (launch_splitk_reduce(a.part, a.bias, a.y, g, pl.splits, pl.out_nchw, pl.bf16, s) != hipSuccess)
+        if (launch_splitk_reduce(a.part, a.bias, a.y, g, pl.splits, pl.out_nchw, pl.dtype, s) != hipSuccess)
             return CONV_ERR_HIP;
     }
     return CONV_OK;
@@ -520,7 +526,7 @@ conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias
     const Geom &g = pl.g;
     char *ws = (char *)workspace;
     if (pl.direct)
-        return launch_direct_conv(x, w, bias, y, g, pl.nhwc, pl.bf16, s) == hipSuccess ? CONV_OK : CONV_ERR_HIP;
+        return launch_direct_conv(x, w, bias, y, g, pl.nhwc, pl.dtype, s) == hipSuccess ? CONV_OK : CONV_ERR_HIP;
 
     GemmArgs a;
     memset(&a, 0, sizeof(a));
@@ -534,7 +540,7 @@ conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias
             gc.N = g.N - n0 < pl.chunk_n ? g.N - n0 : pl.chunk_n;
             gc.M = (long long)gc.N * g.P;
             const char *xs = (const char *)x + (size_t)n0 * g.C * g.H * g.W * es;
-            if (launch_prep(xs, false, xc, g.C, nullptr, nullptr, false, nullptr, gc, pl.bf16, s) != hipSuccess)
+            if (launch_prep(xs, false, xc, g.C, nullptr, nullptr, false, nullptr, gc, pl.e16, s) != hipSuccess)
                 return CONV_ERR_HIP;
             a.g = gc;
             a.bias = bias;
@@ -569,7 +575,7 @@ conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias
         // One launch: the channels-last copy of x (rows of cp channels), the
         // indirection buffer over it and the weights in (kh, kw, ci) order.
         void *xc = ws + pl.off_xcl;
-        if (launch_prep(x, pl.nhwc, xc, pl.cp, ib_build, w, pl.nhwc, wp, g, pl.bf16, s) != hipSuccess)
+        if (launch_prep(x, pl.nhwc, xc, pl.cp, ib_build, w, pl.nhwc, wp, g, pl.e16, s) != hipSuccess)
             return CONV_ERR_HIP;
         a.a_src = xc;
         ib_build = nullptr;
@@ -578,24 +584,24 @@ conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias
     if (ib_build && launch_build_indirection(ib_build, g, ib_rows, s) != hipSuccess) return CONV_ERR_HIP;
     if (pl.need_col) {
         void *xcol = ws + pl.off_col;
-        if (launch_im2col(x, xcol, g, pl.nhwc, pl.bf16, s) != hipSuccess) return CONV_ERR_HIP;
+        if (launch_im2col(x, xcol, g, pl.nhwc, pl.e16, s) != hipSuccess) return CONV_ERR_HIP;
         a.a_src = xcol;
     }
     if (pl.need_win) {
         void *xw = ws + pl.off_win;
         if (pl.feed == FEED_WIN_CHUNK) {
-            if (launch_im2win_pad(x, xw, g, pl.cp, pl.nhwc, pl.bf16, s) != hipSuccess) return CONV_ERR_HIP;
+            if (launch_im2win_pad(x, xw, g, pl.cp, pl.nhwc, pl.e16, s) != hipSuccess) return CONV_ERR_HIP;
             // Weights zero-padded to (kh, kw, cp) order from either layout.
-            if (launch_prep(nullptr, pl.nhwc, nullptr, pl.cp, nullptr, w, pl.nhwc, wp, g, pl.bf16, s) != hipSuccess)
+            if (launch_prep(nullptr, pl.nhwc, nullptr, pl.cp, nullptr, w, pl.nhwc, wp, g, pl.e16, s) != hipSuccess)
                 return CONV_ERR_HIP;
             wp_done = true;
-        } else if (launch_im2win(x, xw, g, pl.nhwc, pl.bf16, s) != hipSuccess) {
+        } else if (launch_im2win(x, xw, g, pl.nhwc, pl.e16, s) != hipSuccess) {
             return CONV_ERR_HIP;
         }
         a.a_src = xw;
     }
     if (wp) {
-        if (!wp_done && launch_pack_weights_ohwi(w, wp, g, pl.bf16, s) != hipSuccess) return CONV_ERR_HIP;
+        if (!wp_done && launch_pack_weights_ohwi(w, wp, g, pl.e16, s) != hipSuccess) return CONV_ERR_HIP;
         a.b = wp;
     }
     if (pl.splits > 1) a.part = (float *)(ws + pl.off_part);
@@ -637,7 +643,7 @@ conv_status_t conv2d_main_loop(const void *lowered, const int32_t *indirection, 
     pl.off_part = 0;
     pl.total = pl.splits > 1 ? align_up((size_t)pl.splits * pl.g.M * pl.g.Co * sizeof(float)) : 0;
     if (pl.total > 0 && (!workspace || workspace_bytes < pl.total)) {
-        const int BK = pl.bf16 ? 64 : 32;
+        const int BK = pl.e16 ? 64 : 32;
         pl.splits = 1;
         pl.kps = (int)((pl.gm.K + BK - 1) / BK * BK);
         pl.total = 0;
@@ -674,14 +680,14 @@ conv_status_t conv2d_im2win_transform(const void *x, void *xwin, int N, int C_in
                                       int stride, int pad, int dilation, conv_layout_t layout, conv_dtype_t dtype,
                                       conv_stream_t stream) {
     if (layout != CONV_LAYOUT_NCHW && layout != CONV_LAYOUT_NHWC) return CONV_ERR_INVALID_ARG;
-    if (dtype != CONV_DTYPE_FP32 && dtype != CONV_DTYPE_BF16) return CONV_ERR_INVALID_ARG;
+    if (!dtype_ok(dtype)) return CONV_ERR_INVALID_ARG;
     Geom g;
     conv_status_t st = make_geom(N, C_in, H, W, 1, KH, KW, stride, pad, dilation, &g);
     if (st != CONV_OK) return st;
-    size_t es = dtype == CONV_DTYPE_BF16 ? 2 : 4;
+    size_t es = dtype_bytes(dtype);
     if (!x || !xwin || (uintptr_t)x % es || (uintptr_t)xwin % es) return CONV_ERR_INVALID_ARG;
     if (!sizes_supported(g)) return CONV_ERR_UNSUPPORTED;
-    if (launch_im2win(x, xwin, g, layout == CONV_LAYOUT_NHWC, dtype == CONV_DTYPE_BF16, (hipStream_t)stream) !=
+    if (launch_im2win(x, xwin, g, layout == CONV_LAYOUT_NHWC, es == 2, (hipStream_t)stream) !=
         hipSuccess)
         return CONV_ERR_HIP;
     return CONV_OK;
@@ -691,14 +697,14 @@ conv_status_t conv2d_im2col_transform(const void *x, void *xcol, int N, int C_in
                                       int stride, int pad, int dilation, conv_layout_t layout, conv_dtype_t dtype,
                                       conv_stream_t stream) {
     if (layout != CONV_LAYOUT_NCHW && layout != CONV_LAYOUT_NHWC) return CONV_ERR_INVALID_ARG;
-    if (dtype != CONV_DTYPE_FP32 && dtype != CONV_DTYPE_BF16) return CONV_ERR_INVALID_ARG;
+    if (!dtype_ok(dtype)) return CONV_ERR_INVALID_ARG;
     Geom g;
     conv_status_t st = make_geom(N, C_in, H, W, 1, KH, KW, stride, pad, dilation, &g);
     if (st != CONV_OK) return st;
-    size_t es = dtype == CONV_DTYPE_BF16 ? 2 : 4;
+    size_t es = dtype_bytes(dtype);
     if (!x || !xcol || (uintptr_t)x % es || (uintptr_t)xcol % es) return CONV_ERR_INVALID_ARG;
     if (!sizes_supported(g) || g.M * g.K > kLimit) return CONV_ERR_UNSUPPORTED;
-    if (launch_im2col(x, xcol, g, layout == CONV_LAYOUT_NHWC, dtype == CONV_DTYPE_BF16, (hipStream_t)stream) !=
+    if (launch_im2col(x, xcol, g, layout == CONV_LAYOUT_NHWC, es == 2, (hipStream_t)stream) !=
         hipSuccess)
         return CONV_ERR_HIP;
     return CONV_OK;

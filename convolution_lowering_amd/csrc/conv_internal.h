@@ -69,15 +69,18 @@ hipError_t launch_igemm_bf16(const GemmArgs &a, int feed, bool out_nchw, bool a_
                              int tile, int splits, hipStream_t st);
 hipError_t launch_igemm_f32(const GemmArgs &a, int feed, bool out_nchw, bool a_vec, bool b_vec,
                             int tile, int splits, hipStream_t st);
+hipError_t launch_igemm_f16(const GemmArgs &a, int feed, bool out_nchw, bool a_vec, bool b_vec,
+                            int tile, int splits, hipStream_t st);
+// dtype: 0 fp32, 1 bf16, 2 fp16 (the conv_dtype_t values).
 hipError_t launch_splitk_reduce(const float *part, const void *bias, void *y, const Geom &g,
-                                int splits, bool out_nchw, bool bf16, hipStream_t st);
+                                int splits, bool out_nchw, int dtype, hipStream_t st);
 hipError_t launch_build_indirection(int32_t *buf, const Geom &g, bool nhwc, hipStream_t st);
 hipError_t launch_im2win(const void *x, void *xwin, const Geom &g, bool nhwc, bool bf16,
                          hipStream_t st);
 // Direct convolution (no lowering, no matrix core): y from x, w and bias in
 // `nhwc` or NCHW layout.
 hipError_t launch_direct_conv(const void *x, const void *w, const void *bias, void *y, const Geom &g, bool nhwc,
-                              bool bf16, hipStream_t st);
+                              int dtype, hipStream_t st);
 
 // X_col, rows (n, ho, wo), columns (ci, kh, kw) for NCHW input, (kh, kw, ci)
 // for NHWC input.

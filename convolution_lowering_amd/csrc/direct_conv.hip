@@ -22,10 +22,12 @@ namespace {
 constexpr int kDirectCT = 8;  // output channels per thread
 
 __device__ __forceinline__ float load_f32(const uint16_t *p, long long i) { return __uint_as_float((uint32_t)p[i] << 16); }
+__device__ __forceinline__ float load_f32(const _Float16 *p, long long i) { return (float)p[i]; }
 __device__ __forceinline__ float load_f32(const float *p, long long i) { return p[i]; }
 __device__ __forceinline__ void store_out(uint16_t *p, long long i, float v) {
     p[i] = __builtin_bit_cast(uint16_t, (__bf16)v);  // round to nearest, ties to even
 }
+__device__ __forceinline__ void store_out(_Float16 *p, long long i, float v) { p[i] = (_Float16)v; }  // RNE
 __device__ __forceinline__ void store_out(float *p, long long i, float v) { p[i] = v; }
 
 template <typename S, bool NHWC>
@@ -89,9 +91,11 @@ hipError_t direct_typed(const void *x, const void *w, const void *bias, void *y,
 }  // namespace
 
 hipError_t launch_direct_conv(const void *x, const void *w, const void *bias, void *y, const Geom &g, bool nhwc,
-                              bool bf16, hipStream_t st) {
+                              int dtype, hipStream_t st) {
     if (g.Co > 65535LL * kDirectCT) return hipErrorInvalidValue;  // grid.y limit
-    return bf16 ? direct_typed<uint16_t>(x, w, bias, y, g, nhwc, st) : direct_typed<float>(x, w, bias, y, g, nhwc, st);
+    if (dtype == 1) return direct_typed<uint16_t>(x, w, bias, y, g, nhwc, st);
+    if (dtype == 2) return direct_typed<_Float16>(x, w, bias, y, g, nhwc, st);
+    return direct_typed<float>(x, w, bias, y, g, nhwc, st);
 }
 
 }  // namespace convlower

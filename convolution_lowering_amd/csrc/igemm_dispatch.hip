@@ -32,4 +32,9 @@ hipError_t launch_igemm_f32(const GemmArgs &a, int feed, bool out_nchw, bool a_v
     return dispatch<float>(a, feed, out_nchw, a_vec, b_vec, tile, splits, st);
 }
 
+hipError_t launch_igemm_f16(const GemmArgs &a, int feed, bool out_nchw, bool a_vec, bool b_vec, int tile,
+                            int splits, hipStream_t st) {
+    return dispatch<_Float16>(a, feed, out_nchw, a_vec, b_vec, tile, splits, st);
+}
+
 }  // namespace convlower

@@ -89,6 +89,24 @@ struct MfmaShape<uint16_t, 32> {  // v_mfma_f32_32x32x16_bf16
     }
 };
 template <>
+struct MfmaShape<_Float16, 16> {  // v_mfma_f32_16x16x32_f16
+    static constexpr int MT = 16, CPG = 4, NQ = 1, QSTEP = 16;
+    typedef f32x4_t acc_t;
+    __device__ static __forceinline__ int qrow(int, int lane) { return 4 * (lane >> 4); }
+    __device__ static __forceinline__ void mma(const uint4 &a, const uint4 &b, acc_t &c) {
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+    }
+};
+template <>
+struct MfmaShape<_Float16, 32> {  // v_mfma_f32_32x32x16_f16
+    static constexpr int MT = 32, CPG = 2, NQ = 4, QSTEP = 8;
+    typedef f32x16_t acc_t;
+    __device__ static __forceinline__ int qrow(int q, int lane) { return 8 * q + 4 * (lane >> 5); }
+    __device__ static __forceinline__ void mma(const uint4 &a, const uint4 &b, acc_t &c) {
+        c = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+    }
+};
+template <>
 struct MfmaShape<float, 16> {  // v_mfma_f32_16x16x4_f32, four per 16-byte chunk
     static constexpr int MT = 16, CPG = 4, NQ = 1, QSTEP = 16;
     typedef f32x4_t acc_t;
@@ -117,6 +135,12 @@ __device__ __forceinline__ void store4(uint16_t *p, float a, float b, float c, f
     uint2 pk;
     pk.x = f32x2_to_bf16x2_rne(a, b);
     pk.y = f32x2_to_bf16x2_rne(c, d);
+    *(uint2 *)p = pk;
+}
+__device__ __forceinline__ void store4(_Float16 *p, float a, float b, float c, float d) {
+    uint2 pk;
+    pk.x = f32x2_to_f16x2_rne(a, b);
+    pk.y = f32x2_to_f16x2_rne(c, d);
     *(uint2 *)p = pk;
 }
 __device__ __forceinline__ void store4(float *p, float a, float b, float c, float d) {

@@ -43,6 +43,7 @@
 namespace convlower {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
@@ -53,16 +54,26 @@ struct Elem<uint16_t> {  // bf16 stored as raw 16-bit words
     static constexpr int VEC = 8;
 };
 template <>
+struct Elem<_Float16> {  // IEEE half
+    static constexpr int VEC = 8;
+};
+template <>
 struct Elem<float> {
     static constexpr int VEC = 4;
 };
 
 __device__ __forceinline__ uint32_t elem_bits(const uint16_t *p, long long i) { return p[i]; }
+__device__ __forceinline__ uint32_t elem_bits(const _Float16 *p, long long i) {
+    return __builtin_bit_cast(uint16_t, p[i]);
+}
 __device__ __forceinline__ uint32_t elem_bits(const float *p, long long i) {
     return __float_as_uint(p[i]);
 }
 
 __device__ __forceinline__ float bits_to_f32(uint16_t, uint32_t b) { return __uint_as_float(b << 16); }
+__device__ __forceinline__ float bits_to_f32(_Float16, uint32_t b) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
 __device__ __forceinline__ float bits_to_f32(float, uint32_t b) { return __uint_as_float(b); }
 
 // fp32 -> bf16, round to nearest, ties to even (NaN stays a NaN): gfx950's
@@ -77,6 +88,13 @@ __device__ __forceinline__ uint32_t f32x2_to_bf16x2_rne(float a, float b) {
 }
 
 __device__ __forceinline__ uint16_t to_out(uint16_t, float v) { return f32_to_bf16_rne(v); }
+// fp32 -> fp16, round to nearest, ties to even (the default rounding mode).
+__device__ __forceinline__ _Float16 to_out(_Float16, float v) { return (_Float16)v; }
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32x2_to_f16x2_rne(float a, float b) {
+    const f32x2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
 __device__ __forceinline__ float to_out(float, float v) { return v; }
 
 // Buffer loads: an offset past the buffer's size reads as zeros, so padding
@@ -406,7 +424,14 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(GemmArgs A) {
             for (int ip = 0; ip < TP; ++ip)
 #pragma unroll
                 for (int ic = 0; ic < TC; ++ic) {
-                    if constexpr (sizeof(S) == 2) {
+                    if constexpr (std::is_same<S, _Float16>::value) {
+                        f16x8_t xa = __builtin_bit_cast(f16x8_t, af[ip]);
+                        f16x8_t xb = __builtin_bit_cast(f16x8_t, bf[ic]);
+                        if constexpr (OUT_NCHW)
+                            acc[ip][ic] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, xb, acc[ip][ic], 0, 0, 0);
+                        else
+                            acc[ip][ic] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xb, xa, acc[ip][ic], 0, 0, 0);
+                    } else if constexpr (sizeof(S) == 2) {
                         bf16x8_t xa = __builtin_bit_cast(bf16x8_t, af[ip]);
                         bf16x8_t xb = __builtin_bit_cast(bf16x8_t, bf[ic]);
                         if constexpr (OUT_NCHW)

@@ -1,6 +1,7 @@
 // One (dtype, feed) slice of the main-loop instantiations.  The build
-// compiles this file once per pair, with IGEMM_BF16 and IGEMM_FEED set, so
-// the many template variants build in parallel.
+// compiles this file once per pair, with IGEMM_DTYPE (0 fp32, 1 bf16,
+// 2 fp16) and IGEMM_FEED set, so the many template variants build in
+// parallel.
 #include "igemm_impl.h"
 
 #ifndef IGEMM_FEED
@@ -8,8 +9,10 @@
 #endif
 
 namespace convlower {
-#if IGEMM_BF16
-using SliceT = uint16_t;
+#if IGEMM_DTYPE == 1
+using SliceT = uint16_t;  // bf16 as raw 16-bit words
+#elif IGEMM_DTYPE == 2
+using SliceT = _Float16;
 #else
 using SliceT = float;
 #endif

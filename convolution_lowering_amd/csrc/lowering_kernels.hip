@@ -523,9 +523,14 @@ hipError_t launch_pack_weights_ohwi(const void *w, void *o, const Geom &g, bool 
 
 // ---------------------------------------------------------------------------
 // Split-K finish: y = round(sum over splits, in split order, + bias).  The
-// fixed order keeps the result bit-for-bit repeatable.
-// (Round to nearest, ties to even: gfx950's v_cvt_pk_bf16_f32.)
-__device__ __forceinline__ uint16_t to_bf16_rne(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+// fixed order keeps the result bit-for-bit repeatable.  Rounding to nearest,
+// ties to even (gfx950's v_cvt_pk_bf16_f32; the default mode for fp16).
+__device__ __forceinline__ float red_load(const uint16_t *p, int i) { return __uint_as_float((uint32_t)p[i] << 16); }
+__device__ __forceinline__ float red_load(const _Float16 *p, int i) { return (float)p[i]; }
+__device__ __forceinline__ float red_load(const float *p, int i) { return p[i]; }
+__device__ __forceinline__ uint16_t red_out(uint16_t, float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+__device__ __forceinline__ _Float16 red_out(_Float16, float f) { return (_Float16)f; }
+__device__ __forceinline__ float red_out(float, float f) { return f; }
 
 template <typename S, bool OUT_NCHW>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ part, const S *bias,
@@ -537,42 +542,36 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
     int co = (int)(e - m * g.Co);
     float acc = 0.f;
     for (int z = 0; z < splits; ++z) acc += part[(long long)z * total + e];
-    if (bias) {
-        if constexpr (sizeof(S) == 2)
-            acc += __uint_as_float((uint32_t)((const uint16_t *)bias)[co] << 16);
-        else
-            acc += ((const float *)bias)[co];
-    }
+    if (bias) acc += red_load(bias, co);
     long long yi = e;
     if constexpr (OUT_NCHW) {
         long long n = m / g.P;
         yi = (n * g.Co + co) * g.P + (m - n * g.P);
     }
-    if constexpr (sizeof(S) == 2)
-        ((uint16_t *)y)[yi] = to_bf16_rne(acc);
+    y[yi] = red_out(S(), acc);
+}
+
+template <typename S>
+static void reduce_typed(const float *part, const void *bias, void *y, const Geom &g, int splits, bool out_nchw,
+                         dim3 grid, hipStream_t st) {
+    if (out_nchw)
+        hipLaunchKernelGGL((splitk_reduce_kernel<S, true>), grid, dim3(256), 0, st, part, (const S *)bias, (S *)y, g,
+                           splits);
     else
-        ((float *)y)[yi] = acc;
+        hipLaunchKernelGGL((splitk_reduce_kernel<S, false>), grid, dim3(256), 0, st, part, (const S *)bias, (S *)y, g,
+                           splits);
 }
 
 hipError_t launch_splitk_reduce(const float *part, const void *bias, void *y, const Geom &g, int splits,
-                                bool out_nchw, bool bf16, hipStream_t st) {
+                                bool out_nchw, int dtype, hipStream_t st) {
     long long total = g.M * g.Co;
     dim3 grid(blocks_for(total, 256));
-    if (bf16) {
-        if (out_nchw)
-            hipLaunchKernelGGL((splitk_reduce_kernel<uint16_t, true>), grid, dim3(256), 0, st, part,
-                               (const uint16_t *)bias, (uint16_t *)y, g, splits);
-        else
-            hipLaunchKernelGGL((splitk_reduce_kernel<uint16_t, false>), grid, dim3(256), 0, st, part,
-                               (const uint16_t *)bias, (uint16_t *)y, g, splits);
-    } else {
-        if (out_nchw)
-            hipLaunchKernelGGL((splitk_reduce_kernel<float, true>), grid, dim3(256), 0, st, part,
-                               (const float *)bias, (float *)y, g, splits);
-        else
-            hipLaunchKernelGGL((splitk_reduce_kernel<float, false>), grid, dim3(256), 0, st, part,
-                               (const float *)bias, (float *)y, g, splits);
-    }
+    if (dtype == 1)
+        reduce_typed<uint16_t>(part, bias, y, g, splits, out_nchw, grid, st);
+    else if (dtype == 2)
+        reduce_typed<_Float16>(part, bias, y, g, splits, out_nchw, grid, st);
+    else
+        reduce_typed<float>(part, bias, y, g, splits, out_nchw, grid, st);
     return hipGetLastError();
 }
 

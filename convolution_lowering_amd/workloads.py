@@ -92,7 +92,7 @@ LAYERS = {
               "7x7 kernel over a 7x7 input, 512->1000 (a dense layer)"),
 }
 
-TORCH_DTYPES = {"fp32": torch.float32, "bf16": torch.bfloat16}
+TORCH_DTYPES = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}
 
 
 def make_inputs(layer: Layer, dtype: str = "bf16", layout: str = "NCHW", *, N: int | None = None,

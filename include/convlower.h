@@ -54,7 +54,9 @@ struct ihipStream_t;
 typedef struct ihipStream_t *conv_stream_t;
 
 typedef enum { CONV_LAYOUT_NCHW = 0, CONV_LAYOUT_NHWC = 1 } conv_layout_t;
-typedef enum { CONV_DTYPE_FP32 = 0, CONV_DTYPE_BF16 = 1 } conv_dtype_t;
+/* Element type of x, w, bias and y (all the same); the sums are fp32 in
+ * every case, rounded once to the element type at the store. */
+typedef enum { CONV_DTYPE_FP32 = 0, CONV_DTYPE_BF16 = 1, CONV_DTYPE_FP16 = 2 } conv_dtype_t;
 
 /* Which lowering feeds the contraction.
  *   AUTO      1x1 stride-1 unpadded, or kernel == whole unpadded input: the

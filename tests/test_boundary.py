@@ -55,12 +55,12 @@ def _args(L, layout="NCHW", dtype="bf16", algo="auto"):
 
 @pytest.mark.parametrize("name", sorted(LAYERS))
 @pytest.mark.parametrize("layout", ["NCHW", "NHWC"])
-@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp16"])
 def test_workspace_below_im2col(name, layout, dtype):
     L = LAYERS[name]
     im2col = cl.im2col_bytes(L.N, L.C, L.H, L.W, L.KH, L.KW, L.stride, L.pad, L.dilation, dtype)
     Ho, Wo = cl.output_size(L.H, L.W, L.KH, L.KW, L.stride, L.pad, L.dilation)
-    assert im2col == L.N * Ho * Wo * L.C * L.KH * L.KW * (2 if dtype == "bf16" else 4)
+    assert im2col == L.N * Ho * Wo * L.C * L.KH * L.KW * (4 if dtype == "fp32" else 2)
     plain_gemm = (L.KH == L.KW == 1 and L.stride == 1 and L.pad == 0) or (L.KH == L.H and L.KW == L.W and L.pad == 0)
     auto = cl.workspace_size(*_args(L, layout, dtype, "auto"))
     assert auto < im2col
@@ -71,7 +71,7 @@ def test_workspace_below_im2col(name, layout, dtype):
         assert win < im2col
         # channels not a whole number of 16-byte chunks with more than 12
         # taps: AUTO takes the window tensor with cells padded to whole chunks
-        es = 2 if dtype == "bf16" else 4
+        es = 4 if dtype == "fp32" else 2
         padded_win = (L.C * es) % 16 != 0 and L.KH * L.KW > 12
         assert auto == (win if padded_win else ind)
     else:
@@ -79,7 +79,7 @@ def test_workspace_below_im2col(name, layout, dtype):
         # half the batch; whole-input kernel: only the split-K partials
         whole = L.KH == L.H and L.KW == L.W
         if not whole:
-            es = 2 if dtype == "bf16" else 4
+            es = 4 if dtype == "fp32" else 2
             half = (L.N + 1) // 2 * L.C * L.H * L.W * es
             assert auto == (0 if layout == "NHWC" else (half + 255) // 256 * 256)
         assert cl.workspace_size(*_args(L, layout, dtype, "gemm")) == auto
@@ -100,7 +100,7 @@ def test_auto_workspace_on_1x1(name):
     assert cl.workspace_size(*_args(one, "NCHW", "bf16", "auto")) == 0
 
 
-@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp16"])
 @pytest.mark.parametrize("layout", ["NCHW", "NHWC"])
 @pytest.mark.parametrize("name", ["C3a", "C5a"])
 def test_auto_padded_window(name, dtype, layout):
@@ -109,7 +109,7 @@ def test_auto_padded_window(name, dtype, layout):
     row) cell's channels padded to whole 16-byte chunks, plus the weights
     padded to (kh, kw, the same channel count)."""
     L = LAYERS[name]
-    es = 2 if dtype == "bf16" else 4
+    es = 4 if dtype == "fp32" else 2
     cp = -(-L.C * es // 16) * 16 // es
     Ho, Wo = cl.output_size(L.H, L.W, L.KH, L.KW, L.stride, L.pad, L.dilation)
     Wwin = (Wo - 1) * L.stride + (L.KW - 1) * L.dilation + 1
@@ -121,7 +121,7 @@ def test_auto_padded_window(name, dtype, layout):
 
 @pytest.mark.parametrize("name", sorted(LAYERS))
 @pytest.mark.parametrize("layout", ["NCHW", "NHWC"])
-@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp16"])
 def test_im2col_baseline_workspace_is_x_col(name, layout, dtype):
     """The materialised-im2col baseline holds X_col itself: its workspace is
     the im2col footprint (256-byte aligned), plus split-K partials of at

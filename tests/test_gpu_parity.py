@@ -20,7 +20,7 @@ from convolution_lowering_amd.workloads import LAYERS, make_inputs
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"fp32": 1e-5, "bf16": 8e-3}
+TOL = {"fp32": 1e-5, "bf16": 8e-3, "fp16": 1e-3}
 DEV = "cuda"
 _ORACLE_CACHE = {}
 
@@ -76,7 +76,7 @@ def _cases():
     for name, L in LAYERS.items():
         plain = (L.KH == L.KW == 1 and L.stride == 1 and L.pad == 0) or (L.KH == L.H and L.KW == L.W and L.pad == 0)
         algos = ["auto", "indirect", "im2win", "im2col", "direct"] + (["gemm"] if plain else [])
-        for dtype in sorted(set(L.dtypes) | {"fp32", "bf16"} if name in ("C1", "C2", "C5a", "C5b", "C5c")
+        for dtype in sorted(set(L.dtypes) | {"fp32", "bf16", "fp16"} if name in ("C1", "C2", "C5a", "C5b", "C5c")
                             else L.dtypes):
             for layout in ("NCHW", "NHWC"):
                 for algo in algos:
@@ -116,6 +116,11 @@ def test_integer_inputs_exact(name, layout, algo):
     yb = _to_nchw(_run(L, "bf16", layout, algo, n, integer=True), layout).float().cpu()
     exp = torch.from_numpy(y_ref).float().to(torch.bfloat16).float()
     assert torch.equal(yb, exp), f"{name} {layout} {algo}: bf16 not the rounded exact result"
+    # fp16: the exact result (an integer well inside fp16's range) rounded
+    # once to nearest, ties to even
+    yh = _to_nchw(_run(L, "fp16", layout, algo, n, integer=True), layout).float().cpu()
+    exp = torch.from_numpy(y_ref).float().to(torch.float16).float()
+    assert torch.equal(yh, exp), f"{name} {layout} {algo}: fp16 not the rounded exact result"
 
 
 # --- full-size layers, in the configuration the benchmark times -------------
@@ -245,7 +250,7 @@ EDGE = [
 
 
 @pytest.mark.parametrize("case", EDGE, ids=[e[0] for e in EDGE])
-@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp16"])
 @pytest.mark.parametrize("layout", ["NCHW", "NHWC"])
 @pytest.mark.parametrize("algo", ["auto", "indirect", "im2win", "im2col", "direct"])
 def test_edge_cases(case, dtype, layout, algo):
