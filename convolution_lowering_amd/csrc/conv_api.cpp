@@ -262,15 +262,13 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
         pl->tile = TILE_256x256_OCT; BM = 256; BN = 256;
     } else if (g.Co <= 64) {
         pl->tile = TILE_128x64; BM = 128; BN = 64;
-    } else if (oct && (tiles256 > 512 || tiles256 <= 256)) {
-        // One 512-thread block per CU (two wavefronts on every SIMD from one
-        // block, whole-cache-line loads): grids of more tiles than two
-        // resident blocks per CU hold in one round, or of no more tiles than
-        // there are CUs.
+    } else if (oct && tiles256 <= 256) {
+        // No more tiles than CUs: one 512-thread block per CU (two wavefronts
+        // on every SIMD from one block, whole-cache-line loads).
         pl->tile = TILE_256x128_OCT; BM = 256; BN = 128;
     } else if (dual) {
-        // Up to one round of two blocks per CU (their prologues and epilogues
-        // overlap each other's main loops).
+        // Two blocks per CU: their prologues and epilogues overlap each
+        // other's main loops, in one round or many.
         pl->tile = TILE_256x128_DUAL; BM = 256; BN = 128;
     } else if (oct) {
         pl->tile = TILE_256x128_OCT; BM = 256; BN = 128;
