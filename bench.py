@@ -262,12 +262,16 @@ def main():
                     # every layer also through the two baselines: the
                     # materialised im2col the lowering avoids, and direct
                     # convolution on the vector ALUs
-                    algos = ["auto", "im2col", "direct"]
+                    algos = ["auto", "im2col", "direct", "im2win_lds"]
                     if name == "C2":
-                        algos = ["auto", "indirect", "im2win", "im2col", "direct"]
+                        algos = ["auto", "indirect", "im2win", "im2col", "direct", "im2win_lds"]
                     for algo in algos:
                         try:
                             r = bench_layer(L, dtype, layout, algo, max(3, args.steps // 4), 2, flush)
+                        except cl.ConvLowerError as e:
+                            if algo == "im2win_lds" and e.code == 2:
+                                continue  # shape outside the window-rows-in-LDS loop
+                            r = {"layer": name, "dtype": dtype, "layout": layout, "algo": algo, "error": str(e)}
                         except Exception as e:  # report, keep going
                             r = {"layer": name, "dtype": dtype, "layout": layout, "algo": algo, "error": str(e)}
                         rows.append(r)

@@ -95,7 +95,7 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
                         bool allow_pad = true) {
     if (layout != CONV_LAYOUT_NCHW && layout != CONV_LAYOUT_NHWC) return CONV_ERR_INVALID_ARG;
     if (!dtype_ok(dtype)) return CONV_ERR_INVALID_ARG;
-    if (algo < CONV_ALGO_AUTO || algo > CONV_ALGO_DIRECT) return CONV_ERR_INVALID_ARG;
+    if (algo < CONV_ALGO_AUTO || algo > CONV_ALGO_IM2WIN_LDS) return CONV_ERR_INVALID_ARG;
     memset(pl, 0, sizeof(*pl));
     conv_status_t st = make_geom(N, C, H, W, Co, KH, KW, s, p, d, &pl->g);
     if (st != CONV_OK) return st;
@@ -131,6 +131,14 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     const long long win_pad = (long long)g.N * g.Ho * g.Wwin * g.KH * cpad;  // elements
     const bool chunk_win =
         pad_c && win_pad <= kLimit && win_pad * (long long)pl->esize + pad_w_bytes + 512 < im2col_bytes;
+    // Window rows in LDS (igemm_rowwin.h): stride 1, dilation 1, three taps
+    // per kernel row, channel slices of whole K tiles, a 256-pixel tile
+    // spanning at most kRowWinMaxSeg output rows, 32-bit byte offsets.
+    const long long kBufMax = (1LL << 31) - 64;
+    const bool rowwin_ok = g.s == 1 && g.d == 1 && g.KW == 3 && g.C % (pl->e16 ? 32 : 16) == 0 &&
+                           255 / g.Wo + 2 <= kRowWinMaxSeg &&
+                           (long long)g.N * g.C * g.H * g.W * (long long)pl->esize <= kBufMax &&
+                           g.K * g.Co * (long long)pl->esize <= kBufMax;
     if (algo == CONV_ALGO_AUTO)
         algo = (whole || one) ? CONV_ALGO_GEMM
                : (!chunk_ind && chunk_win) ? CONV_ALGO_IM2WIN
@@ -189,6 +197,18 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
             } else {
                 pl->feed = FEED_WIN;
                 pl->need_wpack = !pl->nhwc && g.T > 1;  // OIHW regrouped to (kh, kw, ci) order
+            }
+            break;
+        case CONV_ALGO_IM2WIN_LDS:
+            if (!rowwin_ok || t_forced_main_loop != CONV_MAIN_LOOP_AUTO) return CONV_ERR_UNSUPPORTED;
+            pl->feed = FEED_ROWWIN;
+            if (pl->nhwc) {
+                // Reserved for the element-gather fallback on misaligned
+                // pointers; not built otherwise.
+                pl->need_ibuf = true;
+            } else {  // NCHW: the channels-last copy and OHWI weights
+                pl->need_xcl = true;
+                pl->need_wpack = true;
             }
             break;
         case CONV_ALGO_DIRECT:
@@ -277,6 +297,9 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     } else {
         pl->tile = TILE_128x128; BM = 128; BN = 128;
     }
+    if (pl->feed == FEED_ROWWIN) {
+        pl->tile = TILE_256x128_ROWWIN; BM = 256; BN = 128;
+    }
     // A forced variant (ablation) replaces the choice above when the feed
     // and shape allow it.
     const bool chunk_feed = pl->feed == FEED_IND_CHUNK || pl->feed == FEED_WIN_CHUNK;
@@ -328,8 +351,8 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     // Split K only where too few tiles leave most CUs idle: the two-wavefront
     // loops keep a CU busy with a single block, and the partials cost a pass
     // over M x Co fp32 values per split.
-    const bool two_wave = wide_slice(pl->tile);
-    if (blocks < (two_wave ? 64 : 256) && ktiles >= 16) {
+    const bool two_wave = wide_slice(pl->tile) || pl->tile == TILE_256x128_ROWWIN;
+    if (pl->feed != FEED_ROWWIN && blocks < (two_wave ? 64 : 256) && ktiles >= 16) {
         // Enough splits to give every compute unit work, each split at least
         // 4 K tiles, and the whole workspace (partials included) kept below
         // the im2col footprint.
@@ -464,6 +487,7 @@ conv_status_t launch_main(const Plan &pl, GemmArgs &a, hipStream_t s) {
         case FEED_WIN: a_vec = g.C % VEC == 0 && al16(a.a_src); break;
         case FEED_IND_CHUNK:
         case FEED_WIN_CHUNK: a_vec = al16(a.a_src) && wide_slice(pl.tile); break;
+        case FEED_ROWWIN: a_vec = al16(a.a_src); break;
         default: a_vec = false;
     }
     if (pl.force_element) a_vec = false;
@@ -558,12 +582,21 @@ conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias
     a.b = w;
     a.a_src = x;
 
+    if (pl.feed == FEED_ROWWIN && pl.nhwc && ((uintptr_t)x % 16 || (uintptr_t)w % 16)) {
+        // Operands the window-row loop cannot read in 16-byte chunks: the
+        // element-gather loop through the indirection buffer reserved in
+        // the workspace instead.
+        Plan fb = pl;
+        fb.feed = FEED_IND_NHWC;
+        fb.tile = TILE_128x128;
+        return run(fb, x, w, bias, y, prebuilt, stream, workspace, workspace_bytes);
+    }
     // Offsets of the indirection buffer follow the layout the main loop reads.
     const bool ib_rows = pl.feed == FEED_IND_NHWC;
     int32_t *ib_build = nullptr;  // buffer still to build
     if (prebuilt) {
         a.ibuf = prebuilt;
-    } else if (pl.need_ibuf) {
+    } else if (pl.need_ibuf && pl.feed != FEED_ROWWIN) {
         ib_build = (int32_t *)(ws + pl.off_ibuf);
         a.ibuf = ib_build;
     }

@@ -22,8 +22,12 @@ enum Feed : int {
     // tile addressed on its own, tap q / (C/VEC); K = (kh, kw, ci)
     FEED_IND_CHUNK = 5,  // indirection buffer over the padded channels-last copy
     FEED_WIN_CHUNK = 6,  // window-ordered tensor with padded cells
+    FEED_ROWWIN = 7,     // channels-last input, each block's window rows staged in LDS (stride 1, dilation 1,
+                         // KW = 3); K = (ci slice, kh, kw)
 };
-constexpr int kNumFeeds = 7;
+constexpr int kNumFeeds = 8;
+// Output rows a 256-pixel tile of the LDS window-row loop may span.
+constexpr int kRowWinMaxSeg = 64;
 
 struct Geom {
     int N, C, H, W, Co, KH, KW, s, p, d;
@@ -62,7 +66,8 @@ enum Tile : int {
     TILE_256x128_OCT = 5,
     TILE_128x64_QUAD = 6,
     TILE_256x256_OCT = 7,
-    TILE_COUNT = 8
+    TILE_256x128_ROWWIN = 8,  // the LDS window-row loop of igemm_rowwin.h (FEED_ROWWIN only)
+    TILE_COUNT = 9
 };
 
 hipError_t launch_igemm_bf16(const GemmArgs &a, int feed, bool out_nchw, bool a_vec, bool b_vec,

@@ -66,6 +66,7 @@ struct DualCfg {
     static constexpr int WPM = BM / WGM, WCN = BN / WGN;  // wavefront tile
     static constexpr int MT = 32, TP = WPM / MT, TC = WCN / MT;
     static constexpr int NG = KCH / 2;  // MFMA K steps per tile (two chunks per step)
+    static constexpr long long STAGE_BYTES = 3LL * NSLOT * 16;  // the three stages, reused by the epilogue
 
     static_assert(IPW_A * NW * 64 == BM * KCH && IPW_B * NW * 64 == BN * KCH, "loads must split evenly");
     static_assert(TP >= 1 && TC >= 1 && WGM * WGN == NW, "wavefront grid");
@@ -103,6 +104,204 @@ __device__ __forceinline__ constexpr int dual_swz(int r) {
 template <int KCH>
 __device__ __forceinline__ constexpr int dual_slot(int r, int c) {
     return r * KCH + (c ^ dual_swz<KCH>(r));
+}
+
+// The epilogue shared by the main loops of this file: the block's fp32
+// accumulators (wavefront (wp, wc) of the block's WGM x WGN grid) leave as
+// split-K partials, or, bias added and rounded once, through the LDS stage
+// memory `stg` (C::STAGE_BYTES bytes, free once every wavefront has passed
+// the first barrier below) as whole rows of the output.
+template <typename S, bool OUT_NCHW, typename C>
+__device__ __forceinline__ void dual_store(const GemmArgs &A,
+                                           typename MfmaShape<S, 32>::acc_t (&acc)[C::TP][C::TC], uint4 *stg,
+                                           const float *bias_s, uint32_t m0, int co0, int wp, int wc, int lane,
+                                           int tid) {
+    constexpr int BM = C::BM, BN = C::BN, VEC = C::VEC, TP = C::TP, TC = C::TC, WPM = C::WPM, WCN = C::WCN;
+    constexpr int NTHR = C::NTHR;
+    using MF = MfmaShape<S, 32>;
+    constexpr int NQ = MF::NQ;
+    const Geom &g = A.g;
+    const int frow = lane & 31;
+    // ---- epilogue -------------------------------------------------------------
+    S *y = (S *)A.y;
+    if (A.part) {
+        // Split K: this split's fp32 sums go to its slice of the workspace;
+        // the reduce pass adds the bias and rounds.
+#pragma unroll
+        for (int ip = 0; ip < TP; ++ip)
+#pragma unroll
+            for (int ic = 0; ic < TC; ++ic)
+#pragma unroll
+                for (int q = 0; q < NQ; ++q)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int pr = wp * WPM + ip * 32, cr = wc * WCN + ic * 32;
+                        const int ml = OUT_NCHW ? pr + MF::qrow(q, lane) + v : pr + frow;
+                        const int cl = OUT_NCHW ? cr + frow : cr + MF::qrow(q, lane) + v;
+                        const long long m = (long long)m0 + ml;
+                        const int co = co0 + cl;
+                        if (m < g.M && co < g.Co)
+                            A.part[((long long)blockIdx.z * g.M + m) * g.Co + co] = acc[ip][ic][4 * q + v];
+                    }
+        return;
+    }
+    // The tile goes through LDS (the stage memory, free once every wavefront
+    // has passed the barrier below) so that it leaves as whole rows along the
+    // output's contiguous axis: [channel][pixel] for NCHW, [pixel][channel]
+    // for NHWC, each row padded by 16 bytes to spread the bank groups.  A
+    // tile larger than the stage memory (fp32 with 80 KB blocks) goes in two
+    // passes over halves of its rows.
+    constexpr int ROWS = OUT_NCHW ? BN : BM;  // output runs in the tile
+    constexpr int COLS = OUT_NCHW ? BM : BN;  // elements per run
+    constexpr int PADE = 16 / (int)sizeof(S);
+    constexpr int RSTR = COLS + PADE;  // LDS row stride, elements
+    constexpr long long TILE_BYTES = (long long)ROWS * RSTR * (int)sizeof(S);
+    constexpr int NPASS = TILE_BYTES <= C::STAGE_BYTES       ? 1
+                          : TILE_BYTES <= 2 * C::STAGE_BYTES ? 2
+                                                               : 4;
+    constexpr int PROWS = ROWS / NPASS;
+    constexpr int CPR = COLS / VEC;  // 16-byte chunks per run
+    static_assert((long long)PROWS * RSTR * (int)sizeof(S) <= C::STAGE_BYTES, "epilogue tile fits the stages");
+    static_assert(NTHR % CPR == 0, "each thread keeps one chunk column");
+    S *tile = (S *)stg;
+
+    // This thread's chunk column and, for NCHW, the output pixel it starts
+    // at (the same for every run it stores).
+    const int cc = tid % CPR;
+    int n0 = 0, p0 = 0;
+    bool fast = false;  // whole 16-byte chunk inside one image, aligned
+    int sub = 1;        // NCHW: widest piece (elements) that never crosses an image
+    if constexpr (OUT_NCHW) {
+        const uint32_t m = m0 + (uint32_t)(cc * VEC);  // M < 2^31
+        n0 = (int)(m / (uint32_t)g.P);
+        p0 = (int)(m - (uint32_t)n0 * (uint32_t)g.P);
+        if ((uintptr_t)y % 16 == 0) {
+            sub = VEC;
+            while (g.P % sub != 0) sub >>= 1;
+        }
+        fast = sub == VEC && (long long)m + VEC <= g.M;
+    } else {
+        fast = g.Co % VEC == 0 && co0 + cc * VEC + VEC <= g.Co && ((uintptr_t)y % 16) == 0;
+    }
+
+#pragma unroll
+    for (int pass = 0; pass < NPASS; ++pass) {
+        __syncthreads();  // stages (or the previous pass's rows) no longer read
+        const int r_lo = pass * PROWS;
+        // Accumulators -> LDS, bias added in fp32, rounded once.
+#pragma unroll
+        for (int ip = 0; ip < TP; ++ip)
+#pragma unroll
+            for (int ic = 0; ic < TC; ++ic)
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) {
+                    const int pr = wp * WPM + ip * 32, cr = wc * WCN + ic * 32;
+                    const float a0 = acc[ip][ic][4 * q], a1 = acc[ip][ic][4 * q + 1];
+                    const float a2 = acc[ip][ic][4 * q + 2], a3 = acc[ip][ic][4 * q + 3];
+                    if constexpr (OUT_NCHW) {
+                        const int row = cr + frow, col = pr + MF::qrow(q, lane);
+                        if (row < r_lo || row >= r_lo + PROWS) continue;
+                        const float b = bias_s[row];
+                        store4(tile + (row - r_lo) * RSTR + col, a0 + b, a1 + b, a2 + b, a3 + b);
+                    } else {
+                        const int row = pr + frow, col = cr + MF::qrow(q, lane);
+                        if (row < r_lo || row >= r_lo + PROWS) continue;
+                        store4(tile + (row - r_lo) * RSTR + col, a0 + bias_s[col], a1 + bias_s[col + 1],
+                               a2 + bias_s[col + 2], a3 + bias_s[col + 3]);
+                    }
+                }
+        __syncthreads();
+        // LDS -> global, one 16-byte chunk per thread per run.  Where every
+        // chunk of this thread is whole and aligned (the common case), all of
+        // its LDS reads are issued before its stores, so their latencies
+        // overlap; otherwise the general loop below.
+        constexpr int RSTEP = NTHR / CPR;  // runs per sweep of the block
+        constexpr int ITER = PROWS / RSTEP;
+        static_assert(PROWS % RSTEP == 0, "runs split evenly over the threads");
+        if (fast) {
+            uint4 vals[ITER];
+#pragma unroll
+            for (int i = 0; i < ITER; ++i)
+                vals[i] = *(const uint4 *)(tile + (tid / CPR + i * RSTEP) * RSTR + cc * VEC);
+#pragma unroll
+            for (int i = 0; i < ITER; ++i) {
+                const int row = r_lo + tid / CPR + i * RSTEP;
+                if constexpr (OUT_NCHW) {
+                    const int co = co0 + row;
+                    if (co < g.Co) *(uint4 *)(y + ((long long)n0 * g.Co + co) * g.P + p0) = vals[i];
+                } else {
+                    const long long m = (long long)m0 + row;
+                    if (m < g.M) *(uint4 *)(y + m * g.Co + co0 + cc * VEC) = vals[i];
+                }
+            }
+            continue;  // next pass
+        }
+        for (int r = tid / CPR; r < PROWS; r += NTHR / CPR) {
+            const int row = r_lo + r;
+            const uint4 val = *(const uint4 *)(tile + r * RSTR + cc * VEC);
+            if constexpr (OUT_NCHW) {
+                const int co = co0 + row;
+                if (co >= g.Co) continue;
+                if (fast) {
+                    *(uint4 *)(y + ((long long)n0 * g.Co + co) * g.P + p0) = val;
+                } else {
+                    // Pieces of `sub` elements: P and the chunk start are
+                    // multiples of sub, so no piece crosses an image and each
+                    // is aligned to its size.
+                    S e[VEC];
+                    __builtin_memcpy(e, &val, 16);
+                    const long long m = (long long)m0 + cc * VEC;
+                    auto pieces = [&](auto sub_c) {
+                        constexpr int SUB = decltype(sub_c)::value;
+                        int n = n0, p = p0;
+#pragma unroll
+                        for (int v = 0; v < VEC; v += SUB) {
+                            S *dst = y + ((long long)n * g.Co + co) * g.P + p;
+                            if constexpr (SUB * sizeof(S) == 8) {
+                                if (m + v + SUB <= g.M) {
+                                    *(uint2 *)dst = make_uint2(*(const uint32_t *)&e[v], *(const uint32_t *)&e[v + SUB / 2]);
+                                    goto next;
+                                }
+                            } else if constexpr (SUB * sizeof(S) == 4) {
+                                if (m + v + SUB <= g.M) {
+                                    *(uint32_t *)dst = *(const uint32_t *)&e[v];
+                                    goto next;
+                                }
+                            }
+#pragma unroll
+                            for (int u = 0; u < SUB; ++u)
+                                if (m + v + u < g.M) dst[u] = e[v + u];
+                        next:
+                            p += SUB;
+                            if (p == g.P) {
+                                p = 0;
+                                ++n;
+                            }
+                        }
+                    };
+                    if (sub == VEC / 2)
+                        pieces(std::integral_constant<int, VEC / 2>{});
+                    else if (sub == 2 && VEC >= 4)
+                        pieces(std::integral_constant<int, (VEC >= 4 ? 2 : 1)>{});
+                    else
+                        pieces(std::integral_constant<int, 1>{});
+                }
+            } else {
+                const long long m = (long long)m0 + row;
+                if (m >= g.M) continue;
+                const int co = co0 + cc * VEC;
+                if (fast) {
+                    *(uint4 *)(y + m * g.Co + co) = val;
+                } else {
+                    S e[VEC];
+                    __builtin_memcpy(e, &val, 16);
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v)
+                        if (co + v < g.Co) y[m * g.Co + co + v] = e[v];
+                }
+            }
+        }
+    }
 }
 
 template <typename S, int FEED, bool OUT_NCHW, typename C>
@@ -395,186 +594,7 @@ __device__ __forceinline__ void igemm_dual_body(const GemmArgs &A) {
         CONVLOWER_WAIT_VMCNT(0);  // no load may still write LDS when the block ends
     }
 
-    // ---- epilogue -------------------------------------------------------------
-    S *y = (S *)A.y;
-    if (A.part) {
-        // Split K: this split's fp32 sums go to its slice of the workspace;
-        // the reduce pass adds the bias and rounds.
-#pragma unroll
-        for (int ip = 0; ip < TP; ++ip)
-#pragma unroll
-            for (int ic = 0; ic < TC; ++ic)
-#pragma unroll
-                for (int q = 0; q < NQ; ++q)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const int pr = wp * WPM + ip * 32, cr = wc * WCN + ic * 32;
-                        const int ml = OUT_NCHW ? pr + MF::qrow(q, lane) + v : pr + frow;
-                        const int cl = OUT_NCHW ? cr + frow : cr + MF::qrow(q, lane) + v;
-                        const long long m = (long long)m0 + ml;
-                        const int co = co0 + cl;
-                        if (m < g.M && co < g.Co)
-                            A.part[((long long)blockIdx.z * g.M + m) * g.Co + co] = acc[ip][ic][4 * q + v];
-                    }
-        return;
-    }
-    // The tile goes through LDS (the stage memory, free once every wavefront
-    // has passed the barrier below) so that it leaves as whole rows along the
-    // output's contiguous axis: [channel][pixel] for NCHW, [pixel][channel]
-    // for NHWC, each row padded by 16 bytes to spread the bank groups.  A
-    // tile larger than the stage memory (fp32 with 80 KB blocks) goes in two
-    // passes over halves of its rows.
-    constexpr int ROWS = OUT_NCHW ? BN : BM;  // output runs in the tile
-    constexpr int COLS = OUT_NCHW ? BM : BN;  // elements per run
-    constexpr int PADE = 16 / (int)sizeof(S);
-    constexpr int RSTR = COLS + PADE;  // LDS row stride, elements
-    constexpr long long TILE_BYTES = (long long)ROWS * RSTR * (int)sizeof(S);
-    constexpr int NPASS = TILE_BYTES <= 3LL * NSLOT * 16       ? 1
-                          : TILE_BYTES <= 2 * 3LL * NSLOT * 16 ? 2
-                                                               : 4;
-    constexpr int PROWS = ROWS / NPASS;
-    constexpr int CPR = COLS / VEC;  // 16-byte chunks per run
-    static_assert((long long)PROWS * RSTR * (int)sizeof(S) <= 3LL * NSLOT * 16, "epilogue tile fits the stages");
-    static_assert(NTHR % CPR == 0, "each thread keeps one chunk column");
-    S *tile = (S *)&stg[0][0];
-
-    // This thread's chunk column and, for NCHW, the output pixel it starts
-    // at (the same for every run it stores).
-    const int cc = tid % CPR;
-    int n0 = 0, p0 = 0;
-    bool fast = false;  // whole 16-byte chunk inside one image, aligned
-    int sub = 1;        // NCHW: widest piece (elements) that never crosses an image
-    if constexpr (OUT_NCHW) {
-        const uint32_t m = m0 + (uint32_t)(cc * VEC);  // M < 2^31
-        n0 = (int)(m / (uint32_t)g.P);
-        p0 = (int)(m - (uint32_t)n0 * (uint32_t)g.P);
-        if ((uintptr_t)y % 16 == 0) {
-            sub = VEC;
-            while (g.P % sub != 0) sub >>= 1;
-        }
-        fast = sub == VEC && (long long)m + VEC <= g.M;
-    } else {
-        fast = g.Co % VEC == 0 && co0 + cc * VEC + VEC <= g.Co && ((uintptr_t)y % 16) == 0;
-    }
-
-#pragma unroll
-    for (int pass = 0; pass < NPASS; ++pass) {
-        __syncthreads();  // stages (or the previous pass's rows) no longer read
-        const int r_lo = pass * PROWS;
-        // Accumulators -> LDS, bias added in fp32, rounded once.
-#pragma unroll
-        for (int ip = 0; ip < TP; ++ip)
-#pragma unroll
-            for (int ic = 0; ic < TC; ++ic)
-#pragma unroll
-                for (int q = 0; q < NQ; ++q) {
-                    const int pr = wp * WPM + ip * 32, cr = wc * WCN + ic * 32;
-                    const float a0 = acc[ip][ic][4 * q], a1 = acc[ip][ic][4 * q + 1];
-                    const float a2 = acc[ip][ic][4 * q + 2], a3 = acc[ip][ic][4 * q + 3];
-                    if constexpr (OUT_NCHW) {
-                        const int row = cr + frow, col = pr + MF::qrow(q, lane);
-                        if (row < r_lo || row >= r_lo + PROWS) continue;
-                        const float b = bias_s[row];
-                        store4(tile + (row - r_lo) * RSTR + col, a0 + b, a1 + b, a2 + b, a3 + b);
-                    } else {
-                        const int row = pr + frow, col = cr + MF::qrow(q, lane);
-                        if (row < r_lo || row >= r_lo + PROWS) continue;
-                        store4(tile + (row - r_lo) * RSTR + col, a0 + bias_s[col], a1 + bias_s[col + 1],
-                               a2 + bias_s[col + 2], a3 + bias_s[col + 3]);
-                    }
-                }
-        __syncthreads();
-        // LDS -> global, one 16-byte chunk per thread per run.  Where every
-        // chunk of this thread is whole and aligned (the common case), all of
-        // its LDS reads are issued before its stores, so their latencies
-        // overlap; otherwise the general loop below.
-        constexpr int RSTEP = NTHR / CPR;  // runs per sweep of the block
-        constexpr int ITER = PROWS / RSTEP;
-        static_assert(PROWS % RSTEP == 0, "runs split evenly over the threads");
-        if (fast) {
-            uint4 vals[ITER];
-#pragma unroll
-            for (int i = 0; i < ITER; ++i)
-                vals[i] = *(const uint4 *)(tile + (tid / CPR + i * RSTEP) * RSTR + cc * VEC);
-#pragma unroll
-            for (int i = 0; i < ITER; ++i) {
-                const int row = r_lo + tid / CPR + i * RSTEP;
-                if constexpr (OUT_NCHW) {
-                    const int co = co0 + row;
-                    if (co < g.Co) *(uint4 *)(y + ((long long)n0 * g.Co + co) * g.P + p0) = vals[i];
-                } else {
-                    const long long m = (long long)m0 + row;
-                    if (m < g.M) *(uint4 *)(y + m * g.Co + co0 + cc * VEC) = vals[i];
-                }
-            }
-            continue;  // next pass
-        }
-        for (int r = tid / CPR; r < PROWS; r += NTHR / CPR) {
-            const int row = r_lo + r;
-            const uint4 val = *(const uint4 *)(tile + r * RSTR + cc * VEC);
-            if constexpr (OUT_NCHW) {
-                const int co = co0 + row;
-                if (co >= g.Co) continue;
-                if (fast) {
-                    *(uint4 *)(y + ((long long)n0 * g.Co + co) * g.P + p0) = val;
-                } else {
-                    // Pieces of `sub` elements: P and the chunk start are
-                    // multiples of sub, so no piece crosses an image and each
-                    // is aligned to its size.
-                    S e[VEC];
-                    __builtin_memcpy(e, &val, 16);
-                    const long long m = (long long)m0 + cc * VEC;
-                    auto pieces = [&](auto sub_c) {
-                        constexpr int SUB = decltype(sub_c)::value;
-                        int n = n0, p = p0;
-#pragma unroll
-                        for (int v = 0; v < VEC; v += SUB) {
-                            S *dst = y + ((long long)n * g.Co + co) * g.P + p;
-                            if constexpr (SUB * sizeof(S) == 8) {
-                                if (m + v + SUB <= g.M) {
-                                    *(uint2 *)dst = make_uint2(*(const uint32_t *)&e[v], *(const uint32_t *)&e[v + SUB / 2]);
-                                    goto next;
-                                }
-                            } else if constexpr (SUB * sizeof(S) == 4) {
-                                if (m + v + SUB <= g.M) {
-                                    *(uint32_t *)dst = *(const uint32_t *)&e[v];
-                                    goto next;
-                                }
-                            }
-#pragma unroll
-                            for (int u = 0; u < SUB; ++u)
-                                if (m + v + u < g.M) dst[u] = e[v + u];
-                        next:
-                            p += SUB;
-                            if (p == g.P) {
-                                p = 0;
-                                ++n;
-                            }
-                        }
-                    };
-                    if (sub == VEC / 2)
-                        pieces(std::integral_constant<int, VEC / 2>{});
-                    else if (sub == 2 && VEC >= 4)
-                        pieces(std::integral_constant<int, (VEC >= 4 ? 2 : 1)>{});
-                    else
-                        pieces(std::integral_constant<int, 1>{});
-                }
-            } else {
-                const long long m = (long long)m0 + row;
-                if (m >= g.M) continue;
-                const int co = co0 + cc * VEC;
-                if (fast) {
-                    *(uint4 *)(y + m * g.Co + co) = val;
-                } else {
-                    S e[VEC];
-                    __builtin_memcpy(e, &val, 16);
-#pragma unroll
-                    for (int v = 0; v < VEC; ++v)
-                        if (co + v < g.Co) y[m * g.Co + co + v] = e[v];
-                }
-            }
-        }
-    }
+    dual_store<S, OUT_NCHW, C>(A, acc, &stg[0][0], bias_s, m0, co0, wp, wc, lane, tid);
 }
 
 template <typename S, int FEED, bool OUT_NCHW>

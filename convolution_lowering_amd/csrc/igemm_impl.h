@@ -580,6 +580,7 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(GemmArgs A) {
 
 #include "igemm_dma.h"
 #include "igemm_dual.h"
+#include "igemm_rowwin.h"
 
 namespace convlower {
 
@@ -597,7 +598,12 @@ static hipError_t launch_tile(const GemmArgs &a, int tile, int splits, hipStream
         return hipGetLastError();
     };
     constexpr int BKW = sizeof(S) == 2 ? 64 : 32;  // 128-byte LDS rows
-    if constexpr (AVEC && (FEED == FEED_IND_CHUNK || FEED == FEED_WIN_CHUNK)) {  // one tap per chunk: the two-wavefront loops only
+    if constexpr (FEED == FEED_ROWWIN) {  // its own loop only, 16-byte rows only
+        if constexpr (AVEC) {
+            if (tile == TILE_256x128_ROWWIN) return go(igemm_rowwin_kernel<S, OUT_NCHW>, 256, 128, 512);
+        }
+        return hipErrorInvalidValue;
+    } else if constexpr (AVEC && (FEED == FEED_IND_CHUNK || FEED == FEED_WIN_CHUNK)) {  // one tap per chunk: the two-wavefront loops only
         switch (tile) {
             case TILE_256x128_DUAL: return go(igemm_dual_kernel<S, FEED, OUT_NCHW>, 256, 128);
             case TILE_256x128_OCT: return go(igemm_oct_kernel<S, FEED, OUT_NCHW>, 256, 128, 512);
@@ -632,10 +638,10 @@ template <typename S, int FEED>
 hipError_t launch_feed(const GemmArgs &a, bool out_nchw, bool a_vec, bool b_vec, int tile, int splits,
                        hipStream_t st) {
     constexpr bool CAN_AVEC = FEED == FEED_ROWMAJOR || FEED == FEED_IND_NHWC || FEED == FEED_WIN ||
-                              FEED == FEED_IND_CHUNK || FEED == FEED_WIN_CHUNK;
+                              FEED == FEED_IND_CHUNK || FEED == FEED_WIN_CHUNK || FEED == FEED_ROWWIN;
     constexpr bool CAN_NCHW = true;  // every feed can write NCHW output
     constexpr bool CAN_NHWC = FEED == FEED_ROWMAJOR || FEED == FEED_IND_NHWC || FEED == FEED_WIN ||
-                              FEED == FEED_IND_CHUNK || FEED == FEED_WIN_CHUNK;
+                              FEED == FEED_IND_CHUNK || FEED == FEED_WIN_CHUNK || FEED == FEED_ROWWIN;
     if (a_vec && !b_vec) return hipErrorInvalidValue;
     if (out_nchw) {
         if constexpr (CAN_NCHW) {

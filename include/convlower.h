@@ -82,14 +82,24 @@ typedef enum { CONV_DTYPE_FP32 = 0, CONV_DTYPE_BF16 = 1, CONV_DTYPE_FP16 = 2 } c
  *             ALUs, one thread per output pixel and 8 output channels, fp32
  *             accumulation; no lowering, no workspace, no matrix core
  *             ("Im2win: An Efficient Convolution Paradigm on GPU", abstract,
- *             compares against such a kernel).  Never chosen by AUTO.  */
+ *             compares against such a kernel).  Never chosen by AUTO.
+ *   IM2WIN_LDS  the window-ordered layout built in LDS, never in memory:
+ *             each block stages, per channel slice and kernel row, the runs
+ *             of input pixels its output rows' windows cover, and the KW taps
+ *             of that kernel row read their MFMA operands from the one run.
+ *             Stride 1, dilation 1, KW = 3, C_in a multiple of 32 (16-bit
+ *             types) or 16 (fp32) only, else CONV_ERR_UNSUPPORTED.  Workspace:
+ *             for NCHW the channels-last copy of x and OHWI weights; for
+ *             NHWC a spare indirection buffer, used only when x or w is not
+ *             16-byte aligned (then the call runs the element-gather loop).  */
 typedef enum {
     CONV_ALGO_AUTO = 0,
     CONV_ALGO_INDIRECT = 1,
     CONV_ALGO_IM2WIN = 2,
     CONV_ALGO_GEMM = 3,
     CONV_ALGO_IM2COL = 4,
-    CONV_ALGO_DIRECT = 5
+    CONV_ALGO_DIRECT = 5,
+    CONV_ALGO_IM2WIN_LDS = 6
 } conv_algo_t;
 
 typedef enum {

@@ -178,6 +178,34 @@ def test_forced_main_loop_checks_on_the_host():
     assert cl.workspace_size(24, 24, 13, 15, 130, 3, 3, 1, 1, 1, "NHWC", "bf16", "indirect") == odd
 
 
+def _rowwin_eligible(L, dtype):
+    Ho, Wo = cl.output_size(L.H, L.W, L.KH, L.KW, L.stride, L.pad, L.dilation)
+    return (L.stride == 1 and L.dilation == 1 and L.KW == 3 and L.C % (16 if dtype == "fp32" else 32) == 0
+            and 255 // Wo + 2 <= 64)
+
+
+@pytest.mark.parametrize("name", sorted(LAYERS))
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp16"])
+def test_window_rows_in_lds_eligibility_and_workspace(name, dtype):
+    """IM2WIN_LDS serves stride-1, dilation-1, three-tap-wide kernels over
+    whole channel slices and refuses the rest on the host.  Its workspace is
+    the channels-last copy plus OHWI weights for NCHW, and only a spare
+    indirection buffer for NHWC."""
+    L = LAYERS[name]
+    es = 4 if dtype == "fp32" else 2
+    up = lambda v: (v + 255) // 256 * 256
+    if not _rowwin_eligible(L, dtype):
+        for layout in ("NCHW", "NHWC"):
+            with pytest.raises(cl.ConvLowerError) as e:
+                cl.workspace_size(*_args(L, layout, dtype, "im2win_lds"))
+            assert e.value.code == UNSUPPORTED
+        return
+    Ho, Wo = cl.output_size(L.H, L.W, L.KH, L.KW, L.stride, L.pad, L.dilation)
+    assert cl.workspace_size(*_args(L, "NHWC", dtype, "im2win_lds")) == up(Ho * Wo * L.KH * L.KW * 4)
+    want = up(L.N * L.C * L.H * L.W * es) + up(L.Co * L.C * L.KH * L.KW * es)
+    assert cl.workspace_size(*_args(L, "NCHW", dtype, "im2win_lds")) == want
+
+
 def test_gemm_algo_rejected_on_windowed_layer():
     L = LAYERS["C2"]
     with pytest.raises(cl.ConvLowerError) as e:
@@ -211,7 +239,7 @@ def test_invalid_enums_and_null_outputs():
     assert L.conv2d_fwd_workspace_size(*base, 2, 1, 0, ctypes.byref(out)) == INVALID   # layout
     assert L.conv2d_fwd_workspace_size(*base, 0, 7, 0, ctypes.byref(out)) == INVALID   # dtype
     assert L.conv2d_fwd_workspace_size(*base, 0, 1, 9, ctypes.byref(out)) == INVALID   # algo
-    assert L.conv2d_fwd_workspace_size(*base, 0, 1, 6, ctypes.byref(out)) == INVALID   # one past DIRECT
+    assert L.conv2d_fwd_workspace_size(*base, 0, 1, 7, ctypes.byref(out)) == INVALID   # one past IM2WIN_LDS
     assert L.conv2d_fwd_workspace_size(*base, 0, 1, -1, ctypes.byref(out)) == INVALID
     assert L.conv2d_fwd_workspace_size(*base, 0, 1, 0, None) == INVALID
 

@@ -71,6 +71,13 @@ SMALL_N = {"C1": 2, "C2": 2, "C3a": 1, "C3b": 2, "C3c": 2, "C3d": 2, "C3e": 2, "
            "C4c": 1, "C4d": 1, "C4e": 2, "C5a": 2, "C5b": 2, "C5c": 16}
 
 
+def _rowwin_eligible(L, dtype):
+    """The shapes CONV_ALGO_IM2WIN_LDS serves (the header's rule)."""
+    Wo = oracle.out_size(L.W, L.KW, L.stride, L.pad, L.dilation)
+    return (L.stride == 1 and L.dilation == 1 and L.KW == 3 and L.C % (16 if dtype == "fp32" else 32) == 0
+            and 255 // Wo + 2 <= 64)
+
+
 def _cases():
     out = []
     for name, L in LAYERS.items():
@@ -79,7 +86,7 @@ def _cases():
         for dtype in sorted(set(L.dtypes) | {"fp32", "bf16", "fp16"} if name in ("C1", "C2", "C5a", "C5b", "C5c")
                             else L.dtypes):
             for layout in ("NCHW", "NHWC"):
-                for algo in algos:
+                for algo in algos + (["im2win_lds"] if _rowwin_eligible(L, dtype) else []):
                     out.append((name, dtype, layout, algo))
     return out
 
@@ -246,17 +253,24 @@ EDGE = [
     ("C-37-3x3", 2, 37, 13, 11, 70, 3, 3, 1, 1, 1),
     ("C-9-3x3", 2, 9, 17, 15, 33, 3, 3, 1, 1, 1),
     ("C-20-5x5-dilated", 3, 20, 23, 19, 50, 5, 5, 2, 4, 2),
+    # window rows in LDS: tiles crossing output rows and images, narrow
+    # outputs (many segments per tile), ragged channels, unpadded kernels
+    ("rowwin-narrow", 3, 32, 9, 5, 70, 3, 3, 1, 1, 1),
+    ("rowwin-unpadded", 2, 64, 15, 17, 130, 3, 3, 1, 0, 1),
+    ("rowwin-tall-kernel", 2, 32, 12, 11, 40, 5, 3, 1, 2, 1),
 ]
 
 
 @pytest.mark.parametrize("case", EDGE, ids=[e[0] for e in EDGE])
 @pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp16"])
 @pytest.mark.parametrize("layout", ["NCHW", "NHWC"])
-@pytest.mark.parametrize("algo", ["auto", "indirect", "im2win", "im2col", "direct"])
+@pytest.mark.parametrize("algo", ["auto", "indirect", "im2win", "im2col", "direct", "im2win_lds"])
 def test_edge_cases(case, dtype, layout, algo):
     from convolution_lowering_amd.workloads import Layer
     name, N, C, H, W, Co, KH, KW, s, p, d = case
     L = Layer(name, N, C, H, W, Co, KH, KW, s, p, d, seed=77)
+    if algo == "im2win_lds" and not _rowwin_eligible(L, dtype):
+        pytest.skip("shape outside the window-rows-in-LDS loop (refused on the host; CPU-tested)")
     y = _run(L, dtype, layout, algo, N)
     x, w, b = make_inputs(L, dtype, "NCHW")
     y_ref, dn = oracle.conv2d(x, w, b, s, p, d, oracle.NCHW)
