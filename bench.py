@@ -246,7 +246,8 @@ def main():
     nbytes = algorithmic_bytes(H, Ho, Wo, head_dtype)
     rl = roofline(flops, nbytes, ml_ms / 1e3, head_dtype)
     rl["traffic"] = measured_traffic("C2-bf16-NCHW-main-loop")
-    rl["kernel"] = "igemm_dual_kernel (MFMA implicit-GEMM main loop + fused bias epilogue, indirection feed)"
+    rl["kernel"] = ("igemm_rowwin_kernel (MFMA implicit-GEMM main loop over window rows staged in LDS + fused "
+                    "bias epilogue)")
     rl["ms"] = ml_ms
     rl["timing"] = ("mean of the kernel's own start/end stamps (hipExtLaunchKernel events) over a second "
                     "timed pass of the headline steps")

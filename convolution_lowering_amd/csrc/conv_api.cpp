@@ -139,10 +139,16 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
                            255 / g.Wo + 2 <= kRowWinMaxSeg &&
                            (long long)g.N * g.C * g.H * g.W * (long long)pl->esize <= kBufMax &&
                            g.K * g.Co * (long long)pl->esize <= kBufMax;
+    // AUTO takes the window rows in LDS where they apply, the output has more
+    // channels than the loop's 64-wide half tile wastes, and the grid gives
+    // every CU a block without splitting K.
+    const bool rowwin_auto = rowwin_ok && g.Co > 64 && t_forced_main_loop == CONV_MAIN_LOOP_AUTO &&
+                             ((g.M + 255) / 256) * ((g.Co + 127) / 128) >= 256;
     if (algo == CONV_ALGO_AUTO)
         algo = (whole || one) ? CONV_ALGO_GEMM
                : (!chunk_ind && chunk_win) ? CONV_ALGO_IM2WIN
-                                        : CONV_ALGO_INDIRECT;
+               : rowwin_auto             ? CONV_ALGO_IM2WIN_LDS
+                                         : CONV_ALGO_INDIRECT;
     switch (algo) {
         case CONV_ALGO_GEMM:
             if (whole) {

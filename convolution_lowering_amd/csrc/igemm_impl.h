@@ -600,7 +600,7 @@ static hipError_t launch_tile(const GemmArgs &a, int tile, int splits, hipStream
     constexpr int BKW = sizeof(S) == 2 ? 64 : 32;  // 128-byte LDS rows
     if constexpr (FEED == FEED_ROWWIN) {  // its own loop only, 16-byte rows only
         if constexpr (AVEC) {
-            if (tile == TILE_256x128_ROWWIN) return go(igemm_rowwin_kernel<S, OUT_NCHW>, 256, 128, 512);
+            if (tile == TILE_256x128_ROWWIN) return go(igemm_rowwin_kernel<S, OUT_NCHW>, 256, 128, 256);
         }
         return hipErrorInvalidValue;
     } else if constexpr (AVEC && (FEED == FEED_IND_CHUNK || FEED == FEED_WIN_CHUNK)) {  // one tap per chunk: the two-wavefront loops only

@@ -9,9 +9,13 @@
 // row offsets 0 .. KW-1.  Each input pixel crosses from L2 into LDS once per
 // (slice, kh), not KW times.
 //
-// Pipeline, swizzle and epilogue are those of igemm_dual.h; one 512-thread
-// block per compute unit (eight wavefronts of 64 x 64 in a 4 x 2 grid, two
-// on every SIMD); block tile 256 x 128; channels-last input, OHWI weights.
+// Two 256-thread blocks per compute unit (four wavefronts of 128 x 64 each,
+// two wavefronts on every SIMD), so one block's barriers and epilogue hide
+// behind the other's MFMAs; block tile 256 x 128; channels-last input, OHWI
+// weights.  The A runs of a step and the B rows of a tap pipeline
+// separately: two A stages (the next step's runs load during a whole step)
+// and three B stages (each tap's weights load two taps ahead).  Swizzle and
+// epilogue are those of igemm_dual.h.
 #pragma once
 
 namespace convlower {
@@ -26,35 +30,37 @@ struct RowWinCfg {
     static constexpr int ES = (int)sizeof(S);
     static constexpr int VEC = 16 / ES;
     static constexpr int KCH = 4;                    // 16-byte chunks per stage row (one channel slice)
-    static constexpr int NW = 8, NTHR = 512;
+    static constexpr int NW = 4, NTHR = 256;
     static constexpr int RPI = 64 / KCH;             // stage rows one 64-lane load fills
     static constexpr int BK = KCH * VEC;             // channels per slice
-    static constexpr int ROWS_A = BM + (KW - 1) * kRowWinMaxSeg;  // input-pixel runs
-    static constexpr int ROWS_B = KW * BN;           // the KW taps' weights
-    static constexpr int NSLOT = (ROWS_A + ROWS_B) * KCH;
+    static constexpr int ROWS_A = BM + (KW - 1) * kRowWinMaxSeg;  // input-pixel runs of a step
+    static constexpr int A_SLOTS = ROWS_A * KCH, B_SLOTS = BN * KCH;
+    static constexpr int NA = 2, NB = 3;             // A and B stages
     static constexpr int IPW_A = ROWS_A * KCH / 64 / NW;
-    static constexpr int IPW_B = ROWS_B * KCH / 64 / NW;
-    static constexpr int IPW = IPW_A + IPW_B;
-    static constexpr int WGM = 4, WGN = 2;
-    static constexpr int WPM = BM / WGM, WCN = BN / WGN;  // wavefront tile 64 x 64
+    static constexpr int IPW_B = BN * KCH / 64 / NW;
+    static constexpr int WGM = 2, WGN = 2;
+    static constexpr int WPM = BM / WGM, WCN = BN / WGN;  // wavefront tile 128 x 64
     static constexpr int MT = 32, TP = WPM / MT, TC = WCN / MT;
     static constexpr int NG = KCH / 2;
-    static constexpr long long STAGE_BYTES = 3LL * NSLOT * 16;
-    static_assert(IPW_A * NW * 64 == ROWS_A * KCH && IPW_B * NW * 64 == ROWS_B * KCH, "loads must split evenly");
-    static_assert(STAGE_BYTES + BN * 4 <= 160 * 1024, "one block per compute unit");
+    static constexpr int LDS_SLOTS = NA * A_SLOTS + NB * B_SLOTS;
+    static constexpr long long STAGE_BYTES = 16LL * LDS_SLOTS;  // all stages, reused by the epilogue
+    static_assert(IPW_A * NW * 64 == ROWS_A * KCH && IPW_B * NW * 64 == BN * KCH, "loads must split evenly");
+    static_assert(2 * (STAGE_BYTES + BN * 4) <= 160 * 1024, "two blocks per compute unit");
 };
 
 template <typename S, bool OUT_NCHW, typename C>
 __device__ __forceinline__ void igemm_rowwin_body(const GemmArgs &A) {
-    constexpr int BM = C::BM, BN = C::BN, BK = C::BK, VEC = C::VEC, KCH = C::KCH, NSLOT = C::NSLOT;
-    constexpr int IPW_A = C::IPW_A, IPW_B = C::IPW_B, IPW = C::IPW;
+    constexpr int BM = C::BM, BN = C::BN, BK = C::BK, VEC = C::VEC, KCH = C::KCH;
+    constexpr int IPW_A = C::IPW_A, IPW_B = C::IPW_B;
     constexpr int WPM = C::WPM, WCN = C::WCN, TP = C::TP, TC = C::TC, NG = C::NG;
-    constexpr int NW = C::NW, RPI = C::RPI, KW = C::KW, ROWS_A = C::ROWS_A;
+    constexpr int NW = C::NW, RPI = C::RPI, KW = C::KW, A_SLOTS = C::A_SLOTS, B_SLOTS = C::B_SLOTS;
     constexpr uint32_t ES = (uint32_t)sizeof(S);
     using MF = MfmaShape<S, 32>;
+    static_assert(KW == 3, "the schedule below is written for three taps per kernel row");
 
-    __shared__ uint4 stg[3][NSLOT];  // the three stages; the epilogue reuses them
-    uint4 *const st0 = stg[0], *const st1 = stg[1], *const st2 = stg[2];
+    __shared__ uint4 lds[C::LDS_SLOTS];  // A stages, then B stages; the epilogue reuses them
+    uint4 *const sa0 = lds, *const sa1 = lds + A_SLOTS;
+    uint4 *const sb0 = lds + 2 * A_SLOTS, *const sb1 = sb0 + B_SLOTS, *const sb2 = sb1 + B_SLOTS;
     __shared__ float bias_s[BN];
 
     const Geom &g = A.g;
@@ -99,11 +105,11 @@ __device__ __forceinline__ void igemm_rowwin_body(const GemmArgs &A) {
 #pragma unroll
     for (int i = 0; i < IPW_A; ++i) {
         const uint32_t r = (uint32_t)((i * NW + wave) * RPI + lrow);
-        uint32_t start = 0, j = 0;
+        uint32_t start = 0;
         aok[i] = false;
         abase[i] = 0;
         ahi[i] = 0;
-        for (; j < (uint32_t)kRowWinMaxSeg; ++j) {
+        for (uint32_t j = 0; j < (uint32_t)kRowWinMaxSeg; ++j) {
             const uint32_t R = R0 + j;
             const uint32_t first = max(m0, R * Wo);
             if (first >= mend) break;
@@ -125,24 +131,24 @@ __device__ __forceinline__ void igemm_rowwin_body(const GemmArgs &A) {
     bool wok[IPW_B];
 #pragma unroll
     for (int j = 0; j < IPW_B; ++j) {
-        const int rb = (j * NW + wave) * RPI + lrow;  // tap rb / BN, channel co0 + rb % BN
-        const int kw = rb / BN, co = co0 + rb % BN;
+        const int co = co0 + (j * NW + wave) * RPI + lrow;
         wok[j] = co < g.Co;
-        wbase[j] = (co * g.KH * KW + kw) * g.C;  // OHWI, kernel row 0
+        wbase[j] = co * g.KH * KW * g.C;  // OHWI, tap (0, 0)
     }
 
     const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(A.a_src, A.a_bytes);
     const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(A.b, A.b_bytes);
     const uint32_t lds_w = (uint32_t)wave * 1024u;
 
-    // Issue the loads of K step kt into stage st (steps past the end load
-    // nothing but keep the count of loads in flight the same).
-    auto issue = [&](int kt, uint4 *st) {
+    // The A runs of K step kt into stage sa, and the B rows of tap u (step
+    // u / KW, kw = u % KW) into stage sb.  Past the end nothing is loaded,
+    // but the loads are still issued so the count in flight stays fixed.
+    auto issue_a = [&](int kt, uint4 *sa) {
         const bool live = kt < nk;
         const int slice = kt / g.KH, kh = kt - slice * g.KH;
         const int cofs = slice * BK + (int)kc;
-        const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr_t)st + lds_w;
-        uint32_t voff[IPW];
+        const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr_t)sa + lds_w;
+        uint32_t voff[IPW_A];
 #pragma unroll
         for (int i = 0; i < IPW_A; ++i) {
             const int hi = ahi[i] + kh;
@@ -150,13 +156,19 @@ __device__ __forceinline__ void igemm_rowwin_body(const GemmArgs &A) {
             voff[i] = valid ? (uint32_t)(abase[i] + kh * WC + cofs) * ES : kOutOfRange;
         }
 #pragma unroll
-        for (int j = 0; j < IPW_B; ++j)
-            voff[IPW_A + j] = live && wok[j] ? (uint32_t)(wbase[j] + kh * KW * g.C + cofs) * ES : kOutOfRange;
-#pragma unroll
         for (int i = 0; i < IPW_A; ++i) lds_dma16(a_rsrc, voff[i], lds0 + (uint32_t)(i * NW * 1024));
+    };
+    auto issue_b = [&](int u, uint4 *sb) {
+        const int kt = u / KW, kw = u - kt * KW;
+        const bool live = kt < nk;
+        const int slice = kt / g.KH, kh = kt - slice * g.KH;
+        const int wofs = (kh * KW + kw) * g.C + slice * BK + (int)kc;
+        const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr_t)sb + lds_w;
+        uint32_t voff[IPW_B];
 #pragma unroll
-        for (int j = 0; j < IPW_B; ++j)
-            lds_dma16(b_rsrc, voff[IPW_A + j], lds0 + (uint32_t)(ROWS_A * KCH * 16 + j * NW * 1024));
+        for (int j = 0; j < IPW_B; ++j) voff[j] = live && wok[j] ? (uint32_t)(wbase[j] + wofs) * ES : kOutOfRange;
+#pragma unroll
+        for (int j = 0; j < IPW_B; ++j) lds_dma16(b_rsrc, voff[j], lds0 + (uint32_t)(j * NW * 1024));
     };
 
     typename MF::acc_t acc[TP][TC];
@@ -176,12 +188,11 @@ __device__ __forceinline__ void igemm_rowwin_body(const GemmArgs &A) {
         arow[ip] = (int)pl + (KW - 1) * (int)((m0 + pl) / Wo - R0);
     }
     uint4 fa[NG][TP], fb[NG][TC];
-    auto lds_read = [&](const uint4 *st, int kw, int grp) {
+    auto lds_read = [&](const uint4 *sa, const uint4 *sb, int kw, int grp) {
 #pragma unroll
-        for (int ip = 0; ip < TP; ++ip) fa[grp][ip] = st[dual_slot<KCH>(arow[ip] + kw, grp * 2 + fch)];
+        for (int ip = 0; ip < TP; ++ip) fa[grp][ip] = sa[dual_slot<KCH>(arow[ip] + kw, grp * 2 + fch)];
 #pragma unroll
-        for (int ic = 0; ic < TC; ++ic)
-            fb[grp][ic] = st[ROWS_A * KCH + dual_slot<KCH>(kw * BN + wc * WCN + ic * 32 + frow, grp * 2 + fch)];
+        for (int ic = 0; ic < TC; ++ic) fb[grp][ic] = sb[dual_slot<KCH>(wc * WCN + ic * 32 + frow, grp * 2 + fch)];
     };
     auto mfma_group = [&](int grp) {
 #pragma unroll
@@ -194,36 +205,36 @@ __device__ __forceinline__ void igemm_rowwin_body(const GemmArgs &A) {
                     MF::mma(fb[grp][ic], fa[grp][ip], acc[ip][ic]);
             }
     };
-    // Step kt: the fragments of its tap 0 are in registers.  Taps 0 .. KW-2
-    // are multiplied while the next tap's fragments are read from st_cur;
-    // then (all reads of st_cur done) the barrier, st_cur receives step
-    // kt+3, and the last tap is multiplied while step kt+1's tap-0 fragments
-    // are read from st_next.
-    auto phase = [&](int kt, uint4 *st_cur, const uint4 *st_next) {
-#pragma unroll
-        for (int kw = 0; kw + 1 < KW; ++kw) {
-#pragma unroll
-            for (int grp = 0; grp < NG; ++grp) {
-                mfma_group(grp);
-                __builtin_amdgcn_sched_barrier(0);
-                lds_read(st_cur, kw + 1, grp);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
+    // Tap u = (kt, kw): its fragments are in registers.  After its first MFMA
+    // group: wait until tap u+1's weights (and, before the last tap of a
+    // step, step kt+1's runs) have landed and this wavefront's LDS reads are
+    // done, barrier, refill the B stage tap u used with tap u+3's weights
+    // (and, at kw = 0, the other A stage with step kt+1's runs), then read
+    // tap u+1's fragments group by group behind the remaining MFMAs.  Loads
+    // complete in issue order, so each wait allows exactly the loads issued
+    // after the ones it needs: tap u+2's weights (kw = 0 and 2), or tap
+    // u+2's weights and step kt+1's runs (kw = 1; both issued at kw = 0).
+    auto sub = [&](int kt, int kw, uint4 *sa, uint4 *sa_next, uint4 *sb, const uint4 *sb_next) {
         mfma_group(0);
         __builtin_amdgcn_sched_barrier(0);
-        CONVLOWER_WAIT_VMCNT_LDS(IPW);
+        if (kw == 1)
+            CONVLOWER_WAIT_VMCNT_LDS(IPW_A + IPW_B);
+        else
+            CONVLOWER_WAIT_VMCNT_LDS(IPW_B);
         block_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        issue(kt + 3, st_cur);
+        issue_b(kt * KW + kw + 3, sb);
+        if (kw == 0) issue_a(kt + 1, sa_next);
         __builtin_amdgcn_sched_barrier(0);
-        lds_read(st_next, 0, 0);
+        const uint4 *ra = kw + 1 < KW ? sa : sa_next;
+        const int rkw = kw + 1 < KW ? kw + 1 : 0;
+        lds_read(ra, sb_next, rkw, 0);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int grp = 1; grp < NG; ++grp) {
             mfma_group(grp);
             __builtin_amdgcn_sched_barrier(0);
-            lds_read(st_next, 0, grp);
+            lds_read(ra, sb_next, rkw, grp);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -231,29 +242,32 @@ __device__ __forceinline__ void igemm_rowwin_body(const GemmArgs &A) {
     __syncthreads();  // bias_s written
 
     if (nk > 0) {
-        issue(0, st0);
-        issue(1, st1);
-        issue(2, st2);
-        CONVLOWER_WAIT_VMCNT(2 * IPW);
+        issue_a(0, sa0);
+        issue_b(0, sb0);
+        issue_b(1, sb1);
+        issue_b(2, sb2);
+        CONVLOWER_WAIT_VMCNT(2 * IPW_B);  // step 0's runs and tap 0's weights
         block_barrier();
 #pragma unroll
-        for (int grp = 0; grp < NG; ++grp) lds_read(st0, 0, grp);
-        for (int kt = 0;; kt += 3) {
-            phase(kt, st0, st1);
+        for (int grp = 0; grp < NG; ++grp) lds_read(sa0, sb0, 0, grp);
+        for (int kt = 0;; kt += 2) {
+            sub(kt, 0, sa0, sa1, sb0, sb1);
+            sub(kt, 1, sa0, sa1, sb1, sb2);
+            sub(kt, 2, sa0, sa1, sb2, sb0);
             if (kt + 1 >= nk) break;
-            phase(kt + 1, st1, st2);
+            sub(kt + 1, 0, sa1, sa0, sb0, sb1);
+            sub(kt + 1, 1, sa1, sa0, sb1, sb2);
+            sub(kt + 1, 2, sa1, sa0, sb2, sb0);
             if (kt + 2 >= nk) break;
-            phase(kt + 2, st2, st0);
-            if (kt + 3 >= nk) break;
         }
         CONVLOWER_WAIT_VMCNT(0);  // no load may still write LDS when the block ends
     }
 
-    dual_store<S, OUT_NCHW, C>(A, acc, &stg[0][0], bias_s, m0, co0, wp, wc, lane, tid);
+    dual_store<S, OUT_NCHW, C>(A, acc, lds, bias_s, m0, co0, wp, wc, lane, tid);
 }
 
 template <typename S, bool OUT_NCHW>
-__global__ __launch_bounds__(512, 1) void igemm_rowwin_kernel(GemmArgs A) {
+__global__ __launch_bounds__(256, 2) void igemm_rowwin_kernel(GemmArgs A) {
     igemm_rowwin_body<S, OUT_NCHW, RowWinCfg<S, 3>>(A);
 }
 

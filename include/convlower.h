@@ -60,9 +60,11 @@ typedef enum { CONV_DTYPE_FP32 = 0, CONV_DTYPE_BF16 = 1, CONV_DTYPE_FP16 = 2 } c
 
 /* Which lowering feeds the contraction.
  *   AUTO      1x1 stride-1 unpadded, or kernel == whole unpadded input: the
- *             plain-GEMM feed; fewer input channels than one 16-byte chunk
- *             with more than 12 taps: IM2WIN (cells padded to one chunk)
- *             when that tensor is smaller than im2col; otherwise INDIRECT.
+ *             plain-GEMM feed; channels not a whole number of 16-byte chunks
+ *             with more than 12 taps: IM2WIN (cells padded to whole chunks)
+ *             when that tensor is smaller than im2col; shapes IM2WIN_LDS
+ *             serves, with more than 64 output channels and at least 256
+ *             tiles of 256 x 128: IM2WIN_LDS; otherwise INDIRECT.
  *   INDIRECT  indirection buffer of per-(output pixel, tap) input offsets.
  *   IM2WIN    window-ordered copy of the input in the workspace (each
  *             (column, kernel row) cell padded to one 16-byte chunk when

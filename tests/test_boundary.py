@@ -73,7 +73,15 @@ def test_workspace_below_im2col(name, layout, dtype):
         # taps: AUTO takes the window tensor with cells padded to whole chunks
         es = 4 if dtype == "fp32" else 2
         padded_win = (L.C * es) % 16 != 0 and L.KH * L.KW > 12
-        assert auto == (win if padded_win else ind)
+        # the window rows in LDS where they apply, with more than 64 output
+        # channels and at least 256 tiles of 256 x 128
+        M = L.N * Ho * Wo
+        rowwin = (_rowwin_eligible(L, dtype) and L.Co > 64
+                  and -(-M // 256) * -(-L.Co // 128) >= 256)
+        if rowwin:
+            assert auto == cl.workspace_size(*_args(L, layout, dtype, "im2win_lds"))
+        else:
+            assert auto == (win if padded_win else ind)
     else:
         # 1x1 NHWC: no workspace at all; 1x1 NCHW: the channels-last copy of
         # half the batch; whole-input kernel: only the split-K partials
