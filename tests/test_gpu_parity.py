@@ -476,3 +476,40 @@ def test_forced_main_loop_parity(variant, case, dtype, layout, algo):
     x, w, b = make_inputs(L, dtype, "NCHW")
     y_ref, dn = oracle.conv2d(x, w, b, s, p, d, oracle.NCHW)
     _assert_parity(_to_nchw(y, layout), y_ref, dn, dtype, f"{variant} {name} {dtype} {layout} {algo}")
+
+
+# --- operands that are element-aligned but not 16-byte aligned -------------------
+
+def _misaligned_copy(t):
+    """The same values in a device tensor whose data starts one element past
+    an aligned address (so 16-byte vector paths must not be taken)."""
+    buf = torch.empty(t.numel() + 8, dtype=t.dtype, device=DEV)
+    v = buf[1:1 + t.numel()].view(t.shape)
+    v.copy_(t.to(DEV))
+    assert v.data_ptr() % 16 != 0
+    return v
+
+
+@pytest.mark.parametrize("case", FORCED_CASES, ids=[c[0] for c in FORCED_CASES])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("layout", ["NCHW", "NHWC"])
+@pytest.mark.parametrize("algo", ["auto", "indirect", "im2win", "im2win_lds", "im2col", "direct"])
+def test_misaligned_operands(case, dtype, layout, algo):
+    """x, w, bias and y all one element off 16-byte alignment: every
+    algorithm still meets the parity bar (the window-row loop falls back to
+    the element-gather loop for NHWC input)."""
+    from convolution_lowering_amd.workloads import Layer
+    name, N, C, H, W, Co, KH, KW, s, p, d = case
+    L = Layer(name, N, C, H, W, Co, KH, KW, s, p, d, seed=79)
+    x, w, b = make_inputs(L, dtype, layout)
+    _say(f"[gpu] misaligned {name} {dtype} {layout} {algo}")
+    xd, wd, bd = _misaligned_copy(x), _misaligned_copy(w), _misaligned_copy(b)
+    Ho = oracle.out_size(H, KH, s, p, d)
+    Wo = oracle.out_size(W, KW, s, p, d)
+    shape = (N, Co, Ho, Wo) if layout == "NCHW" else (N, Ho, Wo, Co)
+    y = _misaligned_copy(torch.zeros(shape, dtype=x.dtype))
+    cl.conv2d_fwd(xd, wd, bd, s, p, d, layout, algo, out=y)
+    torch.cuda.synchronize()
+    xn, wn, bn = make_inputs(L, dtype, "NCHW")
+    y_ref, dn = oracle.conv2d(xn, wn, bn, s, p, d, oracle.NCHW)
+    _assert_parity(_to_nchw(y, layout), y_ref, dn, dtype, f"misaligned {name} {dtype} {layout} {algo}")
