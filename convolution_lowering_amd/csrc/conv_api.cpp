@@ -12,6 +12,7 @@ namespace convlower {
 namespace {
 
 constexpr long long kLimit = (1LL << 31) - 1;  // element counts the kernels index with 32-bit parts
+constexpr long long kBufMax = (1LL << 31) - 64;  // bytes the vector paths address with 32-bit buffer offsets
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -134,7 +135,6 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     // Window rows in LDS (igemm_rowwin.h): stride 1, dilation 1, three taps
     // per kernel row, channel slices of whole K tiles, a 256-pixel tile
     // spanning at most kRowWinMaxSeg output rows, 32-bit byte offsets.
-    const long long kBufMax = (1LL << 31) - 64;
     const bool rowwin_ok = g.s == 1 && g.d == 1 && g.KW == 3 && g.C % (pl->e16 ? 32 : 16) == 0 &&
                            255 / g.Wo + 2 <= kRowWinMaxSeg &&
                            (long long)g.N * g.C * g.H * g.W * (long long)pl->esize <= kBufMax &&
@@ -499,7 +499,6 @@ conv_status_t launch_main(const Plan &pl, GemmArgs &a, hipStream_t s) {
     if (pl.force_element) a_vec = false;
     bool b_vec = g.K % VEC == 0 && al16(a.b);
     // The vector paths address A and B with 32-bit buffer offsets.
-    const long long kBufMax = (1LL << 31) - 64;
     // The extent of what the A feed reads: the window tensor for im2win
     // (built here or handed in), else the input or its channels-last copy.
     const bool win = pl.feed == FEED_WIN || pl.feed == FEED_WIN_CHUNK;
