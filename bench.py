@@ -237,6 +237,10 @@ def main():
     head = bench_layer(H, head_dtype, head_layout, head_algo, args.steps, args.warmup, flush, stamp_main_loop=True)
     print(f"# headline {H.name} {head_dtype} {head_layout} {head_algo}: {head['ms']:.4f} ms "
           f"{head['tflops']:.1f} TFLOPS", file=sys.stderr, flush=True)
+    try:  # the graphics clock right after the headline steps (amd-smi through torch)
+        clock_mhz = float(torch.cuda.clock_rate())
+    except Exception:
+        clock_mhz = None
 
     # Roofline entry of the dominant kernel, the main loop with its fused
     # epilogue: its own duration inside the timed headline steps.
@@ -320,6 +324,7 @@ def main():
                    "algo": head_algo, "global_batch": H.N,
                    "workspace_bytes": head["workspace_bytes"], "im2col_bytes": head["im2col_bytes"]},
         "roofline": rl,
+        "gpu_clock_mhz_after_headline": clock_mhz,
         "cpu_baseline": cpu,
         "layers": rows,
         "ablation": ablation,
