@@ -27,7 +27,7 @@ enum Feed : int {
 };
 constexpr int kNumFeeds = 8;
 // Output rows a 256-pixel tile of the LDS window-row loop may span.
-constexpr int kRowWinMaxSeg = 64;
+constexpr int kRowWinMaxSeg = 32;
 
 struct Geom {
     int N, C, H, W, Co, KH, KW, s, p, d;

@@ -207,6 +207,33 @@ __device__ __forceinline__ void tile_coords(int ntile_m, int ntile_n, int &mt, i
     nt = b - mt * ntile_n;
 }
 
+// Tile order with the weight bytes in view: each XCD takes a contiguous
+// share of the pixel tiles and, of the channel tiles, the fewest groups
+// whose weight slices together still fit kXcdWeightBudget of its L2, so the
+// blocks of one pixel tile run on one XCD and read its input rows from that
+// XCD's L2 once, not once per XCD.  Group count q (dividing 8 and the
+// channel-tile count, 8 / q dividing the pixel-tile count): XCD x serves
+// channel tiles (x % q) * ntile_n / q .. +ntile_n / q - 1 for pixel tiles
+// (x / q) * ntile_m * q / 8 onwards, channel tile fastest.  With no such q
+// this is tile_coords.
+constexpr long long kXcdWeightBudget = 5LL << 19;  // 2.5 MiB of a 4 MiB L2
+__device__ __forceinline__ void tile_coords_l2(int ntile_m, int ntile_n, long long wbytes_per_ntile, int &mt,
+                                               int &nt) {
+    const int b = blockIdx.x;
+    if ((gridDim.x & 7) == 0) {
+        for (int q = 1; q <= 8; q *= 2) {
+            if (ntile_n % q != 0 || ntile_m % (8 / q) != 0) continue;
+            const int nper = ntile_n / q;
+            if ((long long)nper * wbytes_per_ntile > kXcdWeightBudget) continue;
+            const int xcd = b & 7, j = b >> 3;
+            mt = (xcd / q) * (ntile_m / (8 / q)) + j / nper;
+            nt = (xcd % q) * nper + j % nper;
+            return;
+        }
+    }
+    tile_coords(ntile_m, ntile_n, mt, nt);
+}
+
 constexpr int kThreads = 256;
 constexpr int kIbufLdsEntries = 3072;  // LDS slots for the block's indirection-buffer slice
 

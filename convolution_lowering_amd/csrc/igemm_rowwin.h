@@ -14,7 +14,7 @@
 // behind the other's MFMAs; block tile 256 x 128; channels-last input, OHWI
 // weights.  The A runs of a step and the B rows of a tap pipeline
 // separately: two A stages (the next step's runs load during a whole step)
-// and three B stages (each tap's weights load two taps ahead).  Swizzle and
+// and four B stages (each tap's weights load three taps ahead).  Swizzle and
 // epilogue are those of igemm_dual.h.
 #pragma once
 
@@ -35,7 +35,7 @@ struct RowWinCfg {
     static constexpr int BK = KCH * VEC;             // channels per slice
     static constexpr int ROWS_A = BM + (KW - 1) * kRowWinMaxSeg;  // input-pixel runs of a step
     static constexpr int A_SLOTS = ROWS_A * KCH, B_SLOTS = BN * KCH;
-    static constexpr int NA = 2, NB = 3;             // A and B stages
+    static constexpr int NA = 2, NB = 4;             // A and B stages
     static constexpr int IPW_A = ROWS_A * KCH / 64 / NW;
     static constexpr int IPW_B = BN * KCH / 64 / NW;
     static constexpr int WGM = 2, WGN = 2;
@@ -60,7 +60,7 @@ __device__ __forceinline__ void igemm_rowwin_body(const GemmArgs &A) {
 
     __shared__ uint4 lds[C::LDS_SLOTS];  // A stages, then B stages; the epilogue reuses them
     uint4 *const sa0 = lds, *const sa1 = lds + A_SLOTS;
-    uint4 *const sb0 = lds + 2 * A_SLOTS, *const sb1 = sb0 + B_SLOTS, *const sb2 = sb1 + B_SLOTS;
+    uint4 *const sb0 = lds + 2 * A_SLOTS;  // B stage i at sb0 + i * B_SLOTS; tap u uses stage u % 4
     __shared__ float bias_s[BN];
 
     const Geom &g = A.g;
@@ -69,7 +69,7 @@ __device__ __forceinline__ void igemm_rowwin_body(const GemmArgs &A) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
     int mt, nt;
-    tile_coords((int)((g.M + BM - 1) / BM), (g.Co + BN - 1) / BN, mt, nt);
+    tile_coords_l2((int)((g.M + BM - 1) / BM), (g.Co + BN - 1) / BN, (long long)BN * g.K * (long long)sizeof(S), mt, nt);
     const uint32_t M = (uint32_t)g.M;
     const uint32_t m0 = (uint32_t)mt * BM;
     const int co0 = nt * BN;
@@ -208,23 +208,23 @@ __device__ __forceinline__ void igemm_rowwin_body(const GemmArgs &A) {
     // Tap u = (kt, kw): its fragments are in registers.  After its first MFMA
     // group: wait until tap u+1's weights (and, before the last tap of a
     // step, step kt+1's runs) have landed and this wavefront's LDS reads are
-    // done, barrier, refill the B stage tap u used with tap u+3's weights
-    // (and, at kw = 0, the other A stage with step kt+1's runs), then read
-    // tap u+1's fragments group by group behind the remaining MFMAs.  Loads
-    // complete in issue order, so each wait allows exactly the loads issued
-    // after the ones it needs: tap u+2's weights (kw = 0 and 2), or tap
-    // u+2's weights and step kt+1's runs (kw = 1; both issued at kw = 0).
+    // done, barrier, refill the B stage tap u used with tap u+4's weights
+    // (and, at kw = 0 and before them, the other A stage with step kt+1's
+    // runs), then read tap u+1's fragments group by group behind the
+    // remaining MFMAs.  Loads complete in issue order, so each wait allows
+    // exactly the loads issued after the ones it needs: taps u+2 and u+3's
+    // weights, and at kw = 1 also step kt+1's runs, issued between them.
     auto sub = [&](int kt, int kw, uint4 *sa, uint4 *sa_next, uint4 *sb, const uint4 *sb_next) {
         mfma_group(0);
         __builtin_amdgcn_sched_barrier(0);
         if (kw == 1)
-            CONVLOWER_WAIT_VMCNT_LDS(IPW_A + IPW_B);
+            CONVLOWER_WAIT_VMCNT_LDS(IPW_A + 2 * IPW_B);
         else
-            CONVLOWER_WAIT_VMCNT_LDS(IPW_B);
+            CONVLOWER_WAIT_VMCNT_LDS(2 * IPW_B);
         block_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        issue_b(kt * KW + kw + 3, sb);
         if (kw == 0) issue_a(kt + 1, sa_next);
+        issue_b(kt * KW + kw + 4, sb);
         __builtin_amdgcn_sched_barrier(0);
         const uint4 *ra = kw + 1 < KW ? sa : sa_next;
         const int rkw = kw + 1 < KW ? kw + 1 : 0;
@@ -238,27 +238,34 @@ __device__ __forceinline__ void igemm_rowwin_body(const GemmArgs &A) {
             __builtin_amdgcn_sched_barrier(0);
         }
     };
+    // One K step whose first tap uses B stage b0 (taps rotate through four
+    // B stages, steps through two A stages).
+    auto step = [&](int kt, uint4 *sa, uint4 *sa_next, int b0) {
+#pragma unroll
+        for (int kw = 0; kw < KW; ++kw)
+            sub(kt, kw, sa, sa_next, sb0 + ((b0 + kw) & 3) * B_SLOTS, sb0 + ((b0 + kw + 1) & 3) * B_SLOTS);
+    };
 
     __syncthreads();  // bias_s written
 
     if (nk > 0) {
         issue_a(0, sa0);
-        issue_b(0, sb0);
-        issue_b(1, sb1);
-        issue_b(2, sb2);
-        CONVLOWER_WAIT_VMCNT(2 * IPW_B);  // step 0's runs and tap 0's weights
+#pragma unroll
+        for (int u = 0; u < 4; ++u) issue_b(u, sb0 + u * B_SLOTS);
+        CONVLOWER_WAIT_VMCNT(3 * IPW_B);  // step 0's runs and tap 0's weights
         block_barrier();
 #pragma unroll
         for (int grp = 0; grp < NG; ++grp) lds_read(sa0, sb0, 0, grp);
-        for (int kt = 0;; kt += 2) {
-            sub(kt, 0, sa0, sa1, sb0, sb1);
-            sub(kt, 1, sa0, sa1, sb1, sb2);
-            sub(kt, 2, sa0, sa1, sb2, sb0);
+        // Four steps (twelve taps) bring A and B stages back into phase.
+        for (int kt = 0;; kt += 4) {
+            step(kt, sa0, sa1, 0);
             if (kt + 1 >= nk) break;
-            sub(kt + 1, 0, sa1, sa0, sb0, sb1);
-            sub(kt + 1, 1, sa1, sa0, sb1, sb2);
-            sub(kt + 1, 2, sa1, sa0, sb2, sb0);
+            step(kt + 1, sa1, sa0, 3);
             if (kt + 2 >= nk) break;
+            step(kt + 2, sa0, sa1, 2);
+            if (kt + 3 >= nk) break;
+            step(kt + 3, sa1, sa0, 1);
+            if (kt + 4 >= nk) break;
         }
         CONVLOWER_WAIT_VMCNT(0);  // no load may still write LDS when the block ends
     }

@@ -90,7 +90,9 @@ typedef enum { CONV_DTYPE_FP32 = 0, CONV_DTYPE_BF16 = 1, CONV_DTYPE_FP16 = 2 } c
  *             of input pixels its output rows' windows cover, and the KW taps
  *             of that kernel row read their MFMA operands from the one run.
  *             Stride 1, dilation 1, KW = 3, C_in a multiple of 32 (16-bit
- *             types) or 16 (fp32) only, else CONV_ERR_UNSUPPORTED.  Workspace:
+ *             types) or 16 (fp32), an output at least 9 pixels wide (a
+ *             256-pixel tile then spans at most 32 output rows), x and w
+ *             below 2^31 bytes only, else CONV_ERR_UNSUPPORTED.  Workspace:
  *             for NCHW the channels-last copy of x and OHWI weights; for
  *             NHWC a spare indirection buffer, used only when x or w is not
  *             16-byte aligned (then the call runs the element-gather loop).  */

@@ -189,7 +189,7 @@ def test_forced_main_loop_checks_on_the_host():
 def _rowwin_eligible(L, dtype):
     Ho, Wo = cl.output_size(L.H, L.W, L.KH, L.KW, L.stride, L.pad, L.dilation)
     return (L.stride == 1 and L.dilation == 1 and L.KW == 3 and L.C % (16 if dtype == "fp32" else 32) == 0
-            and 255 // Wo + 2 <= 64)
+            and 255 // Wo + 2 <= 32)
 
 
 @pytest.mark.parametrize("name", sorted(LAYERS))
@@ -212,6 +212,19 @@ def test_window_rows_in_lds_eligibility_and_workspace(name, dtype):
     assert cl.workspace_size(*_args(L, "NHWC", dtype, "im2win_lds")) == up(Ho * Wo * L.KH * L.KW * 4)
     want = up(L.N * L.C * L.H * L.W * es) + up(L.Co * L.C * L.KH * L.KW * es)
     assert cl.workspace_size(*_args(L, "NCHW", dtype, "im2win_lds")) == want
+
+
+@pytest.mark.parametrize("W,ok", [(7, False), (8, False), (9, True), (10, True)])
+def test_window_rows_in_lds_needs_nine_output_columns(W, ok):
+    """A 256-pixel tile of the window-row loop may span at most 32 output
+    rows: 255 // Wo + 2 of them, so Wo = 9 is the narrowest output served."""
+    args = (3, 32, 12, W, 64, 3, 3, 1, 1, 1, "NHWC", "bf16", "im2win_lds")
+    if ok:
+        assert cl.workspace_size(*args) > 0
+    else:
+        with pytest.raises(cl.ConvLowerError) as e:
+            cl.workspace_size(*args)
+        assert e.value.code == UNSUPPORTED
 
 
 def test_gemm_algo_rejected_on_windowed_layer():

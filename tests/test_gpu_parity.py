@@ -75,7 +75,7 @@ def _rowwin_eligible(L, dtype):
     """The shapes CONV_ALGO_IM2WIN_LDS serves (the header's rule)."""
     Wo = oracle.out_size(L.W, L.KW, L.stride, L.pad, L.dilation)
     return (L.stride == 1 and L.dilation == 1 and L.KW == 3 and L.C % (16 if dtype == "fp32" else 32) == 0
-            and 255 // Wo + 2 <= 64)
+            and 255 // Wo + 2 <= 32)
 
 
 def _cases():
@@ -253,9 +253,10 @@ EDGE = [
     ("C-37-3x3", 2, 37, 13, 11, 70, 3, 3, 1, 1, 1),
     ("C-9-3x3", 2, 9, 17, 15, 33, 3, 3, 1, 1, 1),
     ("C-20-5x5-dilated", 3, 20, 23, 19, 50, 5, 5, 2, 4, 2),
-    # window rows in LDS: tiles crossing output rows and images, narrow
-    # outputs (many segments per tile), ragged channels, unpadded kernels
-    ("rowwin-narrow", 3, 32, 9, 5, 70, 3, 3, 1, 1, 1),
+    # window rows in LDS: tiles crossing output rows and images, the
+    # narrowest output served (a tile starting at column 8 of a 9-wide row
+    # spans 30 rows), ragged channels, unpadded kernels
+    ("rowwin-narrow", 10, 32, 9, 9, 70, 3, 3, 1, 1, 1),
     ("rowwin-unpadded", 2, 64, 15, 17, 130, 3, 3, 1, 0, 1),
     ("rowwin-tall-kernel", 2, 32, 12, 11, 40, 5, 3, 1, 2, 1),
 ]
