@@ -75,21 +75,27 @@ __device__ __forceinline__ void igemm_rowwin_body(const GemmArgs &A) {
     const int co0 = nt * BN;
     const int nk = (g.C / BK) * g.KH;  // K steps: channel slice, then kernel row fastest
 
+    // The bias is read only by the epilogue: its load is issued here and its
+    // value goes to LDS after the K loop, so the load's latency passes behind
+    // the main loop instead of delaying the block's first loads.
+    float bias_r = 0.f;
     if (tid < BN) {
         const int co = co0 + tid;
-        float b = 0.f;
-        if (A.bias && co < g.Co) b = bits_to_f32(S(), elem_bits((const S *)A.bias, co));
-        bias_s[tid] = b;
+        if (A.bias && co < g.Co) bias_r = bits_to_f32(S(), elem_bits((const S *)A.bias, co));
     }
 
     // ---- the block's segments ------------------------------------------------
     // Output row R (of all N*Ho) holds pixels R*Wo .. R*Wo + Wo-1.  The tile's
     // pixels [m0, mend) fall into rows R0, R0+1, ...; segment j is the part
     // in row R0 + j, and its stage rows are its pixels plus KW - 1 more, the
-    // segments back to back.
+    // segments back to back.  Segment 0 starts at pixel m0; every later one
+    // starts at the beginning of its row and, except the last, has Wo pixels,
+    // so it takes SW = Wo + KW - 1 stage rows.
     const uint32_t Wo = (uint32_t)g.Wo;
     const uint32_t mend = min(m0 + (uint32_t)BM, M);
     const uint32_t R0 = m0 / Wo;
+    const uint32_t SW = Wo + (uint32_t)(KW - 1);
+    const uint32_t rows0 = min(mend, (R0 + 1) * Wo) - m0 + (uint32_t)(KW - 1);
 
     // ---- per-lane load geometry -------------------------------------------------
     // As in igemm_dual.h: load i of this wavefront covers stage rows
@@ -105,27 +111,24 @@ __device__ __forceinline__ void igemm_rowwin_body(const GemmArgs &A) {
 #pragma unroll
     for (int i = 0; i < IPW_A; ++i) {
         const uint32_t r = (uint32_t)((i * NW + wave) * RPI + lrow);
-        uint32_t start = 0;
-        aok[i] = false;
-        abase[i] = 0;
-        ahi[i] = 0;
-        for (uint32_t j = 0; j < (uint32_t)kRowWinMaxSeg; ++j) {
-            const uint32_t R = R0 + j;
-            const uint32_t first = max(m0, R * Wo);
-            if (first >= mend) break;
-            const uint32_t len = min(mend, (R + 1) * Wo) - first;
-            const uint32_t rows = len + (uint32_t)(KW - 1);
-            if (r < start + rows) {
-                const uint32_t n = R / (uint32_t)g.Ho, ho = R - n * (uint32_t)g.Ho;
-                const int wi = (int)(first - R * Wo) + (int)(r - start) - g.p;
-                const int hi0 = (int)ho - g.p;
-                aok[i] = wi >= 0 && wi < g.W;
-                ahi[i] = hi0;
-                abase[i] = (int)n * HWC + hi0 * WC + wi * g.C;  // may be negative while hi0 < 0
-                break;
-            }
-            start += rows;
+        // Segment j of stage row r and r's place in it (off), in closed form.
+        uint32_t j = 0, off = r;
+        if (r >= rows0) {
+            const uint32_t t = r - rows0;
+            j = 1 + t / SW;
+            off = t - (j - 1) * SW;
         }
+        const uint32_t R = R0 + j;
+        const uint32_t first = max(m0, R * Wo);
+        // A row past the last segment (or in the unused tail of a partial last
+        // segment) loads zeros.
+        const bool live = first < mend && off < min(mend, (R + 1) * Wo) - first + (uint32_t)(KW - 1);
+        const uint32_t n = R / (uint32_t)g.Ho, ho = R - n * (uint32_t)g.Ho;
+        const int wi = (int)(first - R * Wo) + (int)off - g.p;
+        const int hi0 = (int)ho - g.p;
+        aok[i] = live && wi >= 0 && wi < g.W;
+        ahi[i] = hi0;
+        abase[i] = live ? (int)n * HWC + hi0 * WC + wi * g.C : 0;  // may be negative while hi0 < 0
     }
     int wbase[IPW_B];
     bool wok[IPW_B];
@@ -246,8 +249,6 @@ __device__ __forceinline__ void igemm_rowwin_body(const GemmArgs &A) {
             sub(kt, kw, sa, sa_next, sb0 + ((b0 + kw) & 3) * B_SLOTS, sb0 + ((b0 + kw + 1) & 3) * B_SLOTS);
     };
 
-    __syncthreads();  // bias_s written
-
     if (nk > 0) {
         issue_a(0, sa0);
 #pragma unroll
@@ -270,6 +271,9 @@ __device__ __forceinline__ void igemm_rowwin_body(const GemmArgs &A) {
         CONVLOWER_WAIT_VMCNT(0);  // no load may still write LDS when the block ends
     }
 
+    // bias_s is a separate array from the stages; the epilogue's first
+    // barrier publishes it.
+    if (tid < BN) bias_s[tid] = bias_r;
     dual_store<S, OUT_NCHW, C>(A, acc, lds, bias_s, m0, co0, wp, wc, lane, tid);
 }
 
