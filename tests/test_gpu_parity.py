@@ -172,7 +172,7 @@ def test_parity_full_size_sampled(name, dtype, layout, algo):
     assert float(err.max()) <= TOL[dtype], f"{name}: {err.max():.3e}"
 
 
-@pytest.mark.parametrize("name", ["C2", "C3a", "C4a", "C4e", "C5a", "C5c"])
+@pytest.mark.parametrize("name", ["C2", "C3a", "C4a", "C4c", "C4d", "C4e", "C5a", "C5c"])
 @pytest.mark.parametrize("layout", ["NCHW", "NHWC"])
 def test_full_size_integer_exact_sampled(name, layout):
     """Bit-exact at full size: integer inputs make the exact result the only
