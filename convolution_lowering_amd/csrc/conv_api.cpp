@@ -304,7 +304,17 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
         pl->tile = TILE_128x128; BM = 128; BN = 128;
     }
     if (pl->feed == FEED_ROWWIN) {
-        pl->tile = TILE_256x128_ROWWIN; BM = 256; BN = 128;
+        // The ping-pong form (one 512 x 128 block per CU) where all its tiles
+        // fit one round on the 256 CUs and the K loop has at least 72 taps
+        // (channel slices x KH x KW): its faster taps then outweigh its
+        // larger per-tile prologue and epilogue.  Over several rounds, two
+        // 256 x 128 blocks per CU leave a shorter last round.
+        const long long taps = pl->gm.K / (pl->e16 ? 32 : 16);
+        if (((Mt + 511) / 512) * ((g.Co + 127) / 128) <= 256 && taps >= 72) {
+            pl->tile = TILE_512x128_ROWWIN_PP; BM = 512; BN = 128;
+        } else {
+            pl->tile = TILE_256x128_ROWWIN; BM = 256; BN = 128;
+        }
     }
     // A forced variant (ablation) replaces the choice above when the feed
     // and shape allow it.
@@ -357,7 +367,7 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     // Split K only where too few tiles leave most CUs idle: the two-wavefront
     // loops keep a CU busy with a single block, and the partials cost a pass
     // over M x Co fp32 values per split.
-    const bool two_wave = wide_slice(pl->tile) || pl->tile == TILE_256x128_ROWWIN;
+    const bool two_wave = wide_slice(pl->tile) || pl->tile == TILE_256x128_ROWWIN || pl->tile == TILE_512x128_ROWWIN_PP;
     if (pl->feed != FEED_ROWWIN && blocks < (two_wave ? 64 : 256) && ktiles >= 16) {
         // Enough splits to give every compute unit work, each split at least
         // 4 K tiles, and the whole workspace (partials included) kept below

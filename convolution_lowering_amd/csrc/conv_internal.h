@@ -66,8 +66,9 @@ enum Tile : int {
     TILE_256x128_OCT = 5,
     TILE_128x64_QUAD = 6,
     TILE_256x256_OCT = 7,
-    TILE_256x128_ROWWIN = 8,  // the LDS window-row loop of igemm_rowwin.h (FEED_ROWWIN only)
-    TILE_COUNT = 9
+    TILE_256x128_ROWWIN = 8,     // the LDS window-row loop of igemm_rowwin.h (FEED_ROWWIN only)
+    TILE_512x128_ROWWIN_PP = 9,  // its one-block-per-CU ping-pong form, igemm_rowwin_pp.h (FEED_ROWWIN only)
+    TILE_COUNT = 10
 };
 
 hipError_t launch_igemm_bf16(const GemmArgs &a, int feed, bool out_nchw, bool a_vec, bool b_vec,

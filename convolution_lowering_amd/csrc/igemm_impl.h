@@ -608,6 +608,7 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(GemmArgs A) {
 #include "igemm_dma.h"
 #include "igemm_dual.h"
 #include "igemm_rowwin.h"
+#include "igemm_rowwin_pp.h"
 
 namespace convlower {
 
@@ -628,6 +629,7 @@ static hipError_t launch_tile(const GemmArgs &a, int tile, int splits, hipStream
     if constexpr (FEED == FEED_ROWWIN) {  // its own loop only, 16-byte rows only
         if constexpr (AVEC) {
             if (tile == TILE_256x128_ROWWIN) return go(igemm_rowwin_kernel<S, OUT_NCHW>, 256, 128, 256);
+            if (tile == TILE_512x128_ROWWIN_PP) return go(igemm_rowwin_pp_kernel<S, OUT_NCHW>, 512, 128, 512);
         }
         return hipErrorInvalidValue;
     } else if constexpr (AVEC && (FEED == FEED_IND_CHUNK || FEED == FEED_WIN_CHUNK)) {  // one tap per chunk: the two-wavefront loops only

@@ -89,6 +89,10 @@ typedef enum { CONV_DTYPE_FP32 = 0, CONV_DTYPE_BF16 = 1, CONV_DTYPE_FP16 = 2 } c
  *             each block stages, per channel slice and kernel row, the runs
  *             of input pixels its output rows' windows cover, and the KW taps
  *             of that kernel row read their MFMA operands from the one run.
+ *             A grid of at most 256 tiles of 512 x 128 over a K loop of at
+ *             least 72 taps runs as one block per compute unit whose two
+ *             halves alternate between multiplying and loading; other
+ *             shapes as two 256 x 128 blocks per unit.
  *             Stride 1, dilation 1, KW = 3, C_in a multiple of 32 (16-bit
  *             types) or 16 (fp32), an output at least 9 pixels wide (a
  *             256-pixel tile then spans at most 32 output rows), x and w

@@ -217,6 +217,32 @@ def test_many_tiles_odd_planes_sampled(layout, dtype):
         assert float(err.max()) <= TOL[dtype], f"{err.max():.3e}"
 
 
+@pytest.mark.parametrize("shape", [(8, 256, 28), (16, 32, 56), (24, 32, 56)])
+@pytest.mark.parametrize("layout", ["NCHW", "NHWC"])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_window_rows_both_block_forms(shape, layout, dtype):
+    """256 output channels, 3x3: N=8, C=256 at 28x28 (26 tiles of 512 x 128,
+    72 taps) takes the one-block ping-pong form; C=32 at 56x56 (9 taps), at
+    N=16 (one round of 512-row tiles) and N=24 (more), takes two 256 x 128
+    blocks per compute unit.  The whole output is compared: fp32 on integer
+    inputs bit for bit, bf16 within the tolerance."""
+    from convolution_lowering_amd.workloads import Layer
+    n, c, hw = shape
+    L = Layer(f"rowwin-forms-{n}-{c}", n, c, hw, hw, 256, 3, 3, 1, 1, 1, seed=97)
+    integer = dtype == "fp32"
+    x, w, b = make_inputs(L, dtype, layout, integer=integer)
+    _say(f"[gpu] rowwin-forms N={n} C={c} {dtype} {layout}")
+    y = cl.conv2d_fwd(x.to(DEV), w.to(DEV), b.to(DEV), L.stride, L.pad, L.dilation, layout, "im2win_lds")
+    torch.cuda.synchronize()
+    xr, wr, br = make_inputs(L, dtype, "NCHW", integer=integer)
+    y_ref, dn = oracle.conv2d(xr, wr, br, L.stride, L.pad, L.dilation, oracle.NCHW)
+    yn = _to_nchw(y, layout)
+    if integer:
+        assert np.array_equal(yn.double().cpu().numpy(), y_ref)
+    else:
+        _assert_parity(yn, y_ref, dn, dtype, f"rowwin forms N={n} C={c}")
+
+
 # --- edge cases ----------------------------------------------------------------
 
 EDGE = [
