@@ -212,6 +212,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run one 256 MiB device copy (scale reference for HBM byte counters)")
+    ap.add_argument("--only", metavar="LAYER:LAYOUT[:DTYPE]",
+                    help="time only this layer (algo auto, dtype bf16 unless given) and print its row; "
+                         "for profiling one layer's kernels")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path (each GPU would run its own "
@@ -231,6 +234,13 @@ def main():
         for _ in range(20):
             flush()
         torch.cuda.synchronize()
+
+    if args.only:
+        parts = args.only.split(":")
+        L = LAYERS[parts[0]]
+        row = bench_layer(L, parts[2] if len(parts) > 2 else "bf16", parts[1], "auto", args.steps, args.warmup, flush)
+        print(json.dumps(row))
+        return
 
     H = LAYERS["C2"]
     head_dtype, head_layout, head_algo = "bf16", "NCHW", "auto"
