@@ -17,7 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libconvlower.so")
 
 LAYOUTS = {"NCHW": 0, "NHWC": 1}
-ALGOS = {"auto": 0, "indirect": 1, "im2win": 2, "gemm": 3, "im2col": 4, "direct": 5, "im2win_lds": 6}
+ALGOS = {"auto": 0, "indirect": 1, "im2win": 2, "gemm": 3, "im2col": 4, "direct": 5, "im2win_lds": 6, "patch": 7}
 DTYPE_CODES = {"fp32": 0, "bf16": 1, "fp16": 2}
 STATUS = {0: "CONV_OK", 1: "CONV_ERR_INVALID_ARG", 2: "CONV_ERR_UNSUPPORTED", 3: "CONV_ERR_WORKSPACE",
           4: "CONV_ERR_HIP"}

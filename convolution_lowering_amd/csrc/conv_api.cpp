@@ -47,6 +47,7 @@ struct Plan {
     bool need_ibuf, need_win, need_wpack;
     bool need_col;  // X_col materialised (the im2col baseline)
     bool direct;    // the direct-convolution baseline: no lowering, no main loop
+    bool patch;     // C_in <= 4: input patches staged in LDS (patch_conv.hip), no workspace
     bool need_xcl;  // channels-last copy of an NCHW input
     int chunk_n;    // images per main-loop pass (< N: the batch goes through the copy in parts)
     int cp;         // channels per pixel row of the channels-last copy (> C: zero-padded)
@@ -96,7 +97,7 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
                         bool allow_pad = true) {
     if (layout != CONV_LAYOUT_NCHW && layout != CONV_LAYOUT_NHWC) return CONV_ERR_INVALID_ARG;
     if (!dtype_ok(dtype)) return CONV_ERR_INVALID_ARG;
-    if (algo < CONV_ALGO_AUTO || algo > CONV_ALGO_IM2WIN_LDS) return CONV_ERR_INVALID_ARG;
+    if (algo < CONV_ALGO_AUTO || algo > CONV_ALGO_PATCH) return CONV_ERR_INVALID_ARG;
     memset(pl, 0, sizeof(*pl));
     conv_status_t st = make_geom(N, C, H, W, Co, KH, KW, s, p, d, &pl->g);
     if (st != CONV_OK) return st;
@@ -144,8 +145,10 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     // every CU a block without splitting K.
     const bool rowwin_auto = rowwin_ok && g.Co > 64 && t_forced_main_loop == CONV_MAIN_LOOP_AUTO &&
                              ((g.M + 255) / 256) * ((g.Co + 127) / 128) >= 256;
+    const bool patch_ok = patch_conv_plan(g, pl->dtype, nullptr);
     if (algo == CONV_ALGO_AUTO)
         algo = (whole || one) ? CONV_ALGO_GEMM
+               : patch_ok                  ? CONV_ALGO_PATCH
                : (!chunk_ind && chunk_win) ? CONV_ALGO_IM2WIN
                : rowwin_auto             ? CONV_ALGO_IM2WIN_LDS
                                          : CONV_ALGO_INDIRECT;
@@ -217,6 +220,14 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
                 pl->need_wpack = true;
             }
             break;
+        case CONV_ALGO_PATCH:
+            if (!patch_ok) return CONV_ERR_UNSUPPORTED;
+            pl->patch = true;
+            pl->gm = g;
+            pl->out_nchw = !pl->nhwc;
+            pl->splits = 1;
+            pl->total = 0;
+            return CONV_OK;
         case CONV_ALGO_DIRECT:
             pl->direct = true;
             pl->gm = g;
@@ -564,6 +575,8 @@ conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias
     char *ws = (char *)workspace;
     if (pl.direct)
         return launch_direct_conv(x, w, bias, y, g, pl.nhwc, pl.dtype, s) == hipSuccess ? CONV_OK : CONV_ERR_HIP;
+    if (pl.patch)
+        return launch_patch_conv(x, w, bias, y, g, pl.nhwc, pl.dtype, s) == hipSuccess ? CONV_OK : CONV_ERR_HIP;
 
     GemmArgs a;
     memset(&a, 0, sizeof(a));

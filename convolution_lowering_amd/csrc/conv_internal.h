@@ -88,6 +88,13 @@ hipError_t launch_im2win(const void *x, void *xwin, const Geom &g, bool nhwc, bo
 hipError_t launch_direct_conv(const void *x, const void *w, const void *bias, void *y, const Geom &g, bool nhwc,
                               int dtype, hipStream_t st);
 
+// Inputs with at most four channels, input patches staged in LDS
+// (patch_conv.hip): whether a layer fits (and its output rows per unit), and
+// the launch.  Both layouts; x, w and y in `nhwc` or NCHW layout.
+bool patch_conv_plan(const Geom &g, int dtype, int *R_out);
+hipError_t launch_patch_conv(const void *x, const void *w, const void *bias, void *y, const Geom &g, bool nhwc,
+                             int dtype, hipStream_t st);
+
 // X_col, rows (n, ho, wo), columns (ci, kh, kw) for NCHW input, (kh, kw, ci)
 // for NHWC input.
 hipError_t launch_im2col(const void *x, void *xcol, const Geom &g, bool nhwc, bool bf16, hipStream_t st);

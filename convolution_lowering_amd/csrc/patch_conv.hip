@@ -1,0 +1,387 @@
+// Inputs with at most four channels: the indirect convolution of "The
+// Indirect Convolution Algorithm" (abstract), with the input patch of a few
+// output rows staged in LDS and each tap's input pixel addressed there on the
+// fly, instead of an indirection buffer in memory.
+//
+// With C_in <= 4, a 16-byte chunk of the lowered row X_col[m] (K order: tap,
+// then channel, channels padded to 4) is two whole taps for 16-bit types and
+// one for fp32, so each A fragment is one or two aligned LDS reads of a
+// staged pixel.  The weights of a block's 64 output channels, zero-padded the
+// same way, stay in registers as MFMA B fragments for all of K (at most 16
+// K steps).  A block is persistent: it stages the input rows that R output
+// rows of one image need (4 channels per pixel, zeros for padding and for
+// channels past C_in), multiplies every 32-pixel fragment of those rows
+// against its weights, stores the results with the bias added in fp32 and
+// one rounding, and moves on to the next group of rows.  No workspace.
+#include "igemm_impl.h"
+
+namespace convlower {
+namespace {
+
+constexpr int kPatchStageBytes = 32 * 1024;  // LDS of the staged input rows
+constexpr int kPatchMaxKSteps = 16;          // K steps of register-resident weights
+constexpr int kPatchThreads = 256;
+
+struct PatchArgs {
+    const void *x, *w, *bias;
+    void *y;
+    Geom g;
+    int R;              // output rows per unit
+    int RIN, WIN;       // staged input rows and columns of a unit
+    int hgroups;        // ceil(Ho / R)
+    int units;          // N * hgroups
+    int ksteps;         // ceil(KH*KW / taps per K step)
+};
+
+// Four outputs, rounded once to nearest-even, into LDS at p.
+__device__ __forceinline__ void obuf_put4_impl(uint16_t, char *p, float a, float b, float c, float d) {
+    *(uint2 *)p = make_uint2(f32x2_to_bf16x2_rne(a, b), f32x2_to_bf16x2_rne(c, d));
+}
+__device__ __forceinline__ void obuf_put4_impl(_Float16, char *p, float a, float b, float c, float d) {
+    *(uint2 *)p = make_uint2(f32x2_to_f16x2_rne(a, b), f32x2_to_f16x2_rne(c, d));
+}
+__device__ __forceinline__ void obuf_put4_impl(float, char *p, float a, float b, float c, float d) {
+    *(float4 *)p = make_float4(a, b, c, d);
+}
+__device__ __forceinline__ uint16_t raw16(const uint16_t *p, long long i) { return p[i]; }
+__device__ __forceinline__ uint16_t raw16(const _Float16 *p, long long i) {
+    return __builtin_bit_cast(uint16_t, p[i]);
+}
+
+// KS: K steps the kernel holds weights for (4, 8, 13 or 16; the layer's own
+// count P.ksteps is at most that).
+template <typename S, bool NCHW, int KS>
+__global__ __launch_bounds__(kPatchThreads, 2) void patch_conv_kernel(PatchArgs P) {
+    using MF = MfmaShape<S, 32>;
+    constexpr int ES = (int)sizeof(S);
+    auto obuf_put4 = [](char *p, float a, float b, float c, float d) { obuf_put4_impl(S(), p, a, b, c, d); };
+    constexpr int PB = 4 * ES;        // bytes of one staged pixel (4 channels)
+    constexpr int TPC = 16 / PB;      // taps per 16-byte chunk: 2 (16-bit) or 1 (fp32)
+    constexpr int TPS = 2 * TPC;      // taps per MFMA K step (two chunks: lanes 0-31, 32-63)
+    constexpr int NQ = MF::NQ;
+    __shared__ uint4 stage[kPatchStageBytes / 16];
+    char *const sbytes = (char *)stage;
+    // Each wavefront's output tile: rows of the output's contiguous axis
+    // (NCHW: 64 channel rows of 32 pixels; NHWC: 32 pixel rows of 64
+    // channels), each padded by 16 bytes against bank conflicts.
+    constexpr int ORS = (NCHW ? 32 : 64) * ES + 16;  // row stride, bytes
+    constexpr int OROWS = NCHW ? 64 : 32;
+    __shared__ uint4 obuf[4][(OROWS * ORS) / 16];
+    __shared__ float4 bias_s[16];  // the block's 64 channels' bias (0 past C_out or without bias)
+
+    const Geom &g = P.g;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    char *const ob = (char *)obuf[wave];
+    const int half = lane >> 5, col = lane & 31;
+    const int cob = blockIdx.y * 64;
+    const int T = g.KH * g.KW;
+    const S *x = (const S *)P.x;
+    const S *w = (const S *)P.w;
+    S *y = (S *)P.y;
+
+    // ---- weights as B fragments: lane (half, col) of K step ks holds, for
+    // output channel cob + 32*ic + col, the channels 0..3 of taps
+    // ks*TPS + half*TPC .. +TPC-1 (zero past C_in, past the last tap and past
+    // C_out).
+    uint4 bw[KS][2];
+    // Byte offset (within the stage) of each of this lane's taps relative to
+    // its output pixel's first tap, 16 bits per tap (the stage is 32 KB),
+    // 0xFFFF for a tap past the last.
+    uint32_t toff[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        toff[ks] = 0;
+#pragma unroll
+        for (int tt = 0; tt < TPC; ++tt) {
+            const int t = ks * TPS + half * TPC + tt;
+            const uint32_t o = (ks < P.ksteps && t < T)
+                                   ? (uint32_t)(((t / g.KW) * g.d * P.WIN + (t % g.KW) * g.d) * PB)
+                                   : 0xFFFFu;
+            toff[ks] |= o << (16 * tt);
+        }
+#pragma unroll
+        for (int ic = 0; ic < 2; ++ic) {
+            const int co = cob + 32 * ic + col;
+            uint32_t wv[4] = {0u, 0u, 0u, 0u};
+            if (ks < P.ksteps && co < g.Co) {
+#pragma unroll
+                for (int tt = 0; tt < TPC; ++tt) {
+                    const int t = ks * TPS + half * TPC + tt;
+                    if (t >= T) continue;
+                    const int kh = t / g.KW, kw = t % g.KW;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        if (c >= g.C) continue;
+                        const long long wi = NCHW ? (((long long)co * g.C + c) * g.KH + kh) * g.KW + kw
+                                                  : (((long long)co * g.KH + kh) * g.KW + kw) * g.C + c;
+                        if constexpr (ES == 2) {
+                            const uint32_t v = raw16(w, wi);
+                            const int e = tt * 4 + c;  // element of the 8 in the chunk
+                            wv[e >> 1] |= v << (16 * (e & 1));
+                        } else {
+                            wv[c] = __float_as_uint(((const float *)w)[wi]);
+                        }
+                    }
+                }
+            }
+            bw[ks][ic] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+        }
+    }
+
+    if (tid < 64) {
+        const int co = cob + tid;
+        ((float *)bias_s)[tid] = (P.bias && co < g.Co) ? bits_to_f32(S(), elem_bits((const S *)P.bias, co)) : 0.f;
+    }  // published by the barrier at the top of the unit loop
+
+    const int frags_per_row = (g.Wo + 31) / 32;
+    // 16-byte global stores: every piece's address then a multiple of 16.
+    const bool vec_store = NCHW ? ((g.Wo * ES) % 16 == 0 && (uintptr_t)y % 16 == 0)
+                                : ((g.Co * ES) % 16 == 0 && (uintptr_t)y % 16 == 0);
+
+    for (int u = blockIdx.x; u < P.units; u += gridDim.x) {
+        const int n = u / P.hgroups;
+        const int ho0 = (u - n * P.hgroups) * P.R;
+        const int rows = min(P.R, g.Ho - ho0);
+        const int hi_base = ho0 * g.s - g.p;
+
+        __syncthreads();  // the previous unit's reads of the stage are done
+        // ---- stage the input rows: pixel (r, c) = x[n][hi_base + r][c - p],
+        // channels 0..3, zeros outside the image and past C_in.  Each thread
+        // loads SB pixels before it writes any, so their loads overlap.
+        constexpr int SB = 8;
+        const int npix = P.RIN * P.WIN;
+        if constexpr (NCHW) {
+            // A thread per staged pixel: each channel's loads run along a
+            // plane row, contiguous across the wavefront.
+            for (int base = 0; base < npix; base += kPatchThreads * SB) {
+                float v[SB][4];
+#pragma unroll
+                for (int j = 0; j < SB; ++j) {
+                    const int idx = base + j * kPatchThreads + tid;
+                    const int r = idx / P.WIN, c = idx - r * P.WIN;
+                    const int hi = hi_base + r, wi = c - g.p;
+                    const bool in = idx < npix && hi >= 0 && hi < g.H && wi >= 0 && wi < g.W;
+#pragma unroll
+                    for (int ch = 0; ch < 4; ++ch) {
+                        v[j][ch] = 0.f;
+                        if (in && ch < g.C) {
+                            const long long xi = (((long long)n * g.C + ch) * g.H + hi) * g.W + wi;
+                            if constexpr (ES == 2)
+                                v[j][ch] = __uint_as_float((uint32_t)raw16(x, xi));  // the raw 16 bits, carried in a float
+                            else
+                                v[j][ch] = ((const float *)x)[xi];
+                        }
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < SB; ++j) {
+                    const int idx = base + j * kPatchThreads + tid;
+                    if (idx >= npix) continue;
+                    if constexpr (ES == 2) {
+                        const uint32_t b0 = __float_as_uint(v[j][0]), b1 = __float_as_uint(v[j][1]);
+                        const uint32_t b2 = __float_as_uint(v[j][2]), b3 = __float_as_uint(v[j][3]);
+                        *(uint2 *)(sbytes + (size_t)idx * PB) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+                    } else {
+                        *(float4 *)(sbytes + (size_t)idx * PB) = make_float4(v[j][0], v[j][1], v[j][2], v[j][3]);
+                    }
+                }
+            }
+        } else {
+            // A thread per (pixel, channel) slot: along a staged row the
+            // channels-last input is read nearly contiguously.
+            const int nslot = npix * 4;
+            for (int base = 0; base < nslot; base += kPatchThreads * SB) {
+                uint32_t v[SB];
+#pragma unroll
+                for (int j = 0; j < SB; ++j) {
+                    const int sl = base + j * kPatchThreads + tid;
+                    const int idx = sl >> 2, ch = sl & 3;
+                    const int r = idx / P.WIN, c = idx - r * P.WIN;
+                    const int hi = hi_base + r, wi = c - g.p;
+                    const bool in = sl < nslot && ch < g.C && hi >= 0 && hi < g.H && wi >= 0 && wi < g.W;
+                    v[j] = 0u;
+                    if (in) {
+                        const long long xi = (((long long)n * g.H + hi) * g.W + wi) * g.C + ch;
+                        if constexpr (ES == 2)
+                            v[j] = raw16(x, xi);
+                        else
+                            v[j] = __float_as_uint(((const float *)x)[xi]);
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < SB; ++j) {
+                    const int sl = base + j * kPatchThreads + tid;
+                    if (sl >= nslot) continue;
+                    if constexpr (ES == 2)
+                        *(uint16_t *)(sbytes + (size_t)sl * 2) = (uint16_t)v[j];
+                    else
+                        *(uint32_t *)(sbytes + (size_t)sl * 4) = v[j];
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- 32-pixel fragments of the unit's output rows, one wavefront each
+        for (int f = wave; f < rows * frags_per_row; f += kPatchThreads / 64) {
+            const int r = f / frags_per_row;
+            const int wo0 = (f - r * frags_per_row) * 32;
+            const int wo = min(wo0 + col, g.Wo - 1);  // past the row's end: a repeated pixel, not stored
+            const int pbase = (r * g.s * P.WIN + wo * g.s) * PB;
+            typename MF::acc_t acc[2] = {typename MF::acc_t{}, typename MF::acc_t{}};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                if (ks < P.ksteps) {
+                    uint4 a;
+                    const uint32_t o0 = toff[ks] & 0xFFFFu;
+                    if constexpr (ES == 2) {
+                        const uint32_t o1 = toff[ks] >> 16;
+                        const uint2 lo = o0 != 0xFFFFu ? *(const uint2 *)(sbytes + pbase + o0) : make_uint2(0u, 0u);
+                        const uint2 hi = o1 != 0xFFFFu ? *(const uint2 *)(sbytes + pbase + o1) : make_uint2(0u, 0u);
+                        a = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                    } else {
+                        a = o0 != 0xFFFFu ? *(const uint4 *)(sbytes + pbase + o0) : make_uint4(0u, 0u, 0u, 0u);
+                    }
+#pragma unroll
+                    for (int ic = 0; ic < 2; ++ic) {
+                        if constexpr (NCHW)
+                            MF::mma(a, bw[ks][ic], acc[ic]);  // rows: pixels, columns: channels
+                        else
+                            MF::mma(bw[ks][ic], a, acc[ic]);  // rows: channels, columns: pixels
+                    }
+                }
+            }
+            // ---- epilogue: bias in fp32, one rounding; the wavefront's 32 x 64
+            // tile goes through its own LDS buffer so that it leaves in 16-byte
+            // pieces along the output's contiguous axis: for NHWC the 32 pixels'
+            // 64-channel runs (one contiguous block when C_out is 64), for
+            // NCHW 64 channel rows of 32 pixels.
+            const int ho = ho0 + r;
+            const int npx = min(32, g.Wo - wo0), nco = min(64, g.Co - cob);
+#pragma unroll
+            for (int ic = 0; ic < 2; ++ic)
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) {
+                    const int i4 = MF::qrow(q, lane);  // first of the lane's 4 consecutive rows
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = acc[ic][4 * q + e];
+                    int off;
+                    if constexpr (NCHW) {
+                        const float bb = ((const float *)bias_s)[32 * ic + col];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[e] += bb;
+                        off = (32 * ic + col) * ORS + i4 * ES;
+                    } else {
+                        const float4 bb = bias_s[(32 * ic + i4) / 4];
+                        v[0] += bb.x, v[1] += bb.y, v[2] += bb.z, v[3] += bb.w;
+                        off = col * ORS + (32 * ic + i4) * ES;
+                    }
+                    obuf_put4(ob + off, v[0], v[1], v[2], v[3]);
+                }
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the tile is in the buffer
+            if constexpr (NCHW) {
+                constexpr int CPR = 32 * ES / 16;  // 16-byte pieces per channel row
+#pragma unroll
+                for (int i = 0; i < 64 * CPR / 64; ++i) {
+                    const int c = lane + 64 * i;
+                    const int cl = c / CPR, p0 = (c % CPR) * (16 / ES);
+                    const int co = cob + cl;
+                    if (co >= g.Co || p0 >= npx) continue;
+                    const uint4 d = *(const uint4 *)(ob + cl * ORS + p0 * ES);
+                    S *dst = y + (((long long)n * g.Co + co) * g.Ho + ho) * g.Wo + wo0 + p0;
+                    if (vec_store && p0 + 16 / ES <= npx) {
+                        *(uint4 *)dst = d;
+                    } else {
+                        const S *src = (const S *)&d;
+#pragma unroll
+                        for (int e = 0; e < 16 / ES; ++e)
+                            if (p0 + e < npx) dst[e] = src[e];
+                    }
+                }
+            } else {
+                constexpr int CPP = 64 * ES / 16;  // 16-byte pieces per pixel
+#pragma unroll
+                for (int i = 0; i < 32 * CPP / 64; ++i) {
+                    const int c = lane + 64 * i;
+                    const int px = c / CPP, c0 = (c % CPP) * (16 / ES);
+                    if (px >= npx || c0 >= nco) continue;
+                    const uint4 d = *(const uint4 *)(ob + px * ORS + c0 * ES);
+                    S *dst = y + (((long long)n * g.Ho + ho) * g.Wo + wo0 + px) * g.Co + cob + c0;
+                    if (vec_store && c0 + 16 / ES <= nco) {
+                        *(uint4 *)dst = d;
+                    } else {
+                        const S *src = (const S *)&d;
+#pragma unroll
+                        for (int e = 0; e < 16 / ES; ++e)
+                            if (c0 + e < nco) dst[e] = src[e];
+                    }
+                }
+            }
+        }
+    }
+}
+
+}  // namespace
+
+// Plan for one layer: output rows per unit so that the staged rows fit
+// kPatchStageBytes, or false when the layer is outside this kernel.
+bool patch_conv_plan(const Geom &g, int dtype, int *R_out) {
+    const int ES = dtype == CONV_DTYPE_FP32 ? 4 : 2;
+    const int TPS = dtype == CONV_DTYPE_FP32 ? 2 : 4;
+    if (g.C > 4) return false;
+    if ((g.KH * g.KW + TPS - 1) / TPS > kPatchMaxKSteps) return false;
+    const long long WIN = (long long)(g.Wo - 1) * g.s + (long long)(g.KW - 1) * g.d + 1;
+    int R = 0;
+    for (int r = 1; r <= 8 && r <= g.Ho; ++r) {
+        const long long RIN = (long long)(r - 1) * g.s + (long long)(g.KH - 1) * g.d + 1;
+        if (RIN * WIN * 4 * ES <= kPatchStageBytes) R = r;
+    }
+    if (R == 0) return false;
+    if (R_out) *R_out = R;
+    return true;
+}
+
+hipError_t launch_patch_conv(const void *x, const void *w, const void *bias, void *y, const Geom &g, bool nhwc,
+                             int dtype, hipStream_t st) {
+    int R = 0;
+    if (!patch_conv_plan(g, dtype, &R)) return hipErrorInvalidValue;
+    PatchArgs P;
+    P.x = x; P.w = w; P.bias = bias; P.y = y; P.g = g;
+    P.R = R;
+    P.RIN = (R - 1) * g.s + (g.KH - 1) * g.d + 1;
+    P.WIN = (g.Wo - 1) * g.s + (g.KW - 1) * g.d + 1;
+    P.hgroups = (g.Ho + R - 1) / R;
+    P.units = g.N * P.hgroups;
+    const int TPS = dtype == CONV_DTYPE_FP32 ? 2 : 4;
+    P.ksteps = (g.KH * g.KW + TPS - 1) / TPS;
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return hipErrorInvalidValue;
+    const int ntn = (g.Co + 63) / 64;
+    // Two resident blocks per compute unit (register-bound), spread over
+    // the channel tiles.
+    const int per_tile = max(1, min(P.units, (2 * cus + ntn - 1) / ntn));
+    const dim3 grid((unsigned)per_tile, (unsigned)ntn);
+    auto launch = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(kPatchThreads), 0, st, P); };
+    auto by_ks = [&](auto k4, auto k8, auto k13, auto k16) {
+        if (P.ksteps <= 4) launch(k4);
+        else if (P.ksteps <= 8) launch(k8);
+        else if (P.ksteps <= 13) launch(k13);  // 7x7 kernels in 16-bit types
+        else launch(k16);
+    };
+    if (dtype == CONV_DTYPE_FP32) {
+        if (nhwc) by_ks(patch_conv_kernel<float, false, 4>, patch_conv_kernel<float, false, 8>, patch_conv_kernel<float, false, 13>, patch_conv_kernel<float, false, 16>);
+        else by_ks(patch_conv_kernel<float, true, 4>, patch_conv_kernel<float, true, 8>, patch_conv_kernel<float, true, 13>, patch_conv_kernel<float, true, 16>);
+    } else if (dtype == CONV_DTYPE_FP16) {
+        if (nhwc) by_ks(patch_conv_kernel<_Float16, false, 4>, patch_conv_kernel<_Float16, false, 8>, patch_conv_kernel<_Float16, false, 13>, patch_conv_kernel<_Float16, false, 16>);
+        else by_ks(patch_conv_kernel<_Float16, true, 4>, patch_conv_kernel<_Float16, true, 8>, patch_conv_kernel<_Float16, true, 13>, patch_conv_kernel<_Float16, true, 16>);
+    } else {
+        if (nhwc) by_ks(patch_conv_kernel<uint16_t, false, 4>, patch_conv_kernel<uint16_t, false, 8>, patch_conv_kernel<uint16_t, false, 13>, patch_conv_kernel<uint16_t, false, 16>);
+        else by_ks(patch_conv_kernel<uint16_t, true, 4>, patch_conv_kernel<uint16_t, true, 8>, patch_conv_kernel<uint16_t, true, 13>, patch_conv_kernel<uint16_t, true, 16>);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace convlower

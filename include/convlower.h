@@ -62,7 +62,8 @@ typedef enum { CONV_DTYPE_FP32 = 0, CONV_DTYPE_BF16 = 1, CONV_DTYPE_FP16 = 2 } c
  *   AUTO      1x1 stride-1 unpadded, or kernel == whole unpadded input: the
  *             plain-GEMM feed; channels not a whole number of 16-byte chunks
  *             with more than 12 taps: IM2WIN (cells padded to whole chunks)
- *             when that tensor is smaller than im2col; shapes IM2WIN_LDS
+ *             when that tensor is smaller than im2col (PATCH first where
+ *             C_in <= 4 and it applies); shapes IM2WIN_LDS
  *             serves, with more than 64 output channels and at least 256
  *             tiles of 256 x 128: IM2WIN_LDS; otherwise INDIRECT.
  *   INDIRECT  indirection buffer of per-(output pixel, tap) input offsets.
@@ -99,7 +100,15 @@ typedef enum { CONV_DTYPE_FP32 = 0, CONV_DTYPE_BF16 = 1, CONV_DTYPE_FP16 = 2 } c
  *             below 2^31 bytes only, else CONV_ERR_UNSUPPORTED.  Workspace:
  *             for NCHW the channels-last copy of x and OHWI weights; for
  *             NHWC a spare indirection buffer, used only when x or w is not
- *             16-byte aligned (then the call runs the element-gather loop).  */
+ *             16-byte aligned (then the call runs the element-gather loop).
+ *   PATCH     inputs with at most 4 channels: the indirect convolution with
+ *             the input rows of a few output rows staged in LDS (channels
+ *             padded to 4) and each tap's pixel addressed there, so that a
+ *             16-byte MFMA operand chunk is two taps (16-bit types) or one
+ *             (fp32); the weights of 64 output channels stay in registers.
+ *             C_in <= 4, KH*KW <= 64 (16-bit) or 32 (fp32), and the staged
+ *             rows of one output row within 32 KB, else
+ *             CONV_ERR_UNSUPPORTED.  No workspace.  */
 typedef enum {
     CONV_ALGO_AUTO = 0,
     CONV_ALGO_INDIRECT = 1,
@@ -107,7 +116,8 @@ typedef enum {
     CONV_ALGO_GEMM = 3,
     CONV_ALGO_IM2COL = 4,
     CONV_ALGO_DIRECT = 5,
-    CONV_ALGO_IM2WIN_LDS = 6
+    CONV_ALGO_IM2WIN_LDS = 6,
+    CONV_ALGO_PATCH = 7
 } conv_algo_t;
 
 typedef enum {

@@ -53,6 +53,19 @@ def _args(L, layout="NCHW", dtype="bf16", algo="auto"):
     return (L.N, L.C, L.H, L.W, L.Co, L.KH, L.KW, L.stride, L.pad, L.dilation, layout, dtype, algo)
 
 
+def _patch_eligible(L, dtype, Wo):
+    """The small-input-channel kernel applies: C_in <= 4, the weights of all
+    K steps fit its registers (16 steps of 4 taps for 16-bit types, of 2 for
+    fp32), and one output row's staged input rows fit 32 KB."""
+    es = 4 if dtype == "fp32" else 2
+    tps = 2 if dtype == "fp32" else 4
+    if L.C > 4 or -(-(L.KH * L.KW) // tps) > 16:
+        return False
+    win = (Wo - 1) * L.stride + (L.KW - 1) * L.dilation + 1
+    rin = (L.KH - 1) * L.dilation + 1
+    return rin * win * 4 * es <= 32768
+
+
 @pytest.mark.parametrize("name", sorted(LAYERS))
 @pytest.mark.parametrize("layout", ["NCHW", "NHWC"])
 @pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp16"])
@@ -78,7 +91,9 @@ def test_workspace_below_im2col(name, layout, dtype):
         M = L.N * Ho * Wo
         rowwin = (_rowwin_eligible(L, dtype) and L.Co > 64
                   and -(-M // 256) * -(-L.Co // 128) >= 256)
-        if rowwin:
+        if _patch_eligible(L, dtype, Wo):
+            assert auto == 0 == cl.workspace_size(*_args(L, layout, dtype, "patch"))
+        elif rowwin:
             assert auto == cl.workspace_size(*_args(L, layout, dtype, "im2win_lds"))
         else:
             assert auto == (win if padded_win else ind)
@@ -113,9 +128,10 @@ def test_auto_workspace_on_1x1(name):
 @pytest.mark.parametrize("name", ["C3a", "C5a"])
 def test_auto_padded_window(name, dtype, layout):
     """The 7x7 stride-2 stem over 3 channels and the dilated 5x5 layer over
-    37: AUTO's workspace is the window tensor with every (column, kernel
-    row) cell's channels padded to whole 16-byte chunks, plus the weights
-    padded to (kh, kw, the same channel count)."""
+    37: the window tensor with every (column, kernel row) cell's channels
+    padded to whole 16-byte chunks, plus the weights padded to (kh, kw, the
+    same channel count).  AUTO takes it unless the small-input-channel
+    kernel applies (the stem in 16-bit types), which needs no workspace."""
     L = LAYERS[name]
     es = 4 if dtype == "fp32" else 2
     cp = -(-L.C * es // 16) * 16 // es
@@ -123,7 +139,8 @@ def test_auto_padded_window(name, dtype, layout):
     Wwin = (Wo - 1) * L.stride + (L.KW - 1) * L.dilation + 1
     up = lambda v: (v + 255) // 256 * 256
     want = up(L.N * Ho * Wwin * L.KH * cp * es) + up(L.Co * L.KH * L.KW * cp * es)
-    assert cl.workspace_size(*_args(L, layout, dtype, "auto")) == want
+    auto_want = 0 if _patch_eligible(L, dtype, Wo) else want
+    assert cl.workspace_size(*_args(L, layout, dtype, "auto")) == auto_want
     assert cl.workspace_size(*_args(L, layout, dtype, "im2win")) == want
 
 
@@ -260,7 +277,7 @@ def test_invalid_enums_and_null_outputs():
     assert L.conv2d_fwd_workspace_size(*base, 2, 1, 0, ctypes.byref(out)) == INVALID   # layout
     assert L.conv2d_fwd_workspace_size(*base, 0, 7, 0, ctypes.byref(out)) == INVALID   # dtype
     assert L.conv2d_fwd_workspace_size(*base, 0, 1, 9, ctypes.byref(out)) == INVALID   # algo
-    assert L.conv2d_fwd_workspace_size(*base, 0, 1, 7, ctypes.byref(out)) == INVALID   # one past IM2WIN_LDS
+    assert L.conv2d_fwd_workspace_size(*base, 0, 1, 8, ctypes.byref(out)) == INVALID   # one past PATCH
     assert L.conv2d_fwd_workspace_size(*base, 0, 1, -1, ctypes.byref(out)) == INVALID
     assert L.conv2d_fwd_workspace_size(*base, 0, 1, 0, None) == INVALID
 

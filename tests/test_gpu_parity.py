@@ -243,6 +243,47 @@ def test_window_rows_both_block_forms(shape, layout, dtype):
         _assert_parity(yn, y_ref, dn, dtype, f"rowwin forms N={n} C={c}")
 
 
+PATCH_CASES = [
+    # name, N, C, H, W, Co, KH, KW, s, p, d
+    ("c1-3x3", 2, 1, 17, 19, 40, 3, 3, 1, 1, 1),
+    ("c2-5x5-s2-d2", 2, 2, 23, 21, 70, 5, 5, 2, 3, 2),     # two channel tiles, the second ragged
+    ("c3-7x7-s2", 2, 3, 30, 33, 64, 7, 7, 2, 3, 1),        # the stem's shape, small
+    ("c4-1x2", 3, 4, 9, 40, 5, 1, 2, 1, 0, 1),             # 5 output channels, 39-wide rows
+    ("c3-wide-rows", 1, 3, 6, 130, 33, 3, 3, 1, 1, 1),     # 130-wide rows: a ragged last fragment
+    ("c3-odd-planes", 2, 3, 15, 15, 64, 3, 3, 1, 1, 1),    # 225-pixel planes: element stores
+]
+
+
+@pytest.mark.parametrize("case", PATCH_CASES, ids=[c[0] for c in PATCH_CASES])
+@pytest.mark.parametrize("layout", ["NCHW", "NHWC"])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp16"])
+def test_patch_small_channels(case, dtype, layout):
+    """PATCH (inputs with at most four channels, patches staged in LDS)
+    against the whole oracle output: fp32 on integer inputs bit for bit, the
+    16-bit types within the tolerance.  Shapes outside it (fp32 with more
+    than 32 taps) are refused with CONV_ERR_UNSUPPORTED."""
+    from convolution_lowering_amd.workloads import Layer
+    name, N, C, H, W, Co, KH, KW, s, p, d = case
+    L = Layer(name, N, C, H, W, Co, KH, KW, s, p, d, seed=83)
+    if dtype == "fp32" and KH * KW > 32:
+        with pytest.raises(cl.ConvLowerError):
+            cl.workspace_size(N, C, H, W, Co, KH, KW, s, p, d, layout, dtype, "patch")
+        return
+    integer = dtype == "fp32"
+    x, w, b = make_inputs(L, dtype, layout, integer=integer)
+    _say(f"[gpu] patch {name} {dtype} {layout}")
+    assert cl.workspace_size(N, C, H, W, Co, KH, KW, s, p, d, layout, dtype, "patch") == 0
+    y = cl.conv2d_fwd(x.to(DEV), w.to(DEV), b.to(DEV), s, p, d, layout, "patch")
+    torch.cuda.synchronize()
+    xr, wr, br = make_inputs(L, dtype, "NCHW", integer=integer)
+    y_ref, dn = oracle.conv2d(xr, wr, br, s, p, d, oracle.NCHW)
+    yn = _to_nchw(y, layout)
+    if integer:
+        assert np.array_equal(yn.double().cpu().numpy(), y_ref)
+    else:
+        _assert_parity(yn, y_ref, dn, dtype, f"patch {name}")
+
+
 # --- edge cases ----------------------------------------------------------------
 
 EDGE = [
