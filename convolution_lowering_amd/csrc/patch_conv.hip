@@ -280,40 +280,56 @@ __global__ __launch_bounds__(kPatchThreads, 2) void patch_conv_kernel(PatchArgs 
                     obuf_put4(ob + off, v[0], v[1], v[2], v[3]);
                 }
             __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the tile is in the buffer
+            // The fragment's first output: NCHW (n, cob, ho, wo0), whose
+            // channel planes are `plane` apart; NHWC (n, ho, wo0, cob).
+            const long long plane = (long long)g.Ho * g.Wo;
+            S *const yrow = NCHW ? y + ((long long)n * g.Co + cob) * plane + (long long)ho * g.Wo + wo0
+                                 : y + (((long long)n * g.Ho + ho) * g.Wo + wo0) * g.Co + cob;
             if constexpr (NCHW) {
                 constexpr int CPR = 32 * ES / 16;  // 16-byte pieces per channel row
+                constexpr int EPC = 16 / ES;       // elements per piece
+                if (vec_store && npx % EPC == 0) {  // wavefront-uniform: whole pieces only
 #pragma unroll
-                for (int i = 0; i < 64 * CPR / 64; ++i) {
-                    const int c = lane + 64 * i;
-                    const int cl = c / CPR, p0 = (c % CPR) * (16 / ES);
-                    const int co = cob + cl;
-                    if (co >= g.Co || p0 >= npx) continue;
-                    const uint4 d = *(const uint4 *)(ob + cl * ORS + p0 * ES);
-                    S *dst = y + (((long long)n * g.Co + co) * g.Ho + ho) * g.Wo + wo0 + p0;
-                    if (vec_store && p0 + 16 / ES <= npx) {
-                        *(uint4 *)dst = d;
-                    } else {
-                        const S *src = (const S *)&d;
+                    for (int i = 0; i < CPR; ++i) {
+                        const int c = lane + 64 * i;
+                        const int cl = c / CPR, p0 = (c % CPR) * EPC;
+                        const uint4 d = *(const uint4 *)(ob + cl * ORS + p0 * ES);
+                        if (cl < nco && p0 < npx)
+                            *(uint4 *)__builtin_assume_aligned(yrow + (long long)cl * plane + p0, 16) = d;
+                    }
+                } else {
 #pragma unroll
-                        for (int e = 0; e < 16 / ES; ++e)
+                    for (int i = 0; i < CPR; ++i) {
+                        const int c = lane + 64 * i;
+                        const int cl = c / CPR, p0 = (c % CPR) * EPC;
+                        if (cl >= nco) continue;
+                        const S *src = (const S *)(ob + cl * ORS + p0 * ES);
+                        S *dst = yrow + (long long)cl * plane + p0;
+                        for (int e = 0; e < EPC; ++e)
                             if (p0 + e < npx) dst[e] = src[e];
                     }
                 }
             } else {
                 constexpr int CPP = 64 * ES / 16;  // 16-byte pieces per pixel
+                constexpr int EPC = 16 / ES;
+                if (vec_store && nco % EPC == 0) {  // wavefront-uniform: whole pieces only
 #pragma unroll
-                for (int i = 0; i < 32 * CPP / 64; ++i) {
-                    const int c = lane + 64 * i;
-                    const int px = c / CPP, c0 = (c % CPP) * (16 / ES);
-                    if (px >= npx || c0 >= nco) continue;
-                    const uint4 d = *(const uint4 *)(ob + px * ORS + c0 * ES);
-                    S *dst = y + (((long long)n * g.Ho + ho) * g.Wo + wo0 + px) * g.Co + cob + c0;
-                    if (vec_store && c0 + 16 / ES <= nco) {
-                        *(uint4 *)dst = d;
-                    } else {
-                        const S *src = (const S *)&d;
+                    for (int i = 0; i < 32 * CPP / 64; ++i) {
+                        const int c = lane + 64 * i;
+                        const int px = c / CPP, c0 = (c % CPP) * EPC;
+                        const uint4 d = *(const uint4 *)(ob + px * ORS + c0 * ES);
+                        if (px < npx && c0 < nco)
+                            *(uint4 *)__builtin_assume_aligned(yrow + px * g.Co + c0, 16) = d;
+                    }
+                } else {
 #pragma unroll
-                        for (int e = 0; e < 16 / ES; ++e)
+                    for (int i = 0; i < 32 * CPP / 64; ++i) {
+                        const int c = lane + 64 * i;
+                        const int px = c / CPP, c0 = (c % CPP) * EPC;
+                        if (px >= npx) continue;
+                        const S *src = (const S *)(ob + px * ORS + c0 * ES);
+                        S *dst = yrow + px * g.Co + c0;
+                        for (int e = 0; e < EPC; ++e)
                             if (c0 + e < nco) dst[e] = src[e];
                     }
                 }
