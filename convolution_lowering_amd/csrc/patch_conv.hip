@@ -151,72 +151,39 @@ __global__ __launch_bounds__(kPatchThreads, 2) void patch_conv_kernel(PatchArgs 
         // loads SB pixels before it writes any, so their loads overlap.
         constexpr int SB = 8;
         const int npix = P.RIN * P.WIN;
-        if constexpr (NCHW) {
-            // A thread per staged pixel: each channel's loads run along a
-            // plane row, contiguous across the wavefront.
-            for (int base = 0; base < npix; base += kPatchThreads * SB) {
-                float v[SB][4];
+        // A thread per staged pixel, SB pixels' loads before any write (for
+        // NCHW input each channel's loads run along a plane row).
+        for (int base = 0; base < npix; base += kPatchThreads * SB) {
+            float v[SB][4];
 #pragma unroll
-                for (int j = 0; j < SB; ++j) {
-                    const int idx = base + j * kPatchThreads + tid;
-                    const int r = idx / P.WIN, c = idx - r * P.WIN;
-                    const int hi = hi_base + r, wi = c - g.p;
-                    const bool in = idx < npix && hi >= 0 && hi < g.H && wi >= 0 && wi < g.W;
+            for (int j = 0; j < SB; ++j) {
+                const int idx = base + j * kPatchThreads + tid;
+                const int r = idx / P.WIN, c = idx - r * P.WIN;
+                const int hi = hi_base + r, wi = c - g.p;
+                const bool in = idx < npix && hi >= 0 && hi < g.H && wi >= 0 && wi < g.W;
 #pragma unroll
-                    for (int ch = 0; ch < 4; ++ch) {
-                        v[j][ch] = 0.f;
-                        if (in && ch < g.C) {
-                            const long long xi = (((long long)n * g.C + ch) * g.H + hi) * g.W + wi;
-                            if constexpr (ES == 2)
-                                v[j][ch] = __uint_as_float((uint32_t)raw16(x, xi));  // the raw 16 bits, carried in a float
-                            else
-                                v[j][ch] = ((const float *)x)[xi];
-                        }
-                    }
-                }
-#pragma unroll
-                for (int j = 0; j < SB; ++j) {
-                    const int idx = base + j * kPatchThreads + tid;
-                    if (idx >= npix) continue;
-                    if constexpr (ES == 2) {
-                        const uint32_t b0 = __float_as_uint(v[j][0]), b1 = __float_as_uint(v[j][1]);
-                        const uint32_t b2 = __float_as_uint(v[j][2]), b3 = __float_as_uint(v[j][3]);
-                        *(uint2 *)(sbytes + (size_t)idx * PB) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-                    } else {
-                        *(float4 *)(sbytes + (size_t)idx * PB) = make_float4(v[j][0], v[j][1], v[j][2], v[j][3]);
+                for (int ch = 0; ch < 4; ++ch) {
+                    v[j][ch] = 0.f;
+                    if (in && ch < g.C) {
+                        const long long xi = NCHW ? (((long long)n * g.C + ch) * g.H + hi) * g.W + wi
+                                                  : (((long long)n * g.H + hi) * g.W + wi) * g.C + ch;
+                        if constexpr (ES == 2)
+                            v[j][ch] = __uint_as_float((uint32_t)raw16(x, xi));  // the raw 16 bits, carried in a float
+                        else
+                            v[j][ch] = ((const float *)x)[xi];
                     }
                 }
             }
-        } else {
-            // A thread per (pixel, channel) slot: along a staged row the
-            // channels-last input is read nearly contiguously.
-            const int nslot = npix * 4;
-            for (int base = 0; base < nslot; base += kPatchThreads * SB) {
-                uint32_t v[SB];
 #pragma unroll
-                for (int j = 0; j < SB; ++j) {
-                    const int sl = base + j * kPatchThreads + tid;
-                    const int idx = sl >> 2, ch = sl & 3;
-                    const int r = idx / P.WIN, c = idx - r * P.WIN;
-                    const int hi = hi_base + r, wi = c - g.p;
-                    const bool in = sl < nslot && ch < g.C && hi >= 0 && hi < g.H && wi >= 0 && wi < g.W;
-                    v[j] = 0u;
-                    if (in) {
-                        const long long xi = (((long long)n * g.H + hi) * g.W + wi) * g.C + ch;
-                        if constexpr (ES == 2)
-                            v[j] = raw16(x, xi);
-                        else
-                            v[j] = __float_as_uint(((const float *)x)[xi]);
-                    }
-                }
-#pragma unroll
-                for (int j = 0; j < SB; ++j) {
-                    const int sl = base + j * kPatchThreads + tid;
-                    if (sl >= nslot) continue;
-                    if constexpr (ES == 2)
-                        *(uint16_t *)(sbytes + (size_t)sl * 2) = (uint16_t)v[j];
-                    else
-                        *(uint32_t *)(sbytes + (size_t)sl * 4) = v[j];
+            for (int j = 0; j < SB; ++j) {
+                const int idx = base + j * kPatchThreads + tid;
+                if (idx >= npix) continue;
+                if constexpr (ES == 2) {
+                    const uint32_t b0 = __float_as_uint(v[j][0]), b1 = __float_as_uint(v[j][1]);
+                    const uint32_t b2 = __float_as_uint(v[j][2]), b3 = __float_as_uint(v[j][3]);
+                    *(uint2 *)(sbytes + (size_t)idx * PB) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+                } else {
+                    *(float4 *)(sbytes + (size_t)idx * PB) = make_float4(v[j][0], v[j][1], v[j][2], v[j][3]);
                 }
             }
         }
