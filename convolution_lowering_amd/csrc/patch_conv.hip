@@ -84,7 +84,9 @@ __global__ __launch_bounds__(kPatchThreads, 2) void patch_conv_kernel(PatchArgs 
     // output channel cob + 32*ic + col, the channels 0..3 of taps
     // ks*TPS + half*TPC .. +TPC-1 (zero past C_in, past the last tap and past
     // C_out).
-    uint4 bw[KS][2];
+    // Weights in LDS, one copy for the block: registers stay free for the
+    // next unit's input loads.
+    __shared__ uint4 wlds[KS * 2 * 64];
     // Byte offset (within the stage) of each of this lane's taps relative to
     // its output pixel's first tap, 16 bits per tap (the stage is 32 KB),
     // 0xFFFF for a tap past the last.
@@ -100,34 +102,38 @@ __global__ __launch_bounds__(kPatchThreads, 2) void patch_conv_kernel(PatchArgs 
                                    : 0xFFFFu;
             toff[ks] |= o << (16 * tt);
         }
+    }
+    // B fragment of K step ks, channel half ic for this lane: the channels
+    // 0..3 of taps ks*TPS + half*TPC .. +TPC-1 of output channel
+    // cob + 32*ic + col (zero past C_in, past the last tap and past C_out).
+    auto wfrag = [&](int ks, int ic) {
+        const int co = cob + 32 * ic + col;
+        uint32_t wv[4] = {0u, 0u, 0u, 0u};
+        if (ks < P.ksteps && co < g.Co) {
 #pragma unroll
-        for (int ic = 0; ic < 2; ++ic) {
-            const int co = cob + 32 * ic + col;
-            uint32_t wv[4] = {0u, 0u, 0u, 0u};
-            if (ks < P.ksteps && co < g.Co) {
+            for (int tt = 0; tt < TPC; ++tt) {
+                const int t = ks * TPS + half * TPC + tt;
+                if (t >= T) continue;
+                const int kh = t / g.KW, kw = t % g.KW;
 #pragma unroll
-                for (int tt = 0; tt < TPC; ++tt) {
-                    const int t = ks * TPS + half * TPC + tt;
-                    if (t >= T) continue;
-                    const int kh = t / g.KW, kw = t % g.KW;
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        if (c >= g.C) continue;
-                        const long long wi = NCHW ? (((long long)co * g.C + c) * g.KH + kh) * g.KW + kw
-                                                  : (((long long)co * g.KH + kh) * g.KW + kw) * g.C + c;
-                        if constexpr (ES == 2) {
-                            const uint32_t v = raw16(w, wi);
-                            const int e = tt * 4 + c;  // element of the 8 in the chunk
-                            wv[e >> 1] |= v << (16 * (e & 1));
-                        } else {
-                            wv[c] = __float_as_uint(((const float *)w)[wi]);
-                        }
+                for (int c = 0; c < 4; ++c) {
+                    if (c >= g.C) continue;
+                    const long long wi = NCHW ? (((long long)co * g.C + c) * g.KH + kh) * g.KW + kw
+                                              : (((long long)co * g.KH + kh) * g.KW + kw) * g.C + c;
+                    if constexpr (ES == 2) {
+                        const uint32_t v = raw16(w, wi);
+                        const int e = tt * 4 + c;  // element of the 8 in the chunk
+                        wv[e >> 1] |= v << (16 * (e & 1));
+                    } else {
+                        wv[c] = __float_as_uint(((const float *)w)[wi]);
                     }
                 }
             }
-            bw[ks][ic] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
         }
-    }
+        return make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    };
+    for (int ks = wave; ks < KS; ks += kPatchThreads / 64)  // published by the unit loop's first barrier
+        for (int ic = 0; ic < 2; ++ic) wlds[(ks * 2 + ic) * 64 + lane] = wfrag(ks, ic);
 
     if (tid < 64) {
         const int co = cob + tid;
@@ -139,54 +145,66 @@ __global__ __launch_bounds__(kPatchThreads, 2) void patch_conv_kernel(PatchArgs 
     const bool vec_store = NCHW ? ((g.Wo * ES) % 16 == 0 && (uintptr_t)y % 16 == 0)
                                 : ((g.Co * ES) % 16 == 0 && (uintptr_t)y % 16 == 0);
 
+    // ---- staging: pixel (r, c) of unit u's stage is x[n][hi_base + r][c - p],
+    // channels 0..3, zeros outside the image and past C_in.  A thread loads
+    // SB pixels (for NCHW input each channel's loads run along a plane row)
+    // before it writes any; the first SB pixels of the next unit are loaded
+    // while the current one is multiplied.
+    constexpr int SB = 12;
+    const int npix = P.RIN * P.WIN;
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    // 16-bit types: two channels per register (loaded into its halves);
+    // fp32: one per register.
+    u16x2 hv[ES == 2 ? SB : 1][2];
+    float v[ES == 2 ? 1 : SB][4];
+    auto load_batch = [&](int u, int base) {
+        const int n = u / P.hgroups;
+        const int hi_base = (u - n * P.hgroups) * P.R * g.s - g.p;
+#pragma unroll
+        for (int j = 0; j < SB; ++j) {
+            const int idx = base + j * kPatchThreads + tid;
+            const int r = idx / P.WIN, c = idx - r * P.WIN;
+            const int hi = hi_base + r, wi = c - g.p;
+            const bool in = idx < npix && hi >= 0 && hi < g.H && wi >= 0 && wi < g.W;
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch) {
+                const long long xi = NCHW ? (((long long)n * g.C + ch) * g.H + hi) * g.W + wi
+                                          : (((long long)n * g.H + hi) * g.W + wi) * g.C + ch;
+                const bool ld = in && ch < g.C;
+                if constexpr (ES == 2)
+                    hv[j][ch >> 1][ch & 1] = ld ? raw16(x, xi) : (unsigned short)0;
+                else
+                    v[j][ch] = ld ? ((const float *)x)[xi] : 0.f;
+            }
+        }
+    };
+    auto write_batch = [&](int base) {
+#pragma unroll
+        for (int j = 0; j < SB; ++j) {
+            const int idx = base + j * kPatchThreads + tid;
+            if (idx >= npix) continue;
+            if constexpr (ES == 2) {
+                *(uint2 *)(sbytes + (size_t)idx * PB) =
+                    make_uint2(__builtin_bit_cast(uint32_t, hv[j][0]), __builtin_bit_cast(uint32_t, hv[j][1]));
+            } else {
+                *(float4 *)(sbytes + (size_t)idx * PB) = make_float4(v[j][0], v[j][1], v[j][2], v[j][3]);
+            }
+        }
+    };
+
+    if (blockIdx.x < (unsigned)P.units) load_batch(blockIdx.x, 0);
     for (int u = blockIdx.x; u < P.units; u += gridDim.x) {
         const int n = u / P.hgroups;
         const int ho0 = (u - n * P.hgroups) * P.R;
         const int rows = min(P.R, g.Ho - ho0);
-        const int hi_base = ho0 * g.s - g.p;
 
         __syncthreads();  // the previous unit's reads of the stage are done
-        // ---- stage the input rows: pixel (r, c) = x[n][hi_base + r][c - p],
-        // channels 0..3, zeros outside the image and past C_in.  Each thread
-        // loads SB pixels before it writes any, so their loads overlap.
-        constexpr int SB = 8;
-        const int npix = P.RIN * P.WIN;
-        // A thread per staged pixel, SB pixels' loads before any write (for
-        // NCHW input each channel's loads run along a plane row).
-        for (int base = 0; base < npix; base += kPatchThreads * SB) {
-            float v[SB][4];
-#pragma unroll
-            for (int j = 0; j < SB; ++j) {
-                const int idx = base + j * kPatchThreads + tid;
-                const int r = idx / P.WIN, c = idx - r * P.WIN;
-                const int hi = hi_base + r, wi = c - g.p;
-                const bool in = idx < npix && hi >= 0 && hi < g.H && wi >= 0 && wi < g.W;
-#pragma unroll
-                for (int ch = 0; ch < 4; ++ch) {
-                    v[j][ch] = 0.f;
-                    if (in && ch < g.C) {
-                        const long long xi = NCHW ? (((long long)n * g.C + ch) * g.H + hi) * g.W + wi
-                                                  : (((long long)n * g.H + hi) * g.W + wi) * g.C + ch;
-                        if constexpr (ES == 2)
-                            v[j][ch] = __uint_as_float((uint32_t)raw16(x, xi));  // the raw 16 bits, carried in a float
-                        else
-                            v[j][ch] = ((const float *)x)[xi];
-                    }
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < SB; ++j) {
-                const int idx = base + j * kPatchThreads + tid;
-                if (idx >= npix) continue;
-                if constexpr (ES == 2) {
-                    const uint32_t b0 = __float_as_uint(v[j][0]), b1 = __float_as_uint(v[j][1]);
-                    const uint32_t b2 = __float_as_uint(v[j][2]), b3 = __float_as_uint(v[j][3]);
-                    *(uint2 *)(sbytes + (size_t)idx * PB) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-                } else {
-                    *(float4 *)(sbytes + (size_t)idx * PB) = make_float4(v[j][0], v[j][1], v[j][2], v[j][3]);
-                }
-            }
+        write_batch(0);
+        for (int base = kPatchThreads * SB; base < npix; base += kPatchThreads * SB) {
+            load_batch(u, base);
+            write_batch(base);
         }
+        if (u + (int)gridDim.x < P.units) load_batch(u + gridDim.x, 0);  // lands while this unit is multiplied
         __syncthreads();
 
         // ---- 32-pixel fragments of the unit's output rows, one wavefront each
@@ -211,10 +229,11 @@ __global__ __launch_bounds__(kPatchThreads, 2) void patch_conv_kernel(PatchArgs 
                     }
 #pragma unroll
                     for (int ic = 0; ic < 2; ++ic) {
+                        const uint4 b = wlds[(ks * 2 + ic) * 64 + lane];
                         if constexpr (NCHW)
-                            MF::mma(a, bw[ks][ic], acc[ic]);  // rows: pixels, columns: channels
+                            MF::mma(a, b, acc[ic]);  // rows: pixels, columns: channels
                         else
-                            MF::mma(bw[ks][ic], a, acc[ic]);  // rows: channels, columns: pixels
+                            MF::mma(b, a, acc[ic]);  // rows: channels, columns: pixels
                     }
                 }
             }
