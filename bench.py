@@ -239,6 +239,8 @@ def main():
         parts = args.only.split(":")
         L = LAYERS[parts[0]]
         row = bench_layer(L, parts[2] if len(parts) > 2 else "bf16", parts[1], "auto", args.steps, args.warmup, flush)
+        if args.calibration_copy:
+            calibration_copy()
         print(json.dumps(row))
         return
 
