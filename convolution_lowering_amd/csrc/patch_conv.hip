@@ -48,7 +48,7 @@ __device__ __forceinline__ uint16_t raw16(const _Float16 *p, long long i) {
     return __builtin_bit_cast(uint16_t, p[i]);
 }
 
-// KS: K steps the kernel holds weights for (4, 8, 13 or 16; the layer's own
+// KS: K steps the kernel holds weights for (3, 4, 8, 13 or 16; the layer's own
 // count P.ksteps is at most that).
 template <typename S, bool NCHW, int KS>
 __global__ __launch_bounds__(kPatchThreads, 2) void patch_conv_kernel(PatchArgs P) {
@@ -215,8 +215,12 @@ __global__ __launch_bounds__(kPatchThreads, 2) void patch_conv_kernel(PatchArgs 
             const int pbase = (r * g.s * P.WIN + wo * g.s) * PB;
             typename MF::acc_t acc[2] = {typename MF::acc_t{}, typename MF::acc_t{}};
 #pragma unroll
+            // Every K step up to the capacity KS, with no test against the
+            // layer's own count: past it the weights are zeros and every tap
+            // reads as zero, so those MFMAs add exact zeros, and the loop
+            // stays one straight block for the accumulators.
             for (int ks = 0; ks < KS; ++ks) {
-                if (ks < P.ksteps) {
+                {
                     uint4 a;
                     const uint32_t o0 = toff[ks] & 0xFFFFu;
                     if constexpr (ES == 2) {
@@ -367,21 +371,22 @@ hipError_t launch_patch_conv(const void *x, const void *w, const void *bias, voi
     const int per_tile = max(1, min(P.units, (2 * cus + ntn - 1) / ntn));
     const dim3 grid((unsigned)per_tile, (unsigned)ntn);
     auto launch = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(kPatchThreads), 0, st, P); };
-    auto by_ks = [&](auto k4, auto k8, auto k13, auto k16) {
-        if (P.ksteps <= 4) launch(k4);
+    auto by_ks = [&](auto k3, auto k4, auto k8, auto k13, auto k16) {
+        if (P.ksteps <= 3) launch(k3);  // 3x3 kernels in 16-bit types
+        else if (P.ksteps <= 4) launch(k4);
         else if (P.ksteps <= 8) launch(k8);
         else if (P.ksteps <= 13) launch(k13);  // 7x7 kernels in 16-bit types
         else launch(k16);
     };
     if (dtype == CONV_DTYPE_FP32) {
-        if (nhwc) by_ks(patch_conv_kernel<float, false, 4>, patch_conv_kernel<float, false, 8>, patch_conv_kernel<float, false, 13>, patch_conv_kernel<float, false, 16>);
-        else by_ks(patch_conv_kernel<float, true, 4>, patch_conv_kernel<float, true, 8>, patch_conv_kernel<float, true, 13>, patch_conv_kernel<float, true, 16>);
+        if (nhwc) by_ks(patch_conv_kernel<float, false, 3>, patch_conv_kernel<float, false, 4>, patch_conv_kernel<float, false, 8>, patch_conv_kernel<float, false, 13>, patch_conv_kernel<float, false, 16>);
+        else by_ks(patch_conv_kernel<float, true, 3>, patch_conv_kernel<float, true, 4>, patch_conv_kernel<float, true, 8>, patch_conv_kernel<float, true, 13>, patch_conv_kernel<float, true, 16>);
     } else if (dtype == CONV_DTYPE_FP16) {
-        if (nhwc) by_ks(patch_conv_kernel<_Float16, false, 4>, patch_conv_kernel<_Float16, false, 8>, patch_conv_kernel<_Float16, false, 13>, patch_conv_kernel<_Float16, false, 16>);
-        else by_ks(patch_conv_kernel<_Float16, true, 4>, patch_conv_kernel<_Float16, true, 8>, patch_conv_kernel<_Float16, true, 13>, patch_conv_kernel<_Float16, true, 16>);
+        if (nhwc) by_ks(patch_conv_kernel<_Float16, false, 3>, patch_conv_kernel<_Float16, false, 4>, patch_conv_kernel<_Float16, false, 8>, patch_conv_kernel<_Float16, false, 13>, patch_conv_kernel<_Float16, false, 16>);
+        else by_ks(patch_conv_kernel<_Float16, true, 3>, patch_conv_kernel<_Float16, true, 4>, patch_conv_kernel<_Float16, true, 8>, patch_conv_kernel<_Float16, true, 13>, patch_conv_kernel<_Float16, true, 16>);
     } else {
-        if (nhwc) by_ks(patch_conv_kernel<uint16_t, false, 4>, patch_conv_kernel<uint16_t, false, 8>, patch_conv_kernel<uint16_t, false, 13>, patch_conv_kernel<uint16_t, false, 16>);
-        else by_ks(patch_conv_kernel<uint16_t, true, 4>, patch_conv_kernel<uint16_t, true, 8>, patch_conv_kernel<uint16_t, true, 13>, patch_conv_kernel<uint16_t, true, 16>);
+        if (nhwc) by_ks(patch_conv_kernel<uint16_t, false, 3>, patch_conv_kernel<uint16_t, false, 4>, patch_conv_kernel<uint16_t, false, 8>, patch_conv_kernel<uint16_t, false, 13>, patch_conv_kernel<uint16_t, false, 16>);
+        else by_ks(patch_conv_kernel<uint16_t, true, 3>, patch_conv_kernel<uint16_t, true, 4>, patch_conv_kernel<uint16_t, true, 8>, patch_conv_kernel<uint16_t, true, 13>, patch_conv_kernel<uint16_t, true, 16>);
     }
     return hipGetLastError();
 }
