@@ -18,7 +18,7 @@
 namespace convlower {
 namespace {
 
-constexpr int kPatchStageBytes = 32 * 1024;  // LDS of the staged input rows
+constexpr int kPatchStageBytes = 24 * 1024;  // LDS of the staged input rows
 constexpr int kPatchMaxKSteps = 16;          // K steps of register-resident weights
 constexpr int kPatchThreads = 256;
 
@@ -50,8 +50,14 @@ __device__ __forceinline__ uint16_t raw16(const _Float16 *p, long long i) {
 
 // KS: K steps the kernel holds weights for (3, 4, 8, 13 or 16; the layer's own
 // count P.ksteps is at most that).
+// Resident blocks per compute unit: three for channels-last output in 16-bit
+// types with at most 4 K steps (registers and LDS allow it there, and it
+// measured faster: C4a 225 -> 198 us, where NCHW output measured slower),
+// else two.  The persistent grid is sized to exactly the resident blocks.
+constexpr int patch_blocks_per_cu(int ks, int es, bool nchw) { return (ks <= 4 && es == 2 && !nchw) ? 3 : 2; }
+
 template <typename S, bool NCHW, int KS>
-__global__ __launch_bounds__(kPatchThreads, 2) void patch_conv_kernel(PatchArgs P) {
+__global__ __launch_bounds__(kPatchThreads, patch_blocks_per_cu(KS, (int)sizeof(S), NCHW)) void patch_conv_kernel(PatchArgs P) {
     using MF = MfmaShape<S, 32>;
     constexpr int ES = (int)sizeof(S);
     auto obuf_put4 = [](char *p, float a, float b, float c, float d) { obuf_put4_impl(S(), p, a, b, c, d); };
@@ -88,7 +94,7 @@ __global__ __launch_bounds__(kPatchThreads, 2) void patch_conv_kernel(PatchArgs 
     // next unit's input loads.
     __shared__ uint4 wlds[KS * 2 * 64];
     // Byte offset (within the stage) of each of this lane's taps relative to
-    // its output pixel's first tap, 16 bits per tap (the stage is 32 KB),
+    // its output pixel's first tap, 16 bits per tap (the stage is 24 KB),
     // 0xFFFF for a tap past the last.
     uint32_t toff[KS];
 #pragma unroll
@@ -366,9 +372,10 @@ hipError_t launch_patch_conv(const void *x, const void *w, const void *bias, voi
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return hipErrorInvalidValue;
     const int ntn = (g.Co + 63) / 64;
-    // Two resident blocks per compute unit (register-bound), spread over
-    // the channel tiles.
-    const int per_tile = max(1, min(P.units, (2 * cus + ntn - 1) / ntn));
+    // The resident blocks of all compute units, spread over the channel tiles.
+    const int ks_cap = P.ksteps <= 3 ? 3 : P.ksteps <= 4 ? 4 : P.ksteps <= 8 ? 8 : P.ksteps <= 13 ? 13 : 16;
+    const int per_cu = patch_blocks_per_cu(ks_cap, dtype == CONV_DTYPE_FP32 ? 4 : 2, !nhwc);
+    const int per_tile = max(1, min(P.units, (per_cu * cus + ntn - 1) / ntn));
     const dim3 grid((unsigned)per_tile, (unsigned)ntn);
     auto launch = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(kPatchThreads), 0, st, P); };
     auto by_ks = [&](auto k3, auto k4, auto k8, auto k13, auto k16) {

@@ -107,7 +107,7 @@ typedef enum { CONV_DTYPE_FP32 = 0, CONV_DTYPE_BF16 = 1, CONV_DTYPE_FP16 = 2 } c
  *             16-byte MFMA operand chunk is two taps (16-bit types) or one
  *             (fp32); the weights of 64 output channels stay in registers.
  *             C_in <= 4, KH*KW <= 64 (16-bit) or 32 (fp32), and the staged
- *             rows of one output row within 32 KB, else
+ *             rows of one output row within 24 KB, else
  *             CONV_ERR_UNSUPPORTED.  No workspace.  */
 typedef enum {
     CONV_ALGO_AUTO = 0,

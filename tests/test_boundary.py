@@ -56,14 +56,14 @@ def _args(L, layout="NCHW", dtype="bf16", algo="auto"):
 def _patch_eligible(L, dtype, Wo):
     """The small-input-channel kernel applies: C_in <= 4, the weights of all
     K steps fit its registers (16 steps of 4 taps for 16-bit types, of 2 for
-    fp32), and one output row's staged input rows fit 32 KB."""
+    fp32), and one output row's staged input rows fit 24 KB."""
     es = 4 if dtype == "fp32" else 2
     tps = 2 if dtype == "fp32" else 4
     if L.C > 4 or -(-(L.KH * L.KW) // tps) > 16:
         return False
     win = (Wo - 1) * L.stride + (L.KW - 1) * L.dilation + 1
     rin = (L.KH - 1) * L.dilation + 1
-    return rin * win * 4 * es <= 32768
+    return rin * win * 4 * es <= 24576
 
 
 @pytest.mark.parametrize("name", sorted(LAYERS))
