@@ -284,6 +284,34 @@ def test_patch_small_channels(case, dtype, layout):
         _assert_parity(yn, y_ref, dn, dtype, f"patch {name}")
 
 
+@pytest.mark.parametrize("layout", ["NCHW", "NHWC"])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_patch_misaligned_and_twice(layout, dtype):
+    """PATCH with x, w, bias and y one element off 16-byte alignment (its
+    output then goes element by element) meets the parity bar, and two calls
+    on aligned operands write the same bits."""
+    from convolution_lowering_amd.workloads import Layer
+    name, N, C, H, W, Co, KH, KW, s, p, d = ("c3-5x5-s2", 2, 3, 30, 33, 64, 5, 5, 2, 2, 1)
+    L = Layer(name, N, C, H, W, Co, KH, KW, s, p, d, seed=85)
+    x, w, b = make_inputs(L, dtype, layout)
+    _say(f"[gpu] patch misaligned/twice {dtype} {layout}")
+    Ho = oracle.out_size(H, KH, s, p, d)
+    Wo = oracle.out_size(W, KW, s, p, d)
+    shape = (N, Co, Ho, Wo) if layout == "NCHW" else (N, Ho, Wo, Co)
+    y = _misaligned_copy(torch.zeros(shape, dtype=x.dtype))
+    cl.conv2d_fwd(_misaligned_copy(x), _misaligned_copy(w), _misaligned_copy(b), s, p, d, layout, "patch", out=y)
+    torch.cuda.synchronize()
+    xn, wn, bn = make_inputs(L, dtype, "NCHW")
+    y_ref, dn = oracle.conv2d(xn, wn, bn, s, p, d, oracle.NCHW)
+    _assert_parity(_to_nchw(y, layout), y_ref, dn, dtype, f"patch misaligned {dtype} {layout}")
+    xd, wd, bd = x.to(DEV), w.to(DEV), b.to(DEV)
+    y1 = cl.conv2d_fwd(xd, wd, bd, s, p, d, layout, "patch")
+    y2 = cl.conv2d_fwd(xd, wd, bd, s, p, d, layout, "patch")
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16 if dtype == "bf16" else torch.int32),
+                       y2.view(torch.int16 if dtype == "bf16" else torch.int32))
+
+
 # --- edge cases ----------------------------------------------------------------
 
 EDGE = [
@@ -332,13 +360,18 @@ EDGE = [
 @pytest.mark.parametrize("case", EDGE, ids=[e[0] for e in EDGE])
 @pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp16"])
 @pytest.mark.parametrize("layout", ["NCHW", "NHWC"])
-@pytest.mark.parametrize("algo", ["auto", "indirect", "im2win", "im2col", "direct", "im2win_lds"])
+@pytest.mark.parametrize("algo", ["auto", "indirect", "im2win", "im2col", "direct", "im2win_lds", "patch"])
 def test_edge_cases(case, dtype, layout, algo):
     from convolution_lowering_amd.workloads import Layer
     name, N, C, H, W, Co, KH, KW, s, p, d = case
     L = Layer(name, N, C, H, W, Co, KH, KW, s, p, d, seed=77)
     if algo == "im2win_lds" and not _rowwin_eligible(L, dtype):
         pytest.skip("shape outside the window-rows-in-LDS loop (refused on the host; CPU-tested)")
+    if algo == "patch":
+        try:
+            cl.workspace_size(N, C, H, W, Co, KH, KW, s, p, d, layout, dtype, "patch")
+        except cl.ConvLowerError:
+            pytest.skip("shape outside PATCH (more than 4 input channels or too many taps; refused on the host)")
     y = _run(L, dtype, layout, algo, N)
     x, w, b = make_inputs(L, dtype, "NCHW")
     y_ref, dn = oracle.conv2d(x, w, b, s, p, d, oracle.NCHW)
