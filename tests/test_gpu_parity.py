@@ -284,6 +284,50 @@ def test_patch_small_channels(case, dtype, layout):
         _assert_parity(yn, y_ref, dn, dtype, f"patch {name}")
 
 
+POINTWISE_CASES = [
+    # name, N, C, H, W, Co
+    ("c64-co72", 3, 64, 7, 9, 72),        # 189 pixel rows (ragged last unit), a second 8-channel chunk
+    ("c128-co40", 2, 128, 5, 13, 40),     # 130 rows, one partial chunk
+    ("c256-co64", 2, 256, 11, 12, 64),    # 264 rows
+    ("c256-co128", 1, 256, 3, 5, 128),    # 15 rows: less than one unit
+    ("c64-co512", 2, 64, 6, 6, 512),      # the most weights the kernel holds (64 KB)
+    ("c256-co120", 4, 256, 9, 7, 120),    # 120 = 64 + 56 channels
+]
+
+
+@pytest.mark.parametrize("case", POINTWISE_CASES, ids=[c[0] for c in POINTWISE_CASES])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("bias", [True, False])
+@pytest.mark.parametrize("shift", [0, 1])
+def test_pointwise_1x1_channels_last(case, dtype, bias, shift):
+    """1x1, unit-stride, unpadded channels-last layers in 16-bit types (the
+    input itself is the GEMM operand) with ragged pixel counts and channel
+    counts off the 64-channel tile, aligned (shift=0) and with x and y one
+    element off 16-byte alignment (shift=1): "auto" and "gemm" against the
+    whole oracle output, and the two calls write the same bits."""
+    from convolution_lowering_amd.workloads import Layer
+    name, N, C, H, W, Co = case
+    L = Layer(name, N, C, H, W, Co, 1, 1, 1, 0, 1, seed=87)
+    x, w, b = make_inputs(L, dtype, "NHWC", bias=bias)
+    _say(f"[gpu] pointwise {name} {dtype} bias={bias} shift={shift}")
+    assert cl.workspace_size(N, C, H, W, Co, 1, 1, 1, 0, 1, "NHWC", dtype, "gemm") == 0
+    if shift:
+        xd = _misaligned_copy(x)
+        y = _misaligned_copy(torch.zeros((N, H, W, Co), dtype=x.dtype))
+    else:
+        xd = x.to(DEV)
+        y = torch.zeros((N, H, W, Co), dtype=x.dtype, device=DEV)
+    bd = b.to(DEV) if b is not None else None
+    cl.conv2d_fwd(xd, w.to(DEV), bd, 1, 0, 1, "NHWC", "auto", out=y)
+    y2 = torch.full_like(y, 7.0)
+    cl.conv2d_fwd(xd, w.to(DEV), bd, 1, 0, 1, "NHWC", "gemm", out=y2)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    xr, wr, br = make_inputs(L, dtype, "NCHW", bias=bias)
+    y_ref, dn = oracle.conv2d(xr, wr, br, 1, 0, 1, oracle.NCHW)
+    _assert_parity(_to_nchw(y, "NHWC"), y_ref, dn, dtype, f"pointwise {name} {dtype}")
+
+
 @pytest.mark.parametrize("layout", ["NCHW", "NHWC"])
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_patch_misaligned_and_twice(layout, dtype):
