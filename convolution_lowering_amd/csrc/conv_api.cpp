@@ -140,11 +140,12 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
                            255 / g.Wo + 2 <= kRowWinMaxSeg &&
                            (long long)g.N * g.C * g.H * g.W * (long long)pl->esize <= kBufMax &&
                            g.K * g.Co * (long long)pl->esize <= kBufMax;
-    // AUTO takes the window rows in LDS where they apply, the output has more
-    // channels than the loop's 64-wide half tile wastes, and the grid gives
-    // every CU a block without splitting K.
-    const bool rowwin_auto = rowwin_ok && g.Co > 64 && t_forced_main_loop == CONV_MAIN_LOOP_AUTO &&
-                             ((g.M + 255) / 256) * ((g.Co + 127) / 128) >= 256;
+    // AUTO takes the window rows in LDS where they apply and the grid gives
+    // every CU a block without splitting K (tiles 256 x 64 up to 64 output
+    // channels, 256 x 128 above).
+    const int rowwin_bn = g.Co <= 64 ? 64 : 128;
+    const bool rowwin_auto = rowwin_ok && t_forced_main_loop == CONV_MAIN_LOOP_AUTO &&
+                             ((g.M + 255) / 256) * ((g.Co + rowwin_bn - 1) / rowwin_bn) >= 256;
     const bool patch_ok = patch_conv_plan(g, pl->dtype, nullptr);
     if (algo == CONV_ALGO_AUTO)
         algo = (whole || one) ? CONV_ALGO_GEMM
@@ -321,7 +322,9 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
         // larger per-tile prologue and epilogue.  Over several rounds, two
         // 256 x 128 blocks per CU leave a shorter last round.
         const long long taps = pl->gm.K / (pl->e16 ? 32 : 16);
-        if (((Mt + 511) / 512) * ((g.Co + 127) / 128) <= 256 && taps >= 72) {
+        if (g.Co <= 64) {
+            pl->tile = TILE_256x64_ROWWIN; BM = 256; BN = 64;
+        } else if (((Mt + 511) / 512) * ((g.Co + 127) / 128) <= 256 && taps >= 72) {
             pl->tile = TILE_512x128_ROWWIN_PP; BM = 512; BN = 128;
         } else {
             pl->tile = TILE_256x128_ROWWIN; BM = 256; BN = 128;
@@ -378,7 +381,8 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     // Split K only where too few tiles leave most CUs idle: the two-wavefront
     // loops keep a CU busy with a single block, and the partials cost a pass
     // over M x Co fp32 values per split.
-    const bool two_wave = wide_slice(pl->tile) || pl->tile == TILE_256x128_ROWWIN || pl->tile == TILE_512x128_ROWWIN_PP;
+    const bool two_wave = wide_slice(pl->tile) || pl->tile == TILE_256x128_ROWWIN || pl->tile == TILE_512x128_ROWWIN_PP ||
+                          pl->tile == TILE_256x64_ROWWIN;
     if (pl->feed != FEED_ROWWIN && blocks < (two_wave ? 64 : 256) && ktiles >= 16) {
         // Enough splits to give every compute unit work, each split at least
         // 4 K tiles, and the whole workspace (partials included) kept below

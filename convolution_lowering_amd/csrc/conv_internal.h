@@ -68,7 +68,8 @@ enum Tile : int {
     TILE_256x256_OCT = 7,
     TILE_256x128_ROWWIN = 8,     // the LDS window-row loop of igemm_rowwin.h (FEED_ROWWIN only)
     TILE_512x128_ROWWIN_PP = 9,  // its one-block-per-CU ping-pong form, igemm_rowwin_pp.h (FEED_ROWWIN only)
-    TILE_COUNT = 10
+    TILE_256x64_ROWWIN = 10,     // its 256 x 64 form for at most 64 output channels (FEED_ROWWIN only)
+    TILE_COUNT = 11
 };
 
 hipError_t launch_igemm_bf16(const GemmArgs &a, int feed, bool out_nchw, bool a_vec, bool b_vec,

@@ -629,6 +629,7 @@ static hipError_t launch_tile(const GemmArgs &a, int tile, int splits, hipStream
     if constexpr (FEED == FEED_ROWWIN) {  // its own loop only, 16-byte rows only
         if constexpr (AVEC) {
             if (tile == TILE_256x128_ROWWIN) return go(igemm_rowwin_kernel<S, OUT_NCHW>, 256, 128, 256);
+            if (tile == TILE_256x64_ROWWIN) return go(igemm_rowwin_kernel<S, OUT_NCHW, 64>, 256, 64, 256);
             if (tile == TILE_512x128_ROWWIN_PP) return go(igemm_rowwin_pp_kernel<S, OUT_NCHW>, 512, 128, 512);
         }
         return hipErrorInvalidValue;

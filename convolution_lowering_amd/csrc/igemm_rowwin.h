@@ -23,10 +23,14 @@ namespace convlower {
 // Stage geometry for KW taps per kernel row.  A tile of 256 consecutive
 // output pixels spans at most kRowWinMaxSeg output rows (the host checks
 // 255 / Wo + 2 against it); each adds KW - 1 pixels to the stage.
-template <typename S, int KW_>
+// BN_: output channels per block tile, 128 (four 128 x 64 wavefront tiles,
+// 2 x 2) or 64 (four 64 x 64 wavefront tiles stacked along M, for layers with
+// at most 64 output channels, which a 128-wide tile would half waste).
+template <typename S, int KW_, int BN_ = 128>
 struct RowWinCfg {
+    static_assert(BN_ == 128 || BN_ == 64, "block tiles 256 x 128 or 256 x 64");
     static constexpr int KW = KW_;
-    static constexpr int BM = 256, BN = 128;
+    static constexpr int BM = 256, BN = BN_;
     static constexpr int ES = (int)sizeof(S);
     static constexpr int VEC = 16 / ES;
     static constexpr int KCH = 4;                    // 16-byte chunks per stage row (one channel slice)
@@ -38,8 +42,8 @@ struct RowWinCfg {
     static constexpr int NA = 2, NB = 4;             // A and B stages
     static constexpr int IPW_A = ROWS_A * KCH / 64 / NW;
     static constexpr int IPW_B = BN * KCH / 64 / NW;
-    static constexpr int WGM = 2, WGN = 2;
-    static constexpr int WPM = BM / WGM, WCN = BN / WGN;  // wavefront tile 128 x 64
+    static constexpr int WGM = BN_ == 128 ? 2 : 4, WGN = BN_ == 128 ? 2 : 1;
+    static constexpr int WPM = BM / WGM, WCN = BN / WGN;  // wavefront tile 128 x 64 or 64 x 64
     static constexpr int MT = 32, TP = WPM / MT, TC = WCN / MT;
     static constexpr int NG = KCH / 2;
     static constexpr int LDS_SLOTS = NA * A_SLOTS + NB * B_SLOTS;
@@ -277,9 +281,9 @@ __device__ __forceinline__ void igemm_rowwin_body(const GemmArgs &A) {
     dual_store<S, OUT_NCHW, C>(A, acc, lds, bias_s, m0, co0, wp, wc, lane, tid);
 }
 
-template <typename S, bool OUT_NCHW>
+template <typename S, bool OUT_NCHW, int BN = 128>
 __global__ __launch_bounds__(256, 2) void igemm_rowwin_kernel(GemmArgs A) {
-    igemm_rowwin_body<S, OUT_NCHW, RowWinCfg<S, 3>>(A);
+    igemm_rowwin_body<S, OUT_NCHW, RowWinCfg<S, 3, BN>>(A);
 }
 
 }  // namespace convlower

@@ -64,8 +64,9 @@ typedef enum { CONV_DTYPE_FP32 = 0, CONV_DTYPE_BF16 = 1, CONV_DTYPE_FP16 = 2 } c
  *             with more than 12 taps: IM2WIN (cells padded to whole chunks)
  *             when that tensor is smaller than im2col (PATCH first where
  *             C_in <= 4 and it applies); shapes IM2WIN_LDS
- *             serves, with more than 64 output channels and at least 256
- *             tiles of 256 x 128: IM2WIN_LDS; otherwise INDIRECT.
+ *             serves with at least 256 of its tiles (256 x 64 up to 64
+ *             output channels, else 256 x 128): IM2WIN_LDS; otherwise
+ *             INDIRECT.
  *   INDIRECT  indirection buffer of per-(output pixel, tap) input offsets.
  *   IM2WIN    window-ordered copy of the input in the workspace (each
  *             (column, kernel row) cell padded to one 16-byte chunk when

@@ -89,8 +89,8 @@ def test_workspace_below_im2col(name, layout, dtype):
         # the window rows in LDS where they apply, with more than 64 output
         # channels and at least 256 tiles of 256 x 128
         M = L.N * Ho * Wo
-        rowwin = (_rowwin_eligible(L, dtype) and L.Co > 64
-                  and -(-M // 256) * -(-L.Co // 128) >= 256)
+        bn = 64 if L.Co <= 64 else 128  # the window-row tile's width
+        rowwin = _rowwin_eligible(L, dtype) and -(-M // 256) * -(-L.Co // bn) >= 256
         if _patch_eligible(L, dtype, Wo):
             assert auto == 0 == cl.workspace_size(*_args(L, layout, dtype, "patch"))
         elif rowwin:

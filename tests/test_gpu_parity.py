@@ -151,6 +151,8 @@ def _full_cases():
     for algo in ("indirect", "im2win"):
         for layout in ("NCHW", "NHWC"):
             out.append(("C2", "bf16", layout, algo))
+    for layout in ("NCHW", "NHWC"):  # the window-row loop's 256 x 64 tile (64 output channels)
+        out.append(("C3c", "bf16", layout, "im2win_lds"))
     return out
 
 
