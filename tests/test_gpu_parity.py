@@ -245,6 +245,41 @@ def test_window_rows_both_block_forms(shape, layout, dtype):
         _assert_parity(yn, y_ref, dn, dtype, f"rowwin forms N={n} C={c}")
 
 
+ROWWIN64_CASES = [
+    # name, N, C, H, W, Co
+    ("co64-ragged", 2, 64, 30, 29, 64),     # 1740 pixels: 7 tiles of 256, the last ragged
+    ("co48", 3, 32, 17, 60, 48),            # 48 of the tile's 64 channels
+    ("co1-wide", 1, 96, 9, 130, 1),         # one output channel, 130-wide rows
+    ("co64-many", 2, 32, 56, 56, 64),       # 25 tiles
+]
+
+
+@pytest.mark.parametrize("case", ROWWIN64_CASES, ids=[c[0] for c in ROWWIN64_CASES])
+@pytest.mark.parametrize("layout", ["NCHW", "NHWC"])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_window_rows_64_wide_tile(case, layout, dtype):
+    """3x3 stride-1 layers with at most 64 output channels take the window-row
+    loop's 256 x 64 block tile under "im2win_lds" (four 64 x 64 wavefront
+    tiles stacked along M).  The whole output is compared: fp32 on integer
+    inputs bit for bit, bf16 within the tolerance."""
+    from convolution_lowering_amd.workloads import Layer
+    name, N, C, H, W, Co = case
+    L = Layer(f"rowwin64-{name}", N, C, H, W, Co, 3, 3, 1, 1, 1, seed=101)
+    assert _rowwin_eligible(L, dtype)
+    integer = dtype == "fp32"
+    x, w, b = make_inputs(L, dtype, layout, integer=integer)
+    _say(f"[gpu] rowwin64 {name} {dtype} {layout}")
+    y = cl.conv2d_fwd(x.to(DEV), w.to(DEV), b.to(DEV), 1, 1, 1, layout, "im2win_lds")
+    torch.cuda.synchronize()
+    xr, wr, br = make_inputs(L, dtype, "NCHW", integer=integer)
+    y_ref, dn = oracle.conv2d(xr, wr, br, 1, 1, 1, oracle.NCHW)
+    yn = _to_nchw(y, layout)
+    if integer:
+        assert np.array_equal(yn.double().cpu().numpy(), y_ref)
+    else:
+        _assert_parity(yn, y_ref, dn, dtype, f"rowwin64 {name}")
+
+
 PATCH_CASES = [
     # name, N, C, H, W, Co, KH, KW, s, p, d
     ("c1-3x3", 2, 1, 17, 19, 40, 3, 3, 1, 1, 1),
