@@ -522,6 +522,9 @@ conv_status_t launch_main(const Plan &pl, GemmArgs &a, hipStream_t s) {
         default: a_vec = false;
     }
     if (pl.force_element) a_vec = false;
+    // A split plan needs its partial-sum region: without it every K slice
+    // would write its own partial sum (plus bias) straight into y.
+    if (pl.splits > 1 && a.part == nullptr) return CONV_ERR_INVALID_ARG;
     bool b_vec = g.K % VEC == 0 && al16(a.b);
     // The vector paths address A and B with 32-bit buffer offsets.
     // The extent of what the A feed reads: the window tensor for im2win
@@ -587,8 +590,11 @@ conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias
     if (pl.chunk_n < g.N) {
         // NCHW 1x1 in parts: each part of the batch is copied channels-last
         // into the same workspace region, then multiplied as a plain GEMM
-        // whose NCHW output lands in that part's slice of y.
+        // whose NCHW output lands in that part's slice of y.  A split plan
+        // reuses one partial-sum region for every part (the parts run one
+        // after another on the stream, each finished by its own reduce).
         void *xc = ws + pl.off_xcl;
+        float *part = pl.splits > 1 ? (float *)(ws + pl.off_part) : nullptr;
         for (int n0 = 0; n0 < g.N; n0 += pl.chunk_n) {
             Geom gc = g;
             gc.N = g.N - n0 < pl.chunk_n ? g.N - n0 : pl.chunk_n;
@@ -602,6 +608,7 @@ conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias
             a.k_per_split = pl.kps;
             a.b = w;
             a.a_src = xc;
+            a.part = part;
             conv_status_t st = launch_main(pl, a, s);
             if (st != CONV_OK) return st;
         }

@@ -313,3 +313,15 @@ def test_oversized_request_is_unsupported():
     out = ctypes.c_size_t()
     code = cl.lib().conv2d_fwd_workspace_size(4096, 512, 512, 512, 64, 3, 3, 1, 1, 1, 0, 1, 0, ctypes.byref(out))
     assert code == UNSUPPORTED
+
+
+@pytest.mark.parametrize("shape,dtype", [((2, 512, 7, 7, 64), "fp32"), ((4, 1024, 7, 7, 128), "bf16")])
+def test_nchw_1x1_halves_plan_split_partials(shape, dtype):
+    """Late-network 1x1 NCHW shapes: the half-batch copy plus split-K
+    partials, all below the im2col footprint (the partials region is the
+    one every half-batch pass reuses)."""
+    N, C, H, W, Co = shape
+    es = 4 if dtype == "fp32" else 2
+    ws = cl.workspace_size(N, C, H, W, Co, 1, 1, 1, 0, 1, "NCHW", dtype, "auto")
+    copy = ((N + 1) // 2) * C * H * W * es
+    assert copy < ws < cl.im2col_bytes(N, C, H, W, 1, 1, 1, 0, 1, dtype)
