@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libconvlower.so")
 LAYOUTS = {"NCHW": 0, "NHWC": 1}
 ALGOS = {"auto": 0, "indirect": 1, "im2win": 2, "gemm": 3, "im2col": 4, "direct": 5, "im2win_lds": 6, "patch": 7}
 DTYPE_CODES = {"fp32": 0, "bf16": 1, "fp16": 2}
+DTYPE_NAMES = {v: k for k, v in DTYPE_CODES.items()}
 STATUS = {0: "CONV_OK", 1: "CONV_ERR_INVALID_ARG", 2: "CONV_ERR_UNSUPPORTED", 3: "CONV_ERR_WORKSPACE",
           4: "CONV_ERR_HIP"}
 
@@ -91,10 +92,20 @@ def _dtype_code(dtype):
     raise TypeError(f"unsupported dtype {dtype}")
 
 
-def _stream_handle(stream, device):
+def _launch_stream(stream, device):
+    """The stream the library launches on: `stream`, else torch's current
+    stream on `device`."""
     import torch
-    s = stream if stream is not None else torch.cuda.current_stream(device)
-    return ctypes.c_void_p(s.cuda_stream)
+    return stream if stream is not None else torch.cuda.current_stream(device)
+
+
+def _on(stream):
+    """Context in which torch allocates on `stream`: a temporary workspace or
+    output made there is returned to that stream's pool when freed, so the
+    caching allocator cannot hand it to work on another stream while the
+    library's kernels on `stream` still use it."""
+    import torch
+    return torch.cuda.stream(stream)
 
 
 def output_size(H, W, KH, KW, stride=1, pad=0, dilation=1):
@@ -165,8 +176,7 @@ def _prepare(x, w, bias, stride, pad, dilation, layout, algo, out, workspace):
         _check_tensor(out, "out", x.dtype, dev)
         if tuple(out.shape) != shape:
             raise ValueError(f"out has shape {tuple(out.shape)}, expected {shape}")
-    need = workspace_size(N, C, H, W, Co, KH, KW, stride, pad, dilation, layout,
-                          "bf16" if dcode else "fp32", algo)
+    need = workspace_size(N, C, H, W, Co, KH, KW, stride, pad, dilation, layout, DTYPE_NAMES[dcode], algo)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
@@ -182,9 +192,12 @@ def conv2d_fwd(x, w, bias=None, stride=1, pad=0, dilation=1, layout="NCHW", algo
     x, w, bias, out: contiguous device tensors of one dtype (float32 or
     bfloat16) in `layout`.  workspace: optional uint8 device tensor of at
     least workspace_size(...) bytes (allocated here when None)."""
-    out, dims, ws_ptr, ws_bytes, _ = _prepare(x, w, bias, stride, pad, dilation, layout, algo, out, workspace)
-    code = lib().conv2d_fwd(x.data_ptr(), w.data_ptr(), bias.data_ptr() if bias is not None else None,
-                            out.data_ptr(), *dims, _stream_handle(stream, x.device), ws_ptr, ws_bytes, ALGOS[algo])
+    st = _launch_stream(stream, x.device)
+    with _on(st):
+        out, dims, ws_ptr, ws_bytes, _ws = _prepare(x, w, bias, stride, pad, dilation, layout, algo, out, workspace)
+        code = lib().conv2d_fwd(x.data_ptr(), w.data_ptr(), bias.data_ptr() if bias is not None else None,
+                                out.data_ptr(), *dims, ctypes.c_void_p(st.cuda_stream), ws_ptr, ws_bytes,
+                                ALGOS[algo])
     _check("conv2d_fwd", code)
     return out
 
@@ -204,19 +217,22 @@ def conv2d_main_loop(lowered, indirection, w_ohwi, bias, out_shape_nchw, stride=
     dcode = _dtype_code(lowered.dtype)
     Ho, Wo = output_size(H, W, KH, KW, stride, pad, dilation)
     shape = (N, Co, Ho, Wo) if out_layout == "NCHW" else (N, Ho, Wo, Co)
-    if out is None:
-        out = torch.empty(shape, dtype=lowered.dtype, device=dev)
-    # The main loop uses only the split-K part of this (for the im2col plan
-    # the query also counts X_col itself).
-    need = workspace_size(N, C, H, W, Co, KH, KW, stride, pad, dilation, "NHWC", "bf16" if dcode else "fp32", algo)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    code = lib().conv2d_main_loop(lowered.data_ptr(), indirection.data_ptr() if indirection is not None else None,
-                                  w_ohwi.data_ptr(), bias.data_ptr() if bias is not None else None, out.data_ptr(),
-                                  N, C, H, W, Co, KH, KW, stride, pad, dilation, ALGOS[algo], LAYOUTS[out_layout],
-                                  dcode, _stream_handle(stream, dev),
-                                  workspace.data_ptr() if workspace is not None else None,
-                                  workspace.numel() if workspace is not None else 0)
+    st = _launch_stream(stream, dev)
+    with _on(st):
+        if out is None:
+            out = torch.empty(shape, dtype=lowered.dtype, device=dev)
+        # The main loop uses only the split-K part of this (for the im2col
+        # plan the query also counts X_col itself).
+        need = workspace_size(N, C, H, W, Co, KH, KW, stride, pad, dilation, "NHWC", DTYPE_NAMES[dcode], algo)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        code = lib().conv2d_main_loop(lowered.data_ptr(),
+                                      indirection.data_ptr() if indirection is not None else None,
+                                      w_ohwi.data_ptr(), bias.data_ptr() if bias is not None else None,
+                                      out.data_ptr(), N, C, H, W, Co, KH, KW, stride, pad, dilation, ALGOS[algo],
+                                      LAYOUTS[out_layout], dcode, ctypes.c_void_p(st.cuda_stream),
+                                      workspace.data_ptr() if workspace is not None else None,
+                                      workspace.numel() if workspace is not None else 0)
     _check("conv2d_main_loop", code)
     return out
 
@@ -225,10 +241,12 @@ def build_indirection(C, H, W, KH, KW, stride=1, pad=0, dilation=1, layout="NCHW
     """The indirection buffer as an int32 [Ho*Wo, KH*KW] device tensor."""
     import torch
     Ho, Wo = output_size(H, W, KH, KW, stride, pad, dilation)
-    buf = torch.empty((Ho * Wo, KH * KW), dtype=torch.int32, device=device)
+    st = _launch_stream(stream, torch.device(device))
+    with _on(st):
+        buf = torch.empty((Ho * Wo, KH * KW), dtype=torch.int32, device=device)
     _check("conv2d_build_indirection",
            lib().conv2d_build_indirection(buf.data_ptr(), C, H, W, KH, KW, stride, pad, dilation,
-                                          LAYOUTS[layout], _stream_handle(stream, buf.device)))
+                                          LAYOUTS[layout], ctypes.c_void_p(st.cuda_stream)))
     return buf
 
 
@@ -242,11 +260,13 @@ def im2win_transform(x, KH, KW, stride=1, pad=0, dilation=1, layout="NCHW", stre
     _check_tensor(x, "x", x.dtype, x.device)
     Ho, Wo = output_size(H, W, KH, KW, stride, pad, dilation)
     Wwin = (Wo - 1) * stride + (KW - 1) * dilation + 1
-    out = torch.empty((N, Ho, Wwin, KH, C), dtype=x.dtype, device=x.device)
+    st = _launch_stream(stream, x.device)
+    with _on(st):
+        out = torch.empty((N, Ho, Wwin, KH, C), dtype=x.dtype, device=x.device)
     _check("conv2d_im2win_transform",
            lib().conv2d_im2win_transform(x.data_ptr(), out.data_ptr(), N, C, H, W, KH, KW, stride, pad,
                                          dilation, LAYOUTS[layout], _dtype_code(x.dtype),
-                                         _stream_handle(stream, x.device)))
+                                         ctypes.c_void_p(st.cuda_stream)))
     return out
 
 
@@ -260,11 +280,13 @@ def im2col_transform(x, KH, KW, stride=1, pad=0, dilation=1, layout="NCHW", stre
         N, H, W, C = x.shape
     _check_tensor(x, "x", x.dtype, x.device)
     Ho, Wo = output_size(H, W, KH, KW, stride, pad, dilation)
-    out = torch.empty((N * Ho * Wo, C * KH * KW), dtype=x.dtype, device=x.device)
+    st = _launch_stream(stream, x.device)
+    with _on(st):
+        out = torch.empty((N * Ho * Wo, C * KH * KW), dtype=x.dtype, device=x.device)
     _check("conv2d_im2col_transform",
            lib().conv2d_im2col_transform(x.data_ptr(), out.data_ptr(), N, C, H, W, KH, KW, stride, pad,
                                          dilation, LAYOUTS[layout], _dtype_code(x.dtype),
-                                         _stream_handle(stream, x.device)))
+                                         ctypes.c_void_p(st.cuda_stream)))
     return out
 
 

@@ -32,10 +32,15 @@
  *   words.  Products are accumulated in fp32; the bias is added in fp32; bf16
  *   results are rounded once, to nearest-even, at the store.
  * Pointers are device pointers (HIP), except where stated.  The caller owns
- *   every buffer; the library allocates nothing, keeps no state between calls,
- *   never synchronises the device, and enqueues all work on `stream` (NULL =
- *   the default stream).  Buffers must not overlap.  Pointers need only the
- *   alignment of their element type.
+ *   every buffer; the library allocates nothing, never synchronises the
+ *   device, and enqueues all work on `stream` (NULL = the default stream).
+ *   Buffers must not overlap.  Pointers need only the alignment of their
+ *   element type.
+ * State kept between calls: only the calling host thread's main-loop
+ *   override (conv2d_force_main_loop, until it is reset to AUTO) and its
+ *   pending request for timing stamps (conv2d_time_next_main_loop, consumed
+ *   by the next main-loop launch), both thread-local and set by nothing else.
+ *   Every other call's result depends on its arguments alone.
  * Errors are returned as conv_status_t; no call launches anything when it
  *   returns an error detected on the host.
  */
