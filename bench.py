@@ -1,22 +1,26 @@
 """Benchmark: forward convolution TFLOPS and roofline fraction on one MI355X.
 
-A step is one conv2d_fwd call -- every step of the path (the lowering
-structure build, the MFMA main loop and its fused epilogue, and any split-K
-finish) -- over one batch of seeded synthetic input that is already resident
-in HBM.  Before each timed step the 256 MB last-level cache (MALL) is
-overwritten, outside the timed interval, so the input really comes from HBM.
-Each step is bracketed by HIP events on the stream the library launches on;
-ms_per_step is their mean.
+Workload of the headline: the VGG-16-shaped set of 3x3 stride-1 pad-1
+layers at N=128 in bf16, NCHW (C_in -> C_out at H=W: 3->64@224, 64->128@112,
+128->256@56, 256->512@28, 512->512@14), each with its own seeded synthetic
+x ~ U[-1,1], Kaiming-normal w and N(0,1) bias, already resident in HBM.  A
+step is one conv2d_fwd call per layer of the set, every step of the path
+inside it (any lowering launch, the MFMA main loop with its fused epilogue,
+any split-K finish).  Before each timed step the 256 MB last-level cache
+(MALL) is overwritten, outside the timed interval, so the inputs come from
+HBM.  Each step, and each layer inside it, is bracketed by HIP events on the
+stream the library launches on.
 
-Headline: the 3x3 stride-1 pad-1 layer N=32, C_in=64, 56x56, C_out=128 in
-bf16, NCHW, algo auto -- the verification layer of "Unifying Convolutions and
-GEMM", section 5.  The JSON line also carries a per-layer table over every
-layer shape (TFLOPS, roofline fraction, workspace vs im2col bytes), the
-dominant kernel's roofline entry (its duration measured with HIP events on
-the main loop alone), and the fp64 oracle's throughput on this host's cores
-over a bounded sample (a baseline only).
+The last line of stdout is one compact JSON object: the set's TFLOPS, the
+per-layer times, the roofline entry of the dominant kernel (the main loop of
+the 64->128@112 layer, timed by events the kernel stamps itself at its start
+and end), and the fp64 oracle's rate on this host's cores over a bounded
+sample of the same workload (a baseline only).  `--layers all` also times
+every layer shape of the shape table under every algorithm, and the main-loop
+ablation, and writes those rows to the file `--rows-out` names (they also go
+to stderr, one per line), never to the last line.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers all|headline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers headline|all] [--rows-out FILE]
 """
 from __future__ import annotations
 
@@ -36,15 +40,22 @@ PEAK = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}  # MI355X dense MFMA, TFL
 HBM_PEAK = 8000.0  # GB/s
 ESIZE = {"bf16": 2, "fp16": 2, "fp32": 4}
 
+HEAD_SET = ("C4a", "C4b", "C4c", "C4d", "C4e")
+HEAD_DTYPE, HEAD_LAYOUT, HEAD_ALGO = "bf16", "NCHW", "auto"
+HEAD_DOMINANT = "C4b"  # the layer whose main loop takes the largest share of a step
+HEAD_WORKLOAD = ("VGG-16-shaped 3x3 s1 p1 layer set, bf16, N=128, NCHW: 3->64@224, 64->128@112, "
+                 "128->256@56, 256->512@28, 512->512@14")
+# Images of each layer of the set the CPU baseline runs the oracle on.
+CPU_SAMPLE_IMAGES = 16
+
 
 def layer_geometry(L):
     import convolution_lowering_amd as cl
-    Ho, Wo = cl.output_size(L.H, L.W, L.KH, L.KW, L.stride, L.pad, L.dilation)
-    return Ho, Wo
+    return cl.output_size(L.H, L.W, L.KH, L.KW, L.stride, L.pad, L.dilation)
 
 
-def layer_flops(L, Ho, Wo):
-    return 2.0 * L.N * L.Co * Ho * Wo * L.C * L.KH * L.KW
+def layer_flops(L, Ho, Wo, n=None):
+    return 2.0 * (L.N if n is None else n) * L.Co * Ho * Wo * L.C * L.KH * L.KW
 
 
 def algorithmic_bytes(L, Ho, Wo, dtype):
@@ -76,83 +87,107 @@ class Flusher:
         self.buf.fill_(self.i)
 
 
-def time_steps(fn, steps, warmup, flush, stamp_main_loop=False):
-    """Mean and minimum milliseconds of fn() over `steps` calls, each between
-    HIP events on torch's current stream (the stream the library launches
-    on).  With stamp_main_loop, also the mean and minimum duration of the
-    main-loop kernel inside each timed call, from events that kernel stamps
-    itself at its start and end (conv2d_time_next_main_loop)."""
+class Prepared:
+    """One layer's device tensors (inputs, output, workspace) and its call."""
+
+    def __init__(self, L, dtype, layout, algo, keep_host_images=0):
+        import torch
+        import convolution_lowering_amd as cl
+        from convolution_lowering_amd.workloads import make_inputs
+        x, w, b = make_inputs(L, dtype, layout)
+        # The first images of the batch, kept on the host for the oracle.
+        self.host = (x[:keep_host_images].clone(), w.clone(), b.clone()) if keep_host_images else None
+        self.L, self.dtype, self.layout, self.algo = L, dtype, layout, algo
+        self.x, self.w, self.b = x.cuda(), w.cuda(), b.cuda()
+        del x, w, b
+        Ho, Wo = layer_geometry(L)
+        self.Ho, self.Wo = Ho, Wo
+        shape = (L.N, L.Co, Ho, Wo) if layout == "NCHW" else (L.N, Ho, Wo, L.Co)
+        self.y = torch.empty(shape, dtype=self.x.dtype, device="cuda")
+        self.ws_bytes = cl.workspace_size(L.N, L.C, L.H, L.W, L.Co, L.KH, L.KW, L.stride, L.pad, L.dilation,
+                                          layout, dtype, algo)
+        self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device="cuda")
+        self.im2col = cl.im2col_bytes(L.N, L.C, L.H, L.W, L.KH, L.KW, L.stride, L.pad, L.dilation, dtype)
+        self.flops = layer_flops(L, Ho, Wo)
+        self.nbytes = algorithmic_bytes(L, Ho, Wo, dtype)
+
+    def __call__(self):
+        import convolution_lowering_amd as cl
+        L = self.L
+        cl.conv2d_fwd(self.x, self.w, self.b, L.stride, L.pad, L.dilation, self.layout, self.algo, out=self.y,
+                      workspace=self.ws[:self.ws_bytes])
+
+
+def time_set(layers, steps, warmup, flush, stamp=None):
+    """Times `steps` steps, each one call per prepared layer in order, with
+    events on torch's current stream (the stream the library launches on)
+    before the step, after every layer and after the step.  Returns the mean
+    and minimum step time and the mean time of each layer, in ms.
+
+    stamp = index of a layer: in every timed step that layer's main-loop
+    kernel stamps two events itself, at its own start and end
+    (conv2d_time_next_main_loop); the mean and minimum of that duration are
+    returned as well."""
     import torch
     import convolution_lowering_amd as cl
     for _ in range(warmup):
-        fn()
+        for p in layers:
+            p()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    n = len(layers)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(steps)]
     kev = []
-    if stamp_main_loop:
+    if stamp is not None:
         kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         for a, b in kev:  # create the device events before the kernel stamps them
             a.record()
             b.record()
         torch.cuda.synchronize()
-    for i, (a, b) in enumerate(ev):
+    for i in range(steps):
         if flush:
             flush()
-        if kev:
-            cl.time_next_main_loop(*kev[i])
-        a.record()
-        fn()
-        b.record()
+        ev[i][0].record()
+        for j, p in enumerate(layers):
+            if stamp == j:
+                cl.time_next_main_loop(*kev[i])
+            p()
+            ev[i][j + 1].record()
     torch.cuda.synchronize()
-    times = [a.elapsed_time(b) for a, b in ev]
-    out = (sum(times) / len(times), min(times))
+    step = [e[0].elapsed_time(e[n]) for e in ev]
+    per_layer = [sum(e[j].elapsed_time(e[j + 1]) for e in ev) / steps for j in range(n)]
+    out = {"ms": sum(step) / steps, "ms_min": min(step), "layer_ms": per_layer}
     if kev:
         kt = [a.elapsed_time(b) for a, b in kev]
-        out += (sum(kt) / len(kt), min(kt))
+        out["kernel_ms"], out["kernel_ms_min"] = sum(kt) / steps, min(kt)
     return out
 
 
-def bench_layer(L, dtype, layout, algo, steps, warmup, flush, stamp_main_loop=False):
-    import torch
-    import convolution_lowering_amd as cl
-    from convolution_lowering_amd.workloads import make_inputs
-    x, w, b = make_inputs(L, dtype, layout)
-    x, w, b = x.cuda(), w.cuda(), b.cuda()
-    Ho, Wo = layer_geometry(L)
-    shape = (L.N, L.Co, Ho, Wo) if layout == "NCHW" else (L.N, Ho, Wo, L.Co)
-    y = torch.empty(shape, dtype=x.dtype, device="cuda")
-    ws_bytes = cl.workspace_size(L.N, L.C, L.H, L.W, L.Co, L.KH, L.KW, L.stride, L.pad, L.dilation, layout, dtype, algo)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
-
-    def step():
-        cl.conv2d_fwd(x, w, b, L.stride, L.pad, L.dilation, layout, algo, out=y, workspace=ws[:ws_bytes])
-
-    ms, ms_min = time_steps(step, steps, warmup, flush)
-    if stamp_main_loop:
-        # A second pass of the same steps in which the main-loop kernel
-        # stamps its own start and end (a launch with stamps takes a few
-        # microseconds longer to dispatch, so the step time above comes from
-        # the pass without them).
-        t = time_steps(step, steps, 0, flush, True)
-    flops = layer_flops(L, Ho, Wo)
-    nbytes = algorithmic_bytes(L, Ho, Wo, dtype)
-    im2col = cl.im2col_bytes(L.N, L.C, L.H, L.W, L.KH, L.KW, L.stride, L.pad, L.dilation, dtype)
-    row = {"layer": L.name, "shape": L.note, "dtype": dtype, "layout": layout, "algo": algo,
-           "ms": ms, "ms_min": ms_min, "tflops": flops / ms / 1e9, "gbps": nbytes / ms / 1e6,
-           "workspace_bytes": ws_bytes, "im2col_bytes": im2col,
-           "workspace_over_im2col": ws_bytes / im2col}
-    row["roofline"] = roofline(flops, nbytes, ms / 1e3, dtype)
-    if stamp_main_loop:
-        row["main_loop_ms"], row["main_loop_ms_min"] = t[2], t[3]
-    del x, w, b, y, ws
+def layer_row(p, ms, ms_min=None):
+    row = {"layer": p.L.name, "shape": p.L.note, "dtype": p.dtype, "layout": p.layout, "algo": p.algo,
+           "ms": ms, "tflops": p.flops / ms / 1e9, "workspace_bytes": p.ws_bytes, "im2col_bytes": p.im2col,
+           "roofline": roofline(p.flops, p.nbytes, ms / 1e3, p.dtype)}
+    if ms_min is not None:
+        row["ms_min"] = ms_min
     return row
 
 
-# The sources the headline main loop (igemm_rowwin_kernel, its epilogue and
+def bench_layer(L, dtype, layout, algo, steps, warmup, flush):
+    """One layer alone (the sweep and the ablation): its row."""
+    import torch
+    p = Prepared(L, dtype, layout, algo)
+    t = time_set([p], steps, warmup, flush)
+    row = layer_row(p, t["ms"], t["ms_min"])
+    del p
+    torch.cuda.empty_cache()
+    return row
+
+
+# The sources the dominant kernel (the window-row main loop, its epilogue and
 # its launch) and the host planner that picks it are built from; a change to
 # any of them invalidates the committed HBM counters of that kernel.
 HEADLINE_SOURCES = ("conv_api.cpp", "conv_internal.h", "igemm_dma.h", "igemm_dual.h", "igemm_impl.h",
                     "igemm_inst.hip", "igemm_rowwin.h")
+TRAFFIC_KEY = "C4b-bf16-NCHW-main-loop"
 
 
 def kernel_source_digest():
@@ -164,7 +199,7 @@ def kernel_source_digest():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload):
+def measured_traffic(key):
     """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it
     was taken on the current kernel sources (else None)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -172,30 +207,31 @@ def measured_traffic(workload):
         return None
     with open(path) as fh:
         rec = json.load(fh)
-    ent = rec.get(workload)
+    ent = rec.get(key)
     if not ent or ent.get("source_digest") != kernel_source_digest():
         return None
     return ent.get("bytes_per_launch")
 
 
-def cpu_baseline(L, dtype, layout, budget_s=10.0):
-    """The fp64 oracle (untuned) on the headline layer's whole batch, repeated
-    until about budget_s seconds have passed (at least once); its mean rate."""
+def cpu_baseline(prepared, layout, budget_s=10.0):
+    """The fp64 oracle (untuned) on the first CPU_SAMPLE_IMAGES images of every
+    layer of the set, the same values the GPU step multiplies, repeated until
+    about budget_s seconds have passed (at least once); its mean rate."""
     import oracle
-    from convolution_lowering_amd.workloads import make_inputs
-    Ho, Wo = layer_geometry(L)
     lay = oracle.NCHW if layout == "NCHW" else oracle.NHWC
-    x, w, b = make_inputs(L, dtype, layout)
-    reps, t = 0, 0.0
+    reps, t, flops = 0, 0.0, 0.0
     while reps == 0 or t < budget_s:
-        t0 = time.perf_counter()
-        oracle.conv2d(x, w, b, L.stride, L.pad, L.dilation, lay, want_norm=False)
-        t += time.perf_counter() - t0
+        for p in prepared:
+            x, w, b = p.host
+            L = p.L
+            t0 = time.perf_counter()
+            oracle.conv2d(x, w, b, L.stride, L.pad, L.dilation, lay, want_norm=False)
+            t += time.perf_counter() - t0
+            flops += layer_flops(L, p.Ho, p.Wo, n=x.shape[0])
         reps += 1
-    flops = layer_flops(L, Ho, Wo) * reps
     return {"value": flops / t / 1e12, "unit": "TFLOPS", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"the whole batch ({L.N} images) of the headline layer, full fp64 output, "
-                      f"{reps} repetition(s), {t:.1f} s"}
+            "sample": f"the first {CPU_SAMPLE_IMAGES} of the 128 images of each of the five layers of the "
+                      f"set (full fp64 output of each), {reps} repetition(s), {t:.1f} s"}
 
 
 def calibration_copy(nbytes=256 << 20):
@@ -210,22 +246,68 @@ def calibration_copy(nbytes=256 << 20):
     torch.cuda.synchronize()
 
 
+def sweep(args, flush, rows_out):
+    """Every layer shape under every algorithm, then the main-loop ablation;
+    rows to stderr and to rows_out."""
+    import torch
+    import convolution_lowering_amd as cl
+    from convolution_lowering_amd.workloads import LAYERS
+    rows, ablation = [], []
+    steps = max(3, args.steps // 4)
+    for name, L in LAYERS.items():
+        for dtype in (L.dtypes + ("fp16",) if name == "C2" else L.dtypes):
+            for layout in ("NCHW", "NHWC"):
+                algos = ["auto", "im2col", "direct", "im2win_lds"]
+                if name == "C2":
+                    algos = ["auto", "indirect", "im2win", "im2col", "direct", "im2win_lds"]
+                for algo in algos:
+                    try:
+                        r = bench_layer(L, dtype, layout, algo, steps, 2, flush)
+                    except cl.ConvLowerError as e:
+                        if algo == "im2win_lds" and e.code == 2:
+                            continue  # shape outside the window-rows-in-LDS loop
+                        r = {"layer": name, "dtype": dtype, "layout": layout, "algo": algo, "error": str(e)}
+                    rows.append(r)
+                    print("# row " + json.dumps(r), file=sys.stderr, flush=True)
+    for name, dtype, layout in (("C2", "bf16", "NCHW"), ("C2", "bf16", "NHWC"), ("C3c", "bf16", "NHWC"),
+                                ("C4d", "bf16", "NHWC")):
+        L = LAYERS[name]
+        for variant in cl.MAIN_LOOPS:
+            cl.force_main_loop(variant)
+            try:
+                r = bench_layer(L, dtype, layout, "auto", steps, 2, flush)
+                a = {"layer": name, "dtype": dtype, "layout": layout, "main_loop": variant, "ms": r["ms"],
+                     "tflops": r["tflops"]}
+            except cl.ConvLowerError as e:
+                a = {"layer": name, "dtype": dtype, "layout": layout, "main_loop": variant, "error": str(e)}
+            finally:
+                cl.force_main_loop("auto")
+            ablation.append(a)
+            print("# ablation " + json.dumps(a), file=sys.stderr, flush=True)
+            torch.cuda.empty_cache()
+    if rows_out:
+        with open(rows_out, "w") as fh:
+            json.dump({"layers": rows, "ablation": ablation}, fh, indent=1)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--layers", choices=["all", "headline"], default="all")
+    ap.add_argument("--layers", choices=["all", "headline"], default="headline",
+                    help="all: also the per-layer sweep over every shape and algorithm, and the ablation")
+    ap.add_argument("--rows-out", metavar="FILE", help="where --layers all writes its rows (JSON)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run one 256 MiB device copy (scale reference for HBM byte counters)")
-    ap.add_argument("--only", metavar="LAYER:LAYOUT[:DTYPE]",
+    ap.add_argument("--only", metavar="LAYER:LAYOUT[:DTYPE[:ALGO]]",
                     help="time only this layer (algo auto, dtype bf16 unless given) and print its row; "
                          "for profiling one layer's kernels")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path (each GPU would run its own "
-              "share of the batch independently; see the sharding notes in DESIGN.md)", file=sys.stderr)
+              "share of the batch independently)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -245,110 +327,77 @@ def main():
     if args.only:
         parts = args.only.split(":")
         L = LAYERS[parts[0]]
-        row = bench_layer(L, parts[2] if len(parts) > 2 else "bf16", parts[1], "auto", args.steps, args.warmup, flush)
+        row = bench_layer(L, parts[2] if len(parts) > 2 else "bf16", parts[1], parts[3] if len(parts) > 3 else "auto",
+                          args.steps, args.warmup, flush)
         if args.calibration_copy:
             calibration_copy()
         print(json.dumps(row))
         return
 
-    H = LAYERS["C2"]
-    head_dtype, head_layout, head_algo = "bf16", "NCHW", "auto"
-    head = bench_layer(H, head_dtype, head_layout, head_algo, args.steps, args.warmup, flush, stamp_main_loop=True)
-    print(f"# headline {H.name} {head_dtype} {head_layout} {head_algo}: {head['ms']:.4f} ms "
-          f"{head['tflops']:.1f} TFLOPS", file=sys.stderr, flush=True)
-    try:  # the graphics clock right after the headline steps (amd-smi through torch)
-        clock_mhz = float(torch.cuda.clock_rate())
-    except Exception:
-        clock_mhz = None
+    keep = 0 if args.no_cpu_baseline else CPU_SAMPLE_IMAGES
+    prepared = [Prepared(LAYERS[n], HEAD_DTYPE, HEAD_LAYOUT, HEAD_ALGO, keep_host_images=keep) for n in HEAD_SET]
+    t = time_set(prepared, args.steps, args.warmup, flush)
+    total_flops = sum(p.flops for p in prepared)
+    per_layer = []
+    for p, ms in zip(prepared, t["layer_ms"]):
+        r = layer_row(p, ms)
+        per_layer.append({"layer": p.L.name, "ms": round(ms, 5), "tflops": round(r["tflops"], 1),
+                          "bound": r["roofline"]["bound"], "frac": round(r["roofline"]["frac"], 4),
+                          "workspace_bytes": p.ws_bytes, "im2col_bytes": p.im2col})
+        print(f"# {p.L.name} {HEAD_DTYPE} {HEAD_LAYOUT} {HEAD_ALGO}: {ms:.4f} ms {r['tflops']:.1f} TFLOPS "
+              f"{r['roofline']['bound']} frac {r['roofline']['frac']:.3f}", file=sys.stderr, flush=True)
+    value = total_flops / t["ms"] / 1e9
+    print(f"# set: {t['ms']:.4f} ms per step, {value:.1f} TFLOPS", file=sys.stderr, flush=True)
 
-    # Roofline entry of the dominant kernel, the main loop with its fused
-    # epilogue: its own duration inside the timed headline steps.
-    ml_ms = head["main_loop_ms"]
-    Ho, Wo = layer_geometry(H)
-    flops = layer_flops(H, Ho, Wo)
-    nbytes = algorithmic_bytes(H, Ho, Wo, head_dtype)
-    rl = roofline(flops, nbytes, ml_ms / 1e3, head_dtype)
-    rl["traffic"] = measured_traffic("C2-bf16-NCHW-main-loop")
-    rl["kernel"] = ("igemm_rowwin_kernel (MFMA implicit-GEMM main loop over window rows staged in LDS + fused "
-                    "bias epilogue)")
-    rl["ms"] = ml_ms
-    rl["timing"] = ("mean of the kernel's own start/end stamps (hipExtLaunchKernel events) over a second "
-                    "timed pass of the headline steps")
-    rl["per_launch_flops"] = flops
-    rl["per_launch_algorithmic_bytes"] = nbytes
-
-    rows = []
-    if args.layers == "all":
-        for name, L in LAYERS.items():
-            # fp16 on the verification layer too (the second 16-bit type)
-            for dtype in (L.dtypes + ("fp16",) if name == "C2" else L.dtypes):
-                for layout in ("NCHW", "NHWC"):
-                    # every layer also through the two baselines: the
-                    # materialised im2col the lowering avoids, and direct
-                    # convolution on the vector ALUs
-                    algos = ["auto", "im2col", "direct", "im2win_lds"]
-                    if name == "C2":
-                        algos = ["auto", "indirect", "im2win", "im2col", "direct", "im2win_lds"]
-                    for algo in algos:
-                        try:
-                            r = bench_layer(L, dtype, layout, algo, max(3, args.steps // 4), 2, flush)
-                        except cl.ConvLowerError as e:
-                            if algo == "im2win_lds" and e.code == 2:
-                                continue  # shape outside the window-rows-in-LDS loop
-                            r = {"layer": name, "dtype": dtype, "layout": layout, "algo": algo, "error": str(e)}
-                        except Exception as e:  # report, keep going
-                            r = {"layer": name, "dtype": dtype, "layout": layout, "algo": algo, "error": str(e)}
-                        rows.append(r)
-                        print(f"# {name} {dtype} {layout} {algo}: "
-                              f"{r.get('ms', float('nan')):.4f} ms {r.get('tflops', float('nan')):.1f} TFLOPS "
-                              f"{r.get('roofline', {}).get('bound', '?')} "
-                              f"frac {r.get('roofline', {}).get('frac', float('nan')):.3f}", file=sys.stderr, flush=True)
-                        torch.cuda.empty_cache()
-
-    # Ablation of the main loop's techniques: every variant forced on a few
-    # layers (same whole-call timing).
-    ablation = []
-    if args.layers == "all":
-        for name, dtype, layout in (("C2", "bf16", "NCHW"), ("C2", "bf16", "NHWC"), ("C3c", "bf16", "NHWC"),
-                                    ("C4d", "bf16", "NHWC")):
-            L = LAYERS[name]
-            for variant in cl.MAIN_LOOPS:
-                cl.force_main_loop(variant)
-                try:
-                    r = bench_layer(L, dtype, layout, "auto", max(3, args.steps // 4), 2, flush)
-                    ablation.append({"layer": name, "dtype": dtype, "layout": layout, "main_loop": variant,
-                                     "ms": r["ms"], "tflops": r["tflops"]})
-                    print(f"# ablation {name} {dtype} {layout} {variant}: {r['ms']:.4f} ms {r['tflops']:.1f} TFLOPS",
-                          file=sys.stderr, flush=True)
-                except cl.ConvLowerError as e:
-                    ablation.append({"layer": name, "dtype": dtype, "layout": layout, "main_loop": variant,
-                                     "error": str(e)})
-                finally:
-                    cl.force_main_loop("auto")
-                torch.cuda.empty_cache()
+    # Roofline entry of the dominant kernel: the main loop (with its fused
+    # epilogue) of the dominant layer, timed by its own start/end stamps over
+    # a second pass of the same steps (a stamped launch takes a few
+    # microseconds longer to dispatch, so the step time comes from the pass
+    # without them).
+    di = HEAD_SET.index(HEAD_DOMINANT)
+    ts = time_set(prepared, args.steps, 0, flush, stamp=di)
+    dom = prepared[di]
+    rl = roofline(dom.flops, dom.nbytes, ts["kernel_ms"] / 1e3, HEAD_DTYPE)
+    rl["traffic"] = measured_traffic(TRAFFIC_KEY)
+    rl["kernel"] = f"main loop of {HEAD_DOMINANT} (MFMA implicit GEMM over window rows staged in LDS + fused epilogue)"
+    rl["kernel_ms"] = ts["kernel_ms"]
+    rl["per_launch_flops"] = dom.flops
+    rl["per_launch_algorithmic_bytes"] = dom.nbytes
+    print(f"# dominant kernel {HEAD_DOMINANT}: {ts['kernel_ms']:.4f} ms, {rl['achieved']:.1f} {rl['unit']}, "
+          f"frac {rl['frac']:.3f}", file=sys.stderr, flush=True)
 
     if args.calibration_copy:
         calibration_copy()
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(H, head_dtype, head_layout)
+        cpu = cpu_baseline(prepared, HEAD_LAYOUT)
+        print(f"# cpu baseline: {cpu['value']:.4f} TFLOPS on {cpu['cores']} threads", file=sys.stderr, flush=True)
+    for p in prepared:
+        p.host = None
+    del prepared
+    torch.cuda.empty_cache()
 
+    if args.layers == "all":
+        sweep(args, flush, args.rows_out)
+
+    print(summary_line(value, t["ms"], args.steps, args.warmup, per_layer, rl, cpu))
+
+
+def summary_line(value, ms_per_step, steps, warmup, per_layer, rl, cpu):
+    """The last stdout line: one compact JSON object (a few KB at most)."""
     line = {
-        "metric": METRIC, "value": head["tflops"], "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": head["ms"], "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": head_dtype,
-        "data": "synthetic (seeded torch CPU generator; x, w, bias ~ N(0,1)), MALL flushed before each step",
-        "config": {"workload": "conv2d fwd 3x3 s1 p1 N=32 C_in=64 56x56 C_out=128 (C2)", "layout": head_layout,
-                   "algo": head_algo, "global_batch": H.N,
-                   "workspace_bytes": head["workspace_bytes"], "im2col_bytes": head["im2col_bytes"]},
+        "metric": METRIC, "value": value, "unit": "TFLOPS", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": HEAD_DTYPE,
+        "data": "synthetic (seeded torch CPU generator; x ~ U[-1,1], Kaiming-normal w, bias ~ N(0,1)), "
+                "MALL flushed before each step",
+        "config": {"workload": HEAD_WORKLOAD, "layout": HEAD_LAYOUT, "algo": HEAD_ALGO, "global_batch": 128,
+                   "step": "one conv2d_fwd call per layer of the set", "per_layer": per_layer},
         "roofline": rl,
-        "gpu_clock_mhz_after_headline": clock_mhz,
         "cpu_baseline": cpu,
-        "layers": rows,
-        "ablation": ablation,
     }
-    print(json.dumps(line))
+    return json.dumps(line)
 
 
 if __name__ == "__main__":
