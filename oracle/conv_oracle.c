@@ -11,9 +11,10 @@
  *   - zero padding `pad` on every side (same page, section 5: F.unfold with
  *     `padding`, and the output-size formula there),
  *   - dilation `dil` between kernel taps (The Indirect Convolution Algorithm,
- *     abstract: "arbitrary kernel size, padding, stride, and dilation"),
- *   - an optional per-output-channel bias (section 5, "Add bias via
- *     broadcasting").
+ *     abstract: dilation is among the convolution parameters its method
+ *     supports, beside kernel size, padding and stride),
+ *   - an optional per-output-channel bias (section 5: the bias vector is
+ *     added to every output pixel of its channel by broadcasting).
  * It is a cross-correlation (no kernel flip), exactly as the loop indexes
  * X[.., ho*stride+kh, ..] * W[.., kh, ..].
  *
