@@ -26,7 +26,11 @@ STATUS = {0: "CONV_OK", 1: "CONV_ERR_INVALID_ARG", 2: "CONV_ERR_UNSUPPORTED", 3:
 # Every symbol include/convlower.h declares.
 EXPORTS = ("conv_status_string", "conv2d_output_size", "conv2d_fwd_workspace_size", "conv2d_im2col_bytes",
            "conv2d_fwd", "conv2d_main_loop", "conv2d_build_indirection", "conv2d_im2win_transform",
-           "conv2d_im2col_transform", "conv2d_force_main_loop", "conv2d_time_next_main_loop")
+           "conv2d_im2col_transform", "conv2d_force_main_loop", "conv2d_time_next_main_loop",
+           "conv2d_fwd_noalloc")
+# Size of the per-GPU scratch array conv2d_fwd_noalloc works in
+# (CONV_NOALLOC_SCRATCH_BYTES of include/convlower.h).
+NOALLOC_SCRATCH_BYTES = 128 << 20
 MAIN_LOOPS = {"auto": 0, "element_128x128": 1, "dma_128x128": 2, "dma_256x128": 3, "dual_256x128": 4,
               "oct_256x128": 5, "oct_256x256": 6, "quad_128x64": 7}
 
@@ -60,6 +64,8 @@ def lib():
     L.conv2d_im2col_bytes.restype = c_int
     L.conv2d_fwd.argtypes = [vp] * 4 + [c_int] * 12 + [vp, vp, c_size, c_int]
     L.conv2d_fwd.restype = c_int
+    L.conv2d_fwd_noalloc.argtypes = [vp] * 4 + [c_int] * 12 + [vp, c_int]
+    L.conv2d_fwd_noalloc.restype = c_int
     L.conv2d_main_loop.argtypes = [vp] * 5 + [c_int] * 13 + [vp, vp, c_size]
     L.conv2d_main_loop.restype = c_int
     L.conv2d_build_indirection.argtypes = [vp] + [c_int] * 9 + [vp]
@@ -199,6 +205,30 @@ def conv2d_fwd(x, w, bias=None, stride=1, pad=0, dilation=1, layout="NCHW", algo
                                 out.data_ptr(), *dims, ctypes.c_void_p(st.cuda_stream), ws_ptr, ws_bytes,
                                 ALGOS[algo])
     _check("conv2d_fwd", code)
+    return out
+
+
+def conv2d_fwd_noalloc(x, w, bias, out, stride=1, pad=0, dilation=1, layout="NCHW", algo="auto", stream=None):
+    """conv2d_fwd_noalloc: the same convolution as conv2d_fwd into the
+    caller's `out`, with the library's per-GPU scratch array as the
+    workspace; nothing is allocated on the way (see include/convlower.h)."""
+    N, C, H, W, Co, KH, KW = _dims(x, w, layout)
+    dev = x.device
+    for t, name in ((x, "x"), (w, "w"), (out, "out")):
+        _check_tensor(t, name, x.dtype, dev)
+    if bias is not None:
+        _check_tensor(bias, "bias", x.dtype, dev)
+        if bias.numel() != Co:
+            raise ValueError("bias must hold C_out values")
+    Ho, Wo = output_size(H, W, KH, KW, stride, pad, dilation)
+    shape = (N, Co, Ho, Wo) if layout == "NCHW" else (N, Ho, Wo, Co)
+    if tuple(out.shape) != shape:
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {shape}")
+    st = _launch_stream(stream, dev)
+    code = lib().conv2d_fwd_noalloc(x.data_ptr(), w.data_ptr(), bias.data_ptr() if bias is not None else None,
+                                    out.data_ptr(), N, C, H, W, Co, KH, KW, stride, pad, dilation, LAYOUTS[layout],
+                                    _dtype_code(x.dtype), ctypes.c_void_p(st.cuda_stream), ALGOS[algo])
+    _check("conv2d_fwd_noalloc", code)
     return out
 
 

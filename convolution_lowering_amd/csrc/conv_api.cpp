@@ -6,6 +6,9 @@
 // workspace query and the launch agree.
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "conv_internal.h"
 
 namespace convlower {
@@ -679,9 +682,61 @@ conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias
     return launch_main(pl, a, s);
 }
 
+// ---- scratch memory of the no-allocation entry point ------------------------
+// One array per GPU, in the library's own device memory, that
+// conv2d_fwd_noalloc uses as its workspace.  In host code `scratch` names a
+// host-side stand-in, not the device array: its device address is looked up
+// once per device (hipGetSymbolAddress, with that device current) and only
+// that address is ever passed to a kernel.
+constexpr size_t kScratchBytes = (size_t)CONV_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The device address of `scratch` on device `dev` (nullptr on a HIP error).
+void *scratch_on(int dev) {
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p) return p;
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+    void *addr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !addr) return nullptr;
+    g_scratch_ptr[dev].store(addr, std::memory_order_release);
+    return addr;
+}
+
 }  // namespace
 
 extern "C" {
+
+conv_status_t conv2d_fwd_noalloc(const void *x, const void *w, const void *bias, void *y, int N, int C_in, int H,
+                                 int W, int C_out, int KH, int KW, int stride, int pad, int dilation,
+                                 conv_layout_t layout, conv_dtype_t dtype, conv_stream_t stream, conv_algo_t algo) {
+    Plan pl;
+    conv_status_t st = make_plan(N, C_in, H, W, C_out, KH, KW, stride, pad, dilation, layout, dtype, algo, &pl);
+    if (st != CONV_OK) return st;
+    if (pl.total > kScratchBytes) return CONV_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (pl.total > 0) {
+        // The device the work runs on: the stream's, or the current one for
+        // the default stream.
+        int dev = -1;
+        const hipError_t e = stream ? hipStreamGetDevice((hipStream_t)stream, &dev) : hipGetDevice(&dev);
+        if (e != hipSuccess) return CONV_ERR_HIP;
+        ws = scratch_on(dev);
+        if (!ws) return CONV_ERR_HIP;
+    }
+    return run(pl, x, w, bias, y, nullptr, stream, ws, ws ? kScratchBytes : 0);
+}
 
 conv_status_t conv2d_fwd(const void *x, const void *w, const void *bias, void *y, int N, int C_in, int H, int W,
                          int C_out, int KH, int KW, int stride, int pad, int dilation, conv_layout_t layout,

@@ -36,11 +36,13 @@
  *   device, and enqueues all work on `stream` (NULL = the default stream).
  *   Buffers must not overlap.  Pointers need only the alignment of their
  *   element type.
- * State kept between calls: only the calling host thread's main-loop
+ * State kept between calls: only (1) the calling host thread's main-loop
  *   override (conv2d_force_main_loop, until it is reset to AUTO) and its
  *   pending request for timing stamps (conv2d_time_next_main_loop, consumed
- *   by the next main-loop launch), both thread-local and set by nothing else.
- *   Every other call's result depends on its arguments alone.
+ *   by the next main-loop launch), both thread-local and set by nothing else;
+ *   and (2) the scratch array of conv2d_fwd_noalloc, one per GPU, and its
+ *   looked-up device address.  Every other call's result depends on its
+ *   arguments alone.
  * Errors are returned as conv_status_t; no call launches anything when it
  *   returns an error detected on the host.
  */
@@ -177,6 +179,30 @@ conv_status_t conv2d_fwd(const void *x, const void *w, const void *bias, void *y
                          int stride, int pad, int dilation,
                          conv_layout_t layout, conv_dtype_t dtype, conv_stream_t stream,
                          void *workspace, size_t workspace_bytes, conv_algo_t algo);
+
+/* conv2d_fwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The workspace is a scratch array of
+ * CONV_NOALLOC_SCRATCH_BYTES bytes that the library holds in each GPU's
+ * memory from the first call on that GPU until the process ends; the call
+ * itself allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine).  The first call on a device looks up that device's array
+ * (hipGetSymbolAddress); later calls do not.
+ *   Arguments, layouts, ownership and errors as for conv2d_fwd (the caller
+ *   still passes x, w, bias and y).  A call whose conv2d_fwd_workspace_size
+ *   exceeds CONV_NOALLOC_SCRATCH_BYTES returns CONV_ERR_WORKSPACE before any
+ *   launch.  The work runs on the device of `stream` (the current device for
+ *   NULL).
+ *   Every call on one GPU shares that GPU's array, which keeps the last
+ *   call's contents; nothing in it has to start at zero.  Calls that overlap
+ *   on one GPU (on different streams, or from different host threads without
+ *   ordering) race on the array and give undefined results: order them. */
+#define CONV_NOALLOC_SCRATCH_BYTES (128u << 20)
+conv_status_t conv2d_fwd_noalloc(const void *x, const void *w, const void *bias, void *y,
+                                 int N, int C_in, int H, int W, int C_out, int KH, int KW,
+                                 int stride, int pad, int dilation,
+                                 conv_layout_t layout, conv_dtype_t dtype, conv_stream_t stream,
+                                 conv_algo_t algo);
 
 /* Steps (c) and (d) alone -- the MFMA main loop and its fused epilogue -- on
  * operands that are already lowered, for callers that keep the lowering

@@ -28,7 +28,7 @@ def _declared_functions():
 
 def test_library_loads_and_exports_every_declared_symbol():
     names = _declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     L = cl.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -313,6 +313,20 @@ def test_oversized_request_is_unsupported():
     out = ctypes.c_size_t()
     code = cl.lib().conv2d_fwd_workspace_size(4096, 512, 512, 512, 64, 3, 3, 1, 1, 1, 0, 1, 0, ctypes.byref(out))
     assert code == UNSUPPORTED
+
+
+def test_noalloc_rejects_a_workspace_past_the_scratch_array():
+    """conv2d_fwd_noalloc refuses, on the host and before any HIP call, a
+    plan whose workspace exceeds its scratch array (the im2col baseline on
+    the 64->128 layer at 112x112 needs 1.85 GB); bad arguments are still
+    INVALID_ARG first."""
+    L = cl.lib()
+    need = cl.workspace_size(128, 64, 112, 112, 128, 3, 3, 1, 1, 1, "NCHW", "bf16", "im2col")
+    assert need > cl.NOALLOC_SCRATCH_BYTES
+    args = (128, 64, 112, 112, 128, 3, 3, 1, 1, 1, 0, 1, None, cl.ALGOS["im2col"])
+    assert L.conv2d_fwd_noalloc(None, None, None, None, *args) == WORKSPACE
+    bad = (128, 64, 112, 112, 128, 3, 3, 0, 1, 1, 0, 1, None, cl.ALGOS["auto"])  # stride 0
+    assert L.conv2d_fwd_noalloc(None, None, None, None, *bad) == INVALID
 
 
 @pytest.mark.parametrize("shape,dtype", [((2, 512, 7, 7, 64), "fp32"), ((4, 1024, 7, 7, 128), "bf16")])
