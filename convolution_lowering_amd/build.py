@@ -36,7 +36,7 @@ def _units():
              ("direct_conv", "direct_conv.hip", []),
              ("patch_conv", "patch_conv.hip", [])]
     for dt, tag in ((1, "bf16"), (2, "f16"), (0, "f32")):  # IGEMM_DTYPE: 0 fp32, 1 bf16, 2 fp16
-        for feed in range(8):  # the Feed values of conv_internal.h
+        for feed in range(9):  # the Feed values of conv_internal.h
             units.append((f"igemm_{tag}_feed{feed}", "igemm_inst.hip",
                           [f"-DIGEMM_DTYPE={dt}", f"-DIGEMM_FEED={feed}"]))
     return units

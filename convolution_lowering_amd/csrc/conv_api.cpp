@@ -6,8 +6,10 @@
 // workspace query and the launch agree.
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
+#include <numeric>
 
 #include "conv_internal.h"
 
@@ -82,6 +84,30 @@ conv_status_t make_geom(int N, int C, int H, int W, int Co, int KH, int KW, int 
     return CONV_OK;
 }
 
+// Raw chunks (8 in-image input columns of one channel, starting at a
+// multiple of 8 columns) the NCHW window-row loop stages per channel for one
+// 256-pixel tile, the most over the layer's tiles.  The count depends only on
+// where a tile starts within its output row -- which repeats every
+// Wo / gcd(256, Wo) tiles -- and, for the last tile, on where M cuts it.
+int rowwin_nchw_chunks(const Geom &g) {
+    const long long Wo = g.Wo, M = g.M;
+    auto tile_chunks = [&](long long m0) {
+        const long long mend = std::min(m0 + 256, M);
+        int total = 0;
+        for (long long R = m0 / Wo; R * Wo < mend; ++R) {
+            const long long first = std::max(m0, R * Wo), last = std::min(mend, (R + 1) * Wo);
+            const int wi0 = (int)(first - R * Wo) - g.p;
+            const int vlo = std::max(wi0, 0), vhi = std::min(wi0 + (int)(last - first) + g.KW - 1, g.W);
+            if (vhi > vlo) total += (vhi - 1) / 8 - vlo / 8 + 1;
+        }
+        return total;
+    };
+    const long long ntiles = (M + 255) / 256, period = Wo / std::gcd(256LL, Wo);
+    int worst = tile_chunks((ntiles - 1) * 256);
+    for (long long t = 0; t < std::min(period, ntiles); ++t) worst = std::max(worst, tile_chunks(t * 256));
+    return worst;
+}
+
 // Element counts of every tensor must stay inside 32-bit signed range (the
 // kernels form 64-bit addresses but index within one image in 32 bits).
 bool sizes_supported(const Geom &g) {
@@ -143,6 +169,18 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
                            255 / g.Wo + 2 <= kRowWinMaxSeg &&
                            (long long)g.N * g.C * g.H * g.W * (long long)pl->esize <= kBufMax &&
                            g.K * g.Co * (long long)pl->esize <= kBufMax;
+    // NCHW input read where it lies by the window-row loop (16-bit types):
+    // every tile's raw chunks must fit the loop's LDS buffer, and an even W
+    // keeps each chunk of a run on 4-byte boundaries of x, so the loads'
+    // per-dword range check never drops an in-image element at the end of x.
+    // The in-place loop transposes each block's input rows in LDS, once for
+    // every 128-channel output tile; the channels-last copy moves x once.
+    // Up to 256 output channels the copy costs more (measured on the 3x3
+    // layers 64->128@56, 64->64@56, 64->128@112, 128->256@56: 4-12% faster
+    // whole calls in place); at 512 it costs less (256->512@28, 512->512@14:
+    // 3-5% slower in place), so wider layers keep the copy.
+    const bool rowwin_inplace = rowwin_ok && !pl->nhwc && pl->e16 && g.W % 2 == 0 && g.Co <= 256 &&
+                                rowwin_nchw_chunks(g) <= kRowWinRawChunks;
     // AUTO takes the window rows in LDS where they apply and the grid gives
     // every CU a block without splitting K (tiles 256 x 64 up to 64 output
     // channels, 256 x 128 above).
@@ -218,6 +256,14 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
             if (pl->nhwc) {
                 // Reserved for the element-gather fallback on misaligned
                 // pointers; not built otherwise.
+                pl->need_ibuf = true;
+            } else if (rowwin_inplace) {
+                // NCHW read where it lies: the weights regrouped tap-major
+                // ([slice][kh][kw][co][32 channels]), and an indirection
+                // buffer reserved for the element-gather fallback on a
+                // misaligned x.
+                pl->feed = FEED_ROWWIN_NCHW;
+                pl->need_wpack = true;
                 pl->need_ibuf = true;
             } else {  // NCHW: the channels-last copy and OHWI weights
                 pl->need_xcl = true;
@@ -318,16 +364,17 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     } else {
         pl->tile = TILE_128x128; BM = 128; BN = 128;
     }
-    if (pl->feed == FEED_ROWWIN) {
+    if (pl->feed == FEED_ROWWIN || pl->feed == FEED_ROWWIN_NCHW) {
         // The ping-pong form (one 512 x 128 block per CU) where all its tiles
         // fit one round on the 256 CUs and the K loop has at least 72 taps
         // (channel slices x KH x KW): its faster taps then outweigh its
         // larger per-tile prologue and epilogue.  Over several rounds, two
-        // 256 x 128 blocks per CU leave a shorter last round.
+        // 256 x 128 blocks per CU leave a shorter last round.  (NCHW input
+        // read in place has the two-block forms only.)
         const long long taps = pl->gm.K / (pl->e16 ? 32 : 16);
         if (g.Co <= 64) {
             pl->tile = TILE_256x64_ROWWIN; BM = 256; BN = 64;
-        } else if (((Mt + 511) / 512) * ((g.Co + 127) / 128) <= 256 && taps >= 72) {
+        } else if (pl->feed == FEED_ROWWIN && ((Mt + 511) / 512) * ((g.Co + 127) / 128) <= 256 && taps >= 72) {
             pl->tile = TILE_512x128_ROWWIN_PP; BM = 512; BN = 128;
         } else {
             pl->tile = TILE_256x128_ROWWIN; BM = 256; BN = 128;
@@ -386,7 +433,7 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     // over M x Co fp32 values per split.
     const bool two_wave = wide_slice(pl->tile) || pl->tile == TILE_256x128_ROWWIN || pl->tile == TILE_512x128_ROWWIN_PP ||
                           pl->tile == TILE_256x64_ROWWIN;
-    if (pl->feed != FEED_ROWWIN && blocks < (two_wave ? 64 : 256) && ktiles >= 16) {
+    if (pl->feed != FEED_ROWWIN && pl->feed != FEED_ROWWIN_NCHW && blocks < (two_wave ? 64 : 256) && ktiles >= 16) {
         // Enough splits to give every compute unit work, each split at least
         // 4 K tiles, and the whole workspace (partials included) kept below
         // the im2col footprint.
@@ -521,7 +568,8 @@ conv_status_t launch_main(const Plan &pl, GemmArgs &a, hipStream_t s) {
         case FEED_WIN: a_vec = g.C % VEC == 0 && al16(a.a_src); break;
         case FEED_IND_CHUNK:
         case FEED_WIN_CHUNK: a_vec = al16(a.a_src) && wide_slice(pl.tile); break;
-        case FEED_ROWWIN: a_vec = al16(a.a_src); break;
+        case FEED_ROWWIN:
+        case FEED_ROWWIN_NCHW: a_vec = al16(a.a_src); break;
         default: a_vec = false;
     }
     if (pl.force_element) a_vec = false;
@@ -633,12 +681,22 @@ conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias
         fb.tile = TILE_128x128;
         return run(fb, x, w, bias, y, prebuilt, stream, workspace, workspace_bytes);
     }
+    if (pl.feed == FEED_ROWWIN_NCHW && (uintptr_t)x % 16) {
+        // An x the window-row loop cannot load in 16-byte chunks: the
+        // element-gather loop through the indirection buffer reserved in the
+        // workspace, with the weights as they lie (K in (ci, kh, kw) order).
+        Plan fb = pl;
+        fb.feed = FEED_IND_NCHW;
+        fb.tile = TILE_128x128;
+        fb.need_wpack = false;
+        return run(fb, x, w, bias, y, prebuilt, stream, workspace, workspace_bytes);
+    }
     // Offsets of the indirection buffer follow the layout the main loop reads.
     const bool ib_rows = pl.feed == FEED_IND_NHWC;
     int32_t *ib_build = nullptr;  // buffer still to build
     if (prebuilt) {
         a.ibuf = prebuilt;
-    } else if (pl.need_ibuf && pl.feed != FEED_ROWWIN) {
+    } else if (pl.need_ibuf && pl.feed != FEED_ROWWIN && pl.feed != FEED_ROWWIN_NCHW) {
         ib_build = (int32_t *)(ws + pl.off_ibuf);
         a.ibuf = ib_build;
     }
@@ -674,7 +732,11 @@ conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias
         a.a_src = xw;
     }
     if (wp) {
-        if (!wp_done && launch_pack_weights_ohwi(w, wp, g, pl.e16, s) != hipSuccess) return CONV_ERR_HIP;
+        if (pl.feed == FEED_ROWWIN_NCHW) {
+            if (launch_pack_weights_tapmajor(w, wp, g, 32, s) != hipSuccess) return CONV_ERR_HIP;
+        } else if (!wp_done && launch_pack_weights_ohwi(w, wp, g, pl.e16, s) != hipSuccess) {
+            return CONV_ERR_HIP;
+        }
         a.b = wp;
     }
     if (pl.splits > 1) a.part = (float *)(ws + pl.off_part);

@@ -24,8 +24,13 @@ enum Feed : int {
     FEED_WIN_CHUNK = 6,  // window-ordered tensor with padded cells
     FEED_ROWWIN = 7,     // channels-last input, each block's window rows staged in LDS (stride 1, dilation 1,
                          // KW = 3); K = (ci slice, kh, kw)
+    FEED_ROWWIN_NCHW = 8,  // the same window rows, read from NCHW input where it lies (16-bit types); K as
+                           // FEED_ROWWIN, weights in (kh, kw, ci) order
 };
-constexpr int kNumFeeds = 8;
+constexpr int kNumFeeds = 9;
+// Raw chunks (8 input columns each) one 256-pixel tile of the NCHW window-row
+// loop stages per channel, at most.
+constexpr int kRowWinRawChunks = 40;
 // Output rows a 256-pixel tile of the LDS window-row loop may span.
 constexpr int kRowWinMaxSeg = 32;
 
@@ -66,9 +71,9 @@ enum Tile : int {
     TILE_256x128_OCT = 5,
     TILE_128x64_QUAD = 6,
     TILE_256x256_OCT = 7,
-    TILE_256x128_ROWWIN = 8,     // the LDS window-row loop of igemm_rowwin.h (FEED_ROWWIN only)
+    TILE_256x128_ROWWIN = 8,     // the LDS window-row loop of igemm_rowwin.h (FEED_ROWWIN[_NCHW] only)
     TILE_512x128_ROWWIN_PP = 9,  // its one-block-per-CU ping-pong form, igemm_rowwin_pp.h (FEED_ROWWIN only)
-    TILE_256x64_ROWWIN = 10,     // its 256 x 64 form for at most 64 output channels (FEED_ROWWIN only)
+    TILE_256x64_ROWWIN = 10,     // its 256 x 64 form for at most 64 output channels (FEED_ROWWIN[_NCHW] only)
     TILE_COUNT = 11
 };
 
@@ -114,6 +119,9 @@ hipError_t launch_im2win_pad(const void *x, void *xwin, const Geom &g, int cp, b
 // with cp channels (from OIHW or OHWI).  Channels past C are zeros.
 hipError_t launch_prep(const void *x, bool nhwc_in, void *x_cl, int cp, int32_t *ib, const void *w, bool w_ohwi,
                        void *w_out, const Geom &g, bool bf16, hipStream_t st);
+// 16-bit OIHW weights regrouped tap-major, [C/bk][KH][KW][Co][bk], for the NCHW
+// window-row loop (C a multiple of bk).
+hipError_t launch_pack_weights_tapmajor(const void *w, void *o, const Geom &g, int bk, hipStream_t st);
 hipError_t launch_pack_weights_ohwi(const void *w_oihw, void *w_ohwi, const Geom &g, bool bf16,
                                     hipStream_t st);
 

@@ -37,6 +37,8 @@ namespace convlower {
 // ... and also every LDS access of this wavefront complete (lgkmcnt 0).
 #define CONVLOWER_WAIT_VMCNT_LDS(n) \
     __builtin_amdgcn_s_waitcnt((((n) & 15) | (7 << 4) | (0 << 8) | (((n) >> 4) << 14)))
+// Only every LDS access of this wavefront complete (vmcnt left at its maximum, 63).
+#define CONVLOWER_WAIT_LDS() CONVLOWER_WAIT_VMCNT_LDS(63)
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 

@@ -633,6 +633,12 @@ static hipError_t launch_tile(const GemmArgs &a, int tile, int splits, hipStream
             if (tile == TILE_512x128_ROWWIN_PP) return go(igemm_rowwin_pp_kernel<S, OUT_NCHW>, 512, 128, 512);
         }
         return hipErrorInvalidValue;
+    } else if constexpr (FEED == FEED_ROWWIN_NCHW) {  // NCHW read in place: 16-bit types, NCHW output
+        if constexpr (AVEC && sizeof(S) == 2 && OUT_NCHW) {
+            if (tile == TILE_256x128_ROWWIN) return go(igemm_rowwin_kernel<S, OUT_NCHW, 128, true>, 256, 128, 256);
+            if (tile == TILE_256x64_ROWWIN) return go(igemm_rowwin_kernel<S, OUT_NCHW, 64, true>, 256, 64, 256);
+        }
+        return hipErrorInvalidValue;
     } else if constexpr (AVEC && (FEED == FEED_IND_CHUNK || FEED == FEED_WIN_CHUNK)) {  // one tap per chunk: the two-wavefront loops only
         switch (tile) {
             case TILE_256x128_DUAL: return go(igemm_dual_kernel<S, FEED, OUT_NCHW>, 256, 128);
@@ -668,10 +674,12 @@ template <typename S, int FEED>
 hipError_t launch_feed(const GemmArgs &a, bool out_nchw, bool a_vec, bool b_vec, int tile, int splits,
                        hipStream_t st) {
     constexpr bool CAN_AVEC = FEED == FEED_ROWMAJOR || FEED == FEED_IND_NHWC || FEED == FEED_WIN ||
-                              FEED == FEED_IND_CHUNK || FEED == FEED_WIN_CHUNK || FEED == FEED_ROWWIN;
+                              FEED == FEED_IND_CHUNK || FEED == FEED_WIN_CHUNK || FEED == FEED_ROWWIN ||
+                              FEED == FEED_ROWWIN_NCHW;
     constexpr bool CAN_NCHW = true;  // every feed can write NCHW output
     constexpr bool CAN_NHWC = FEED == FEED_ROWMAJOR || FEED == FEED_IND_NHWC || FEED == FEED_WIN ||
-                              FEED == FEED_IND_CHUNK || FEED == FEED_WIN_CHUNK || FEED == FEED_ROWWIN;
+                              FEED == FEED_IND_CHUNK || FEED == FEED_WIN_CHUNK || FEED == FEED_ROWWIN ||
+                              FEED == FEED_ROWWIN_NCHW;
     if (a_vec && !b_vec) return hipErrorInvalidValue;
     if (out_nchw) {
         if constexpr (CAN_NCHW) {

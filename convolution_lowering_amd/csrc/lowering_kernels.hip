@@ -521,6 +521,32 @@ hipError_t launch_pack_weights_ohwi(const void *w, void *o, const Geom &g, bool 
     return hipGetLastError();
 }
 
+// OIHW weights regrouped tap-major for the NCHW window-row loop:
+// o[((s*T + t)*Co + co)*bk + c] = w[co][s*bk + c][t] for channel slices s of
+// bk channels (the loop's K tiles), so that the B rows one tap of one slice
+// needs for consecutive output channels are consecutive.  One thread per
+// destination element; sizes are below 2^31 elements.
+template <typename S>
+__global__ __launch_bounds__(256) void pack_tapmajor_kernel(const S *__restrict__ w, S *__restrict__ o, Geom g,
+                                                            int bk) {
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    const int total = g.Co * g.T * g.C;
+    if (e >= total) return;
+    const int c = e % bk;
+    const int r = e / bk;
+    const int co = r % g.Co;
+    const int st = r / g.Co;  // s*T + t
+    const int t = st % g.T, sl = st / g.T;
+    o[e] = w[(co * g.C + sl * bk + c) * g.T + t];
+}
+
+hipError_t launch_pack_weights_tapmajor(const void *w, void *o, const Geom &g, int bk, hipStream_t st) {
+    const long long total = (long long)g.Co * g.T * g.C;
+    hipLaunchKernelGGL(pack_tapmajor_kernel<uint16_t>, dim3(blocks_for(total, 256)), dim3(256), 0, st,
+                       (const uint16_t *)w, (uint16_t *)o, g, bk);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // Split-K finish: y = round(sum over splits, in split order, + bias).  The
 // fixed order keeps the result bit-for-bit repeatable.  Rounding to nearest,

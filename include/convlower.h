@@ -105,10 +105,17 @@ typedef enum { CONV_DTYPE_FP32 = 0, CONV_DTYPE_BF16 = 1, CONV_DTYPE_FP16 = 2 } c
  *             Stride 1, dilation 1, KW = 3, C_in a multiple of 32 (16-bit
  *             types) or 16 (fp32), an output at least 9 pixels wide (a
  *             256-pixel tile then spans at most 32 output rows), x and w
- *             below 2^31 bytes only, else CONV_ERR_UNSUPPORTED.  Workspace:
- *             for NCHW the channels-last copy of x and OHWI weights; for
- *             NHWC a spare indirection buffer, used only when x or w is not
- *             16-byte aligned (then the call runs the element-gather loop).
+ *             below 2^31 bytes only, else CONV_ERR_UNSUPPORTED.  NCHW input
+ *             of a 16-bit type with an even W and at most 256 output
+ *             channels is read where it lies when each 256-pixel tile's
+ *             input runs fit the loop's LDS buffer (at most 40 runs of 8
+ *             in-image columns per channel; true for outputs at least 14
+ *             wide): its workspace is the weights regrouped tap-major plus a
+ *             spare indirection buffer, used only when x is not 16-byte
+ *             aligned (then the element-gather loop runs).  Other NCHW
+ *             input: the channels-last copy of x and OHWI weights.  NHWC: a spare
+ *             indirection buffer, used only when x or w is not 16-byte
+ *             aligned (then the call runs the element-gather loop).
  *   PATCH     inputs with at most 4 channels: the indirect convolution with
  *             the input rows of a few output rows staged in LDS (channels
  *             padded to 4) and each tap's pixel addressed there, so that a

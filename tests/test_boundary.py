@@ -226,9 +226,51 @@ def test_window_rows_in_lds_eligibility_and_workspace(name, dtype):
             assert e.value.code == UNSUPPORTED
         return
     Ho, Wo = cl.output_size(L.H, L.W, L.KH, L.KW, L.stride, L.pad, L.dilation)
-    assert cl.workspace_size(*_args(L, "NHWC", dtype, "im2win_lds")) == up(Ho * Wo * L.KH * L.KW * 4)
-    want = up(L.N * L.C * L.H * L.W * es) + up(L.Co * L.C * L.KH * L.KW * es)
+    ibuf = up(Ho * Wo * L.KH * L.KW * 4)
+    assert cl.workspace_size(*_args(L, "NHWC", dtype, "im2win_lds")) == ibuf
+    if dtype != "fp32" and L.W % 2 == 0 and L.Co <= 256 and _raw_runs(L.N * Ho * Wo, Wo, L.W, L.pad) <= 40:
+        # NCHW read in place: regrouped weights and a spare indirection buffer
+        want = up(L.Co * L.C * L.KH * L.KW * es) + ibuf
+    else:
+        want = up(L.N * L.C * L.H * L.W * es) + up(L.Co * L.C * L.KH * L.KW * es)
     assert cl.workspace_size(*_args(L, "NCHW", dtype, "im2win_lds")) == want
+
+
+def _raw_runs(M, Wo, W, p):
+    """Runs of 8 in-image input columns (starting at multiples of 8) that the
+    busiest 256-pixel tile of a 3-wide window needs per channel: for each
+    output row the tile touches, the in-image part of the columns its
+    windows cover, counted tile by tile."""
+    worst = 0
+    for m0 in range(0, M, 256):
+        mend = min(m0 + 256, M)
+        runs = 0
+        for R in range(m0 // Wo, (mend - 1) // Wo + 1):
+            first, last = max(m0, R * Wo), min(mend, (R + 1) * Wo)
+            lo = first - R * Wo - p
+            hi = lo + (last - first) + 2
+            lo, hi = max(lo, 0), min(hi, W)
+            if hi > lo:
+                runs += len(range(lo // 8, (hi - 1) // 8 + 1))
+        worst = max(worst, runs)
+    return worst
+
+
+@pytest.mark.parametrize("shape", [(2, 32, 16, 16), (3, 32, 18, 14), (1, 64, 20, 30), (2, 32, 12, 12),
+                                   (1, 32, 9, 11), (2, 32, 40, 10)])
+def test_nchw_window_rows_read_in_place_where_runs_fit(shape):
+    """The in-place NCHW form of the window-row loop (16-bit, even W, at most
+    256 output channels, every tile's runs within 40 per channel) needs no
+    copy of x; elsewhere the channels-last copy stays."""
+    N, C, H, W = shape
+    Ho, Wo = cl.output_size(H, W, 3, 3, 1, 1, 1)
+    if 255 // Wo + 2 > 32:
+        pytest.skip("outside the window-row loop")
+    ws = cl.workspace_size(N, C, H, W, 64, 3, 3, 1, 1, 1, "NCHW", "bf16", "im2win_lds")
+    up = lambda v: (v + 255) // 256 * 256
+    inplace = W % 2 == 0 and _raw_runs(N * Ho * Wo, Wo, W, 1) <= 40
+    small = up(64 * C * 9 * 2) + up(Ho * Wo * 9 * 4)
+    assert (ws == small) == inplace, (shape, ws, small)
 
 
 @pytest.mark.parametrize("W,ok", [(7, False), (8, False), (9, True), (10, True)])

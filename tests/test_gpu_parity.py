@@ -745,3 +745,43 @@ def test_nchw_1x1_halves_with_split_k(shape, dtype, integer):
         assert np.array_equal(y.double().cpu().numpy(), y_ref)
     else:
         _assert_parity(y, y_ref, dn, dtype, f"split 1x1 {shape}")
+
+
+# NCHW input read in place by the window-row loop: widths that are and are
+# not multiples of the 8-column load (14, 20, 22, 28, 30, 34), padding 0 and 1,
+# ragged last tiles, one and several channel slices, 64- and 128-wide tiles.
+INPLACE_CASES = [
+    ("w56", 2, 64, 56, 56, 128, 1), ("w14", 3, 64, 14, 14, 64, 1), ("w28", 2, 96, 28, 28, 160, 1),
+    ("w20", 3, 32, 17, 20, 64, 1), ("w30p0", 2, 32, 21, 30, 128, 0), ("w16", 5, 32, 16, 16, 48, 1),
+    ("w112", 1, 32, 112, 112, 64, 1), ("w22", 2, 32, 9, 22, 96, 1), ("w34p0", 2, 32, 11, 34, 64, 0),
+]
+
+
+@pytest.mark.parametrize("case", INPLACE_CASES, ids=[c[0] for c in INPLACE_CASES])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_nchw_window_rows_in_place(case, dtype):
+    """The in-place NCHW path meets the bar against the oracle and equals the
+    NHWC window-row path bit for bit (same K order, same stage contents);
+    integer inputs give the exact result rounded once."""
+    from convolution_lowering_amd.workloads import Layer
+    name, N, C, H, W, Co, p = case
+    L = Layer("inplace", N, C, H, W, Co, 3, 3, 1, p, 1, "normal", "normal", 8100 + C + W, (dtype,))
+    Ho, Wo = cl.output_size(H, W, 3, 3, 1, p, 1)
+    ws = cl.workspace_size(N, C, H, W, Co, 3, 3, 1, p, 1, "NCHW", dtype, "im2win_lds")
+    up = lambda v: (v + 255) // 256 * 256
+    assert ws == up(Co * C * 9 * 2) + up(Ho * Wo * 9 * 4), f"{name}: expected the in-place plan, workspace {ws}"
+    for integer in (False, True):
+        x, w, b = make_inputs(L, dtype, "NCHW", integer=integer)
+        _say(f"[gpu] in-place NCHW {name} {dtype} integer={integer}")
+        y = cl.conv2d_fwd(x.to(DEV), w.to(DEV), b.to(DEV), 1, p, 1, "NCHW", "im2win_lds")
+        xn, wn = x.permute(0, 2, 3, 1).contiguous(), w.permute(0, 2, 3, 1).contiguous()
+        yn = cl.conv2d_fwd(xn.to(DEV), wn.to(DEV), b.to(DEV), 1, p, 1, "NHWC", "im2win_lds")
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), yn.permute(0, 3, 1, 2).contiguous().view(torch.int16)), name
+        y_ref, dn = oracle.conv2d(x, w, b, 1, p, 1, oracle.NCHW)
+        if integer:
+            # the exact result (an integer exact in fp32) rounded once
+            exact = torch.from_numpy(y_ref).float().to(y.dtype).float()
+            assert torch.equal(y.float().cpu(), exact), name
+        else:
+            _assert_parity(y, y_ref, dn, dtype, f"in-place NCHW {name}")
