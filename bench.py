@@ -269,10 +269,9 @@ def sweep(args, flush, rows_out):
                         r = {"layer": name, "dtype": dtype, "layout": layout, "algo": algo, "error": str(e)}
                     rows.append(r)
                     print("# row " + json.dumps(r), file=sys.stderr, flush=True)
-    for name, dtype, layout in (("C2", "bf16", "NCHW"), ("C2", "bf16", "NHWC"), ("C3c", "bf16", "NHWC"),
-                                ("C4d", "bf16", "NHWC")):
+    for name, dtype, layout in (("C2", "bf16", "NHWC"), ("C4b", "bf16", "NHWC"), ("C4d", "bf16", "NHWC")):
         L = LAYERS[name]
-        for variant in cl.MAIN_LOOPS:
+        for variant in list(cl.MAIN_LOOPS) + list(cl.ABLATIONS):
             cl.force_main_loop(variant)
             try:
                 r = bench_layer(L, dtype, layout, "auto", steps, 2, flush)

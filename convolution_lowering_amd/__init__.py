@@ -33,6 +33,9 @@ EXPORTS = ("conv_status_string", "conv2d_output_size", "conv2d_fwd_workspace_siz
 NOALLOC_SCRATCH_BYTES = 128 << 20
 MAIN_LOOPS = {"auto": 0, "element_128x128": 1, "dma_128x128": 2, "dma_256x128": 3, "dual_256x128": 4,
               "oct_256x128": 5, "oct_256x256": 6, "quad_128x64": 7}
+# The ablation loop's variants (CONV_MAIN_LOOP_ABL_*): one technique off each.
+ABLATIONS = {"abl_full": 8, "abl_no_lds": 9, "abl_one_stage": 10, "abl_no_prefetch": 11, "abl_mfma16": 12,
+             "abl_valu": 13, "abl_tile64": 14}
 
 
 class ConvLowerError(RuntimeError):
@@ -323,7 +326,8 @@ def im2col_transform(x, KH, KW, stride=1, pad=0, dilation=1, layout="NCHW", stre
 def force_main_loop(variant="auto"):
     """Force the main-loop variant of this thread's plans (ablation); "auto"
     restores the library's choice (conv2d_force_main_loop)."""
-    _check("conv2d_force_main_loop", lib().conv2d_force_main_loop(MAIN_LOOPS[variant]))
+    code = MAIN_LOOPS[variant] if variant in MAIN_LOOPS else ABLATIONS[variant]
+    _check("conv2d_force_main_loop", lib().conv2d_force_main_loop(code))
 
 
 def time_next_main_loop(start, stop):

@@ -34,7 +34,8 @@ def _units():
              ("igemm_dispatch", "igemm_dispatch.hip", []),
              ("lowering_kernels", "lowering_kernels.hip", []),
              ("direct_conv", "direct_conv.hip", []),
-             ("patch_conv", "patch_conv.hip", [])]
+             ("patch_conv", "patch_conv.hip", []),
+             ("igemm_ablate", "igemm_ablate.hip", [])]
     for dt, tag in ((1, "bf16"), (2, "f16"), (0, "f32")):  # IGEMM_DTYPE: 0 fp32, 1 bf16, 2 fp16
         for feed in range(9):  # the Feed values of conv_internal.h
             units.append((f"igemm_{tag}_feed{feed}", "igemm_inst.hip",

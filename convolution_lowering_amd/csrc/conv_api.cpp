@@ -59,6 +59,7 @@ struct Plan {
     Geom gm;        // geometry the main loop sees (C = cp, K = T*cp)
     bool rows16;  // the feed can read X_col rows in 16-byte chunks (by shape)
     bool force_element;  // main loop forced to the element-gather loop
+    int ablate;          // a CONV_MAIN_LOOP_ABL_ variant forced (0: none)
     size_t off_ibuf, off_win, off_xcl, off_wpack, off_col, off_part, total;
     size_t esize;
 };
@@ -188,6 +189,9 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     const bool rowwin_auto = rowwin_ok && t_forced_main_loop == CONV_MAIN_LOOP_AUTO &&
                              ((g.M + 255) / 256) * ((g.Co + rowwin_bn - 1) / rowwin_bn) >= 256;
     const bool patch_ok = patch_conv_plan(g, pl->dtype, nullptr);
+    // The ablation loops run on the indirection feed only.
+    const bool ablate = t_forced_main_loop >= CONV_MAIN_LOOP_ABL_FULL;
+    if (ablate && algo == CONV_ALGO_AUTO) algo = CONV_ALGO_INDIRECT;
     if (algo == CONV_ALGO_AUTO)
         algo = (whole || one) ? CONV_ALGO_GEMM
                : patch_ok                  ? CONV_ALGO_PATCH
@@ -413,6 +417,18 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
             if (!dual) return CONV_ERR_UNSUPPORTED;
             pl->tile = TILE_128x64_QUAD; BM = 128; BN = 64;
             break;
+        case CONV_MAIN_LOOP_ABL_FULL:
+        case CONV_MAIN_LOOP_ABL_NO_LDS:
+        case CONV_MAIN_LOOP_ABL_ONE_STAGE:
+        case CONV_MAIN_LOOP_ABL_NO_PREFETCH:
+        case CONV_MAIN_LOOP_ABL_MFMA16:
+        case CONV_MAIN_LOOP_ABL_VALU:
+        case CONV_MAIN_LOOP_ABL_TILE64:
+            if (!pl->e16 || pl->feed != FEED_IND_NHWC || pl->gm.C % 32 != 0) return CONV_ERR_UNSUPPORTED;
+            pl->ablate = t_forced_main_loop;
+            pl->tile = TILE_128x128;  // bookkeeping only: the ablation loop has its own tiles
+            BM = BN = t_forced_main_loop == CONV_MAIN_LOOP_ABL_TILE64 ? 64 : 128;
+            break;
         default:
             return CONV_ERR_INVALID_ARG;
     }
@@ -433,7 +449,8 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     // over M x Co fp32 values per split.
     const bool two_wave = wide_slice(pl->tile) || pl->tile == TILE_256x128_ROWWIN || pl->tile == TILE_512x128_ROWWIN_PP ||
                           pl->tile == TILE_256x64_ROWWIN;
-    if (pl->feed != FEED_ROWWIN && pl->feed != FEED_ROWWIN_NCHW && blocks < (two_wave ? 64 : 256) && ktiles >= 16) {
+    if (pl->feed != FEED_ROWWIN && pl->feed != FEED_ROWWIN_NCHW && !pl->ablate && blocks < (two_wave ? 64 : 256) &&
+        ktiles >= 16) {
         // Enough splits to give every compute unit work, each split at least
         // 4 K tiles, and the whole workspace (partials included) kept below
         // the im2col footprint.
@@ -576,6 +593,13 @@ conv_status_t launch_main(const Plan &pl, GemmArgs &a, hipStream_t s) {
     // A split plan needs its partial-sum region: without it every K slice
     // would write its own partial sum (plus bias) straight into y.
     if (pl.splits > 1 && a.part == nullptr) return CONV_ERR_INVALID_ARG;
+    if (pl.ablate) {
+        // The ablation loop loads x and w in 16-byte pieces.
+        if (!al16(a.a_src) || !al16(a.b)) return CONV_ERR_UNSUPPORTED;
+        a.a_bytes = (uint32_t)((long long)g.N * g.C * g.H * g.W * (long long)pl.esize);
+        a.b_bytes = (uint32_t)((long long)g.Co * g.K * (long long)pl.esize);
+        return launch_ablate(a, pl.ablate, pl.out_nchw, pl.dtype, s) == hipSuccess ? CONV_OK : CONV_ERR_HIP;
+    }
     bool b_vec = g.K % VEC == 0 && al16(a.b);
     // The vector paths address A and B with 32-bit buffer offsets.
     // The extent of what the A feed reads: the window tensor for im2win
@@ -839,7 +863,7 @@ conv_status_t conv2d_main_loop(const void *lowered, const int32_t *indirection, 
 }
 
 conv_status_t conv2d_force_main_loop(conv_main_loop_t variant) {
-    if (variant < CONV_MAIN_LOOP_AUTO || variant > CONV_MAIN_LOOP_QUAD_128x64) return CONV_ERR_INVALID_ARG;
+    if (variant < CONV_MAIN_LOOP_AUTO || variant > CONV_MAIN_LOOP_ABL_TILE64) return CONV_ERR_INVALID_ARG;
     t_forced_main_loop = variant;
     return CONV_OK;
 }

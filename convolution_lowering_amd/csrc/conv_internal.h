@@ -105,6 +105,10 @@ hipError_t launch_patch_conv(const void *x, const void *w, const void *bias, voi
 // for NHWC input.
 hipError_t launch_im2col(const void *x, void *xcol, const Geom &g, bool nhwc, bool bf16, hipStream_t st);
 
+// The ablation main loop (igemm_ablate.h): `variant` a CONV_MAIN_LOOP_ABL_
+// value, 16-bit dtype, channels-last input through the NHWC indirection buffer.
+hipError_t launch_ablate(const GemmArgs &a, int variant, bool out_nchw, int dtype, hipStream_t st);
+
 // Events the next main-loop launch of this host thread stamps (null: none);
 // reading them clears the request.
 void take_main_loop_events(hipEvent_t *start, hipEvent_t *stop);

@@ -289,7 +289,22 @@ conv_status_t conv2d_im2col_transform(const void *x, void *xcol, int N, int C_in
  *   OCT_256x128     one 512-thread block per CU, two wavefronts per SIMD,
  *                   wavefront tiles 64 x 64, 128-byte K rows.
  *   OCT_256x256     one 512-thread block per CU, 256 x 256 block tile.
- *   QUAD_128x64     four 256-thread blocks per CU, 128 x 64 block tile.  */
+ *   QUAD_128x64     four 256-thread blocks per CU, 128 x 64 block tile.
+ * The ABL_ variants are one plain implicit-GEMM main loop (indirection
+ * buffer over channels-last input, K tiles of 32 channels of one tap,
+ * 16-bit types, C_in a multiple of 32; AUTO then means INDIRECT) with the
+ * techniques the Im2win abstract ablates switched off one at a time; they
+ * share loads and epilogue, and never split K:
+ *   ABL_FULL        LDS staging, two LDS stages, prefetch (tile k+1's global
+ *                   loads before tile k's MFMAs), v_mfma 32x32x16, 128 x 128
+ *                   block tile of four 64 x 64 wavefront tiles;
+ *   ABL_NO_LDS      no LDS: each wavefront loads its own fragments;
+ *   ABL_ONE_STAGE   one LDS stage (no double buffer);
+ *   ABL_NO_PREFETCH tile k+1's loads issued after tile k's MFMAs;
+ *   ABL_MFMA16      micro-kernel v_mfma 16x16x32;
+ *   ABL_VALU        micro-kernel on the vector ALUs (fp32 FMA, 8 x 8 outputs
+ *                   per lane);
+ *   ABL_TILE64      64 x 64 block tile, one wavefront per block.  */
 typedef enum {
     CONV_MAIN_LOOP_AUTO = 0,
     CONV_MAIN_LOOP_ELEMENT_128x128 = 1,
@@ -298,7 +313,14 @@ typedef enum {
     CONV_MAIN_LOOP_DUAL_256x128 = 4,
     CONV_MAIN_LOOP_OCT_256x128 = 5,
     CONV_MAIN_LOOP_OCT_256x256 = 6,
-    CONV_MAIN_LOOP_QUAD_128x64 = 7
+    CONV_MAIN_LOOP_QUAD_128x64 = 7,
+    CONV_MAIN_LOOP_ABL_FULL = 8,
+    CONV_MAIN_LOOP_ABL_NO_LDS = 9,
+    CONV_MAIN_LOOP_ABL_ONE_STAGE = 10,
+    CONV_MAIN_LOOP_ABL_NO_PREFETCH = 11,
+    CONV_MAIN_LOOP_ABL_MFMA16 = 12,
+    CONV_MAIN_LOOP_ABL_VALU = 13,
+    CONV_MAIN_LOOP_ABL_TILE64 = 14
 } conv_main_loop_t;
 
 /* Force the main-loop variant of every plan the calling host thread makes
@@ -306,7 +328,8 @@ typedef enum {
  * ablation and benchmarking; CONV_MAIN_LOOP_AUTO restores the library's
  * choice.  A call whose feed or shape the forced variant cannot serve (the
  * two-wavefront loops need K tiles inside one tap; the DMA loops need
- * 16-byte rows) returns CONV_ERR_UNSUPPORTED before any launch.  Query the
+ * 16-byte rows; the ABL_ loops the conditions above, and 16-byte aligned x
+ * and w) returns CONV_ERR_UNSUPPORTED before any launch.  Query the
  * workspace under the same setting as the call.  Returns
  * CONV_ERR_INVALID_ARG for an unknown variant, else CONV_OK. */
 conv_status_t conv2d_force_main_loop(conv_main_loop_t variant);

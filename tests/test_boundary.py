@@ -195,7 +195,7 @@ def test_forced_main_loop_checks_on_the_host():
         assert e.value.code == UNSUPPORTED
         cl.force_main_loop("element_128x128")
         assert cl.workspace_size(24, 24, 13, 15, 130, 3, 3, 1, 1, 1, "NHWC", "bf16", "indirect") >= 0
-        assert cl.lib().conv2d_force_main_loop(8) == INVALID
+        assert cl.lib().conv2d_force_main_loop(15) == INVALID
         assert cl.lib().conv2d_force_main_loop(-1) == INVALID
     finally:
         cl.force_main_loop("auto")
@@ -381,3 +381,28 @@ def test_nchw_1x1_halves_plan_split_partials(shape, dtype):
     ws = cl.workspace_size(N, C, H, W, Co, 1, 1, 1, 0, 1, "NCHW", dtype, "auto")
     copy = ((N + 1) // 2) * C * H * W * es
     assert copy < ws < cl.im2col_bytes(N, C, H, W, 1, 1, 1, 0, 1, dtype)
+
+
+def test_ablation_loops_plan_on_the_host():
+    """The ablation loop's variants run the indirection feed on 16-bit types
+    with C_in a multiple of 32: AUTO becomes INDIRECT (the workspace is the
+    indirection buffer for NHWC, never split-K partials), fp32, C_in = 24 and
+    the window-ordered feed are refused before any launch."""
+    L = LAYERS["C2"]
+    up = lambda v: (v + 255) // 256 * 256
+    ibuf = up(56 * 56 * 9 * 4)
+    try:
+        for v in cl.ABLATIONS:
+            cl.force_main_loop(v)
+            assert cl.workspace_size(*_args(L, "NHWC", "bf16", "auto")) == ibuf
+            assert cl.workspace_size(*_args(L, "NHWC", "fp16", "indirect")) == ibuf
+            # a skinny layer that the other loops split over K
+            assert cl.workspace_size(2, 512, 7, 7, 64, 3, 3, 1, 1, 1, "NHWC", "bf16", "auto") == up(49 * 9 * 4)
+            for args in ((*_args(L, "NHWC", "fp32", "auto")[:-1], "auto"),
+                         (24, 24, 13, 15, 130, 3, 3, 1, 1, 1, "NHWC", "bf16", "indirect"),
+                         (*_args(L, "NHWC", "bf16", "im2win")[:-1], "im2win")):
+                with pytest.raises(cl.ConvLowerError) as e:
+                    cl.workspace_size(*args)
+                assert e.value.code == UNSUPPORTED, (v, args)
+    finally:
+        cl.force_main_loop("auto")

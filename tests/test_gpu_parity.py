@@ -785,3 +785,41 @@ def test_nchw_window_rows_in_place(case, dtype):
             assert torch.equal(y.float().cpu(), exact), name
         else:
             _assert_parity(y, y_ref, dn, dtype, f"in-place NCHW {name}")
+
+
+
+# --- the ablation loop: each technique switched off, to the same bar --------
+
+ABL_CASES = [
+    # name, N, C, H, W, Co, KH, KW, s, p, d
+    ("C2-one-image", 1, 64, 56, 56, 128, 3, 3, 1, 1, 1),
+    ("ragged", 2, 32, 13, 11, 40, 3, 3, 1, 1, 1),
+    ("s2-3x3", 2, 64, 17, 19, 150, 3, 3, 2, 1, 1),
+]
+
+
+@pytest.mark.parametrize("variant", list(cl.ABLATIONS))
+@pytest.mark.parametrize("case", ABL_CASES, ids=[c[0] for c in ABL_CASES])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("layout", ["NCHW", "NHWC"])
+def test_ablation_loop_parity(variant, case, dtype, layout):
+    """Every ablation variant meets the bar against the oracle, and on
+    integer inputs gives the exact result rounded once."""
+    from convolution_lowering_amd.workloads import Layer
+    name, N, C, H, W, Co, KH, KW, s, p, d = case
+    L = Layer(name, N, C, H, W, Co, KH, KW, s, p, d, seed=91)
+    cl.force_main_loop(variant)
+    try:
+        for integer in (False, True):
+            _say(f"[gpu] ablation {variant} {name} {dtype} {layout} integer={integer}")
+            y = _run(L, dtype, layout, "auto", N, integer=integer)
+            x, w, b = make_inputs(L, dtype, "NCHW", integer=integer)
+            y_ref, dn = oracle.conv2d(x, w, b, s, p, d, oracle.NCHW)
+            yn = _to_nchw(y, layout)
+            if integer:
+                exact = torch.from_numpy(y_ref).float().to(y.dtype).float()
+                assert torch.equal(yn.float().cpu(), exact), f"{variant} {name} {dtype} {layout}"
+            else:
+                _assert_parity(yn, y_ref, dn, dtype, f"{variant} {name} {dtype} {layout}")
+    finally:
+        cl.force_main_loop("auto")
