@@ -36,9 +36,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "conv fwd TFLOPS & fraction of MFMA peak per layer; workspace bytes"
-PEAK = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}  # MI355X dense MFMA, TFLOP/s
+PEAK = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3, "fp8": 5000.0}  # MI355X dense MFMA, TFLOP/s
 HBM_PEAK = 8000.0  # GB/s
-ESIZE = {"bf16": 2, "fp16": 2, "fp32": 4}
+ESIZE = {"bf16": 2, "fp16": 2, "fp32": 4, "fp8": 1}
+OUT_ESIZE = {"bf16": 2, "fp16": 2, "fp32": 4, "fp8": 2}  # y and bias (bf16 for fp8 inputs)
 
 HEAD_SET = ("C4a", "C4b", "C4c", "C4d", "C4e")
 HEAD_DTYPE, HEAD_LAYOUT, HEAD_ALGO = "bf16", "NCHW", "auto"
@@ -60,8 +61,8 @@ def layer_flops(L, Ho, Wo, n=None):
 
 def algorithmic_bytes(L, Ho, Wo, dtype):
     """Each tensor moved once: |x| + |w| + |bias| + |y|."""
-    e = ESIZE[dtype]
-    return e * (L.N * L.C * L.H * L.W + L.Co * L.C * L.KH * L.KW + L.Co + L.N * L.Co * Ho * Wo)
+    e, eo = ESIZE[dtype], OUT_ESIZE[dtype]
+    return e * (L.N * L.C * L.H * L.W + L.Co * L.C * L.KH * L.KW) + eo * (L.Co + L.N * L.Co * Ho * Wo)
 
 
 def roofline(flops, nbytes, seconds, dtype):
@@ -103,7 +104,7 @@ class Prepared:
         Ho, Wo = layer_geometry(L)
         self.Ho, self.Wo = Ho, Wo
         shape = (L.N, L.Co, Ho, Wo) if layout == "NCHW" else (L.N, Ho, Wo, L.Co)
-        self.y = torch.empty(shape, dtype=self.x.dtype, device="cuda")
+        self.y = torch.empty(shape, dtype=self.b.dtype, device="cuda")
         self.ws_bytes = cl.workspace_size(L.N, L.C, L.H, L.W, L.Co, L.KH, L.KW, L.stride, L.pad, L.dilation,
                                           layout, dtype, algo)
         self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device="cuda")
@@ -255,7 +256,9 @@ def sweep(args, flush, rows_out):
     rows, ablation = [], []
     steps = max(3, args.steps // 4)
     for name, L in LAYERS.items():
-        for dtype in (L.dtypes + ("fp16",) if name == "C2" else L.dtypes):
+        extra = ("fp16",) if name == "C2" else ()
+        extra += ("fp8",) if name in ("C2", "C3c", "C4b", "C4c", "C4d", "C4e") else ()
+        for dtype in L.dtypes + extra:
             for layout in ("NCHW", "NHWC"):
                 algos = ["auto", "im2col", "direct", "im2win_lds"]
                 if name == "C2":
@@ -264,8 +267,8 @@ def sweep(args, flush, rows_out):
                     try:
                         r = bench_layer(L, dtype, layout, algo, steps, 2, flush)
                     except cl.ConvLowerError as e:
-                        if algo == "im2win_lds" and e.code == 2:
-                            continue  # shape outside the window-rows-in-LDS loop
+                        if e.code == 2 and (algo == "im2win_lds" or dtype == "fp8"):
+                            continue  # shape or layout outside the window-rows-in-LDS loop
                         r = {"layer": name, "dtype": dtype, "layout": layout, "algo": algo, "error": str(e)}
                     rows.append(r)
                     print("# row " + json.dumps(r), file=sys.stderr, flush=True)

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libconvlower.so")
 
 LAYOUTS = {"NCHW": 0, "NHWC": 1}
 ALGOS = {"auto": 0, "indirect": 1, "im2win": 2, "gemm": 3, "im2col": 4, "direct": 5, "im2win_lds": 6, "patch": 7}
-DTYPE_CODES = {"fp32": 0, "bf16": 1, "fp16": 2}
+DTYPE_CODES = {"fp32": 0, "bf16": 1, "fp16": 2, "fp8": 3}
 DTYPE_NAMES = {v: k for k, v in DTYPE_CODES.items()}
 STATUS = {0: "CONV_OK", 1: "CONV_ERR_INVALID_ARG", 2: "CONV_ERR_UNSUPPORTED", 3: "CONV_ERR_WORKSPACE",
           4: "CONV_ERR_HIP"}
@@ -98,7 +98,15 @@ def _dtype_code(dtype):
         return 1
     if dtype == torch.float16:
         return 2
+    if dtype == torch.float8_e4m3fn:
+        return 3
     raise TypeError(f"unsupported dtype {dtype}")
+
+
+def _out_dtype(dtype):
+    """Element type of y and bias for inputs of `dtype` (bf16 for fp8)."""
+    import torch
+    return torch.bfloat16 if dtype == torch.float8_e4m3fn else dtype
 
 
 def _launch_stream(stream, device):
@@ -172,17 +180,18 @@ def _prepare(x, w, bias, stride, pad, dilation, layout, algo, out, workspace):
     dev = x.device
     _check_tensor(x, "x", x.dtype, dev)
     _check_tensor(w, "w", x.dtype, dev)
+    ot = _out_dtype(x.dtype)
     if bias is not None:
-        _check_tensor(bias, "bias", x.dtype, dev)
+        _check_tensor(bias, "bias", ot, dev)
         if bias.numel() != Co:
             raise ValueError("bias must hold C_out values")
     dcode = _dtype_code(x.dtype)
     Ho, Wo = output_size(H, W, KH, KW, stride, pad, dilation)
     shape = (N, Co, Ho, Wo) if layout == "NCHW" else (N, Ho, Wo, Co)
     if out is None:
-        out = torch.empty(shape, dtype=x.dtype, device=dev)
+        out = torch.empty(shape, dtype=ot, device=dev)
     else:
-        _check_tensor(out, "out", x.dtype, dev)
+        _check_tensor(out, "out", ot, dev)
         if tuple(out.shape) != shape:
             raise ValueError(f"out has shape {tuple(out.shape)}, expected {shape}")
     need = workspace_size(N, C, H, W, Co, KH, KW, stride, pad, dilation, layout, DTYPE_NAMES[dcode], algo)
@@ -198,8 +207,9 @@ def conv2d_fwd(x, w, bias=None, stride=1, pad=0, dilation=1, layout="NCHW", algo
                workspace=None, stream=None):
     """y = conv(x, w) + bias on the GPU through conv2d_fwd; returns y.
 
-    x, w, bias, out: contiguous device tensors of one dtype (float32 or
-    bfloat16) in `layout`.  workspace: optional uint8 device tensor of at
+    x, w, bias, out: contiguous device tensors of one dtype (float32, bfloat16
+    or float16) in `layout`; for float8_e4m3fn x and w, bias and out are
+    bfloat16.  workspace: optional uint8 device tensor of at
     least workspace_size(...) bytes (allocated here when None)."""
     st = _launch_stream(stream, x.device)
     with _on(st):
@@ -217,10 +227,11 @@ def conv2d_fwd_noalloc(x, w, bias, out, stride=1, pad=0, dilation=1, layout="NCH
     workspace; nothing is allocated on the way (see include/convlower.h)."""
     N, C, H, W, Co, KH, KW = _dims(x, w, layout)
     dev = x.device
-    for t, name in ((x, "x"), (w, "w"), (out, "out")):
+    for t, name in ((x, "x"), (w, "w")):
         _check_tensor(t, name, x.dtype, dev)
+    _check_tensor(out, "out", _out_dtype(x.dtype), dev)
     if bias is not None:
-        _check_tensor(bias, "bias", x.dtype, dev)
+        _check_tensor(bias, "bias", _out_dtype(x.dtype), dev)
         if bias.numel() != Co:
             raise ValueError("bias must hold C_out values")
     Ho, Wo = output_size(H, W, KH, KW, stride, pad, dilation)

@@ -40,6 +40,8 @@ def _units():
         for feed in range(9):  # the Feed values of conv_internal.h
             units.append((f"igemm_{tag}_feed{feed}", "igemm_inst.hip",
                           [f"-DIGEMM_DTYPE={dt}", f"-DIGEMM_FEED={feed}"]))
+    # fp8 e4m3 (IGEMM_DTYPE 3): the window-row feed (7) only
+    units.append(("igemm_fp8_feed7", "igemm_inst.hip", ["-DIGEMM_DTYPE=3", "-DIGEMM_FEED=7"]))
     return units
 
 

@@ -22,8 +22,11 @@ constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
-bool dtype_ok(conv_dtype_t d) { return d == CONV_DTYPE_FP32 || d == CONV_DTYPE_BF16 || d == CONV_DTYPE_FP16; }
-size_t dtype_bytes(conv_dtype_t d) { return d == CONV_DTYPE_FP32 ? 4 : 2; }
+bool dtype_ok(conv_dtype_t d) {
+    return d == CONV_DTYPE_FP32 || d == CONV_DTYPE_BF16 || d == CONV_DTYPE_FP16 || d == CONV_DTYPE_FP8_E4M3;
+}
+// Bytes of one element of x (and w); y and bias are bf16 for fp8 inputs.
+size_t dtype_bytes(conv_dtype_t d) { return d == CONV_DTYPE_FP32 ? 4 : d == CONV_DTYPE_FP8_E4M3 ? 1 : 2; }
 
 // Main-loop variant forced on this thread's plans (CONV_MAIN_LOOP_AUTO: none).
 thread_local int t_forced_main_loop = CONV_MAIN_LOOP_AUTO;
@@ -135,10 +138,27 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     pl->cp = C;
     const Geom &g = pl->g;
     if (!sizes_supported(g)) return CONV_ERR_UNSUPPORTED;
-    pl->e16 = dtype != CONV_DTYPE_FP32;
+    pl->e16 = dtype == CONV_DTYPE_BF16 || dtype == CONV_DTYPE_FP16;
     pl->dtype = dtype;
     pl->nhwc = layout == CONV_LAYOUT_NHWC;
-    pl->esize = pl->e16 ? 2 : 4;
+    pl->esize = dtype_bytes(dtype);
+    if (dtype == CONV_DTYPE_FP8_E4M3) {
+        // fp8 e4m3 inputs: channels-last tensors through the window-row loop
+        // (K tiles of 64 channels), no workspace.
+        if (algo != CONV_ALGO_AUTO && algo != CONV_ALGO_IM2WIN_LDS) return CONV_ERR_UNSUPPORTED;
+        if (!pl->nhwc || t_forced_main_loop != CONV_MAIN_LOOP_AUTO) return CONV_ERR_UNSUPPORTED;
+        const bool ok = g.s == 1 && g.d == 1 && g.KW == 3 && g.C % 64 == 0 && 255 / g.Wo + 2 <= kRowWinMaxSeg &&
+                        (long long)g.N * g.C * g.H * g.W <= kBufMax && g.K * g.Co <= kBufMax;
+        if (!ok) return CONV_ERR_UNSUPPORTED;
+        pl->feed = FEED_ROWWIN;
+        pl->gm = g;
+        pl->out_nchw = false;
+        pl->tile = g.Co <= 64 ? TILE_256x64_ROWWIN : TILE_256x128_ROWWIN;
+        pl->splits = 1;
+        pl->kps = (int)((g.K + 127) / 128 * 128);
+        pl->total = 0;
+        return CONV_OK;
+    }
 
     // A 1x1 stride-1 unpadded convolution is a GEMM call (The Indirect
     // Convolution Algorithm, abstract); a kernel that covers the whole
@@ -631,7 +651,8 @@ conv_status_t launch_main(const Plan &pl, GemmArgs &a, hipStream_t s) {
         a.c_shift = sh;
         a.c_inv = inv;
     }
-    hipError_t e = pl.dtype == CONV_DTYPE_FP16 ? launch_igemm_f16(a, pl.feed, pl.out_nchw, a_vec, b_vec, tile, pl.splits, s)
+    hipError_t e = pl.dtype == CONV_DTYPE_FP8_E4M3 ? launch_igemm_fp8(a, pl.feed, pl.out_nchw, a_vec, b_vec, tile, pl.splits, s)
+                   : pl.dtype == CONV_DTYPE_FP16 ? launch_igemm_f16(a, pl.feed, pl.out_nchw, a_vec, b_vec, tile, pl.splits, s)
                    : pl.e16 ? launch_igemm_bf16(a, pl.feed, pl.out_nchw, a_vec, b_vec, tile, pl.splits, s)
                             : launch_igemm_f32(a, pl.feed, pl.out_nchw, a_vec, b_vec, tile, pl.splits, s);
     if (e != hipSuccess) return CONV_ERR_HIP;
@@ -647,8 +668,10 @@ conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias
                   conv_stream_t stream, void *workspace, size_t workspace_bytes) {
     if (!x || !w || !y) return CONV_ERR_INVALID_ARG;
     const size_t es = pl.esize;
-    if ((uintptr_t)x % es || (uintptr_t)w % es || (uintptr_t)y % es || (bias && (uintptr_t)bias % es))
+    const size_t eo = pl.dtype == CONV_DTYPE_FP8_E4M3 ? 2 : es;  // y and bias elements
+    if ((uintptr_t)x % es || (uintptr_t)w % es || (uintptr_t)y % eo || (bias && (uintptr_t)bias % eo))
         return CONV_ERR_INVALID_ARG;
+    if (pl.dtype == CONV_DTYPE_FP8_E4M3 && ((uintptr_t)x % 16 || (uintptr_t)w % 16)) return CONV_ERR_UNSUPPORTED;
     if (pl.total > 0 && (!workspace || workspace_bytes < pl.total)) return CONV_ERR_WORKSPACE;
     if (pl.total > 0 && (uintptr_t)workspace % 16) return CONV_ERR_INVALID_ARG;
 
@@ -892,6 +915,7 @@ conv_status_t conv2d_im2win_transform(const void *x, void *xwin, int N, int C_in
                                       conv_stream_t stream) {
     if (layout != CONV_LAYOUT_NCHW && layout != CONV_LAYOUT_NHWC) return CONV_ERR_INVALID_ARG;
     if (!dtype_ok(dtype)) return CONV_ERR_INVALID_ARG;
+    if (dtype == CONV_DTYPE_FP8_E4M3) return CONV_ERR_UNSUPPORTED;  // 16- and 32-bit elements only
     Geom g;
     conv_status_t st = make_geom(N, C_in, H, W, 1, KH, KW, stride, pad, dilation, &g);
     if (st != CONV_OK) return st;
@@ -909,6 +933,7 @@ conv_status_t conv2d_im2col_transform(const void *x, void *xcol, int N, int C_in
                                       conv_stream_t stream) {
     if (layout != CONV_LAYOUT_NCHW && layout != CONV_LAYOUT_NHWC) return CONV_ERR_INVALID_ARG;
     if (!dtype_ok(dtype)) return CONV_ERR_INVALID_ARG;
+    if (dtype == CONV_DTYPE_FP8_E4M3) return CONV_ERR_UNSUPPORTED;  // 16- and 32-bit elements only
     Geom g;
     conv_status_t st = make_geom(N, C_in, H, W, 1, KH, KW, stride, pad, dilation, &g);
     if (st != CONV_OK) return st;

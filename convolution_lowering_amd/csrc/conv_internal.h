@@ -83,6 +83,9 @@ hipError_t launch_igemm_f32(const GemmArgs &a, int feed, bool out_nchw, bool a_v
                             int tile, int splits, hipStream_t st);
 hipError_t launch_igemm_f16(const GemmArgs &a, int feed, bool out_nchw, bool a_vec, bool b_vec,
                             int tile, int splits, hipStream_t st);
+// fp8 e4m3 inputs, bf16 bias and output; FEED_ROWWIN only.
+hipError_t launch_igemm_fp8(const GemmArgs &a, int feed, bool out_nchw, bool a_vec, bool b_vec,
+                            int tile, int splits, hipStream_t st);
 // dtype: 0 fp32, 1 bf16, 2 fp16 (the conv_dtype_t values).
 hipError_t launch_splitk_reduce(const float *part, const void *bias, void *y, const Geom &g,
                                 int splits, bool out_nchw, int dtype, hipStream_t st);

@@ -34,6 +34,13 @@ hipError_t launch_igemm_f32(const GemmArgs &a, int feed, bool out_nchw, bool a_v
     return dispatch<float>(a, feed, out_nchw, a_vec, b_vec, tile, splits, st);
 }
 
+// fp8 e4m3 inputs (bf16 output): the window-row feed only.
+hipError_t launch_igemm_fp8(const GemmArgs &a, int feed, bool out_nchw, bool a_vec, bool b_vec, int tile,
+                            int splits, hipStream_t st) {
+    if (feed != FEED_ROWWIN) return hipErrorInvalidValue;
+    return launch_feed<uint8_t, FEED_ROWWIN>(a, out_nchw, a_vec, b_vec, tile, splits, st);
+}
+
 hipError_t launch_igemm_f16(const GemmArgs &a, int feed, bool out_nchw, bool a_vec, bool b_vec, int tile,
                             int splits, hipStream_t st) {
     return dispatch<_Float16>(a, feed, out_nchw, a_vec, b_vec, tile, splits, st);

@@ -131,6 +131,19 @@ struct MfmaShape<float, 32> {  // v_mfma_f32_32x32x2_f32, four per 16-byte chunk
     }
 };
 
+template <>
+struct MfmaShape<uint8_t, 32> {  // v_mfma_f32_32x32x16_fp8_fp8 (OCP e4m3 on gfx950), two per 16-byte chunk
+    static constexpr int MT = 32, CPG = 2, NQ = 4, QSTEP = 8;
+    typedef f32x16_t acc_t;
+    __device__ static __forceinline__ int qrow(int q, int lane) { return 8 * q + 4 * (lane >> 5); }
+    __device__ static __forceinline__ void mma(const uint4 &a, const uint4 &b, acc_t &c) {
+        const long a0 = (long)(((unsigned long)a.y << 32) | a.x), a1 = (long)(((unsigned long)a.w << 32) | a.z);
+        const long b0 = (long)(((unsigned long)b.y << 32) | b.x), b1 = (long)(((unsigned long)b.w << 32) | b.z);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a0, b0, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a1, b1, c, 0, 0, 0);
+    }
+};
+
 // Four consecutive outputs, rounded once, in one 8-byte (bf16) or 16-byte
 // (fp32) store; the address must be aligned to that size.
 __device__ __forceinline__ void store4(uint16_t *p, float a, float b, float c, float d) {

@@ -116,7 +116,9 @@ __device__ __forceinline__ void dual_store(const GemmArgs &A,
                                            typename MfmaShape<S, 32>::acc_t (&acc)[C::TP][C::TC], uint4 *stg,
                                            const float *bias_s, uint32_t m0, int co0, int wp, int wc, int lane,
                                            int tid) {
-    constexpr int BM = C::BM, BN = C::BN, VEC = C::VEC, TP = C::TP, TC = C::TC, WPM = C::WPM, WCN = C::WCN;
+    // S is the output type (the input type too, except for 8-bit inputs).
+    constexpr int BM = C::BM, BN = C::BN, VEC = 16 / (int)sizeof(S), TP = C::TP, TC = C::TC, WPM = C::WPM,
+                  WCN = C::WCN;
     constexpr int NTHR = C::NTHR;
     using MF = MfmaShape<S, 32>;
     constexpr int NQ = MF::NQ;

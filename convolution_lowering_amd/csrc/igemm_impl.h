@@ -54,6 +54,10 @@ struct Elem<uint16_t> {  // bf16 stored as raw 16-bit words
     static constexpr int VEC = 8;
 };
 template <>
+struct Elem<uint8_t> {  // OCP fp8 e4m3 as raw bytes (inputs only; the output is bf16)
+    static constexpr int VEC = 16;
+};
+template <>
 struct Elem<_Float16> {  // IEEE half
     static constexpr int VEC = 8;
 };
@@ -630,7 +634,8 @@ static hipError_t launch_tile(const GemmArgs &a, int tile, int splits, hipStream
         if constexpr (AVEC) {
             if (tile == TILE_256x128_ROWWIN) return go(igemm_rowwin_kernel<S, OUT_NCHW>, 256, 128, 256);
             if (tile == TILE_256x64_ROWWIN) return go(igemm_rowwin_kernel<S, OUT_NCHW, 64>, 256, 64, 256);
-            if (tile == TILE_512x128_ROWWIN_PP) return go(igemm_rowwin_pp_kernel<S, OUT_NCHW>, 512, 128, 512);
+            if constexpr (sizeof(S) > 1)
+                if (tile == TILE_512x128_ROWWIN_PP) return go(igemm_rowwin_pp_kernel<S, OUT_NCHW>, 512, 128, 512);
         }
         return hipErrorInvalidValue;
     } else if constexpr (FEED == FEED_ROWWIN_NCHW) {  // NCHW read in place: 16-bit types, NCHW output

@@ -13,6 +13,8 @@ namespace convlower {
 using SliceT = uint16_t;  // bf16 as raw 16-bit words
 #elif IGEMM_DTYPE == 2
 using SliceT = _Float16;
+#elif IGEMM_DTYPE == 3
+using SliceT = uint8_t;  // fp8 e4m3 as raw bytes (the window-row feed only)
 #else
 using SliceT = float;
 #endif

@@ -32,6 +32,8 @@
 // the LDS of the two NHWC stages; the copy costs one more barrier per step.
 #pragma once
 
+#include <type_traits>
+
 namespace convlower {
 
 // Stage geometry for KW taps per kernel row.  A tile of 256 consecutive
@@ -91,6 +93,8 @@ __device__ __forceinline__ void igemm_rowwin_body(const GemmArgs &A) {
     constexpr int IPW_AL = NCHW_IN ? IPW_RAW : IPW_A;  // A-side loads per wavefront per step
     constexpr uint32_t ES = (uint32_t)sizeof(S);
     using MF = MfmaShape<S, 32>;
+    // Output (and bias) type: the input type, except bf16 for fp8 inputs.
+    using O = typename std::conditional<sizeof(S) == 1, uint16_t, S>::type;
     static_assert(KW == 3, "the schedule below is written for three taps per kernel row");
 
     // A stages (NHWC: two; NCHW: one, then the raw buffer), then B stages;
@@ -119,7 +123,7 @@ __device__ __forceinline__ void igemm_rowwin_body(const GemmArgs &A) {
     float bias_r = 0.f;
     if (tid < BN) {
         const int co = co0 + tid;
-        if (A.bias && co < g.Co) bias_r = bits_to_f32(S(), elem_bits((const S *)A.bias, co));
+        if (A.bias && co < g.Co) bias_r = bits_to_f32(O(), elem_bits((const O *)A.bias, co));
     }
 
     // ---- the block's segments ------------------------------------------------
@@ -513,7 +517,7 @@ __device__ __forceinline__ void igemm_rowwin_body(const GemmArgs &A) {
     // bias_s is a separate array from the stages; the epilogue's first
     // barrier publishes it.
     if (tid < BN) bias_s[tid] = bias_r;
-    dual_store<S, OUT_NCHW, C>(A, acc, lds, bias_s, m0, co0, wp, wc, lane, tid);
+    dual_store<O, OUT_NCHW, C>(A, acc, lds, bias_s, m0, co0, wp, wc, lane, tid);
 }
 
 template <typename S, bool OUT_NCHW, int BN = 128, bool IN_NCHW = false>

@@ -13,8 +13,8 @@ C_out=128, 3x3, stride 1, pad 1), and a generality sweep.
 
 Draw recipe (one torch CPU generator per layer, seed = 1000*set + index):
 x, then w, then bias, all float32, then cast to the requested dtype with
-round-to-nearest-even.  Distributions: N(0,1) inputs for C1/C2/C3/C5,
-uniform[-1,1] for C4; N(0,1) weights for C1/C2/C5, Kaiming-normal
+round-to-nearest-even (for fp8: x and w to e4m3, the bias to bf16).
+Distributions: N(0,1) inputs for C1/C2/C3/C5, uniform[-1,1] for C4; N(0,1) weights for C1/C2/C5, Kaiming-normal
 (std = sqrt(2 / (C_in*KH*KW))) for C3/C4; bias N(0,1) everywhere.
 Values are drawn in the logical NCHW / OIHW order and permuted for NHWC /
 OHWI, so both layouts of one layer hold the same numbers.
@@ -92,7 +92,7 @@ LAYERS = {
               "7x7 kernel over a 7x7 input, 512->1000 (a dense layer)"),
 }
 
-TORCH_DTYPES = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}
+TORCH_DTYPES = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16, "fp8": torch.float8_e4m3fn}
 
 
 def make_inputs(layer: Layer, dtype: str = "bf16", layout: str = "NCHW", *, N: int | None = None,
@@ -120,7 +120,8 @@ def make_inputs(layer: Layer, dtype: str = "bf16", layout: str = "NCHW", *, N: i
             w = w * (2.0 / (layer.C * layer.KH * layer.KW)) ** 0.5
         b = torch.randn((layer.Co,), generator=g)
     td = TORCH_DTYPES[dtype]
-    x, w, b = x.to(td), w.to(td), b.to(td)
+    # fp8: x and w in e4m3 (torch rounds to nearest even), bias in bf16
+    x, w, b = x.to(td), w.to(td), b.to(torch.bfloat16 if dtype == "fp8" else td)
     if layout == "NHWC":
         x = x.permute(0, 2, 3, 1).contiguous()
         w = w.permute(0, 2, 3, 1).contiguous()

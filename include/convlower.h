@@ -62,8 +62,14 @@ typedef struct ihipStream_t *conv_stream_t;
 
 typedef enum { CONV_LAYOUT_NCHW = 0, CONV_LAYOUT_NHWC = 1 } conv_layout_t;
 /* Element type of x, w, bias and y (all the same); the sums are fp32 in
- * every case, rounded once to the element type at the store. */
-typedef enum { CONV_DTYPE_FP32 = 0, CONV_DTYPE_BF16 = 1, CONV_DTYPE_FP16 = 2 } conv_dtype_t;
+ * every case, rounded once to the element type at the store.
+ * CONV_DTYPE_FP8_E4M3 is the exception: x and w hold OCP fp8 e4m3 bytes
+ * (1 sign, 4 exponent, 3 mantissa bits, bias 7, no infinities), bias and y
+ * are bf16, and y is rounded once to bf16.  It is served for channels-last
+ * (NHWC) tensors by the window-row loop (CONV_ALGO_IM2WIN_LDS, which AUTO
+ * means here) with C_in a multiple of 64 and x and w 16-byte aligned; any
+ * other fp8 request returns CONV_ERR_UNSUPPORTED. */
+typedef enum { CONV_DTYPE_FP32 = 0, CONV_DTYPE_BF16 = 1, CONV_DTYPE_FP16 = 2, CONV_DTYPE_FP8_E4M3 = 3 } conv_dtype_t;
 
 /* Which lowering feeds the contraction.
  *   AUTO      1x1 stride-1 unpadded, or kernel == whole unpadded input: the

@@ -406,3 +406,21 @@ def test_ablation_loops_plan_on_the_host():
                 assert e.value.code == UNSUPPORTED, (v, args)
     finally:
         cl.force_main_loop("auto")
+
+
+def test_fp8_plans_only_channels_last_window_rows():
+    """fp8 e4m3 inputs run the window-row loop on channels-last tensors with
+    C_in a multiple of 64 (no workspace); NCHW, other algorithms, C_in not a
+    multiple of 64 and the lowering transforms are refused on the host."""
+    L = LAYERS["C2"]
+    assert cl.workspace_size(*_args(L, "NHWC", "fp8", "auto")) == 0
+    assert cl.workspace_size(*_args(L, "NHWC", "fp8", "im2win_lds")) == 0
+    for args in (_args(L, "NCHW", "fp8", "auto"), _args(L, "NHWC", "fp8", "indirect"),
+                 _args(L, "NHWC", "fp8", "im2col"), (2, 32, 16, 16, 64, 3, 3, 1, 1, 1, "NHWC", "fp8", "auto"),
+                 (2, 64, 16, 16, 64, 3, 3, 2, 1, 1, "NHWC", "fp8", "auto")):
+        with pytest.raises(cl.ConvLowerError) as e:
+            cl.workspace_size(*args)
+        assert e.value.code == UNSUPPORTED, args
+    assert cl.lib().conv2d_im2win_transform(None, None, 1, 64, 8, 8, 3, 3, 1, 1, 1, 1, 3, None) == UNSUPPORTED
+    assert cl.lib().conv2d_im2col_transform(None, None, 1, 64, 8, 8, 3, 3, 1, 1, 1, 1, 3, None) == UNSUPPORTED
+    assert cl.im2col_bytes(L.N, L.C, L.H, L.W, 3, 3, 1, 1, 1, "fp8") == L.N * 56 * 56 * 64 * 9

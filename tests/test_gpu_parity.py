@@ -823,3 +823,37 @@ def test_ablation_loop_parity(variant, case, dtype, layout):
                 _assert_parity(yn, y_ref, dn, dtype, f"{variant} {name} {dtype} {layout}")
     finally:
         cl.force_main_loop("auto")
+
+
+
+# --- fp8 e4m3 inputs (bf16 bias and output) through the window-row loop ------
+
+FP8_CASES = [
+    # name, N, C, H, W, Co
+    ("64to128-56", 2, 64, 56, 56, 128), ("128to64-14", 3, 128, 14, 14, 64), ("ragged", 2, 64, 17, 20, 96),
+    ("192to256-28", 1, 192, 28, 28, 256),
+]
+
+
+@pytest.mark.parametrize("case", FP8_CASES, ids=[c[0] for c in FP8_CASES])
+def test_fp8_window_rows(case):
+    """e4m3 x and w, fp32 sums, bf16 y: on integer inputs (exact in e4m3) y is
+    the exact result rounded once to bf16; on normal inputs the bf16 bar
+    holds against the oracle, which reads the e4m3 values exactly."""
+    from convolution_lowering_amd.workloads import Layer
+    name, N, C, H, W, Co = case
+    L = Layer(name, N, C, H, W, Co, 3, 3, 1, 1, 1, "normal", "kaiming", 9300 + C, ("fp8",))
+    for integer in (True, False):
+        x, w, b = make_inputs(L, "fp8", "NHWC", integer=integer)
+        _say(f"[gpu] fp8 {name} integer={integer}")
+        y = cl.conv2d_fwd(x.to(DEV), w.to(DEV), b.to(DEV), 1, 1, 1, "NHWC", "auto")
+        torch.cuda.synchronize()
+        assert y.dtype == torch.bfloat16
+        xr, wr, br = make_inputs(L, "fp8", "NCHW", integer=integer)
+        y_ref, dn = oracle.conv2d(xr, wr, br, 1, 1, 1, oracle.NCHW)
+        yn = y.permute(0, 3, 1, 2)
+        if integer:
+            exact = torch.from_numpy(y_ref).float().to(torch.bfloat16).float()
+            assert torch.equal(yn.float().cpu(), exact), name
+        else:
+            _assert_parity(yn, y_ref, dn, "bf16", f"fp8 {name}")
