@@ -303,9 +303,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run one 256 MiB device copy (scale reference for HBM byte counters)")
-    ap.add_argument("--only", metavar="LAYER:LAYOUT[:DTYPE[:ALGO]]",
-                    help="time only this layer (algo auto, dtype bf16 unless given) and print its row; "
-                         "for profiling one layer's kernels")
+    ap.add_argument("--only", metavar="LAYER:LAYOUT[:DTYPE[:ALGO]][,...]",
+                    help="time only these layers (algo auto, dtype bf16 unless given), one JSON row each; "
+                         "for profiling a few layers' kernels")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path (each GPU would run its own "
@@ -327,13 +327,14 @@ def main():
         torch.cuda.synchronize()
 
     if args.only:
-        parts = args.only.split(":")
-        L = LAYERS[parts[0]]
-        row = bench_layer(L, parts[2] if len(parts) > 2 else "bf16", parts[1], parts[3] if len(parts) > 3 else "auto",
-                          args.steps, args.warmup, flush)
+        for spec in args.only.split(","):
+            parts = spec.split(":")
+            L = LAYERS[parts[0]]
+            row = bench_layer(L, parts[2] if len(parts) > 2 else "bf16", parts[1],
+                              parts[3] if len(parts) > 3 else "auto", args.steps, args.warmup, flush)
+            print(json.dumps(row), flush=True)
         if args.calibration_copy:
             calibration_copy()
-        print(json.dumps(row))
         return
 
     keep = 0 if args.no_cpu_baseline else CPU_SAMPLE_IMAGES
