@@ -37,7 +37,7 @@ def _units():
              ("patch_conv", "patch_conv.hip", []),
              ("igemm_ablate", "igemm_ablate.hip", [])]
     for dt, tag in ((1, "bf16"), (2, "f16"), (0, "f32")):  # IGEMM_DTYPE: 0 fp32, 1 bf16, 2 fp16
-        for feed in range(9):  # the Feed values of conv_internal.h
+        for feed in range(10):  # the Feed values of conv_internal.h
             units.append((f"igemm_{tag}_feed{feed}", "igemm_inst.hip",
                           [f"-DIGEMM_DTYPE={dt}", f"-DIGEMM_FEED={feed}"]))
     # fp8 e4m3 (IGEMM_DTYPE 3): the window-row feed (7) only

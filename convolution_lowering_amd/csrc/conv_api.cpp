@@ -208,6 +208,14 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     const int rowwin_bn = g.Co <= 64 ? 64 : 128;
     const bool rowwin_auto = rowwin_ok && t_forced_main_loop == CONV_MAIN_LOOP_AUTO &&
                              ((g.M + 255) / 256) * ((g.Co + rowwin_bn - 1) / rowwin_bn) >= 256;
+    // A 1x1 NCHW input read where it lies (16-bit types): K tiles of whole
+    // channel rows (C a multiple of 32), 16-byte pixel chunks that never
+    // cross an image (P a multiple of 8), 32-bit offsets, and the library's
+    // own choice of main loop.
+    const bool gemm_nchw = one && !pl->nhwc && pl->e16 && g.C % 32 == 0 && g.P % 8 == 0 && g.M > 64 &&
+                           (long long)g.N * g.C * g.H * g.W * (long long)pl->esize <= kBufMax &&
+                           g.K * g.Co * (long long)pl->esize <= kBufMax &&
+                           t_forced_main_loop == CONV_MAIN_LOOP_AUTO;
     const bool patch_ok = patch_conv_plan(g, pl->dtype, nullptr);
     // The ablation loops run on the indirection feed only.
     const bool ablate = t_forced_main_loop >= CONV_MAIN_LOOP_ABL_FULL;
@@ -224,6 +232,10 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
                 pl->feed = FEED_ROWMAJOR;  // Ho = Wo = 1: both layouts store y as [N][Co]
             } else if (one && pl->nhwc) {
                 pl->feed = FEED_ROWMAJOR;
+            } else if (gemm_nchw) {
+                // x[n] is the GEMM's A operand transposed ([C][pixels]), the
+                // weights [Co][C] are W_row as they lie: no workspace.
+                pl->feed = FEED_GEMM_NCHW;
             } else if (one && g.C % (pl->e16 ? 8 : 4) == 0 && g.N >= 2) {
                 // NCHW 1x1: half the batch at a time is copied channels-last
                 // and multiplied as a plain GEMM (the copy of all of x would
@@ -336,6 +348,7 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
         case FEED_IND_CHUNK: rows16 = true; break;
         case FEED_WIN: rows16 = g.C % VEC == 0; break;
         case FEED_WIN_CHUNK: rows16 = true; break;
+        case FEED_GEMM_NCHW: rows16 = true; break;
         default: rows16 = false;
     }
     pl->rows16 = rows16;
@@ -359,6 +372,9 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
         }
         case FEED_IND_CHUNK: break;  // slice checked when the feed was chosen
         case FEED_WIN_CHUNK: break;
+        case FEED_GEMM_NCHW:  // C a multiple of 32 (checked when the feed was chosen): dual always holds
+            oct = oct && g.C % BK8 == 0;
+            break;
         default: dual = oct = false;
     }
     const long long tiles256 = ((Mt + 255) / 256) * ((g.Co + 127) / 128);
@@ -606,7 +622,8 @@ conv_status_t launch_main(const Plan &pl, GemmArgs &a, hipStream_t s) {
         case FEED_IND_CHUNK:
         case FEED_WIN_CHUNK: a_vec = al16(a.a_src) && wide_slice(pl.tile); break;
         case FEED_ROWWIN:
-        case FEED_ROWWIN_NCHW: a_vec = al16(a.a_src); break;
+        case FEED_ROWWIN_NCHW:
+        case FEED_GEMM_NCHW: a_vec = al16(a.a_src); break;
         default: a_vec = false;
     }
     if (pl.force_element) a_vec = false;
@@ -637,6 +654,9 @@ conv_status_t launch_main(const Plan &pl, GemmArgs &a, hipStream_t s) {
 
     // Misaligned pointers fall back to the element-gather loop, which has no
     // 256x128 variant; the split count (and so the workspace) is unchanged.
+    // (The in-place 1x1 NCHW feed falls back to its element-gather twin,
+    // which needs no workspace either.)
+    const int feed = pl.feed == FEED_GEMM_NCHW && !a_vec ? (int)FEED_NCHW_1X1 : pl.feed;
     int tile = pl.tile;
     if (!a_vec && (tile == TILE_256x128 || wide_slice(tile)))
         tile = tile == TILE_128x64_QUAD ? TILE_128x64 : TILE_128x128;
@@ -651,10 +671,10 @@ conv_status_t launch_main(const Plan &pl, GemmArgs &a, hipStream_t s) {
         a.c_shift = sh;
         a.c_inv = inv;
     }
-    hipError_t e = pl.dtype == CONV_DTYPE_FP8_E4M3 ? launch_igemm_fp8(a, pl.feed, pl.out_nchw, a_vec, b_vec, tile, pl.splits, s)
-                   : pl.dtype == CONV_DTYPE_FP16 ? launch_igemm_f16(a, pl.feed, pl.out_nchw, a_vec, b_vec, tile, pl.splits, s)
-                   : pl.e16 ? launch_igemm_bf16(a, pl.feed, pl.out_nchw, a_vec, b_vec, tile, pl.splits, s)
-                            : launch_igemm_f32(a, pl.feed, pl.out_nchw, a_vec, b_vec, tile, pl.splits, s);
+    hipError_t e = pl.dtype == CONV_DTYPE_FP8_E4M3 ? launch_igemm_fp8(a, feed, pl.out_nchw, a_vec, b_vec, tile, pl.splits, s)
+                   : pl.dtype == CONV_DTYPE_FP16 ? launch_igemm_f16(a, feed, pl.out_nchw, a_vec, b_vec, tile, pl.splits, s)
+                   : pl.e16 ? launch_igemm_bf16(a, feed, pl.out_nchw, a_vec, b_vec, tile, pl.splits, s)
+                            : launch_igemm_f32(a, feed, pl.out_nchw, a_vec, b_vec, tile, pl.splits, s);
     if (e != hipSuccess) return CONV_ERR_HIP;
     if (pl.splits > 1) {
         if (launch_splitk_reduce(a.part, a.bias, a.y, g, pl.splits, pl.out_nchw, pl.dtype, s) != hipSuccess)

@@ -26,8 +26,11 @@ enum Feed : int {
                          // KW = 3); K = (ci slice, kh, kw)
     FEED_ROWWIN_NCHW = 8,  // the same window rows, read from NCHW input where it lies (16-bit types); K as
                            // FEED_ROWWIN, weights in (kh, kw, ci) order
+    FEED_GEMM_NCHW = 9,  // 1x1 stride-1 NCHW input read where it lies (16-bit types): each K tile's channel
+                         // rows of BM pixels staged in LDS as they lie, MFMA fragments formed by transpose
+                         // reads; K = ci, weights [Co][C] as they lie
 };
-constexpr int kNumFeeds = 9;
+constexpr int kNumFeeds = 10;
 // Raw chunks (8 input columns each) one 256-pixel tile of the NCHW window-row
 // loop stages per channel, at most.
 constexpr int kRowWinRawChunks = 40;

@@ -20,6 +20,7 @@ static hipError_t dispatch(const GemmArgs &a, int feed, bool out_nchw, bool a_ve
         case FEED_WIN_CHUNK: return launch_feed<S, FEED_WIN_CHUNK>(a, out_nchw, a_vec, b_vec, tile, splits, st);
         case FEED_ROWWIN: return launch_feed<S, FEED_ROWWIN>(a, out_nchw, a_vec, b_vec, tile, splits, st);
         case FEED_ROWWIN_NCHW: return launch_feed<S, FEED_ROWWIN_NCHW>(a, out_nchw, a_vec, b_vec, tile, splits, st);
+        case FEED_GEMM_NCHW: return launch_feed<S, FEED_GEMM_NCHW>(a, out_nchw, a_vec, b_vec, tile, splits, st);
         default: return hipErrorInvalidValue;
     }
 }

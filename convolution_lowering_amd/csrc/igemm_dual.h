@@ -317,6 +317,19 @@ __device__ __forceinline__ void igemm_dual_body(const GemmArgs &A) {
     constexpr bool CHUNK = FEED == FEED_IND_CHUNK || WCHUNK;  // each 16-byte chunk its own (tap, channels)
     constexpr bool IND = FEED == FEED_IND_NHWC || FEED == FEED_IND_CHUNK;
     constexpr bool TAPS = FEED == FEED_IND_NHWC || FEED == FEED_WIN;  // K tiles inside one tap
+    // 1x1 NCHW read in place: the A part of a stage is the tile's BK channel
+    // rows of BM pixels as they lie in x ([channel][pixel], CPRA chunks of
+    // VEC pixels per row, RPIA rows per 64-lane load), chunk columns
+    // XOR-ed by 4 * (row mod 4).  Each MFMA A fragment (32 pixels x 16
+    // channels) is two transpose reads of 4 channels x 16 pixels per
+    // 16-lane group; the XOR puts the 16 chunks a 32-lane half of such a
+    // read touches (4 rows x 4 chunks) on 16 distinct bank groups.
+    constexpr bool GN = FEED == FEED_GEMM_NCHW;
+    static_assert(!GN || sizeof(S) == 2, "the transpose reads move 16-bit elements");
+    constexpr int CPRA = GN ? BM / VEC : 1;
+    constexpr int RPIA = GN ? 64 / CPRA : 1;
+    static_assert(!GN || (CPRA >= 16 && CPRA <= 64 && BK * CPRA == BM * KCH && (NW * RPIA) % 4 == 0),
+                  "A rows of whole 64-byte groups; each lane's swizzle the same in all its loads");
     using MF = MfmaShape<S, 32>;
     constexpr int NQ = MF::NQ;
 
@@ -381,8 +394,25 @@ __device__ __forceinline__ void igemm_dual_body(const GemmArgs &A) {
     const uint32_t kc = (uint32_t)(((lane % KCH) ^ dual_swz<KCH>(wave * RPI + lrow)) * VEC);
     uint32_t rbA[IPW_A], rbB[IPW_B];
     int ib_row[IPW_A];
+    if constexpr (GN) {
+        // Slot L of A load i: channel row (i*NW + wave)*RPIA + L/CPRA of the
+        // tile, chunk column (L % CPRA) ^ swizzle, i.e. pixels m0 + 8*column;
+        // rows of pixels past M read zeros.  P is a multiple of VEC, so no
+        // chunk crosses an image.
+        const int lr = lane / CPRA;
+        const int col = (lane % CPRA) ^ (4 * ((wave * RPIA + lr) & 3));
+        const uint32_t m = m0 + (uint32_t)(col * VEC);
+        const uint32_t n = m / (uint32_t)g.P;
+        const uint32_t pix = n * (uint32_t)g.C * (uint32_t)g.P + (m - n * (uint32_t)g.P);
 #pragma unroll
-    for (int i = 0; i < IPW_A; ++i) {
+        for (int i = 0; i < IPW_A; ++i) {
+            const uint32_t k = (uint32_t)((i * NW + wave) * RPIA + lr);
+            rbA[i] = m < M ? (pix + k * (uint32_t)g.P) * ES : kOutOfRange;
+            ib_row[i] = 0;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < (GN ? 0 : IPW_A); ++i) {
         const int r = (i * NW + wave) * RPI + lrow;
         ib_row[i] = r * g.T;
         const uint32_t m = m0 + (uint32_t)r;
@@ -487,6 +517,9 @@ __device__ __forceinline__ void igemm_dual_body(const GemmArgs &A) {
             if constexpr (FEED == FEED_ROWMAJOR) {
                 o = rbA[i] + (k0 + kc) * ES;
                 valid = k0 + kc < (uint32_t)kend;
+            } else if constexpr (GN) {  // channels k0 + row of this lane's pixels
+                o = rbA[i] + k0 * (uint32_t)g.P * ES;
+                valid = k0 < (uint32_t)kend && rbA[i] != kOutOfRange;
             } else if constexpr (WCHUNK) {  // this lane's chunk of the window cell
                 o = rbA[i] + wtap * ES;
                 valid = live && wtap != ~0u;
@@ -528,10 +561,44 @@ __device__ __forceinline__ void igemm_dual_body(const GemmArgs &A) {
 
     const int wp = wave / C::WGN, wc = wave % C::WGN;
     const int frow = lane & 31, fch = lane >> 5;
+    // GN: byte offset in the stage of this lane's first transpose read for
+    // fragment row block ip.  In 16-lane group G, lane t reads channel row
+    // 8*(G/2) + t/4 (+4 for the second read, +16 per MFMA K step), pixels
+    // 16*(G%2) + 4*(t%4) .. +3 of the block; it receives the 4 channels of
+    // pixel 16*(G%2) + t, so lanes 0-31 get channels 0-7 and lanes 32-63
+    // channels 8-15 of pixels lane%32: the MFMA A operand.
+    uint32_t aoff[GN ? TP : 1];
+    if constexpr (GN) {
+        const int G = lane >> 4, t = lane & 15;
+        const int kr = 8 * (G >> 1) + (t >> 2);
+        const int px = 16 * (G & 1) + 4 * (t & 3);
+#pragma unroll
+        for (int ip = 0; ip < TP; ++ip) {
+            const int p = wp * WPM + ip * 32 + px;
+            aoff[ip] = (uint32_t)((kr * CPRA + ((p / VEC) ^ (4 * (t >> 2)))) * 16 + (p % VEC) * 2);
+        }
+    }
+    typedef short v4s_t __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4s_t *lds_v4s_ptr;
+    typedef __attribute__((address_space(3))) char *lds_byte_ptr;
     uint4 fa[NG][TP], fb[NG][TC];
     auto lds_read = [&](const uint4 *st, int grp) {
+        if constexpr (GN) {
+            const lds_byte_ptr sb = (lds_byte_ptr)(lds_ptr_t)st;
 #pragma unroll
-        for (int ip = 0; ip < TP; ++ip) fa[grp][ip] = st[dual_slot<KCH>(wp * WPM + ip * 32 + frow, grp * 2 + fch)];
+            for (int ip = 0; ip < TP; ++ip) {
+                const v4s_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_v4s_ptr)(sb + aoff[ip] + grp * 16 * CPRA * 16));
+                const v4s_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_v4s_ptr)(sb + aoff[ip] + (grp * 16 + 4) * CPRA * 16));
+                const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+                fa[grp][ip] = make_uint4(l2.x, l2.y, h2.x, h2.y);
+            }
+        } else {
+#pragma unroll
+            for (int ip = 0; ip < TP; ++ip)
+                fa[grp][ip] = st[dual_slot<KCH>(wp * WPM + ip * 32 + frow, grp * 2 + fch)];
+        }
 #pragma unroll
         for (int ic = 0; ic < TC; ++ic)
             fb[grp][ic] = st[BM * KCH + dual_slot<KCH>(wc * WCN + ic * 32 + frow, grp * 2 + fch)];

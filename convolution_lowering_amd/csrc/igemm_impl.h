@@ -644,6 +644,17 @@ static hipError_t launch_tile(const GemmArgs &a, int tile, int splits, hipStream
             if (tile == TILE_256x64_ROWWIN) return go(igemm_rowwin_kernel<S, OUT_NCHW, 64, true>, 256, 64, 256);
         }
         return hipErrorInvalidValue;
+    } else if constexpr (FEED == FEED_GEMM_NCHW) {  // 1x1 NCHW read in place: 16-bit types, NCHW output
+        if constexpr (AVEC && sizeof(S) == 2 && OUT_NCHW) {
+            switch (tile) {
+                case TILE_256x128_DUAL: return go(igemm_dual_kernel<S, FEED, OUT_NCHW>, 256, 128);
+                case TILE_256x128_OCT: return go(igemm_oct_kernel<S, FEED, OUT_NCHW>, 256, 128, 512);
+                case TILE_128x64_QUAD: return go(igemm_quad_kernel<S, FEED, OUT_NCHW>, 128, 64);
+                case TILE_256x256_OCT: return go(igemm_oct_sq_kernel<S, FEED, OUT_NCHW>, 256, 256, 512);
+                default: return hipErrorInvalidValue;
+            }
+        }
+        return hipErrorInvalidValue;
     } else if constexpr (AVEC && (FEED == FEED_IND_CHUNK || FEED == FEED_WIN_CHUNK)) {  // one tap per chunk: the two-wavefront loops only
         switch (tile) {
             case TILE_256x128_DUAL: return go(igemm_dual_kernel<S, FEED, OUT_NCHW>, 256, 128);
@@ -680,7 +691,7 @@ hipError_t launch_feed(const GemmArgs &a, bool out_nchw, bool a_vec, bool b_vec,
                        hipStream_t st) {
     constexpr bool CAN_AVEC = FEED == FEED_ROWMAJOR || FEED == FEED_IND_NHWC || FEED == FEED_WIN ||
                               FEED == FEED_IND_CHUNK || FEED == FEED_WIN_CHUNK || FEED == FEED_ROWWIN ||
-                              FEED == FEED_ROWWIN_NCHW;
+                              FEED == FEED_ROWWIN_NCHW || FEED == FEED_GEMM_NCHW;
     constexpr bool CAN_NCHW = true;  // every feed can write NCHW output
     constexpr bool CAN_NHWC = FEED == FEED_ROWMAJOR || FEED == FEED_IND_NHWC || FEED == FEED_WIN ||
                               FEED == FEED_IND_CHUNK || FEED == FEED_WIN_CHUNK || FEED == FEED_ROWWIN ||

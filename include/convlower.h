@@ -88,7 +88,16 @@ typedef enum { CONV_DTYPE_FP32 = 0, CONV_DTYPE_BF16 = 1, CONV_DTYPE_FP16 = 2, CO
  *             valid for the two plain-GEMM shapes named under AUTO (The
  *             Indirect Convolution Algorithm, abstract: a 1x1 convolution is
  *             a GEMM call; "Unifying Convolutions and GEMM", section 4: a
- *             whole-input kernel is a dense layer).
+ *             whole-input kernel is a dense layer).  1x1 NCHW in a 16-bit
+ *             type with C_in a multiple of 32, H*W a multiple of 8 and more
+ *             than 64 output pixels: x[n] ([C_in][H*W]) is the operand
+ *             transposed and is read where it lies, MFMA fragments formed by
+ *             LDS transpose reads; no workspace beyond split-K partials (x
+ *             or w not 16-byte aligned: the element-gather loop, same
+ *             workspace).  Other 1x1 NCHW input with N >= 2 and C_in a
+ *             multiple of 8 (16-bit) or 4 (fp32): half the batch at a time
+ *             copied channels-last (workspace |x|/2); else the
+ *             element-gather loop.
  *   IM2COL    the baseline the lowering avoids: X_col materialised in the
  *             workspace ("Unifying Convolutions and GEMM", section 2; the
  *             workspace is then the whole im2col footprint), then the same

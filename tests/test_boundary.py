@@ -98,29 +98,67 @@ def test_workspace_below_im2col(name, layout, dtype):
         else:
             assert auto == (win if padded_win else ind)
     else:
-        # 1x1 NHWC: no workspace at all; 1x1 NCHW: the channels-last copy of
-        # half the batch; whole-input kernel: only the split-K partials
+        # 1x1 NHWC: no workspace at all; 1x1 NCHW: read in place for 16-bit
+        # types with C a multiple of 32 and H*W of 8, else the channels-last
+        # copy of half the batch; whole-input kernel: only the split-K partials
         whole = L.KH == L.H and L.KW == L.W
         if not whole:
             es = 4 if dtype == "fp32" else 2
             half = (L.N + 1) // 2 * L.C * L.H * L.W * es
-            assert auto == (0 if layout == "NHWC" else (half + 255) // 256 * 256)
+            if layout == "NHWC" or _gemm_nchw_eligible(L, dtype):
+                assert auto == 0
+            else:
+                assert auto == (half + 255) // 256 * 256
         assert cl.workspace_size(*_args(L, layout, dtype, "gemm")) == auto
+
+
+def _gemm_nchw_eligible(L, dtype):
+    """The 1x1 NCHW input read where it lies: 16-bit types, C a multiple of
+    32, H*W of 8, more than 64 output pixels."""
+    return (dtype != "fp32" and L.C % 32 == 0 and (L.H * L.W) % 8 == 0 and L.N * L.H * L.W > 64)
 
 
 @pytest.mark.parametrize("name", ["C3b", "C3d", "C5b"])
 def test_auto_workspace_on_1x1(name):
-    """NHWC 1x1 reads x as the GEMM operand in place; NCHW 1x1 copies half
-    the batch at a time channels-last (half of the im2col footprint, which
-    for 1x1 is |x|); a single NCHW image stays on the in-place NCHW feed."""
+    """NHWC 1x1 reads x as the GEMM operand in place, and so does NCHW 1x1
+    in 16-bit types (x[n] is the operand transposed); fp32 NCHW 1x1 copies
+    half the batch at a time channels-last (half of the im2col footprint,
+    which for 1x1 is |x|); a single fp32 NCHW image stays on the
+    element-gather NCHW feed."""
     L = LAYERS[name]
-    assert cl.workspace_size(*_args(L, "NHWC", "bf16", "auto")) == 0
-    assert cl.workspace_size(*_args(L, "NHWC", "bf16", "gemm")) == 0
-    im2col = cl.im2col_bytes(L.N, L.C, L.H, L.W, L.KH, L.KW, L.stride, L.pad, L.dilation, "bf16")
-    ws = cl.workspace_size(*_args(L, "NCHW", "bf16", "auto"))
+    for dt in ("bf16", "fp16"):
+        assert cl.workspace_size(*_args(L, "NHWC", dt, "auto")) == 0
+        assert cl.workspace_size(*_args(L, "NHWC", dt, "gemm")) == 0
+        assert cl.workspace_size(*_args(L, "NCHW", dt, "auto")) == 0
+        assert cl.workspace_size(*_args(L, "NCHW", dt, "gemm")) == 0
+    im2col = cl.im2col_bytes(L.N, L.C, L.H, L.W, L.KH, L.KW, L.stride, L.pad, L.dilation, "fp32")
+    ws = cl.workspace_size(*_args(L, "NCHW", "fp32", "auto"))
     assert 0 < ws <= (im2col // 2 + 255) // 256 * 256 < im2col
     one = L.with_batch(1)
-    assert cl.workspace_size(*_args(one, "NCHW", "bf16", "auto")) == 0
+    assert cl.workspace_size(*_args(one, "NCHW", "fp32", "auto")) == 0
+
+
+@pytest.mark.parametrize("shape,dtype,split", [
+    ((2, 1024, 8, 8, 100), "bf16", True), ((2, 1024, 8, 8, 100), "fp16", True),
+    ((3, 32, 6, 20, 40), "bf16", False), ((1, 64, 16, 24, 128), "fp16", False),
+    ((1, 64, 8, 8, 128), "bf16", None),   # 64 pixels: the half-batch/element forms
+    ((2, 48, 8, 8, 64), "bf16", None),    # C not a multiple of 32
+    ((2, 64, 7, 7, 64), "bf16", None),    # H*W not a multiple of 8
+])
+def test_nchw_1x1_in_place_plan(shape, dtype, split):
+    """The in-place 1x1 NCHW plan: no workspace, or only split-K partials
+    where few tiles leave CUs idle (split=True); shapes outside it keep the
+    half-batch copy or the element-gather feed (split=None)."""
+    N, C, H, W, Co = shape
+    ws = cl.workspace_size(N, C, H, W, Co, 1, 1, 1, 0, 1, "NCHW", dtype, "auto")
+    if split is None:
+        half = ((N + 1) // 2) * C * H * W * 2
+        assert ws == 0 if N == 1 else ws >= half
+    elif split:
+        assert 0 < ws < cl.im2col_bytes(N, C, H, W, 1, 1, 1, 0, 1, dtype)
+        assert ws % (N * H * W * Co * 4) == 0  # whole fp32 partial sums, one [M][Co] plane per split
+    else:
+        assert ws == 0
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp16"])

@@ -747,6 +747,55 @@ def test_nchw_1x1_halves_with_split_k(shape, dtype, integer):
         _assert_parity(y, y_ref, dn, dtype, f"split 1x1 {shape}")
 
 
+# 1x1 NCHW input read where it lies (16-bit types): x[n] is the GEMM's A
+# operand transposed, staged in LDS as it lies and turned into MFMA fragments
+# by transpose reads.  The four block shapes (128x64 for at most 64 output
+# channels, 256x128 with 32- and 64-channel K tiles, 256x256), ragged pixel
+# and channel counts, tiles across image boundaries, one image, and split K.
+GEMM_NCHW_CASES = [
+    # name, N, C, H, W, Co
+    ("quad-c3b", 2, 256, 56, 56, 64), ("dual-c3d", 2, 64, 56, 56, 256), ("oct-c5b", 3, 512, 28, 28, 512),
+    ("ragged", 3, 32, 6, 20, 40), ("one-image", 1, 64, 16, 24, 128), ("split-k", 2, 1024, 8, 8, 100),
+    ("dual-c96", 2, 96, 10, 12, 200), ("oct-sq", 42, 512, 28, 28, 512),
+]
+
+
+@pytest.mark.parametrize("case", GEMM_NCHW_CASES, ids=[c[0] for c in GEMM_NCHW_CASES])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_nchw_1x1_in_place(case, dtype):
+    """Against the whole oracle output, to the bar and (integer inputs) to
+    the exact result rounded once; the same bits as the channels-last call
+    (same tile, same K order); one element off 16-byte alignment, the
+    element-gather fallback meets the bar too."""
+    from convolution_lowering_amd.workloads import Layer
+    name, N, C, H, W, Co = case
+    L = Layer(name, N, C, H, W, Co, 1, 1, 1, 0, 1, "normal", "kaiming", 9100 + C + Co, (dtype,))
+    ws = cl.workspace_size(N, C, H, W, Co, 1, 1, 1, 0, 1, "NCHW", dtype, "auto")
+    assert (ws > 0) == (name == "split-k"), f"{name}: workspace {ws}"
+    for integer in (False, True):
+        x, w, b = make_inputs(L, dtype, "NCHW", integer=integer)
+        _say(f"[gpu] in-place 1x1 NCHW {name} {dtype} integer={integer}")
+        y = cl.conv2d_fwd(x.to(DEV), w.to(DEV), b.to(DEV), 1, 0, 1, "NCHW", "auto")
+        yn = cl.conv2d_fwd(x.permute(0, 2, 3, 1).contiguous().to(DEV), w.permute(0, 2, 3, 1).contiguous().to(DEV),
+                           b.to(DEV), 1, 0, 1, "NHWC", "auto")
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), yn.permute(0, 3, 1, 2).contiguous().view(torch.int16)), name
+        y_ref, dn = oracle.conv2d(x, w, b, 1, 0, 1, oracle.NCHW)
+        if integer:
+            exact = torch.from_numpy(y_ref).float().to(y.dtype).float()
+            assert torch.equal(y.float().cpu(), exact), name
+        else:
+            _assert_parity(y, y_ref, dn, dtype, f"in-place 1x1 NCHW {name}")
+    if N * C * H * W <= (1 << 22):
+        x, w, b = make_inputs(L, dtype, "NCHW")
+        _say(f"[gpu] in-place 1x1 NCHW {name} {dtype} misaligned x")
+        xd = _misaligned_copy(x)
+        y = cl.conv2d_fwd(xd, w.to(DEV), b.to(DEV), 1, 0, 1, "NCHW", "auto")
+        torch.cuda.synchronize()
+        y_ref, dn = oracle.conv2d(x, w, b, 1, 0, 1, oracle.NCHW)
+        _assert_parity(y, y_ref, dn, dtype, f"in-place 1x1 NCHW {name} misaligned")
+
+
 # NCHW input read in place by the window-row loop: widths that are and are
 # not multiples of the 8-column load (14, 20, 22, 28, 30, 34), padding 0 and 1,
 # ragged last tiles, one and several channel slices, 64- and 128-wide tiles.
