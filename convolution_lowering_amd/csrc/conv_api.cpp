@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <climits>
 #include <atomic>
 #include <mutex>
 #include <numeric>
@@ -67,22 +68,31 @@ struct Plan {
     size_t esize;
 };
 
-int out_extent(int in, int k, int s, int p, int d) {
+// Window placements along one axis (0: none fits); may exceed int for
+// extreme padding, which the callers refuse.
+long long out_extent(int in, int k, int s, int p, int d) {
     long long span = (long long)in + 2LL * p - (long long)d * (k - 1) - 1;
     if (span < 0) return 0;
-    return (int)(span / s) + 1;
+    return span / s + 1;
 }
 
 conv_status_t make_geom(int N, int C, int H, int W, int Co, int KH, int KW, int s, int p, int d, Geom *g) {
     if (N <= 0 || C <= 0 || H <= 0 || W <= 0 || Co <= 0 || KH <= 0 || KW <= 0 || s <= 0 || d <= 0 || p < 0)
         return CONV_ERR_INVALID_ARG;
-    int Ho = out_extent(H, KH, s, p, d), Wo = out_extent(W, KW, s, p, d);
-    if (Ho <= 0 || Wo <= 0) return CONV_ERR_INVALID_ARG;
+    const long long Hl = out_extent(H, KH, s, p, d), Wl = out_extent(W, KW, s, p, d);
+    if (Hl <= 0 || Wl <= 0) return CONV_ERR_INVALID_ARG;
+    // Extents, per-image and per-window counts kept as int: valid requests
+    // beyond that are not served.
+    if (Hl > INT_MAX || Wl > INT_MAX) return CONV_ERR_UNSUPPORTED;
+    const int Ho = (int)Hl, Wo = (int)Wl;
+    const long long P = (long long)Ho * Wo, T = (long long)KH * KW;
+    const long long Wwin = (long long)(Wo - 1) * s + (long long)(KW - 1) * d + 1;
+    if (P > INT_MAX || T > INT_MAX || Wwin > INT_MAX) return CONV_ERR_UNSUPPORTED;
     g->N = N; g->C = C; g->H = H; g->W = W; g->Co = Co; g->KH = KH; g->KW = KW;
     g->s = s; g->p = p; g->d = d; g->Ho = Ho; g->Wo = Wo;
-    g->P = Ho * Wo;  // checked below against the limit via M
-    g->T = KH * KW;
-    g->Wwin = (Wo - 1) * s + (KW - 1) * d + 1;
+    g->P = (int)P;
+    g->T = (int)T;
+    g->Wwin = (int)Wwin;
     g->M = (long long)N * Ho * Wo;
     g->K = (long long)C * KH * KW;
     return CONV_OK;
@@ -569,11 +579,13 @@ const char *conv_status_string(conv_status_t s) {
 
 conv_status_t conv2d_output_size(int H, int W, int KH, int KW, int stride, int pad, int dilation, int *ho_out,
                                  int *wo_out) {
-    Geom g;
-    conv_status_t st = make_geom(1, 1, H, W, 1, KH, KW, stride, pad, dilation, &g);
-    if (st != CONV_OK) return st;
-    if (ho_out) *ho_out = g.Ho;
-    if (wo_out) *wo_out = g.Wo;
+    if (H <= 0 || W <= 0 || KH <= 0 || KW <= 0 || stride <= 0 || dilation <= 0 || pad < 0)
+        return CONV_ERR_INVALID_ARG;
+    const long long Ho = out_extent(H, KH, stride, pad, dilation), Wo = out_extent(W, KW, stride, pad, dilation);
+    if (Ho <= 0 || Wo <= 0) return CONV_ERR_INVALID_ARG;
+    if (Ho > INT_MAX || Wo > INT_MAX) return CONV_ERR_UNSUPPORTED;
+    if (ho_out) *ho_out = (int)Ho;
+    if (wo_out) *wo_out = (int)Wo;
     return CONV_OK;
 }
 

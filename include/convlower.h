@@ -163,8 +163,9 @@ const char *conv_status_string(conv_status_t status);
 
 /* Output extents for the geometry (host only, no HIP call).  Returns
  * CONV_ERR_INVALID_ARG if a size is not positive, pad < 0, or no window
- * placement fits.  Formula: "Unifying Convolutions and GEMM", section 5,
- * with the dilation term.  ho_out / wo_out may be NULL. */
+ * placement fits; CONV_ERR_UNSUPPORTED if an extent exceeds INT_MAX.
+ * Formula: "Unifying Convolutions and GEMM", section 5, with the dilation
+ * term.  ho_out / wo_out may be NULL. */
 conv_status_t conv2d_output_size(int H, int W, int KH, int KW, int stride, int pad, int dilation,
                                  int *ho_out, int *wo_out);
 
