@@ -13,6 +13,8 @@
 // channels past C_in), multiplies every 32-pixel fragment of those rows
 // against its weights, stores the results with the bias added in fp32 and
 // one rounding, and moves on to the next group of rows.  No workspace.
+#include <type_traits>
+
 #include "igemm_impl.h"
 
 namespace convlower {
@@ -31,6 +33,12 @@ struct PatchArgs {
     int hgroups;        // ceil(Ho / R)
     int units;          // N * hgroups
     int ksteps;         // ceil(KH*KW / taps per K step)
+    // 16-bit input staged in 16-byte loads of 8 consecutive input columns
+    // (W a multiple of 8, x 16-byte aligned, below 2^31 bytes, at most
+    // 2 * kPatchThreads such loads of each channel per unit), else one
+    // element at a time.
+    int vec;
+    unsigned x_bytes;   // |x| in bytes when vec (the loads' range check)
 };
 
 // Four outputs, rounded once to nearest-even, into LDS at p.
@@ -56,8 +64,10 @@ __device__ __forceinline__ uint16_t raw16(const _Float16 *p, long long i) {
 // else two.  The persistent grid is sized to exactly the resident blocks.
 constexpr int patch_blocks_per_cu(int ks, int es, bool nchw) { return (ks <= 4 && es == 2 && !nchw) ? 3 : 2; }
 
-template <typename S, bool NCHW, int KS>
+// VS: the input staged in 16-byte loads (PatchArgs::vec; 16-bit types).
+template <typename S, bool NCHW, int KS, bool VS = false>
 __global__ __launch_bounds__(kPatchThreads, patch_blocks_per_cu(KS, (int)sizeof(S), NCHW)) void patch_conv_kernel(PatchArgs P) {
+    static_assert(!VS || sizeof(S) == 2, "16-byte staging for 16-bit types");
     using MF = MfmaShape<S, 32>;
     constexpr int ES = (int)sizeof(S);
     auto obuf_put4 = [](char *p, float a, float b, float c, float d) { obuf_put4_impl(S(), p, a, b, c, d); };
@@ -161,7 +171,7 @@ __global__ __launch_bounds__(kPatchThreads, patch_blocks_per_cu(KS, (int)sizeof(
     typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
     // 16-bit types: two channels per register (loaded into its halves);
     // fp32: one per register.
-    u16x2 hv[ES == 2 ? SB : 1][2];
+    u16x2 hv[ES == 2 && !VS ? SB : 1][2];
     float v[ES == 2 ? 1 : SB][4];
     auto load_batch = [&](int u, int base) {
         const int n = u / P.hgroups;
@@ -198,19 +208,109 @@ __global__ __launch_bounds__(kPatchThreads, patch_blocks_per_cu(KS, (int)sizeof(
         }
     };
 
-    if (blockIdx.x < (unsigned)P.units) load_batch(blockIdx.x, 0);
+    // ---- 16-bit input in 16-byte loads (P.vec): item i of a unit is input
+    // row hi_base + i / NCK, columns 8*(i % NCK) .. +7, all C_in channels: one
+    // load per channel plane (NCHW) or C_in loads of the 8 pixels' channel
+    // vectors (NHWC).  Every load is issued, with an offset past x where the
+    // row is outside the image (the range check returns zeros), so no load
+    // waits behind a branch.  A thread takes items tid and tid + 256.  The
+    // stage starts zeroed and its padding columns are never written.
+    const int NCK = g.W >> 3;  // 8-column chunks of an input row
+    const int nitems = P.RIN * NCK;
+    uint4 vb[VS ? 2 : 1][4];
+    const __amdgpu_buffer_rsrc_t x_rsrc = make_rsrc(P.x, VS ? P.x_bytes : 0u);
+    auto vload = [&](int u) {
+        if constexpr (!VS) return;
+        const int n = u / P.hgroups;
+        const int hi_base = (u - n * P.hgroups) * P.R * g.s - g.p;
+#pragma unroll
+        for (int k = 0; k < (VS ? 2 : 0); ++k) {
+            const int i = tid + k * kPatchThreads;
+            const int r = i / NCK, q = i - r * NCK;
+            const int hi = hi_base + r;
+            const bool in = i < nitems && hi >= 0 && hi < g.H;
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch) {
+                uint32_t off = kOutOfRange;
+                if (in && ch < g.C)
+                    off = NCHW ? (uint32_t)((((n * g.C + ch) * g.H + hi) * g.W + 8 * q) * 2)
+                               : (uint32_t)((((n * g.H + hi) * g.W + 8 * q) * g.C) * 2 + 16 * ch);
+                vb[k][ch] = ch < g.C ? __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, off, 0, 0))
+                                     : make_uint4(0u, 0u, 0u, 0u);
+            }
+        }
+    };
+    // Element e (16-bit) of the 16 bytes d.
+    auto h16 = [](const uint4 &d, int e) -> uint32_t {
+        const uint32_t w = e < 2 ? d.x : e < 4 ? d.y : e < 6 ? d.z : d.w;
+        return (e & 1) ? (w >> 16) : (w & 0xFFFFu);
+    };
+    auto vwrite = [&]() {
+        if constexpr (!VS) return;
+#pragma unroll
+        for (int k = 0; k < (VS ? 2 : 0); ++k) {
+            const int i = tid + k * kPatchThreads;
+            if (i >= nitems) continue;
+            const int r = i / NCK, q = i - r * NCK;
+            char *const row = sbytes + (size_t)r * P.WIN * PB;
+            // Pixel j (input column 8q + j, stage column 8q + p + j): its
+            // channels 0..3 as two words (zeros past C_in).
+            auto put = [&](int j, uint32_t lo, uint32_t hi) {
+                const int col = 8 * q + g.p + j;
+                if (col < P.WIN) *(uint2 *)(row + (size_t)col * PB) = make_uint2(lo, hi);
+            };
+            if constexpr (NCHW) {
+                // channel ch of the 8 pixels is load ch
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    put(j, h16(vb[k][0], j) | (h16(vb[k][1], j) << 16), h16(vb[k][2], j) | (h16(vb[k][3], j) << 16));
+            } else if (g.C == 4) {
+                // the 8 pixels' channel vectors are the stage pixels as they are
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const uint4 &v = vb[k][j >> 1];
+                    put(j, (j & 1) ? v.z : v.x, (j & 1) ? v.w : v.y);
+                }
+            } else {
+                // pixel j channel ch is element j*C + ch of the 8*C loaded
+                auto unpack = [&](auto cc) {
+                    constexpr int CC = decltype(cc)::value;
+                    auto el = [&](int j, int ch) -> uint32_t {
+                        return ch < CC ? h16(vb[k][(j * CC + ch) / 8], (j * CC + ch) % 8) : 0u;
+                    };
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) put(j, el(j, 0) | (el(j, 1) << 16), el(j, 2) | (el(j, 3) << 16));
+                };
+                if (g.C == 1) unpack(std::integral_constant<int, 1>{});
+                else if (g.C == 2) unpack(std::integral_constant<int, 2>{});
+                else unpack(std::integral_constant<int, 3>{});
+            }
+        }
+    };
+
+    if constexpr (VS) {
+        for (int i = tid; i < kPatchStageBytes / 16; i += kPatchThreads) stage[i] = make_uint4(0u, 0u, 0u, 0u);
+        if (blockIdx.x < (unsigned)P.units) vload(blockIdx.x);
+    } else if (blockIdx.x < (unsigned)P.units) {
+        load_batch(blockIdx.x, 0);
+    }
     for (int u = blockIdx.x; u < P.units; u += gridDim.x) {
         const int n = u / P.hgroups;
         const int ho0 = (u - n * P.hgroups) * P.R;
         const int rows = min(P.R, g.Ho - ho0);
 
-        __syncthreads();  // the previous unit's reads of the stage are done
-        write_batch(0);
-        for (int base = kPatchThreads * SB; base < npix; base += kPatchThreads * SB) {
-            load_batch(u, base);
-            write_batch(base);
+        __syncthreads();  // the previous unit's reads of the stage are done (and the stage zeroed)
+        if constexpr (VS) {
+            vwrite();
+            if (u + (int)gridDim.x < P.units) vload(u + gridDim.x);  // lands while this unit is multiplied
+        } else {
+            write_batch(0);
+            for (int base = kPatchThreads * SB; base < npix; base += kPatchThreads * SB) {
+                load_batch(u, base);
+                write_batch(base);
+            }
+            if (u + (int)gridDim.x < P.units) load_batch(u + gridDim.x, 0);  // lands while this unit is multiplied
         }
-        if (u + (int)gridDim.x < P.units) load_batch(u + gridDim.x, 0);  // lands while this unit is multiplied
         __syncthreads();
 
         // ---- 32-pixel fragments of the unit's output rows, one wavefront each
@@ -367,6 +467,10 @@ hipError_t launch_patch_conv(const void *x, const void *w, const void *bias, voi
     P.units = g.N * P.hgroups;
     const int TPS = dtype == CONV_DTYPE_FP32 ? 2 : 4;
     P.ksteps = (g.KH * g.KW + TPS - 1) / TPS;
+    const long long x_bytes = (long long)g.N * g.C * g.H * g.W * (dtype == CONV_DTYPE_FP32 ? 4 : 2);
+    P.vec = dtype != CONV_DTYPE_FP32 && g.W % 8 == 0 && (uintptr_t)x % 16 == 0 && x_bytes < (1LL << 31) - 16 &&
+            (long long)P.RIN * (g.W / 8) <= 2LL * kPatchThreads;
+    P.x_bytes = P.vec ? (unsigned)x_bytes : 0u;
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
@@ -388,12 +492,20 @@ hipError_t launch_patch_conv(const void *x, const void *w, const void *bias, voi
     if (dtype == CONV_DTYPE_FP32) {
         if (nhwc) by_ks(patch_conv_kernel<float, false, 3>, patch_conv_kernel<float, false, 4>, patch_conv_kernel<float, false, 8>, patch_conv_kernel<float, false, 13>, patch_conv_kernel<float, false, 16>);
         else by_ks(patch_conv_kernel<float, true, 3>, patch_conv_kernel<float, true, 4>, patch_conv_kernel<float, true, 8>, patch_conv_kernel<float, true, 13>, patch_conv_kernel<float, true, 16>);
-    } else if (dtype == CONV_DTYPE_FP16) {
-        if (nhwc) by_ks(patch_conv_kernel<_Float16, false, 3>, patch_conv_kernel<_Float16, false, 4>, patch_conv_kernel<_Float16, false, 8>, patch_conv_kernel<_Float16, false, 13>, patch_conv_kernel<_Float16, false, 16>);
-        else by_ks(patch_conv_kernel<_Float16, true, 3>, patch_conv_kernel<_Float16, true, 4>, patch_conv_kernel<_Float16, true, 8>, patch_conv_kernel<_Float16, true, 13>, patch_conv_kernel<_Float16, true, 16>);
     } else {
-        if (nhwc) by_ks(patch_conv_kernel<uint16_t, false, 3>, patch_conv_kernel<uint16_t, false, 4>, patch_conv_kernel<uint16_t, false, 8>, patch_conv_kernel<uint16_t, false, 13>, patch_conv_kernel<uint16_t, false, 16>);
-        else by_ks(patch_conv_kernel<uint16_t, true, 3>, patch_conv_kernel<uint16_t, true, 4>, patch_conv_kernel<uint16_t, true, 8>, patch_conv_kernel<uint16_t, true, 13>, patch_conv_kernel<uint16_t, true, 16>);
+        // 16-bit types: the two staging forms, each layout.
+        auto by_form = [&](auto s_tag) {
+            using T = decltype(s_tag);
+            if (P.vec) {
+                if (nhwc) by_ks(patch_conv_kernel<T, false, 3, true>, patch_conv_kernel<T, false, 4, true>, patch_conv_kernel<T, false, 8, true>, patch_conv_kernel<T, false, 13, true>, patch_conv_kernel<T, false, 16, true>);
+                else by_ks(patch_conv_kernel<T, true, 3, true>, patch_conv_kernel<T, true, 4, true>, patch_conv_kernel<T, true, 8, true>, patch_conv_kernel<T, true, 13, true>, patch_conv_kernel<T, true, 16, true>);
+            } else {
+                if (nhwc) by_ks(patch_conv_kernel<T, false, 3>, patch_conv_kernel<T, false, 4>, patch_conv_kernel<T, false, 8>, patch_conv_kernel<T, false, 13>, patch_conv_kernel<T, false, 16>);
+                else by_ks(patch_conv_kernel<T, true, 3>, patch_conv_kernel<T, true, 4>, patch_conv_kernel<T, true, 8>, patch_conv_kernel<T, true, 13>, patch_conv_kernel<T, true, 16>);
+            }
+        };
+        if (dtype == CONV_DTYPE_FP16) by_form(_Float16());
+        else by_form(uint16_t());
     }
     return hipGetLastError();
 }

@@ -321,6 +321,49 @@ def test_patch_small_channels(case, dtype, layout):
         _assert_parity(yn, y_ref, dn, dtype, f"patch {name}")
 
 
+# Rows of a multiple of 8 columns, 16-bit types: PATCH stages the input in
+# 16-byte loads of 8 columns.  Paddings past a load's width, a staged width
+# short of the last input column (stride 2), several images per grid pass.
+PATCH_VEC_CASES = [
+    # name, N, C, H, W, Co, KH, KW, s, p, d
+    ("c1-3x3-w16", 3, 1, 11, 16, 40, 3, 3, 1, 1, 1),
+    ("c2-5x5-s2-d2-w24", 2, 2, 19, 24, 70, 5, 5, 2, 3, 2),
+    ("c3-7x7-s2-w32", 2, 3, 30, 32, 64, 7, 7, 2, 3, 1),
+    ("c3-3x3-w128", 2, 3, 9, 128, 33, 3, 3, 1, 1, 1),
+    ("c3-3x3-s2-p0-w24", 4, 3, 13, 24, 64, 3, 3, 2, 0, 1),   # staged width 23: column 23 unused
+    ("c4-3x3-p9-w8", 2, 4, 7, 8, 20, 3, 3, 1, 9, 1),          # padding wider than a load
+    ("c2-1x1-w48", 5, 2, 5, 48, 64, 1, 1, 1, 0, 1),
+]
+
+
+@pytest.mark.parametrize("case", PATCH_VEC_CASES, ids=[c[0] for c in PATCH_VEC_CASES])
+@pytest.mark.parametrize("layout", ["NCHW", "NHWC"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_patch_vector_staging(case, dtype, layout):
+    """The 16-byte staging against the whole oracle output (integer inputs:
+    the exact result rounded once) and against the element-by-element
+    staging, which an x one element off 16-byte alignment selects: the same
+    bits."""
+    from convolution_lowering_amd.workloads import Layer
+    name, N, C, H, W, Co, KH, KW, s, p, d = case
+    L = Layer(name, N, C, H, W, Co, KH, KW, s, p, d, seed=91)
+    for integer in (True, False):
+        x, w, b = make_inputs(L, dtype, layout, integer=integer)
+        _say(f"[gpu] patch 16-byte staging {name} {dtype} {layout} integer={integer}")
+        y = cl.conv2d_fwd(x.to(DEV), w.to(DEV), b.to(DEV), s, p, d, layout, "patch")
+        y2 = cl.conv2d_fwd(_misaligned_copy(x), w.to(DEV), b.to(DEV), s, p, d, layout, "patch")
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), name
+        xr, wr, br = make_inputs(L, dtype, "NCHW", integer=integer)
+        y_ref, dn = oracle.conv2d(xr, wr, br, s, p, d, oracle.NCHW)
+        yn = _to_nchw(y, layout)
+        if integer:
+            exact = torch.from_numpy(y_ref).float().to(y.dtype).float()
+            assert torch.equal(yn.float().cpu(), exact), name
+        else:
+            _assert_parity(yn, y_ref, dn, dtype, f"patch 16-byte staging {name}")
+
+
 POINTWISE_CASES = [
     # name, N, C, H, W, Co
     ("c64-co72", 3, 64, 7, 9, 72),        # 189 pixel rows (ragged last unit), a second 8-channel chunk
