@@ -417,6 +417,14 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
             const int c = (int)(e - pix * CP);
             ((S *)a.xc)[e] = c < g.C ? ((const S *)a.x)[pix * g.C + c] : S(0);
         } else {
+            // Blocks go to the eight XCDs in turn (block b to XCD b % 8).  Each
+            // XCD takes a contiguous run of the tiles instead, so neighbouring
+            // pixel tiles of one channel group run on one XCD, one after the
+            // other, and the cache line a tile's rows share with the next
+            // tile's (plane rows need not start on a line) is read from HBM
+            // once, not by two XCDs.
+            const int nt8 = a.nt & ~7;
+            if (b < nt8) b = (b & 7) * (nt8 >> 3) + (b >> 3);
             const int pt = b % a.tiles_p;
             b /= a.tiles_p;
             const int ct = b % a.tiles_c, n = b / a.tiles_c;
