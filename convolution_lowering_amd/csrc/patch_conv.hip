@@ -313,45 +313,20 @@ __global__ __launch_bounds__(kPatchThreads, patch_blocks_per_cu(KS, (int)sizeof(
         }
         __syncthreads();
 
-        // ---- 32-pixel fragments of the unit's output rows, one wavefront each
-        for (int f = wave; f < rows * frags_per_row; f += kPatchThreads / 64) {
+        // ---- 32-pixel fragments of the unit's output rows.  A wavefront
+        // multiplies NF fragments together (two for long K loops: the two
+        // independent accumulator chains hide each other's LDS latency, and
+        // each weight fragment read serves both), then stores them one by one.
+        constexpr int NF = KS >= 8 ? 2 : 1;
+        const int nfrag = rows * frags_per_row;
+        // The epilogue of fragment f: bias in fp32, one rounding; the
+        // wavefront's 32 x 64 tile goes through its own LDS buffer so that it
+        // leaves in 16-byte pieces along the output's contiguous axis: for
+        // NHWC the 32 pixels' 64-channel runs (one contiguous block when
+        // C_out is 64), for NCHW 64 channel rows of 32 pixels.
+        auto emit = [&](int f, typename MF::acc_t (&acc)[2]) {
             const int r = f / frags_per_row;
             const int wo0 = (f - r * frags_per_row) * 32;
-            const int wo = min(wo0 + col, g.Wo - 1);  // past the row's end: a repeated pixel, not stored
-            const int pbase = (r * g.s * P.WIN + wo * g.s) * PB;
-            typename MF::acc_t acc[2] = {typename MF::acc_t{}, typename MF::acc_t{}};
-#pragma unroll
-            // Every K step up to the capacity KS, with no test against the
-            // layer's own count: past it the weights are zeros and every tap
-            // reads as zero, so those MFMAs add exact zeros, and the loop
-            // stays one straight block for the accumulators.
-            for (int ks = 0; ks < KS; ++ks) {
-                {
-                    uint4 a;
-                    const uint32_t o0 = toff[ks] & 0xFFFFu;
-                    if constexpr (ES == 2) {
-                        const uint32_t o1 = toff[ks] >> 16;
-                        const uint2 lo = o0 != 0xFFFFu ? *(const uint2 *)(sbytes + pbase + o0) : make_uint2(0u, 0u);
-                        const uint2 hi = o1 != 0xFFFFu ? *(const uint2 *)(sbytes + pbase + o1) : make_uint2(0u, 0u);
-                        a = make_uint4(lo.x, lo.y, hi.x, hi.y);
-                    } else {
-                        a = o0 != 0xFFFFu ? *(const uint4 *)(sbytes + pbase + o0) : make_uint4(0u, 0u, 0u, 0u);
-                    }
-#pragma unroll
-                    for (int ic = 0; ic < 2; ++ic) {
-                        const uint4 b = wlds[(ks * 2 + ic) * 64 + lane];
-                        if constexpr (NCHW)
-                            MF::mma(a, b, acc[ic]);  // rows: pixels, columns: channels
-                        else
-                            MF::mma(b, a, acc[ic]);  // rows: channels, columns: pixels
-                    }
-                }
-            }
-            // ---- epilogue: bias in fp32, one rounding; the wavefront's 32 x 64
-            // tile goes through its own LDS buffer so that it leaves in 16-byte
-            // pieces along the output's contiguous axis: for NHWC the 32 pixels'
-            // 64-channel runs (one contiguous block when C_out is 64), for
-            // NCHW 64 channel rows of 32 pixels.
             const int ho = ho0 + r;
             const int npx = min(32, g.Wo - wo0), nco = min(64, g.Co - cob);
 #pragma unroll
@@ -430,6 +405,54 @@ __global__ __launch_bounds__(kPatchThreads, patch_blocks_per_cu(KS, (int)sizeof(
                     }
                 }
             }
+        };
+        for (int f0 = wave * NF; f0 < nfrag; f0 += NF * (kPatchThreads / 64)) {
+            int pbase[NF];
+#pragma unroll
+            for (int j = 0; j < NF; ++j) {
+                const int f = min(f0 + j, nfrag - 1);  // past the last fragment: a repeated one, not stored
+                const int r = f / frags_per_row;
+                const int wo0 = (f - r * frags_per_row) * 32;
+                const int wo = min(wo0 + col, g.Wo - 1);  // past the row's end: a repeated pixel, not stored
+                pbase[j] = (r * g.s * P.WIN + wo * g.s) * PB;
+            }
+            typename MF::acc_t acc[NF][2];
+#pragma unroll
+            for (int j = 0; j < NF; ++j) acc[j][0] = acc[j][1] = typename MF::acc_t{};
+            // Every K step up to the capacity KS, with no test against the
+            // layer's own count: past it the weights are zeros and every tap
+            // reads as zero, so those MFMAs add exact zeros, and the loop
+            // stays one straight block for the accumulators.
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                uint4 a[NF];
+                const uint32_t o0 = toff[ks] & 0xFFFFu;
+#pragma unroll
+                for (int j = 0; j < NF; ++j) {
+                    if constexpr (ES == 2) {
+                        const uint32_t o1 = toff[ks] >> 16;
+                        const uint2 lo = o0 != 0xFFFFu ? *(const uint2 *)(sbytes + pbase[j] + o0) : make_uint2(0u, 0u);
+                        const uint2 hi = o1 != 0xFFFFu ? *(const uint2 *)(sbytes + pbase[j] + o1) : make_uint2(0u, 0u);
+                        a[j] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                    } else {
+                        a[j] = o0 != 0xFFFFu ? *(const uint4 *)(sbytes + pbase[j] + o0) : make_uint4(0u, 0u, 0u, 0u);
+                    }
+                }
+#pragma unroll
+                for (int ic = 0; ic < 2; ++ic) {
+                    const uint4 b = wlds[(ks * 2 + ic) * 64 + lane];
+#pragma unroll
+                    for (int j = 0; j < NF; ++j) {
+                        if constexpr (NCHW)
+                            MF::mma(a[j], b, acc[j][ic]);  // rows: pixels, columns: channels
+                        else
+                            MF::mma(b, a[j], acc[j][ic]);  // rows: channels, columns: pixels
+                    }
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < NF; ++j)
+                if (f0 + j < nfrag) emit(f0 + j, acc[j]);
         }
     }
 }
