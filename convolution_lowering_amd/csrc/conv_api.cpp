@@ -186,7 +186,12 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     const bool pad_c = allow_pad && g.C % VEC != 0;
     const long long im2col_bytes = g.M * g.K * (long long)pl->esize;
     const long long pad_w_bytes = (long long)g.Co * g.T * cpad * pl->esize;
-    const bool chunk_ind = pad_c && g.T <= 12 && (long long)g.H * g.W <= 65535 &&
+    // Up to 12 taps every two-wavefront loop holds the block's slice of the
+    // buffer in LDS; up to 32 only the 128 x 64 block (at most 64 output
+    // channels, more than 64 output pixels, the library's own loop choice).
+    const bool chunk_taps = g.T <= 12 || (g.T <= 32 && g.Co <= 64 && g.M > 64 &&
+                                          t_forced_main_loop == CONV_MAIN_LOOP_AUTO);
+    const bool chunk_ind = pad_c && chunk_taps && (long long)g.H * g.W <= 65535 &&
                            (long long)g.N * g.H * g.W * cpad * pl->esize + pad_w_bytes + (long long)g.P * g.T * 4 +
                                    1024 <
                                im2col_bytes;

@@ -45,6 +45,9 @@
 namespace convlower {
 
 constexpr int kDualMaxTaps = 12;  // KH*KW taps the LDS slice of the indirection buffer holds
+// ... and in the 128-row block of the padded-channel indirection feed (5x5
+// kernels over few channels), where the larger slice costs 8 KB of LDS.
+constexpr int kQuadChunkMaxTaps = 32;
 
 // Shape of one main-loop variant: block tile BM x BN, KCH 16-byte chunks
 // per stage row, NW wavefronts in a WGM x (NW / WGM) grid.
@@ -335,8 +338,9 @@ __device__ __forceinline__ void igemm_dual_body(const GemmArgs &A) {
 
     __shared__ uint4 stg[3][NSLOT];  // the three stages; the epilogue reuses them
     uint4 *const st0 = stg[0], *const st1 = stg[1], *const st2 = stg[2];
-    __shared__ uint16_t ibs[IND ? BM * kDualMaxTaps : 2];
-    static_assert((BM * kDualMaxTaps) % NTHR == 0, "slice must split evenly");
+    constexpr int MAXT = FEED == FEED_IND_CHUNK && BM == 128 ? kQuadChunkMaxTaps : kDualMaxTaps;
+    __shared__ uint16_t ibs[IND ? BM * MAXT : 2];
+    static_assert((BM * MAXT) % NTHR == 0, "slice must split evenly");
     __shared__ float bias_s[BN];
 
     const Geom &g = A.g;
@@ -360,7 +364,7 @@ __device__ __forceinline__ void igemm_dual_body(const GemmArgs &A) {
     // read some valid entry; their loads are out of range anyway.
     if constexpr (IND) {
         const uint32_t PT = (uint32_t)g.P * (uint32_t)g.T;
-        constexpr int NJ = BM * kDualMaxTaps / NTHR;
+        constexpr int NJ = BM * MAXT / NTHR;
         const int nent = BM * g.T;
         uint32_t idx = ((m0 % (uint32_t)g.P) * (uint32_t)g.T + (uint32_t)tid) % PT;
         int v[NJ];

@@ -82,10 +82,14 @@ def test_workspace_below_im2col(name, layout, dtype):
     if not plain_gemm:
         win = cl.workspace_size(*_args(L, layout, dtype, "im2win"))
         assert win < im2col
-        # channels not a whole number of 16-byte chunks with more than 12
-        # taps: AUTO takes the window tensor with cells padded to whole chunks
+        # channels not a whole number of 16-byte chunks with more taps than
+        # the indirection feed's LDS slice holds (12; 32 for at most 64
+        # output channels): AUTO takes the window tensor with cells padded to
+        # whole chunks
         es = 4 if dtype == "fp32" else 2
-        padded_win = (L.C * es) % 16 != 0 and L.KH * L.KW > 12
+        T = L.KH * L.KW
+        slice_ok = T <= 12 or (T <= 32 and L.Co <= 64 and L.N * Ho * Wo > 64)
+        padded_win = (L.C * es) % 16 != 0 and not slice_ok
         # the window rows in LDS where they apply, with more than 64 output
         # channels and at least 256 tiles of 256 x 128
         M = L.N * Ho * Wo
@@ -166,20 +170,32 @@ def test_nchw_1x1_in_place_plan(shape, dtype, split):
 @pytest.mark.parametrize("name", ["C3a", "C5a"])
 def test_auto_padded_window(name, dtype, layout):
     """The 7x7 stride-2 stem over 3 channels and the dilated 5x5 layer over
-    37: the window tensor with every (column, kernel row) cell's channels
-    padded to whole 16-byte chunks, plus the weights padded to (kh, kw, the
-    same channel count).  AUTO takes it unless the small-input-channel
-    kernel applies (the stem in 16-bit types), which needs no workspace."""
+    37.  IM2WIN: the window tensor with every (column, kernel row) cell's
+    channels padded to whole 16-byte chunks, plus the weights padded to (kh,
+    kw, the same channel count).  AUTO: the small-input-channel kernel where
+    it applies (the stem in 16-bit types: no workspace); else, for the 25-tap
+    5x5 layer with at most 64 output channels, the indirection feed over a
+    channels-last copy padded the same way (buffer + copy + weights); else
+    the padded window tensor."""
     L = LAYERS[name]
     es = 4 if dtype == "fp32" else 2
     cp = -(-L.C * es // 16) * 16 // es
     Ho, Wo = cl.output_size(L.H, L.W, L.KH, L.KW, L.stride, L.pad, L.dilation)
     Wwin = (Wo - 1) * L.stride + (L.KW - 1) * L.dilation + 1
     up = lambda v: (v + 255) // 256 * 256
-    want = up(L.N * Ho * Wwin * L.KH * cp * es) + up(L.Co * L.KH * L.KW * cp * es)
-    auto_want = 0 if _patch_eligible(L, dtype, Wo) else want
-    assert cl.workspace_size(*_args(L, layout, dtype, "auto")) == auto_want
+    T = L.KH * L.KW
+    want = up(L.N * Ho * Wwin * L.KH * cp * es) + up(L.Co * T * cp * es)
     assert cl.workspace_size(*_args(L, layout, dtype, "im2win")) == want
+    auto = cl.workspace_size(*_args(L, layout, dtype, "auto"))
+    if _patch_eligible(L, dtype, Wo):
+        assert auto == 0
+    elif T <= 32 and L.Co <= 64:
+        ind = up(Ho * Wo * T * 4) + up(L.N * L.H * L.W * cp * es) + up(L.Co * T * cp * es)
+        assert auto == cl.workspace_size(*_args(L, layout, dtype, "indirect"))
+        assert auto == ind
+        assert auto < cl.im2col_bytes(L.N, L.C, L.H, L.W, L.KH, L.KW, L.stride, L.pad, L.dilation, dtype)
+    else:
+        assert auto == want
 
 
 @pytest.mark.parametrize("name", sorted(LAYERS))
