@@ -153,20 +153,31 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
     pl->nhwc = layout == CONV_LAYOUT_NHWC;
     pl->esize = dtype_bytes(dtype);
     if (dtype == CONV_DTYPE_FP8_E4M3) {
-        // fp8 e4m3 inputs: channels-last tensors through the window-row loop
-        // (K tiles of 64 channels), no workspace.
+        // fp8 e4m3 inputs through the window-row loop (K tiles of 64
+        // channels).  Channels-last tensors are read as they lie (no
+        // workspace); NCHW input is first copied channels-last (|x| bytes,
+        // H*W a multiple of 4 so the copy reads whole 4-byte pieces) and its
+        // OIHW weights regrouped to (kh, kw, ci) (|w| bytes), as the 16-bit
+        // NCHW layers too wide for the in-place read are.
         if (algo != CONV_ALGO_AUTO && algo != CONV_ALGO_IM2WIN_LDS) return CONV_ERR_UNSUPPORTED;
-        if (!pl->nhwc || t_forced_main_loop != CONV_MAIN_LOOP_AUTO) return CONV_ERR_UNSUPPORTED;
+        if (t_forced_main_loop != CONV_MAIN_LOOP_AUTO) return CONV_ERR_UNSUPPORTED;
         const bool ok = g.s == 1 && g.d == 1 && g.KW == 3 && g.C % 64 == 0 && 255 / g.Wo + 2 <= kRowWinMaxSeg &&
-                        (long long)g.N * g.C * g.H * g.W <= kBufMax && g.K * g.Co <= kBufMax;
+                        (long long)g.N * g.C * g.H * g.W <= kBufMax && g.K * g.Co <= kBufMax &&
+                        (pl->nhwc || (g.H * g.W) % 4 == 0);
         if (!ok) return CONV_ERR_UNSUPPORTED;
         pl->feed = FEED_ROWWIN;
         pl->gm = g;
-        pl->out_nchw = false;
+        pl->out_nchw = !pl->nhwc;
         pl->tile = g.Co <= 64 ? TILE_256x64_ROWWIN : TILE_256x128_ROWWIN;
         pl->splits = 1;
         pl->kps = (int)((g.K + 127) / 128 * 128);
         pl->total = 0;
+        if (!pl->nhwc) {
+            pl->need_xcl = pl->need_wpack = true;
+            pl->off_xcl = 0;
+            pl->off_wpack = align_up((size_t)g.N * g.C * g.H * g.W);
+            pl->total = align_up(pl->off_wpack + (size_t)g.Co * g.K);
+        }
         return CONV_OK;
     }
 
@@ -735,7 +746,7 @@ conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias
             gc.N = g.N - n0 < pl.chunk_n ? g.N - n0 : pl.chunk_n;
             gc.M = (long long)gc.N * g.P;
             const char *xs = (const char *)x + (size_t)n0 * g.C * g.H * g.W * es;
-            if (launch_prep(xs, false, xc, g.C, nullptr, nullptr, false, nullptr, gc, pl.e16, s) != hipSuccess)
+            if (launch_prep(xs, false, xc, g.C, nullptr, nullptr, false, nullptr, gc, (int)pl.esize, s) != hipSuccess)
                 return CONV_ERR_HIP;
             a.g = gc;
             a.bias = bias;
@@ -790,7 +801,7 @@ conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias
         // One launch: the channels-last copy of x (rows of cp channels), the
         // indirection buffer over it and the weights in (kh, kw, ci) order.
         void *xc = ws + pl.off_xcl;
-        if (launch_prep(x, pl.nhwc, xc, pl.cp, ib_build, w, pl.nhwc, wp, g, pl.e16, s) != hipSuccess)
+        if (launch_prep(x, pl.nhwc, xc, pl.cp, ib_build, w, pl.nhwc, wp, g, (int)pl.esize, s) != hipSuccess)
             return CONV_ERR_HIP;
         a.a_src = xc;
         ib_build = nullptr;
@@ -807,7 +818,7 @@ conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias
         if (pl.feed == FEED_WIN_CHUNK) {
             if (launch_im2win_pad(x, xw, g, pl.cp, pl.nhwc, pl.e16, s) != hipSuccess) return CONV_ERR_HIP;
             // Weights zero-padded to (kh, kw, cp) order from either layout.
-            if (launch_prep(nullptr, pl.nhwc, nullptr, pl.cp, nullptr, w, pl.nhwc, wp, g, pl.e16, s) != hipSuccess)
+            if (launch_prep(nullptr, pl.nhwc, nullptr, pl.cp, nullptr, w, pl.nhwc, wp, g, (int)pl.esize, s) != hipSuccess)
                 return CONV_ERR_HIP;
             wp_done = true;
         } else if (launch_im2win(x, xw, g, pl.nhwc, pl.e16, s) != hipSuccess) {

@@ -128,7 +128,7 @@ hipError_t launch_im2win_pad(const void *x, void *xwin, const Geom &g, int cp, b
 // indirection buffer over that copy and the weights in (kh, kw, ci) order
 // with cp channels (from OIHW or OHWI).  Channels past C are zeros.
 hipError_t launch_prep(const void *x, bool nhwc_in, void *x_cl, int cp, int32_t *ib, const void *w, bool w_ohwi,
-                       void *w_out, const Geom &g, bool bf16, hipStream_t st);
+                       void *w_out, const Geom &g, int es, hipStream_t st);
 // 16-bit OIHW weights regrouped tap-major, [C/bk][KH][KW][Co][bk], for the NCHW
 // window-row loop (C a multiple of bk).
 hipError_t launch_pack_weights_tapmajor(const void *w, void *o, const Geom &g, int bk, hipStream_t st);

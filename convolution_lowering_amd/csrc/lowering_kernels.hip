@@ -457,8 +457,9 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
 }
 
 hipError_t launch_prep(const void *x, bool nhwc_in, void *x_cl, int cp, int32_t *ib, const void *w, bool w_ohwi,
-                       void *w_out, const Geom &g, bool bf16, hipStream_t st) {
-    const int ES = bf16 ? 2 : 4, HW = g.H * g.W;
+                       void *w_out, const Geom &g, int es, hipStream_t st) {
+    const int ES = es, HW = g.H * g.W;
+    const bool bf16 = es == 2;
     PrepArgs a;
     a.x = x;
     a.xc = x_cl;
@@ -486,6 +487,16 @@ hipError_t launch_prep(const void *x, bool nhwc_in, void *x_cl, int cp, int32_t 
         hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, st, a);
         return hipGetLastError();
     };
+    if (es == 1) {
+        // 8-bit elements (fp8 inputs): NCHW input read in 4- to 16-byte pieces only.
+        if (nhwc_in) return hipErrorInvalidValue;
+        switch (lw) {
+            case 16: return go(prep_kernel<uint8_t, 16, false>);
+            case 8: return go(prep_kernel<uint8_t, 8, false>);
+            case 4: return go(prep_kernel<uint8_t, 4, false>);
+            default: return hipErrorInvalidValue;
+        }
+    }
     if (nhwc_in) return bf16 ? go(prep_kernel<uint16_t, 2, true>) : go(prep_kernel<float, 4, true>);
     if (bf16) {
         switch (lw) {

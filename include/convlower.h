@@ -65,10 +65,13 @@ typedef enum { CONV_LAYOUT_NCHW = 0, CONV_LAYOUT_NHWC = 1 } conv_layout_t;
  * every case, rounded once to the element type at the store.
  * CONV_DTYPE_FP8_E4M3 is the exception: x and w hold OCP fp8 e4m3 bytes
  * (1 sign, 4 exponent, 3 mantissa bits, bias 7, no infinities), bias and y
- * are bf16, and y is rounded once to bf16.  It is served for channels-last
- * (NHWC) tensors by the window-row loop (CONV_ALGO_IM2WIN_LDS, which AUTO
- * means here) with C_in a multiple of 64 and x and w 16-byte aligned; any
- * other fp8 request returns CONV_ERR_UNSUPPORTED. */
+ * are bf16, and y is rounded once to bf16.  It is served by the window-row
+ * loop (CONV_ALGO_IM2WIN_LDS, which AUTO means here) for 3x3-wide stride-1
+ * layers with C_in a multiple of 64 and x and w 16-byte aligned:
+ * channels-last tensors as they lie (no workspace), NCHW tensors with H*W a
+ * multiple of 4 through a channels-last copy of x and the weights regrouped
+ * (kh, kw, ci) in the workspace (|x| + |w| bytes); any other fp8 request
+ * returns CONV_ERR_UNSUPPORTED. */
 typedef enum { CONV_DTYPE_FP32 = 0, CONV_DTYPE_BF16 = 1, CONV_DTYPE_FP16 = 2, CONV_DTYPE_FP8_E4M3 = 3 } conv_dtype_t;
 
 /* Which lowering feeds the contraction.

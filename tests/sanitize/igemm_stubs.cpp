@@ -24,7 +24,7 @@ hipError_t launch_direct_conv(const void *, const void *, const void *, void *, 
 hipError_t launch_im2col(const void *, void *, const Geom &, bool, bool, hipStream_t) { return never(); }
 hipError_t launch_ablate(const GemmArgs &, int, bool, int, hipStream_t) { return never(); }
 hipError_t launch_im2win_pad(const void *, void *, const Geom &, int, bool, bool, hipStream_t) { return never(); }
-hipError_t launch_prep(const void *, bool, void *, int, int32_t *, const void *, bool, void *, const Geom &, bool,
+hipError_t launch_prep(const void *, bool, void *, int, int32_t *, const void *, bool, void *, const Geom &, int,
                        hipStream_t) {
     return never();
 }

@@ -462,16 +462,22 @@ def test_ablation_loops_plan_on_the_host():
         cl.force_main_loop("auto")
 
 
-def test_fp8_plans_only_channels_last_window_rows():
-    """fp8 e4m3 inputs run the window-row loop on channels-last tensors with
-    C_in a multiple of 64 (no workspace); NCHW, other algorithms, C_in not a
-    multiple of 64 and the lowering transforms are refused on the host."""
+def test_fp8_plans_only_window_rows():
+    """fp8 e4m3 inputs run the window-row loop with C_in a multiple of 64:
+    channels-last tensors with no workspace, NCHW tensors (H*W a multiple of
+    4) with the channels-last copy of x and the regrouped weights (|x| + |w|
+    bytes); other algorithms, C_in not a multiple of 64, stride 2, NCHW with
+    H*W not a multiple of 4 and the lowering transforms are refused on the
+    host."""
     L = LAYERS["C2"]
+    up = lambda v: (v + 255) // 256 * 256
     assert cl.workspace_size(*_args(L, "NHWC", "fp8", "auto")) == 0
     assert cl.workspace_size(*_args(L, "NHWC", "fp8", "im2win_lds")) == 0
-    for args in (_args(L, "NCHW", "fp8", "auto"), _args(L, "NHWC", "fp8", "indirect"),
+    assert cl.workspace_size(*_args(L, "NCHW", "fp8", "auto")) == up(L.N * L.C * L.H * L.W) + up(L.Co * L.C * 9)
+    for args in (_args(L, "NHWC", "fp8", "indirect"), _args(L, "NCHW", "fp8", "indirect"),
                  _args(L, "NHWC", "fp8", "im2col"), (2, 32, 16, 16, 64, 3, 3, 1, 1, 1, "NHWC", "fp8", "auto"),
-                 (2, 64, 16, 16, 64, 3, 3, 2, 1, 1, "NHWC", "fp8", "auto")):
+                 (2, 64, 16, 16, 64, 3, 3, 2, 1, 1, "NHWC", "fp8", "auto"),
+                 (2, 64, 15, 15, 64, 3, 3, 1, 1, 1, "NCHW", "fp8", "auto")):
         with pytest.raises(cl.ConvLowerError) as e:
             cl.workspace_size(*args)
         assert e.value.code == UNSUPPORTED, args

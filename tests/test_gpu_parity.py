@@ -930,6 +930,34 @@ FP8_CASES = [
 
 
 @pytest.mark.parametrize("case", FP8_CASES, ids=[c[0] for c in FP8_CASES])
+def test_fp8_window_rows_nchw(case):
+    """NCHW fp8: the channels-last copy and (kh, kw, ci) weights in the
+    workspace, then the same loop: the same bits as the NHWC call, and the
+    bar against the oracle (integer inputs: the exact result rounded once)."""
+    from convolution_lowering_amd.workloads import Layer
+    name, N, C, H, W, Co = case
+    L = Layer(name, N, C, H, W, Co, 3, 3, 1, 1, 1, "normal", "kaiming", 9300 + C, ("fp8",))
+    ws = cl.workspace_size(N, C, H, W, Co, 3, 3, 1, 1, 1, "NCHW", "fp8", "auto")
+    up = lambda v: (v + 255) // 256 * 256
+    assert ws == up(N * C * H * W) + up(Co * C * 9), name
+    for integer in (True, False):
+        x, w, b = make_inputs(L, "fp8", "NCHW", integer=integer)
+        _say(f"[gpu] fp8 NCHW {name} integer={integer}")
+        y = cl.conv2d_fwd(x.to(DEV), w.to(DEV), b.to(DEV), 1, 1, 1, "NCHW", "auto")
+        xn, wn = x.permute(0, 2, 3, 1).contiguous(), w.permute(0, 2, 3, 1).contiguous()
+        yn = cl.conv2d_fwd(xn.to(DEV), wn.to(DEV), b.to(DEV), 1, 1, 1, "NHWC", "auto")
+        torch.cuda.synchronize()
+        assert y.dtype == torch.bfloat16
+        assert torch.equal(y.view(torch.int16), yn.permute(0, 3, 1, 2).contiguous().view(torch.int16)), name
+        y_ref, dn = oracle.conv2d(x, w, b, 1, 1, 1, oracle.NCHW)
+        if integer:
+            exact = torch.from_numpy(y_ref).float().to(torch.bfloat16).float()
+            assert torch.equal(y.float().cpu(), exact), name
+        else:
+            _assert_parity(y, y_ref, dn, "bf16", f"fp8 NCHW {name}")
+
+
+@pytest.mark.parametrize("case", FP8_CASES, ids=[c[0] for c in FP8_CASES])
 def test_fp8_window_rows(case):
     """e4m3 x and w, fp32 sums, bf16 y: on integer inputs (exact in e4m3) y is
     the exact result rounded once to bf16; on normal inputs the bf16 bar
