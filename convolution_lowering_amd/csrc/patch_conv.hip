@@ -84,6 +84,8 @@ __global__ __launch_bounds__(kPatchThreads, patch_blocks_per_cu(KS, (int)sizeof(
     constexpr int OROWS = NCHW ? 64 : 32;
     __shared__ uint4 obuf[4][(OROWS * ORS) / 16];
     __shared__ float4 bias_s[16];  // the block's 64 channels' bias (0 past C_out or without bias)
+    __shared__ uint4 zero16;       // what a tap past the last reads
+    const char *const zb = (const char *)&zero16;
 
     const Geom &g = P.g;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -151,6 +153,7 @@ __global__ __launch_bounds__(kPatchThreads, patch_blocks_per_cu(KS, (int)sizeof(
     for (int ks = wave; ks < KS; ks += kPatchThreads / 64)  // published by the unit loop's first barrier
         for (int ic = 0; ic < 2; ++ic) wlds[(ks * 2 + ic) * 64 + lane] = wfrag(ks, ic);
 
+    if (tid == 64) zero16 = make_uint4(0u, 0u, 0u, 0u);  // published by the unit loop's first barrier
     if (tid < 64) {
         const int co = cob + tid;
         ((float *)bias_s)[tid] = (P.bias && co < g.Co) ? bits_to_f32(S(), elem_bits((const S *)P.bias, co)) : 0.f;
@@ -422,33 +425,42 @@ __global__ __launch_bounds__(kPatchThreads, patch_blocks_per_cu(KS, (int)sizeof(
             // Every K step up to the capacity KS, with no test against the
             // layer's own count: past it the weights are zeros and every tap
             // reads as zero, so those MFMAs add exact zeros, and the loop
-            // stays one straight block for the accumulators.
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                uint4 a[NF];
+            // stays one straight block for the accumulators.  A tap past the
+            // last reads the 16 zero bytes at zb (an address select, not a
+            // branch), and each K step's fragments are read from LDS while
+            // the previous step's MFMAs run.
+            auto frags = [&](int ks, uint4 (&a)[NF], uint4 (&b)[2]) {
                 const uint32_t o0 = toff[ks] & 0xFFFFu;
 #pragma unroll
                 for (int j = 0; j < NF; ++j) {
+                    const char *p0 = o0 != 0xFFFFu ? sbytes + pbase[j] + o0 : zb;
                     if constexpr (ES == 2) {
                         const uint32_t o1 = toff[ks] >> 16;
-                        const uint2 lo = o0 != 0xFFFFu ? *(const uint2 *)(sbytes + pbase[j] + o0) : make_uint2(0u, 0u);
-                        const uint2 hi = o1 != 0xFFFFu ? *(const uint2 *)(sbytes + pbase[j] + o1) : make_uint2(0u, 0u);
+                        const char *p1 = o1 != 0xFFFFu ? sbytes + pbase[j] + o1 : zb;
+                        const uint2 lo = *(const uint2 *)p0, hi = *(const uint2 *)p1;
                         a[j] = make_uint4(lo.x, lo.y, hi.x, hi.y);
                     } else {
-                        a[j] = o0 != 0xFFFFu ? *(const uint4 *)(sbytes + pbase[j] + o0) : make_uint4(0u, 0u, 0u, 0u);
+                        a[j] = *(const uint4 *)p0;
                     }
                 }
 #pragma unroll
-                for (int ic = 0; ic < 2; ++ic) {
-                    const uint4 b = wlds[(ks * 2 + ic) * 64 + lane];
+                for (int ic = 0; ic < 2; ++ic) b[ic] = wlds[(ks * 2 + ic) * 64 + lane];
+            };
+            uint4 fa[2][NF], fb[2][2];
+            frags(0, fa[0], fb[0]);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int c = ks & 1;
+                if (ks + 1 < KS) frags(ks + 1, fa[c ^ 1], fb[c ^ 1]);
+#pragma unroll
+                for (int ic = 0; ic < 2; ++ic)
 #pragma unroll
                     for (int j = 0; j < NF; ++j) {
                         if constexpr (NCHW)
-                            MF::mma(a[j], b, acc[j][ic]);  // rows: pixels, columns: channels
+                            MF::mma(fa[c][j], fb[c][ic], acc[j][ic]);  // rows: pixels, columns: channels
                         else
-                            MF::mma(b, a[j], acc[j][ic]);  // rows: channels, columns: pixels
+                            MF::mma(fb[c][ic], fa[c][j], acc[j][ic]);  // rows: channels, columns: pixels
                     }
-                }
             }
 #pragma unroll
             for (int j = 0; j < NF; ++j)
