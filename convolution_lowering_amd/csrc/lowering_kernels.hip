@@ -409,13 +409,20 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     const int CP = a.cp;
     int b = blockIdx.x;
     if (b < a.nt) {
-        if constexpr (NHWC_IN) {  // one thread per (pixel, channel) of the copy
+        if constexpr (NHWC_IN) {  // one thread per 16-byte chunk (pixel, channels 8q.. or 4q..) of the copy
+            constexpr int V = 16 / (int)sizeof(S);
+            const int CQ = CP / V;  // chunks per pixel row of the copy
             const long long e = (long long)b * 256 + threadIdx.x;
-            const long long total = (long long)g.N * g.H * g.W * CP;
-            if (e >= total) return;
-            const long long pix = e / CP;
-            const int c = (int)(e - pix * CP);
-            ((S *)a.xc)[e] = c < g.C ? ((const S *)a.x)[pix * g.C + c] : S(0);
+            if (e >= (long long)g.N * g.H * g.W * CQ) return;
+            const long long pix = e / CQ;
+            const int c0 = (int)(e - pix * CQ) * V;
+            const S *src = (const S *)a.x + pix * g.C;
+            S v[V];
+#pragma unroll
+            for (int j = 0; j < V; ++j) v[j] = c0 + j < g.C ? src[c0 + j] : S(0);
+            uint4 out;
+            __builtin_memcpy(&out, v, 16);
+            *(uint4 *)((S *)a.xc + pix * CP + c0) = out;
         } else {
             // Blocks go to the eight XCDs in turn (block b to XCD b % 8).  Each
             // XCD takes a contiguous run of the tiles instead, so neighbouring
@@ -472,7 +479,7 @@ hipError_t launch_prep(const void *x, bool nhwc_in, void *x_cl, int cp, int32_t 
     a.tiles_p = (HW + kTrP - 1) / kTrP;
     a.tiles_c = (cp + kTrC - 1) / kTrC;
     if (x_cl)
-        a.nt = nhwc_in ? (int)blocks_for((long long)g.N * HW * cp, 256) : g.N * a.tiles_c * a.tiles_p;
+        a.nt = nhwc_in ? (int)blocks_for((long long)g.N * HW * (cp / (16 / ES)), 256) : g.N * a.tiles_c * a.tiles_p;
     else
         a.nt = 0;
     a.nib = ib ? (int)blocks_for((long long)g.P * g.T, 256) : 0;
