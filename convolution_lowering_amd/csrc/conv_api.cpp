@@ -64,7 +64,8 @@ struct Plan {
     bool rows16;  // the feed can read X_col rows in 16-byte chunks (by shape)
     bool force_element;  // main loop forced to the element-gather loop
     int ablate;          // a CONV_MAIN_LOOP_ABL_ variant forced (0: none)
-    size_t off_ibuf, off_win, off_xcl, off_wpack, off_col, off_part, total;
+    bool sk;             // the ping-pong loop in its stream-K form (partial tiles and flags in the workspace)
+    size_t off_ibuf, off_win, off_xcl, off_wpack, off_col, off_part, off_sk, total;
     size_t esize;
 };
 
@@ -559,6 +560,21 @@ conv_status_t make_plan(int N, int C, int H, int W, int Co, int KH, int KW, int 
         pl->off_part = off;
         off = align_up(off + (size_t)splits * Mt * g.Co * sizeof(float));
     }
+    // The ping-pong loop runs one 512 x 128 tile per CU.  With well under one
+    // tile per CU, its stream-K form shares all tiles' K steps among
+    // kSkBlocks blocks instead, at the cost of one fp32 partial tile per
+    // block written and read back, kept below the im2col footprint.  Measured
+    // on 3x3 512->512 @14 (channels-last): fp32 with 196 tiles 1116 -> 929-950
+    // us; bf16 with 100 tiles 110 -> 91 us, 147 tiles 125 -> 116 us, but 196
+    // tiles unchanged (the chip is then near what this loop reaches in bf16
+    // with fewer CUs busy), so 16-bit types take it up to 3/4 of a tile per CU.
+    const long long sk_bytes = (long long)kSkBlocks * (long long)kSkSlotBytes + 4LL * kSkBlocks;
+    const bool sk_few = pl->e16 ? blocks * 4 <= kSkBlocks * 3 : blocks * 8 <= kSkBlocks * 7;
+    if (pl->tile == TILE_512x128_ROWWIN_PP && sk_few && (long long)off + sk_bytes < im2col_bytes) {
+        pl->sk = true;
+        pl->off_sk = off;
+        off = align_up(off + (size_t)sk_bytes);
+    }
     pl->total = off;
     return CONV_OK;
 }
@@ -774,6 +790,7 @@ conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias
         Plan fb = pl;
         fb.feed = FEED_IND_NHWC;
         fb.tile = TILE_128x128;
+        fb.sk = false;
         return run(fb, x, w, bias, y, prebuilt, stream, workspace, workspace_bytes);
     }
     if (pl.feed == FEED_ROWWIN_NCHW && (uintptr_t)x % 16) {
@@ -784,6 +801,7 @@ conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias
         fb.feed = FEED_IND_NCHW;
         fb.tile = TILE_128x128;
         fb.need_wpack = false;
+        fb.sk = false;
         return run(fb, x, w, bias, y, prebuilt, stream, workspace, workspace_bytes);
     }
     // Offsets of the indirection buffer follow the layout the main loop reads.
@@ -797,17 +815,28 @@ conv_status_t run(const Plan &pl, const void *x, const void *w, const void *bias
     }
     void *wp = pl.need_wpack ? (void *)(ws + pl.off_wpack) : nullptr;
     bool wp_done = false;
+    // Stream-K: partial tiles, then the flags, which start each call at zero.
+    uint32_t *skf = nullptr;
+    if (pl.sk) {
+        a.skp = (float *)(ws + pl.off_sk);
+        skf = (uint32_t *)(ws + pl.off_sk + (size_t)kSkBlocks * kSkSlotBytes);
+        a.skf = skf;
+    }
     if (pl.need_xcl) {
         // One launch: the channels-last copy of x (rows of cp channels), the
-        // indirection buffer over it and the weights in (kh, kw, ci) order.
+        // indirection buffer over it and the weights in (kh, kw, ci) order
+        // (and the stream-K flags cleared).
         void *xc = ws + pl.off_xcl;
-        if (launch_prep(x, pl.nhwc, xc, pl.cp, ib_build, w, pl.nhwc, wp, g, (int)pl.esize, s) != hipSuccess)
+        if (launch_prep(x, pl.nhwc, xc, pl.cp, ib_build, w, pl.nhwc, wp, g, (int)pl.esize, s, skf,
+                        skf ? kSkBlocks : 0) != hipSuccess)
             return CONV_ERR_HIP;
+        skf = nullptr;
         a.a_src = xc;
         ib_build = nullptr;
         wp_done = true;
     }
     if (ib_build && launch_build_indirection(ib_build, g, ib_rows, s) != hipSuccess) return CONV_ERR_HIP;
+    if (skf && launch_zero_words(skf, kSkBlocks, s) != hipSuccess) return CONV_ERR_HIP;
     if (pl.need_col) {
         void *xcol = ws + pl.off_col;
         if (launch_im2col(x, xcol, g, pl.nhwc, pl.e16, s) != hipSuccess) return CONV_ERR_HIP;
@@ -881,6 +910,10 @@ conv_status_t conv2d_fwd_noalloc(const void *x, const void *w, const void *bias,
     Plan pl;
     conv_status_t st = make_plan(N, C_in, H, W, C_out, KH, KW, stride, pad, dilation, layout, dtype, algo, &pl);
     if (st != CONV_OK) return st;
+    if (pl.total > kScratchBytes && pl.sk) {  // the stream-K regions are the last: without them it may fit
+        pl.sk = false;
+        pl.total = pl.off_sk;
+    }
     if (pl.total > kScratchBytes) return CONV_ERR_WORKSPACE;
     void *ws = nullptr;
     if (pl.total > 0) {

@@ -56,7 +56,19 @@ struct GemmArgs {
     uint32_t b_bytes;     // size of b in bytes (< 2^31 on the vector paths)
     uint32_t c_shift;     // C = c_odd << c_shift; c_inv * c_odd == 1 (mod 2^32): exact
     uint32_t c_inv;       // division of a channels-last indirection entry by C
+    // Stream-K form of the ping-pong window-row loop (null: one block per
+    // tile): the K steps of all tiles shared evenly by kSkBlocks blocks.  A
+    // tile split between blocks is finished by the block that holds its last
+    // K step, which adds the fp32 partial tiles of the others (one slot of
+    // kSkSlotBytes per block in skp, and a ready flag per block in skf,
+    // zero when the launch starts).
+    float *skp;
+    uint32_t *skf;
 };
+// Stream-K grid: 32 blocks on each of MI355X's 8 XCDs (one per compute unit),
+// and the bytes of one block's partial tile (512 x 128 fp32 sums).
+constexpr int kSkBlocks = 256;
+constexpr size_t kSkSlotBytes = 512 * 128 * sizeof(float);
 
 // Tile shapes of the main loop (block = 256 threads = 4 wavefronts, 2x2).
 // TILE_256x128_DUAL and TILE_256x128_OCT are the 256 x 128 main loops with
@@ -127,8 +139,12 @@ hipError_t launch_im2win_pad(const void *x, void *xwin, const Geom &g, int cp, b
 // (from NCHW or NHWC input; null x_cl: none), plus (when given) the
 // indirection buffer over that copy and the weights in (kh, kw, ci) order
 // with cp channels (from OIHW or OHWI).  Channels past C are zeros.
+// `zero` (when given): nzero 32-bit words set to zero by the same launch.
 hipError_t launch_prep(const void *x, bool nhwc_in, void *x_cl, int cp, int32_t *ib, const void *w, bool w_ohwi,
-                       void *w_out, const Geom &g, int es, hipStream_t st);
+                       void *w_out, const Geom &g, int es, hipStream_t st, uint32_t *zero = nullptr,
+                       int nzero = 0);
+// n 32-bit words set to zero (a kernel, not a memset: safe in captured graphs).
+hipError_t launch_zero_words(uint32_t *p, int n, hipStream_t st);
 // 16-bit OIHW weights regrouped tap-major, [C/bk][KH][KW][Co][bk], for the NCHW
 // window-row loop (C a multiple of bk).
 hipError_t launch_pack_weights_tapmajor(const void *w, void *o, const Geom &g, int bk, hipStream_t st);

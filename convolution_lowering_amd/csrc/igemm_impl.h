@@ -619,8 +619,9 @@ namespace convlower {
 template <typename S, int FEED, bool AVEC, bool BVEC, bool OUT_NCHW>
 static hipError_t launch_tile(const GemmArgs &a, int tile, int splits, hipStream_t st) {
     const Geom &g = a.g;
-    auto go = [&](auto kern, int BM, int BN, int threads = kThreads) {
+    auto go = [&](auto kern, int BM, int BN, int threads = kThreads, bool sk = false) {
         dim3 grid((unsigned)(((g.M + BM - 1) / BM) * ((g.Co + BN - 1) / BN)), 1, (unsigned)splits);
+        if (sk) grid = dim3((unsigned)kSkBlocks);
         hipEvent_t t0, t1;
         take_main_loop_events(&t0, &t1);
         if (t0 || t1)
@@ -635,7 +636,10 @@ static hipError_t launch_tile(const GemmArgs &a, int tile, int splits, hipStream
             if (tile == TILE_256x128_ROWWIN) return go(igemm_rowwin_kernel<S, OUT_NCHW>, 256, 128, 256);
             if (tile == TILE_256x64_ROWWIN) return go(igemm_rowwin_kernel<S, OUT_NCHW, 64>, 256, 64, 256);
             if constexpr (sizeof(S) > 1)
-                if (tile == TILE_512x128_ROWWIN_PP) return go(igemm_rowwin_pp_kernel<S, OUT_NCHW>, 512, 128, 512);
+                if (tile == TILE_512x128_ROWWIN_PP) {
+                    if (a.skp) return go(igemm_rowwin_pp_kernel<S, OUT_NCHW, true>, 512, 128, 512, true);
+                    return go(igemm_rowwin_pp_kernel<S, OUT_NCHW>, 512, 128, 512);
+                }
         }
         return hipErrorInvalidValue;
     } else if constexpr (FEED == FEED_ROWWIN_NCHW) {  // NCHW read in place: 16-bit types, NCHW output

@@ -400,6 +400,8 @@ struct PrepArgs {
     int nt, nib;           // blocks of the first two kinds
     long long nw;          // weight elements to write (0: none)
     int w_ohwi;            // weights given as OHWI (else OIHW)
+    uint32_t *zero;        // words block 0 sets to zero (nzero of them), or null
+    int nzero;
 };
 
 template <typename S, int LW, bool NHWC_IN>
@@ -408,6 +410,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     const Geom &g = a.g;
     const int CP = a.cp;
     int b = blockIdx.x;
+    if (b == 0)
+        for (int i = threadIdx.x; i < a.nzero; i += 256) a.zero[i] = 0u;
     if (b < a.nt) {
         if constexpr (NHWC_IN) {  // one thread per 16-byte chunk (pixel, channels 8q.. or 4q..) of the copy
             constexpr int V = 16 / (int)sizeof(S);
@@ -464,7 +468,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
 }
 
 hipError_t launch_prep(const void *x, bool nhwc_in, void *x_cl, int cp, int32_t *ib, const void *w, bool w_ohwi,
-                       void *w_out, const Geom &g, int es, hipStream_t st) {
+                       void *w_out, const Geom &g, int es, hipStream_t st, uint32_t *zero, int nzero) {
     const int ES = es, HW = g.H * g.W;
     const bool bf16 = es == 2;
     PrepArgs a;
@@ -484,7 +488,10 @@ hipError_t launch_prep(const void *x, bool nhwc_in, void *x_cl, int cp, int32_t 
         a.nt = 0;
     a.nib = ib ? (int)blocks_for((long long)g.P * g.T, 256) : 0;
     a.nw = w_out ? (long long)g.Co * g.T * cp : 0;
-    const long long blocks = (long long)a.nt + a.nib + blocks_for(a.nw, 256);
+    a.zero = zero;
+    a.nzero = zero ? nzero : 0;
+    long long blocks = (long long)a.nt + a.nib + blocks_for(a.nw, 256);
+    if (blocks == 0 && a.nzero > 0) blocks = 1;
     if (blocks == 0) return hipSuccess;
     // Widest load that keeps every chunk inside its channel plane and aligned.
     int lw = 16;
@@ -624,6 +631,17 @@ hipError_t launch_splitk_reduce(const float *part, const void *bias, void *y, co
         reduce_typed<_Float16>(part, bias, y, g, splits, out_nchw, grid, st);
     else
         reduce_typed<float>(part, bias, y, g, splits, out_nchw, grid, st);
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t *p, int n) {
+    const int i = (int)blockIdx.x * 256 + (int)threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+hipError_t launch_zero_words(uint32_t *p, int n, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)blocks_for(n, 256)), dim3(256), 0, st, p, n);
     return hipGetLastError();
 }
 

@@ -133,7 +133,12 @@ typedef enum { CONV_DTYPE_FP32 = 0, CONV_DTYPE_BF16 = 1, CONV_DTYPE_FP16 = 2, CO
  *             aligned (then the element-gather loop runs).  Other NCHW
  *             input: the channels-last copy of x and OHWI weights.  NHWC: a spare
  *             indirection buffer, used only when x or w is not 16-byte
- *             aligned (then the call runs the element-gather loop).
+ *             aligned (then the call runs the element-gather loop).  Deep
+ *             channels-last layers with fewer 512 x 128 output tiles than
+ *             compute units (3/4 of them for 16-bit types, 7/8 for fp32)
+ *             share the tiles' K steps among 256 blocks; their workspace adds
+ *             256 fp32 partial tiles of 512 x 128 and 256 flags (64 MB + 1
+ *             KB), where the total stays below the im2col footprint.
  *   PATCH     inputs with at most 4 channels: the indirect convolution with
  *             the input rows of a few output rows staged in LDS (channels
  *             padded to 4) and each tap's pixel addressed there, so that a
@@ -177,7 +182,8 @@ conv_status_t conv2d_output_size(int H, int W, int KH, int KW, int stride, int p
  * chosen algorithm (indirection buffer, or window-ordered input plus, for
  * NCHW, the weights regrouped channel-innermost), the channels-last copy of
  * an NCHW input where the path reads one (for a 1x1 layer, of half the
- * batch at a time), and fp32 split-K partials on skinny layers.  It is 0 for
+ * batch at a time), fp32 split-K partials on skinny layers, and the fp32
+ * partial tiles of the window-row loop's stream-K form.  It is 0 for
  * the plain-GEMM feed on NHWC input, and below the im2col footprint
  * N*Ho*Wo*C_in*KH*KW elements for every algorithm except CONV_ALGO_IM2COL,
  * whose workspace is that footprint (plus, on skinny layers, split-K
@@ -216,9 +222,10 @@ conv_status_t conv2d_fwd(const void *x, const void *w, const void *bias, void *y
  * (hipGetSymbolAddress); later calls do not.
  *   Arguments, layouts, ownership and errors as for conv2d_fwd (the caller
  *   still passes x, w, bias and y).  A call whose conv2d_fwd_workspace_size
- *   exceeds CONV_NOALLOC_SCRATCH_BYTES returns CONV_ERR_WORKSPACE before any
- *   launch.  The work runs on the device of `stream` (the current device for
- *   NULL).
+ *   exceeds CONV_NOALLOC_SCRATCH_BYTES runs without the stream-K form where
+ *   that brings it within the array, else returns CONV_ERR_WORKSPACE before
+ *   any launch.  The work runs on the device of `stream` (the current device
+ *   for NULL).
  *   Every call on one GPU shares that GPU's array, which keeps the last
  *   call's contents; nothing in it has to start at zero.  Calls that overlap
  *   on one GPU (on different streams, or from different host threads without

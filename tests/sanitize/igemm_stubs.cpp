@@ -25,9 +25,10 @@ hipError_t launch_im2col(const void *, void *, const Geom &, bool, bool, hipStre
 hipError_t launch_ablate(const GemmArgs &, int, bool, int, hipStream_t) { return never(); }
 hipError_t launch_im2win_pad(const void *, void *, const Geom &, int, bool, bool, hipStream_t) { return never(); }
 hipError_t launch_prep(const void *, bool, void *, int, int32_t *, const void *, bool, void *, const Geom &, int,
-                       hipStream_t) {
+                       hipStream_t, uint32_t *, int) {
     return never();
 }
+hipError_t launch_zero_words(uint32_t *, int, hipStream_t) { return never(); }
 hipError_t launch_pack_weights_tapmajor(const void *, void *, const Geom &, int, hipStream_t) { return never(); }
 hipError_t launch_pack_weights_ohwi(const void *, void *, const Geom &, bool, hipStream_t) { return never(); }
 }  // namespace convlower

@@ -281,13 +281,32 @@ def test_window_rows_in_lds_eligibility_and_workspace(name, dtype):
         return
     Ho, Wo = cl.output_size(L.H, L.W, L.KH, L.KW, L.stride, L.pad, L.dilation)
     ibuf = up(Ho * Wo * L.KH * L.KW * 4)
-    assert cl.workspace_size(*_args(L, "NHWC", dtype, "im2win_lds")) == ibuf
+    assert cl.workspace_size(*_args(L, "NHWC", dtype, "im2win_lds")) == ibuf + _stream_k_bytes(L, Ho, Wo, es, ibuf)
     if dtype != "fp32" and L.W % 2 == 0 and L.Co <= 256 and _raw_runs(L.N * Ho * Wo, Wo, L.W, L.pad) <= 40:
         # NCHW read in place: regrouped weights and a spare indirection buffer
         want = up(L.Co * L.C * L.KH * L.KW * es) + ibuf
     else:
         want = up(L.N * L.C * L.H * L.W * es) + up(L.Co * L.C * L.KH * L.KW * es)
+        want += _stream_k_bytes(L, Ho, Wo, es, want)
     assert cl.workspace_size(*_args(L, "NCHW", dtype, "im2win_lds")) == want
+
+
+def _stream_k_bytes(L, Ho, Wo, es, before):
+    """The stream-K region of a channels-last window-row call: 256 partial
+    tiles of 512 x 128 fp32 sums and 256 flags, where the layer takes the
+    one-block-per-CU form (more than 64 output channels, at least 72 K steps
+    of 32 channels (16 for fp32), at most 256 tiles of 512 x 128) with at
+    most 3/4 of a tile per block (7/8 for fp32), and the workspace stays
+    below im2col."""
+    M, K = L.N * Ho * Wo, L.C * L.KH * L.KW
+    tiles = -(-M // 512) * -(-L.Co // 128)
+    few = tiles * 8 <= 256 * 7 if es == 4 else tiles * 4 <= 256 * 3
+    if L.Co <= 64 or K // (16 if es == 4 else 32) < 72 or tiles > 256 or not few:
+        return 0
+    sk = 256 * 512 * 128 * 4 + 4 * 256
+    if before + sk >= M * K * es:
+        return 0
+    return (sk + 255) // 256 * 256
 
 
 def _raw_runs(M, Wo, W, p):
