@@ -7,6 +7,7 @@ same scratch array, the second with a smaller batch, so the second call
 starts from whatever the first left there.
 """
 import sys
+from dataclasses import replace
 
 import pytest
 import torch
@@ -66,3 +67,24 @@ def test_noalloc_on_a_side_stream():
         cl.conv2d_fwd_noalloc(x, w, b, out, L.stride, L.pad, L.dilation, "NCHW", "auto", stream=s)
     s.synchronize()
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+def test_noalloc_without_the_stream_k_regions():
+    """Where the stream-K partial tiles would take the workspace past the
+    scratch array, the no-allocation call runs the one-tile-per-block loop
+    instead: fp32 3x3 256->128 @28, NCHW, N = 88 (135 tiles of 512 x 128),
+    138.9 MB of workspace with the partial tiles and 71.8 MB without.  On
+    small-integer inputs every partial sum is exact, so the two calls give
+    the same bits although they add in different orders."""
+    L = replace(LAYERS["C4d"], Co=128, N=88)
+    need = cl.workspace_size(L.N, L.C, L.H, L.W, L.Co, L.KH, L.KW, L.stride, L.pad, L.dilation, "NCHW", "fp32",
+                             "auto")
+    assert need > cl.NOALLOC_SCRATCH_BYTES >= need - 256 * 512 * 128 * 4 - 1024
+    _say(f"[gpu] noalloc without stream-K: fp32 256->128@28 N=88 workspace={need}")
+    x, w, b = make_inputs(L, "fp32", "NCHW", integer=True)
+    x, w, b = x.cuda(), w.cuda(), b.cuda()
+    ref = cl.conv2d_fwd(x, w, b, L.stride, L.pad, L.dilation, "NCHW", "auto")
+    out = torch.full_like(ref, float("nan"))
+    cl.conv2d_fwd_noalloc(x, w, b, out, L.stride, L.pad, L.dilation, "NCHW", "auto")
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int32), ref.view(torch.int32))
