@@ -72,7 +72,7 @@ struct RowWinPPCfg {
 // (deterministic results).  The partial sums and flags move with device-
 // coherent loads and stores, so no cache needs flushing.  The wait is
 // bounded (kSkSpinMax polls); blocks start in index order, so it always ends
-// long before that.
+// long before that (were it ever to run out, the tile is written as NaN).
 constexpr int kSkSpinMax = 1 << 16;
 constexpr int kCachePolicySc1 = 16;  // buffer-instruction cache policy: coherent across the device
 
@@ -380,17 +380,30 @@ __device__ __forceinline__ void igemm_rowwin_pp_body(const GemmArgs &A) {
                 // then add their sums in block order.
                 int jf = jb;
                 while (jf > 0 && sbeg(jf) > ts) --jf;
+                __shared__ int sk_late;  // a wait ran out: the tile is written as NaN, not silently wrong
                 if (tid == 0) {
+                    int late = 0;
                     for (int j = jf; j < jb; ++j) {
                         if (sbeg(j) >= sbeg(j + 1)) continue;
                         const uint32_t *f = &A.skf[xcd + 8 * j];
-                        for (int it = 0; it < kSkSpinMax; ++it) {
+                        int it = 0;
+                        for (; it < kSkSpinMax; ++it) {
                             if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) break;
                             __builtin_amdgcn_s_sleep(8);
                         }
+                        if (it == kSkSpinMax) late = 1;
                     }
+                    sk_late = late;
                 }
                 __syncthreads();
+                if (sk_late) {
+#pragma unroll
+                    for (int ip = 0; ip < TP; ++ip)
+#pragma unroll
+                        for (int ic = 0; ic < TC; ++ic)
+#pragma unroll
+                            for (int e = 0; e < 4 * NQ; ++e) acc[ip][ic][e] = __builtin_nanf("");
+                }
                 for (int j = jf; j < jb; ++j) {
                     if (sbeg(j) >= sbeg(j + 1)) continue;
                     const uint32_t base = (uint32_t)(xcd + 8 * j) * (uint32_t)kSkSlotBytes;

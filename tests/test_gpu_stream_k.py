@@ -13,6 +13,7 @@ bound, fp32 on small-integer inputs bit for bit (every partial sum is an
 exact integer, so the order the blocks add them in cannot matter).
 """
 import sys
+from dataclasses import replace
 
 import numpy as np
 import pytest
@@ -61,6 +62,35 @@ def test_stream_k_whole_output(n, layout, dtype):
     worst = 0.0
     for n0 in range(0, n, 16):
         sl = slice(n0, min(n0 + 16, n))
+        if integer:
+            y_ref = oracle.conv2d(x[sl], w, b, L.stride, L.pad, L.dilation, oracle.NCHW, want_norm=False)
+            bad = int(np.count_nonzero(y[sl].double().numpy() != y_ref))
+            assert bad == 0, f"images {n0}..: {bad} outputs differ from the exact result"
+        else:
+            y_ref, dn = oracle.conv2d(x[sl], w, b, L.stride, L.pad, L.dilation, oracle.NCHW)
+            yn = y[sl].double().numpy()
+            assert np.all(np.isfinite(yn))
+            worst = max(worst, float(np.max(np.abs(yn - y_ref) / dn)))
+    assert worst <= 8e-3, f"normalised error {worst:.3e}"
+    _say(f"[gpu]   worst normalised error {worst:.3e}")
+
+
+@pytest.mark.parametrize("layout,dtype", [("NHWC", "bf16"), ("NHWC", "fp32"), ("NCHW", "fp32")])
+def test_stream_k_ragged_tiles(layout, dtype):
+    """3x3 256->200 @14, N = 128: the last of 49 pixel tiles is partial and
+    the second of two channel tiles holds 72 of its 128 channels (98 tiles
+    split over 256 blocks)."""
+    L = replace(_layer(128), C=256, Co=200)
+    ws = cl.workspace_size(L.N, L.C, L.H, L.W, L.Co, L.KH, L.KW, L.stride, L.pad, L.dilation, layout, dtype,
+                           "im2win_lds")
+    assert ws >= SK_BYTES, ws
+    integer = dtype == "fp32"
+    x, w, b = make_inputs(L, dtype, "NCHW", integer=integer)
+    _say(f"[gpu] stream-K ragged {L.C}->{L.Co}@{L.H} N={L.N} {layout} {dtype} workspace={ws}")
+    y = _call(L, x, w, b, layout)
+    worst = 0.0
+    for n0 in range(0, L.N, 32):
+        sl = slice(n0, min(n0 + 32, L.N))
         if integer:
             y_ref = oracle.conv2d(x[sl], w, b, L.stride, L.pad, L.dilation, oracle.NCHW, want_norm=False)
             bad = int(np.count_nonzero(y[sl].double().numpy() != y_ref))
