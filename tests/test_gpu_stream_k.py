@@ -104,6 +104,23 @@ def test_stream_k_ragged_tiles(layout, dtype):
     _say(f"[gpu]   worst normalised error {worst:.3e}")
 
 
+def test_stream_k_without_bias():
+    """No bias: the epilogues of whole, finished and split tiles add nothing
+    (N = 64, channels-last, fp32 on small-integer inputs: exact)."""
+    L = _layer(64)
+    x, w, _ = make_inputs(L, "fp32", "NCHW", integer=True)
+    _say("[gpu] stream-K without bias N=64 NHWC fp32")
+    xl, wl = x.permute(0, 2, 3, 1).contiguous().cuda(), w.permute(0, 2, 3, 1).contiguous().cuda()
+    y = cl.conv2d_fwd(xl, wl, None, L.stride, L.pad, L.dilation, "NHWC", "im2win_lds")
+    torch.cuda.synchronize()
+    y = y.cpu().permute(0, 3, 1, 2)
+    for n0 in range(0, L.N, 16):
+        sl = slice(n0, n0 + 16)
+        y_ref = oracle.conv2d(x[sl], w, None, L.stride, L.pad, L.dilation, oracle.NCHW, want_norm=False)
+        bad = int(np.count_nonzero(y[sl].double().numpy() != y_ref))
+        assert bad == 0, f"images {n0}..: {bad} outputs differ from the exact result"
+
+
 def test_stream_k_runs_are_bitwise_equal():
     """The finishing blocks add the others' sums in a fixed order: two calls
     give the same bits."""
