@@ -104,6 +104,27 @@ def test_stream_k_ragged_tiles(layout, dtype):
     _say(f"[gpu]   worst normalised error {worst:.3e}")
 
 
+def test_stream_k_fp16():
+    """fp16 runs its own instantiation of the loop: N = 64, channels-last,
+    against the oracle to the fp16 bound (1e-3 normalised)."""
+    L = _layer(64)
+    ws = cl.workspace_size(L.N, L.C, L.H, L.W, L.Co, L.KH, L.KW, L.stride, L.pad, L.dilation, "NHWC", "fp16",
+                           "im2win_lds")
+    assert ws >= SK_BYTES, ws
+    x, w, b = make_inputs(L, "fp16", "NCHW")
+    _say(f"[gpu] stream-K fp16 N=64 NHWC workspace={ws}")
+    y = _call(L, x, w, b, "NHWC")
+    worst = 0.0
+    for n0 in range(0, L.N, 16):
+        sl = slice(n0, n0 + 16)
+        y_ref, dn = oracle.conv2d(x[sl], w, b, L.stride, L.pad, L.dilation, oracle.NCHW)
+        yn = y[sl].double().numpy()
+        assert np.all(np.isfinite(yn))
+        worst = max(worst, float(np.max(np.abs(yn - y_ref) / dn)))
+    assert worst <= 1e-3, f"normalised error {worst:.3e}"
+    _say(f"[gpu]   worst normalised error {worst:.3e}")
+
+
 def test_stream_k_without_bias():
     """No bias: the epilogues of whole, finished and split tiles add nothing
     (N = 64, channels-last, fp32 on small-integer inputs: exact)."""
