@@ -291,6 +291,19 @@ def test_window_rows_in_lds_eligibility_and_workspace(name, dtype):
     assert cl.workspace_size(*_args(L, "NCHW", dtype, "im2win_lds")) == want
 
 
+@pytest.mark.parametrize("dtype,n,taken", [("bf16", 384, True), ("bf16", 385, False), ("fp16", 384, True),
+                                          ("fp16", 385, False), ("fp32", 448, True), ("fp32", 449, False)])
+def test_stream_k_taken_up_to_its_tile_bound(dtype, n, taken):
+    """3x3 512->128 @16x16, channels-last: N*256 pixels give 192 tiles of
+    512 x 128 at N = 384 and 224 at N = 448.  The stream-K form is taken up
+    to 3/4 of a tile per block for 16-bit types and 7/8 for fp32, and its
+    partial tiles and flags are the last workspace region."""
+    ibuf = (16 * 16 * 9 * 4 + 255) // 256 * 256
+    sk = (256 * 512 * 128 * 4 + 4 * 256 + 255) // 256 * 256
+    ws = cl.workspace_size(n, 512, 16, 16, 128, 3, 3, 1, 1, 1, "NHWC", dtype, "auto")
+    assert ws == ibuf + (sk if taken else 0)
+
+
 def _stream_k_bytes(L, Ho, Wo, es, before):
     """The stream-K region of a channels-last window-row call: 256 partial
     tiles of 512 x 128 fp32 sums and 256 flags, where the layer takes the
