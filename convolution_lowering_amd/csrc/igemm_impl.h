@@ -191,24 +191,22 @@ __device__ __forceinline__ uint32_t a_elem(const GemmArgs &A, const ARow &r, int
 // then stays in that XCD's L2 -- and a contiguous share of the pixel tiles
 // (the input rows of neighbouring pixel tiles overlap).  Otherwise each XCD
 // takes a contiguous run of pairs, channel tiles of one pixel tile adjacent
-// (those blocks read the same X_col rows).
+// (those blocks read the same X_col rows); with a grid that is not a
+// multiple of 8, XCD x holds total/8 blocks, one more for the first
+// total % 8 XCDs, and its run starts where the previous XCDs' runs end.
 __device__ __forceinline__ void tile_coords(int ntile_m, int ntile_n, int &mt, int &nt) {
     const int b = blockIdx.x, total = gridDim.x;
-    if ((total & 7) == 0) {
-        const int xcd = b & 7, j = b >> 3;
-        if ((8 % ntile_n) == 0 && (ntile_m % (8 / ntile_n)) == 0) {
-            const int groups = 8 / ntile_n;
-            nt = xcd % ntile_n;
-            mt = (xcd / ntile_n) * (ntile_m / groups) + j;
-            return;
-        }
-        const int l = xcd * (total >> 3) + j;
-        mt = l / ntile_n;
-        nt = l - mt * ntile_n;
+    const int xcd = b & 7, j = b >> 3;
+    if ((total & 7) == 0 && (8 % ntile_n) == 0 && (ntile_m % (8 / ntile_n)) == 0) {
+        const int groups = 8 / ntile_n;
+        nt = xcd % ntile_n;
+        mt = (xcd / ntile_n) * (ntile_m / groups) + j;
         return;
     }
-    mt = b / ntile_n;
-    nt = b - mt * ntile_n;
+    const int q = total >> 3, r = total & 7;
+    const int l = xcd * q + min(xcd, r) + j;
+    mt = l / ntile_n;
+    nt = l - mt * ntile_n;
 }
 
 // Tile order with the weight bytes in view: each XCD takes a contiguous
