@@ -9,8 +9,10 @@ inside it (any lowering launch, the MFMA main loop with its fused epilogue,
 any split-K finish).  Before each timed step, outside the timed interval,
 512 MB are overwritten and then another 512 MB buffer is read, so the 256 MB
 last-level cache (MALL) holds none of the step's inputs (they come from HBM)
-and no lines still to be written back.  Each step, and each layer inside it, is bracketed by HIP events on the
-stream the library launches on.
+and no lines still to be written back.  Each step, and each layer inside
+it, is bracketed by HIP events on the stream the library launches on.  The
+warm-up steps are preceded by half a second of untimed steps, so that the
+shader clock has settled before anything is timed.
 
 The last line of stdout is one compact JSON object: the set's TFLOPS, the
 per-layer times, the roofline entry of the dominant kernel (the main loop of
@@ -311,6 +313,9 @@ def main():
                     help="all: also the per-layer sweep over every shape and algorithm, and the ablation")
     ap.add_argument("--rows-out", metavar="FILE", help="where --layers all writes its rows (JSON)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--clock-warmup", type=float, default=0.5, metavar="SECONDS",
+                    help="untimed steps of the set run for this long before the warm-up steps, so the "
+                         "shader clock has settled (0: none)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run one 256 MiB device copy (scale reference for HBM byte counters)")
     ap.add_argument("--only", metavar="LAYER:LAYOUT[:DTYPE[:ALGO]][,...]",
@@ -349,6 +354,15 @@ def main():
 
     keep = 0 if args.no_cpu_baseline else CPU_SAMPLE_IMAGES
     prepared = [Prepared(LAYERS[n], HEAD_DTYPE, HEAD_LAYOUT, HEAD_ALGO, keep_host_images=keep) for n in HEAD_SET]
+    # The shader clock climbs for tens of milliseconds of matrix work: after
+    # memory traffic alone, the 64->128 @112 main loop took 400 us in the
+    # first steps and 300 us some thirty steps later.  So the set runs
+    # untimed for a while first, until the clock has settled.
+    t_end = time.perf_counter() + args.clock_warmup
+    while time.perf_counter() < t_end:
+        for p in prepared:
+            p()
+        torch.cuda.synchronize()
     t = time_set(prepared, args.steps, args.warmup, flush)
     total_flops = sum(p.flops for p in prepared)
     per_layer = []
